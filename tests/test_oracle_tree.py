@@ -1,0 +1,154 @@
+"""Pins for top-k and tree construction (CPU only).
+
+* top-k = first k of a full sort by (value desc, index asc), on adversarial ties;
+* EAGLE-2 value never grows along a path, and the reranked set is a connected
+  tree (study note section 10.3, the two properties and exercise 5);
+* expand and rerank equal brute-force definitions on a fully enumerated tiny
+  draft tree, with value = product of confidences in fp64;
+* the static templates have the stated shapes.
+"""
+import itertools
+
+import numpy as np
+import scipy.special
+
+from oracle import tree as T
+from oracle.numerics import softmax
+from oracle.topk import row_lse, row_topk, softmax_topk
+from workloads import TEMPLATES, template_child_counts
+
+
+def test_topk_brute_force_with_ties():
+    g = np.random.default_rng(0)
+    for trial in range(200):
+        V = int(g.integers(1, 60))
+        row = g.integers(-3, 4, size=V).astype(np.float32)  # many ties
+        if trial % 3 == 0:
+            row[g.integers(0, V, size=3)] = -0.0
+        k = int(g.integers(1, V + 1))
+        ref = sorted(range(V), key=lambda i: (-float(row[i]), i))[:k]
+        assert list(row_topk(row, k)) == ref
+
+
+def test_topk_negative_zero_ties_with_positive_zero():
+    row = np.array([-0.0, 0.0, -0.0, -1.0], dtype=np.float32)
+    assert list(row_topk(row, 3)) == [0, 1, 2]
+
+
+def test_lse_and_logq():
+    g = np.random.default_rng(1)
+    x = (g.standard_normal((3, 1000)) * 2).astype(np.float32)
+    lse, idx, logq = softmax_topk(x, 5)
+    for r in range(3):
+        assert np.isclose(lse[r], scipy.special.logsumexp(x[r].astype(np.float64)), rtol=0, atol=1e-12)
+        assert np.allclose(np.exp(logq[r]), scipy.special.softmax(x[r].astype(np.float64))[idx[r]])
+
+
+def _toy_draft(V, seed):
+    """A deterministic toy draft model: q(. | prefix) from a hash of the prefix."""
+    def q_of(prefix):
+        g = np.random.default_rng([seed] + list(prefix) + [99])
+        return softmax(g.standard_normal(V) * 2.0)
+    return q_of
+
+
+def test_eagle2_against_brute_force_definitions():
+    V, k, depth, m = 6, 3, 4, 12
+    for seed in range(20):
+        q_of = _toy_draft(V, seed)
+        pool = T.Pool(0, 0)
+        frontier = [0]
+        prefix_of = {0: ()}
+        for s in range(depth):
+            idx, lq = [], []
+            for u in frontier:
+                row = np.log(q_of(prefix_of[u])).astype(np.float32)
+                order = row_topk(row, k)
+                idx.append(order)
+                lq.append(row[order] - np.float32(row_lse(row)))
+            before = len(pool)
+            frontier = T.expand(pool, frontier, idx, lq, k)
+            for c in range(before, len(pool)):
+                prefix_of[c] = prefix_of[pool.parent[c]] + (pool.token[c],)
+            # brute force: the new frontier = the k new nodes of largest value
+            new = list(range(before, len(pool)))
+            val = {c: np.prod([q_of(prefix_of[c][:j])[prefix_of[c][j]] for j in range(len(prefix_of[c]))])
+                   for c in new}
+            best = sorted(new, key=lambda c: (-val[c], c))[:k]
+            assert set(best) == set(frontier), seed
+        # value never grows along a path (fp32 log-values)
+        for c in range(1, len(pool)):
+            assert pool.logv[c] <= pool.logv[pool.parent[c]]
+        tr = T.finalize(pool, m)
+        kept = set(int(i) for i in tr["pool_id"][1:])
+        # brute force rerank: the m most valuable nodes of the pool
+        allv = {c: np.prod([q_of(prefix_of[c][:j])[prefix_of[c][j]] for j in range(len(prefix_of[c]))])
+                for c in range(1, len(pool))}
+        ref = sorted(allv, key=lambda c: (-allv[c], pool.depth[c], c))[:m]
+        assert kept == set(ref), seed
+        # connected, parents precede children, siblings in creation order
+        for t in range(1, len(tr["parent"])):
+            p = int(tr["parent"][t])
+            assert 0 <= p < t
+            assert int(tr["pool_id"][p]) == pool.parent[int(tr["pool_id"][t])]
+            assert int(tr["depth"][t]) == int(tr["depth"][p]) + 1
+
+
+def test_rerank_tie_prefers_shallower():
+    # child logq = 0 so child value == parent value exactly
+    pool = T.Pool(0, 0)
+    a = pool.add(0, 1, np.float32(-0.5))
+    b = pool.add(a, 2, np.float32(0.0))
+    c = pool.add(0, 3, np.float32(-0.5))
+    tr = T.finalize(pool, 2)
+    assert [int(x) for x in tr["pool_id"]] == [0, a, c]  # b ties with a and c but is deeper
+    tr = T.finalize(pool, 3)
+    assert [int(x) for x in tr["pool_id"]] == [0, a, c, b]
+
+
+def test_static_templates():
+    s26 = TEMPLATES["static26"]
+    depth = [0] * len(s26)
+    for i in range(1, len(s26)):
+        depth[i] = depth[s26[i]] + 1
+    counts = np.bincount(depth)
+    assert list(counts) == [1, 4, 6, 8, 5, 2] and len(s26) == 26 and max(depth) == 5
+    assert all(s26[i] <= s26[i + 1] for i in range(1, len(s26) - 1))  # BFS, siblings contiguous
+    # rank rule up to depth 4: a node at depth t with sibling rank r has max(0, b_t - r) children
+    b = [4, 3, 2, 1]
+    nch = template_child_counts(s26)
+    rank = [0] * len(s26)
+    for i in range(1, len(s26)):
+        rank[i] = sum(1 for j in range(1, i) if s26[j] == s26[i])
+    for i in range(len(s26)):
+        if depth[i] < 4:
+            assert nch[i] == max(0, b[depth[i]] - rank[i]), i
+    # the two extra depth-5 nodes sit under the depth-4 nodes with least path rank-sum
+    def rsum(i):
+        s = 0
+        while i > 0:
+            s += rank[i]
+            i = s26[i]
+        return s
+    d4 = [i for i in range(len(s26)) if depth[i] == 4]
+    best = sorted(d4, key=lambda i: (rsum(i), i))[:2]
+    assert sorted(i for i in d4 if nch[i] > 0) == sorted(best)
+    assert TEMPLATES["chain5"] == [-1, 0, 1, 2, 3]
+
+
+def test_static_expand_reproduces_template():
+    s26 = TEMPLATES["static26"]
+    nch = template_child_counts(s26)
+    pool = T.Pool(0, 0)
+    frontier = [0]
+    for s in range(5):
+        idx = [[100 * u + r for r in range(4)] for u in frontier]
+        lq = [[-0.1 * (r + 1) for r in range(4)] for u in frontier]
+        frontier = T.expand(pool, frontier, idx, lq, 4, nch)
+    assert pool.parent == s26
+    tr = T.finalize(pool, 0)
+    assert [int(x) for x in tr["pool_id"]] == list(range(26))
+    # rank r child of node u carries the parent's r-th token
+    for i in range(1, 26):
+        r = sum(1 for j in range(1, i) if s26[j] == s26[i])
+        assert pool.token[i] == 100 * s26[i] + r
