@@ -1,0 +1,133 @@
+"""MI355X (gfx950) EAGLE draft-and-verify hot path: Python binding.
+
+The functions below carry the C ABI's names (include/eagle.h) and only marshal
+arguments: torch tensors give device pointers, torch's current stream gives the
+HIP stream.  Every step of the path runs in libeagle.so's HIP kernels; if the
+library is not built (python -m eagle_feature_level_amd.build) or the device
+is not a gfx950, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _abi
+from ._abi import (EAGLE_BF16, EAGLE_F32, EAGLE_HEAD_ONLY, EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK, EAGLE_VERIFY_GREEDY,
+                   EAGLE_VERIFY_IID, EagleError, eagle_draft_out, eagle_kv, eagle_pool, eagle_rows, eagle_shape,
+                   eagle_weights)
+
+__all__ = ["eagle_workspace_bytes", "eagle_draft_step", "eagle_softmax_topk", "eagle_tree_init", "eagle_tree_expand",
+           "eagle_tree_finalize", "eagle_verify", "make_shape", "make_weights", "make_rows", "make_kv", "make_out",
+           "make_pool", "EagleError", "EAGLE_HEAD_ONLY", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
+           "EAGLE_F32", "EAGLE_MAX_SLOTS", "EAGLE_MAX_TOPK"]
+
+WEIGHT_NAMES = [f[0] for f in eagle_weights._fields_]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _keep(struct, *tensors):
+    """The structs hold raw device pointers; keep the tensors they point into
+    alive for as long as the struct lives."""
+    struct._keep = tuple(t for t in tensors if t is not None and not isinstance(t, int))
+    return struct
+
+
+def make_shape(d, n_heads, n_kv_heads, head_dim, ffn, vocab, rms_eps=1e-5, rope_theta=1e4, dtype="bf16"):
+    return eagle_shape(d, n_heads, n_kv_heads, head_dim, ffn, vocab, rms_eps, rope_theta,
+                       EAGLE_BF16 if dtype == "bf16" else EAGLE_F32)
+
+
+def make_weights(tensors: dict):
+    return _keep(eagle_weights(*[_ptr(tensors[n]) for n in WEIGHT_NAMES]), *[tensors[n] for n in WEIGHT_NAMES])
+
+
+def make_rows(n_rows, batch, max_rows_per_seq, row_start, token, parent, pos=None, slot=None, mask=None):
+    return _keep(eagle_rows(n_rows, batch, max_rows_per_seq, _ptr(row_start), _ptr(token), _ptr(parent), _ptr(pos),
+                            _ptr(slot), _ptr(mask)), row_start, token, parent, pos, slot, mask)
+
+
+def make_kv(prefix_k, prefix_v, prefix_off, prefix_len, max_prefix_len, tree_k, tree_v):
+    return _keep(eagle_kv(_ptr(prefix_k), _ptr(prefix_v), _ptr(prefix_off), _ptr(prefix_len), max_prefix_len,
+                          _ptr(tree_k), _ptr(tree_v)), prefix_k, prefix_v, prefix_off, prefix_len, tree_k, tree_v)
+
+
+def make_out(feat, logits, lse, topk, topk_idx, topk_logq):
+    return _keep(eagle_draft_out(_ptr(feat), _ptr(logits), _ptr(lse), topk, _ptr(topk_idx), _ptr(topk_logq)), feat,
+                 logits, lse, topk_idx, topk_logq)
+
+
+def make_pool(cap, parent, token, depth, logv, feat_row, slot, mask, count, frontier):
+    ts = (parent, token, depth, logv, feat_row, slot, mask, count, frontier)
+    return _keep(eagle_pool(cap, *[_ptr(t) for t in ts]), *ts)
+
+
+def eagle_workspace_bytes(shape, max_rows, max_batch, max_prefix_len) -> int:
+    lib = _abi.load()
+    return int(lib.eagle_workspace_bytes(ctypes.byref(shape), max_rows, max_batch, max_prefix_len))
+
+
+def eagle_draft_step(shape, weights, flags, rows, feat_in, kv, out, workspace, stream=None):
+    lib = _abi.load()
+    rc = lib.eagle_draft_step(ctypes.byref(shape), ctypes.byref(weights), flags, ctypes.byref(rows), _ptr(feat_in),
+                              ctypes.byref(kv) if kv is not None else None, ctypes.byref(out), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _abi.check("eagle_draft_step", rc)
+
+
+def eagle_softmax_topk(n_rows, vocab, logits, topk, lse, topk_idx, topk_logq, workspace, stream=None):
+    lib = _abi.load()
+    rc = lib.eagle_softmax_topk(n_rows, vocab, _ptr(logits), topk, _ptr(lse), _ptr(topk_idx), _ptr(topk_logq),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _abi.check("eagle_softmax_topk", rc)
+
+
+def eagle_tree_init(batch, pool, root_token, root_feat_row0, stream=None):
+    lib = _abi.load()
+    _abi.check("eagle_tree_init", lib.eagle_tree_init(batch, ctypes.byref(pool), _ptr(root_token), root_feat_row0,
+                                                      _stream(stream)))
+
+
+def eagle_tree_expand(batch, k, step, static_nchild, pool, n_prev, topk, topk_idx, topk_logq, n_next, feat_row0,
+                      prefix_len, next_token, next_parent, next_pos, next_slot, next_mask, next_row_start,
+                      stream=None):
+    lib = _abi.load()
+    rc = lib.eagle_tree_expand(batch, k, step, _ptr(static_nchild), ctypes.byref(pool), n_prev, topk, _ptr(topk_idx),
+                               _ptr(topk_logq), n_next, feat_row0, _ptr(prefix_len), _ptr(next_token),
+                               _ptr(next_parent), _ptr(next_pos), _ptr(next_slot), _ptr(next_mask),
+                               _ptr(next_row_start), _stream(stream))
+    _abi.check("eagle_tree_expand", rc)
+
+
+def eagle_tree_finalize(batch, m, n_nodes, pool, prefix_len, tree_parent, tree_token, tree_depth, tree_pool,
+                        tree_mask, tree_qrow, row_token, row_parent, row_pos, row_slot, row_mask, row_start,
+                        stream=None):
+    lib = _abi.load()
+    rc = lib.eagle_tree_finalize(batch, m, n_nodes, ctypes.byref(pool), _ptr(prefix_len), _ptr(tree_parent),
+                                 _ptr(tree_token), _ptr(tree_depth), _ptr(tree_pool), _ptr(tree_mask),
+                                 _ptr(tree_qrow), _ptr(row_token), _ptr(row_parent), _ptr(row_pos), _ptr(row_slot),
+                                 _ptr(row_mask), _ptr(row_start), _stream(stream))
+    _abi.check("eagle_tree_finalize", rc)
+
+
+def eagle_verify(batch, n_nodes, vocab, tree_parent, tree_token, target_logits, draft_logits, draft_row, seed, round_,
+                 flags, out_path, out_accept_len, out_next_token, out_flags, stream=None):
+    lib = _abi.load()
+    rc = lib.eagle_verify(batch, n_nodes, vocab, _ptr(tree_parent), _ptr(tree_token), _ptr(target_logits),
+                          _ptr(draft_logits), _ptr(draft_row), seed, round_, flags, _ptr(out_path),
+                          _ptr(out_accept_len), _ptr(out_next_token), _ptr(out_flags), _stream(stream))
+    _abi.check("eagle_verify", rc)

@@ -1,0 +1,484 @@
+// C ABI of the EAGLE draft-and-verify hot path (declared in include/eagle.h).
+// Host-side argument checks, workspace carving and the launch sequence of a
+// draft step; every computation runs in the HIP kernels.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "../../include/eagle.h"
+#include "gemm.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return EAGLE_EHIP;
+}
+
+// gfx950 check, cached per device.
+int check_device() {
+  static signed char state[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return EAGLE_EUNSUPPORTED;
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    state[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  return state[dev] == 1 ? EAGLE_OK : EAGLE_EUNSUPPORTED;
+}
+
+bool shape_ok(const eagle_shape* s) {
+  if (!s) return false;
+  if (s->d <= 0 || s->n_heads <= 0 || s->n_kv_heads <= 0 || s->head_dim <= 0 || s->ffn <= 0 || s->vocab <= 0)
+    return false;
+  if (s->n_heads % s->n_kv_heads) return false;
+  if (s->head_dim % 2) return false;
+  if (!(s->rms_eps > 0.f) || !(s->rope_theta > 0.f)) return false;
+  if (s->dtype != EAGLE_F32 && s->dtype != EAGLE_BF16) return false;
+  return true;
+}
+
+// Supported sizes of the kernels (beyond plain validity).
+int shape_supported(const eagle_shape* s) {
+  if (s->vocab % 4) return EAGLE_EUNSUPPORTED;
+  if (s->dtype == EAGLE_BF16) {
+    if (s->head_dim != 128) return EAGLE_EUNSUPPORTED;
+    if (s->d % 128 || s->ffn % 128 || (s->n_heads * s->head_dim) % 128) return EAGLE_EUNSUPPORTED;
+  } else {
+    if (s->head_dim != 16 && s->head_dim != 64 && s->head_dim != 128) return EAGLE_EUNSUPPORTED;
+  }
+  return EAGLE_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct DraftWs {
+  int32_t* seq_of_row;
+  float* x;
+  float* sumsq1;
+  float* qkv;
+  void* qrot;
+  float* attn_part;
+  void* attn;
+  float* h;
+  float* sumsq2;
+  void* act;
+  float* gemm_part;
+  void* topk;
+  size_t total;
+};
+
+// Carves the workspace; with base == nullptr only computes the size.
+DraftWs carve(const eagle_shape* s, int M, int B, int max_prefix, char* base) {
+  DraftWs w{};
+  const int hq = s->n_heads * s->head_dim, hkv = s->n_kv_heads * s->head_dim;
+  const int nqkv = hq + 2 * hkv;
+  const int npart = s->d / 16 + 2;  // >= partial tiles of any GEMM producing a d-wide output
+  const int split_len = attn_split_len(max_prefix, B, s->n_kv_heads);
+  const int nsplit = attn_n_splits(max_prefix, split_len);
+  size_t gp = 0;
+  if (s->dtype == EAGLE_BF16) {
+    const int Ns[6] = {s->d, nqkv, s->d, 2 * s->ffn, s->d, s->vocab};
+    const int Ks[6] = {2 * s->d, s->d, hq, s->d, s->ffn, s->d};
+    for (int i = 0; i < 6; ++i) {
+      const size_t b = gemm_bf16_partial_bytes(M, Ns[i], Ks[i]);
+      if (b > gp) gp = b;
+    }
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return (void*)p;
+  };
+  w.seq_of_row = (int32_t*)take((size_t)M * 4);
+  w.x = (float*)take((size_t)M * s->d * 4);
+  w.sumsq1 = (float*)take((size_t)npart * M * 4);
+  w.qkv = (float*)take((size_t)M * nqkv * 4);
+  w.qrot = take((size_t)M * hq * 4);
+  w.attn_part = (float*)take((size_t)nsplit * M * s->n_heads * (s->head_dim + 2) * 4);
+  w.attn = take((size_t)M * hq * 4);
+  w.h = (float*)take((size_t)M * s->d * 4);
+  w.sumsq2 = (float*)take((size_t)npart * M * 4);
+  w.act = take((size_t)M * s->ffn * 4);
+  w.gemm_part = (float*)take(gp);
+  w.topk = take(topk_workspace_bytes(M, s->vocab));
+  w.total = off;
+  return w;
+}
+
+GemmArgs gemm_base(int M, int N, int K) {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.n_seg0 = N;
+  a.splits = 1;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* eagle_strerror(int code) {
+  switch (code) {
+    case EAGLE_OK: return "ok";
+    case EAGLE_EINVAL: return "invalid argument";
+    case EAGLE_EUNSUPPORTED: return "unsupported shape, size or device";
+    case EAGLE_EWORKSPACE: return "workspace too small";
+    case EAGLE_EHIP: return "HIP error";
+    default: return "unknown error";
+  }
+}
+
+int eagle_last_hip_error(void) { return g_last_hip; }
+
+size_t eagle_workspace_bytes(const eagle_shape* shape, int32_t max_rows, int32_t max_batch, int32_t max_prefix_len) {
+  if (!shape_ok(shape) || max_rows <= 0 || max_batch <= 0 || max_prefix_len < 0) return 0;
+  return carve(shape, max_rows, max_batch, max_prefix_len, nullptr).total;
+}
+
+int eagle_softmax_topk(int32_t n_rows, int32_t vocab, const float* logits, int32_t topk, float* lse,
+                       int32_t* topk_idx, float* topk_logq, void* workspace, size_t workspace_bytes,
+                       eagle_stream_t stream) {
+  if (n_rows < 0 || vocab <= 0 || topk < 1 || topk > vocab) return EAGLE_EINVAL;
+  if (n_rows == 0) return EAGLE_OK;
+  if (!logits || !lse || !topk_idx || !topk_logq || !workspace) return EAGLE_EINVAL;
+  if (topk > EAGLE_MAX_TOPK || vocab % 4) return EAGLE_EUNSUPPORTED;
+  if (workspace_bytes < topk_workspace_bytes(n_rows, vocab)) return EAGLE_EWORKSPACE;
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = launch_softmax_topk(n_rows, vocab, logits, topk, lse, topk_idx, topk_logq, workspace,
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? EAGLE_OK : hip_fail(e);
+}
+
+int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t flags, const eagle_rows* rows,
+                     const float* feat_in, const eagle_kv* kv, const eagle_draft_out* out, void* workspace,
+                     size_t workspace_bytes, eagle_stream_t stream) {
+  if (!shape_ok(shape) || !w || !rows || !out) return EAGLE_EINVAL;
+  if (flags & ~EAGLE_HEAD_ONLY) return EAGLE_EINVAL;
+  const bool head_only = flags & EAGLE_HEAD_ONLY;
+  const int M = rows->n_rows;
+  if (M < 0 || rows->batch <= 0) return EAGLE_EINVAL;
+  if (M == 0) return EAGLE_OK;
+  if (!feat_in || !rows->parent || !out->logits || !out->lse || !out->topk_idx || !out->topk_logq || !workspace)
+    return EAGLE_EINVAL;
+  if (!w->lm_head) return EAGLE_EINVAL;
+  if (out->topk < 1 || out->topk > shape->vocab) return EAGLE_EINVAL;
+  if (out->topk > EAGLE_MAX_TOPK) return EAGLE_EUNSUPPORTED;
+  int rc = shape_supported(shape);
+  if (rc) return rc;
+  const eagle_shape& s = *shape;
+  const bool bf16 = s.dtype == EAGLE_BF16;
+  if (!head_only) {
+    if (!kv || !out->feat || !rows->row_start || !rows->token || !rows->pos || !rows->slot || !rows->mask)
+      return EAGLE_EINVAL;
+    if (!w->embed || !w->fc_w || !w->fc_b || !w->norm1 || !w->norm2 || !w->wq || !w->wk || !w->wv || !w->wo ||
+        !w->w_gate || !w->w_up || !w->w_down)
+      return EAGLE_EINVAL;
+    if (!kv->prefix_len || !kv->tree_k || !kv->tree_v || kv->max_prefix_len < 0) return EAGLE_EINVAL;
+    if (kv->max_prefix_len > 0 && (!kv->prefix_k || !kv->prefix_v || !kv->prefix_off)) return EAGLE_EINVAL;
+    if (rows->max_rows_per_seq <= 0 || rows->max_rows_per_seq > M) return EAGLE_EINVAL;
+  }
+  const int maxL = head_only ? 0 : kv->max_prefix_len;
+  DraftWs ws = carve(shape, M, rows->batch, maxL, (char*)workspace);
+  if (workspace_bytes < ws.total) return EAGLE_EWORKSPACE;
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  auto gemm = [&](GemmArgs a, int load, int epi, int* np) -> hipError_t {
+    int dummy = 0;
+    a.part = ws.gemm_part;  // split-K partials of the tiled kernel
+    return bf16 ? launch_gemm_bf16(a, load, epi, np ? np : &dummy, st)
+                : launch_gemm_f32(a, load, epi, np ? np : &dummy, st);
+  };
+  hipError_t e;
+  const int d = s.d, hq = s.n_heads * s.head_dim, hkv = s.n_kv_heads * s.head_dim, F = s.ffn;
+
+  if (!head_only) {
+    e = launch_row_seq(rows->row_start, rows->batch, M, ws.seq_of_row, st);
+    if (e != hipSuccess) return hip_fail(e);
+    // a1, a2: [f_parent ; e(token)] -> FC (+bias) = x, sum of squares for RMSNorm 1
+    int np1 = 0, np2 = 0;
+    {
+      GemmArgs a = gemm_base(M, d, 2 * d);
+      a.w0 = w->fc_w;
+      a.feat = feat_in;
+      a.parent = rows->parent;
+      a.embed = w->embed;
+      a.token = rows->token;
+      a.d = d;
+      a.bias = w->fc_b;
+      a.y = ws.x;
+      a.ldy = d;
+      a.sumsq_out = ws.sumsq1;
+      e = gemm(a, LOAD_GATHER, EPI_BIAS_SUMSQ, &np1);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    // a3: RMSNorm -> [q; k; v]
+    {
+      GemmArgs a = gemm_base(M, hq + 2 * hkv, d);
+      a.w0 = w->wq;
+      a.n_seg0 = hq;
+      a.w1 = w->wk;
+      a.n_seg1 = hkv;
+      a.w2 = w->wv;
+      a.x = ws.x;
+      a.ldx = d;
+      a.sumsq_in = ws.sumsq1;
+      a.n_part_in = np1;
+      a.gain = w->norm1;
+      a.eps = s.rms_eps;
+      a.y = ws.qkv;
+      a.ldy = hq + 2 * hkv;
+      e = gemm(a, LOAD_F32_NORM, EPI_STORE, nullptr);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    // a4: RoPE at each row's position; k, v into the rows' tree slots
+    {
+      RopeArgs r;
+      r.qkv = ws.qkv;
+      r.pos = rows->pos;
+      r.slot = rows->slot;
+      r.seq_of_row = ws.seq_of_row;
+      r.q_out = (float*)ws.qrot;
+      r.tree_k = kv->tree_k;
+      r.tree_v = kv->tree_v;
+      r.n_rows = M;
+      r.hq = s.n_heads;
+      r.hkv = s.n_kv_heads;
+      r.hd = s.head_dim;
+      r.theta = s.rope_theta;
+      e = launch_rope_kv(r, bf16, st);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    // a5: tree attention
+    {
+      AttnArgs at;
+      at.q = (const float*)ws.qrot;
+      at.mask = rows->mask;
+      at.row_start = rows->row_start;
+      at.prefix_k = kv->prefix_k;
+      at.prefix_v = kv->prefix_v;
+      at.prefix_off = kv->prefix_off;
+      at.prefix_len = kv->prefix_len;
+      at.tree_k = kv->tree_k;
+      at.tree_v = kv->tree_v;
+      at.part = ws.attn_part;
+      at.out = (float*)ws.attn;
+      at.n_rows = M;
+      at.batch = rows->batch;
+      at.hq = s.n_heads;
+      at.hkv = s.n_kv_heads;
+      at.split_len = attn_split_len(maxL, rows->batch, s.n_kv_heads);
+      at.n_splits = attn_n_splits(maxL, at.split_len);
+      e = launch_attention(at, bf16, s.head_dim, st);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    // a6: h = x + attn wo^T, sum of squares for RMSNorm 2
+    {
+      GemmArgs a = gemm_base(M, d, hq);
+      a.w0 = w->wo;
+      a.x = ws.attn;
+      a.ldx = hq;
+      a.resid = ws.x;
+      a.ldr = d;
+      a.y = ws.h;
+      a.ldy = d;
+      a.sumsq_out = ws.sumsq2;
+      e = gemm(a, LOAD_F32, EPI_RESID_SUMSQ, &np2);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    // a7: RMSNorm -> SwiGLU
+    {
+      GemmArgs a = gemm_base(M, 2 * F, d);
+      a.w0 = w->w_gate;
+      a.n_seg0 = F;
+      a.w1 = w->w_up;
+      a.n_seg1 = F;
+      a.ffn = F;
+      a.x = ws.h;
+      a.ldx = d;
+      a.sumsq_in = ws.sumsq2;
+      a.n_part_in = np2;
+      a.gain = w->norm2;
+      a.eps = s.rms_eps;
+      a.yb = ws.act;
+      a.ldyb = F;
+      a.part = ws.gemm_part;
+      e = gemm(a, LOAD_F32_NORM, EPI_SWIGLU, nullptr);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    // f^ = h + act w_down^T
+    {
+      GemmArgs a = gemm_base(M, d, F);
+      a.w0 = w->w_down;
+      a.x = ws.act;
+      a.ldx = F;
+      a.resid = ws.h;
+      a.ldr = d;
+      a.y = out->feat;
+      a.ldy = d;
+      a.part = ws.gemm_part;
+      e = gemm(a, LOAD_F32, EPI_RESID, nullptr);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+  }
+  // a8 (a0 with HEAD_ONLY): logits = f lm_head^T
+  {
+    GemmArgs a = gemm_base(M, s.vocab, d);
+    a.w0 = w->lm_head;
+    a.x = head_only ? feat_in : out->feat;
+    a.xrows = head_only ? rows->parent : nullptr;
+    a.ldx = d;
+    a.y = out->logits;
+    a.ldy = s.vocab;
+    a.part = ws.gemm_part;
+    e = gemm(a, LOAD_F32, EPI_STORE, nullptr);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  // a9: softmax normaliser + top-k
+  e = launch_softmax_topk(M, s.vocab, out->logits, out->topk, out->lse, out->topk_idx, out->topk_logq, ws.topk, st);
+  if (e != hipSuccess) return hip_fail(e);
+  return EAGLE_OK;
+}
+
+int eagle_tree_init(int32_t batch, const eagle_pool* pool, const int32_t* root_token, int32_t root_feat_row0,
+                    eagle_stream_t stream) {
+  if (batch <= 0 || !pool || !root_token || root_feat_row0 < 0) return EAGLE_EINVAL;
+  if (pool->cap < 1 || !pool->parent || !pool->token || !pool->depth || !pool->logv || !pool->feat_row ||
+      !pool->slot || !pool->mask || !pool->count || !pool->frontier)
+    return EAGLE_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  PoolArgs p{pool->cap, pool->parent, pool->token, pool->depth, pool->logv, pool->feat_row, pool->slot, pool->mask,
+             pool->count, pool->frontier};
+  hipError_t e = launch_tree_init(batch, p, root_token, root_feat_row0, (hipStream_t)stream);
+  return e == hipSuccess ? EAGLE_OK : hip_fail(e);
+}
+
+int eagle_tree_expand(int32_t batch, int32_t k, int32_t step, const int32_t* static_nchild, const eagle_pool* pool,
+                      int32_t n_prev, int32_t topk, const int32_t* topk_idx, const float* topk_logq, int32_t n_next,
+                      int32_t feat_row0, const int32_t* prefix_len, int32_t* next_token, int32_t* next_parent,
+                      int32_t* next_pos, int32_t* next_slot, uint64_t* next_mask, int32_t* next_row_start,
+                      eagle_stream_t stream) {
+  if (batch <= 0 || !pool || k < 1 || step < 0 || n_prev < 1 || n_prev > EAGLE_MAX_SLOTS || n_next < 0 ||
+      n_next > EAGLE_MAX_SLOTS || topk < 1 || feat_row0 < 0)
+    return EAGLE_EINVAL;
+  if (!topk_idx || !topk_logq || !prefix_len || !next_token || !next_parent || !next_pos || !next_slot ||
+      !next_mask || !next_row_start)
+    return EAGLE_EINVAL;
+  if (pool->cap < 1 || !pool->parent || !pool->count || !pool->frontier) return EAGLE_EINVAL;
+  if (k > topk || topk > EAGLE_MAX_TOPK) return EAGLE_EUNSUPPORTED;
+  if (!static_nchild) {
+    if (n_next != k && n_next != 0) return EAGLE_EINVAL;  // 0: last expansion, no next draft step
+    if ((step + 1) * k > EAGLE_MAX_SLOTS) return EAGLE_EUNSUPPORTED;  // slots step*k + f < 64
+    if (n_prev * k > 256) return EAGLE_EUNSUPPORTED;
+  } else {
+    if (pool->cap > EAGLE_MAX_SLOTS) return EAGLE_EUNSUPPORTED;  // static slot = pool id < 64
+  }
+  int rc = check_device();
+  if (rc) return rc;
+  ExpandArgs a;
+  a.pool = PoolArgs{pool->cap, pool->parent, pool->token, pool->depth, pool->logv, pool->feat_row, pool->slot,
+                    pool->mask, pool->count, pool->frontier};
+  a.k = k;
+  a.step = step;
+  a.n_prev = n_prev;
+  a.topk = topk;
+  a.n_next = n_next;
+  a.feat_row0 = feat_row0;
+  a.nchild = static_nchild;
+  a.topk_idx = topk_idx;
+  a.topk_logq = topk_logq;
+  a.prefix_len = prefix_len;
+  a.next_token = next_token;
+  a.next_parent = next_parent;
+  a.next_pos = next_pos;
+  a.next_slot = next_slot;
+  a.next_row_start = next_row_start;
+  a.next_mask = next_mask;
+  a.batch = batch;
+  hipError_t e = launch_tree_expand(a, (hipStream_t)stream);
+  return e == hipSuccess ? EAGLE_OK : hip_fail(e);
+}
+
+int eagle_tree_finalize(int32_t batch, int32_t m, int32_t n_nodes, const eagle_pool* pool, const int32_t* prefix_len,
+                        int32_t* tree_parent, int32_t* tree_token, int32_t* tree_depth, int32_t* tree_pool,
+                        uint64_t* tree_mask, int32_t* tree_qrow, int32_t* row_token, int32_t* row_parent,
+                        int32_t* row_pos, int32_t* row_slot, uint64_t* row_mask, int32_t* row_start,
+                        eagle_stream_t stream) {
+  if (batch <= 0 || !pool || m < 0 || n_nodes < 1 || !prefix_len) return EAGLE_EINVAL;
+  if (!tree_parent || !tree_token || !tree_depth || !tree_pool || !tree_mask || !tree_qrow || !row_token ||
+      !row_parent || !row_pos || !row_slot || !row_mask || !row_start)
+    return EAGLE_EINVAL;
+  if (n_nodes > EAGLE_MAX_SLOTS) return EAGLE_EUNSUPPORTED;
+  if (pool->cap < 1 || pool->cap > 2048) return EAGLE_EUNSUPPORTED;
+  int rc = check_device();
+  if (rc) return rc;
+  FinalizeArgs a;
+  a.pool = PoolArgs{pool->cap, pool->parent, pool->token, pool->depth, pool->logv, pool->feat_row, pool->slot,
+                    pool->mask, pool->count, pool->frontier};
+  a.m = m;
+  a.n_nodes = n_nodes;
+  a.batch = batch;
+  a.prefix_len = prefix_len;
+  a.tree_parent = tree_parent;
+  a.tree_token = tree_token;
+  a.tree_depth = tree_depth;
+  a.tree_pool = tree_pool;
+  a.tree_qrow = tree_qrow;
+  a.tree_mask = tree_mask;
+  a.row_token = row_token;
+  a.row_parent = row_parent;
+  a.row_pos = row_pos;
+  a.row_slot = row_slot;
+  a.row_start = row_start;
+  a.row_mask = row_mask;
+  hipError_t e = launch_tree_finalize(a, (hipStream_t)stream);
+  return e == hipSuccess ? EAGLE_OK : hip_fail(e);
+}
+
+int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t* tree_parent, const int32_t* tree_token,
+                 const float* target_logits, const float* draft_logits, const int32_t* draft_row, uint64_t seed,
+                 uint64_t round, int32_t flags, int32_t* out_path, int32_t* out_accept_len, int32_t* out_next_token,
+                 int32_t* out_flags, eagle_stream_t stream) {
+  if (batch < 0 || n_nodes < 1 || vocab < 1) return EAGLE_EINVAL;
+  if (batch == 0) return EAGLE_OK;
+  if (!tree_parent || !tree_token || !target_logits || !draft_logits || !draft_row || !out_path ||
+      !out_accept_len || !out_next_token || !out_flags)
+    return EAGLE_EINVAL;
+  if (flags & ~(EAGLE_VERIFY_GREEDY | EAGLE_VERIFY_IID)) return EAGLE_EINVAL;
+  if (n_nodes > EAGLE_MAX_SLOTS || vocab > 32768) return EAGLE_EUNSUPPORTED;
+  int rc = check_device();
+  if (rc) return rc;
+  VerifyArgs a;
+  a.batch = batch;
+  a.n_nodes = n_nodes;
+  a.vocab = vocab;
+  a.parent = tree_parent;
+  a.token = tree_token;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.draft_row = draft_row;
+  a.seed = seed;
+  a.round = round;
+  a.flags = flags;
+  a.path = out_path;
+  a.accept_len = out_accept_len;
+  a.next_token = out_next_token;
+  a.out_flags = out_flags;
+  hipError_t e = launch_verify(a, (hipStream_t)stream);
+  return e == hipSuccess ? EAGLE_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Shared device helpers for the gfx950 kernels: bf16 conversion, vector
+// types, wave/block reductions.  Wavefronts are 64 lanes wide.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // storage type; arithmetic is fp32
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define WAVE 64
+
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// Reductions over a full wave with shuffles (fixed order -> deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, WAVE);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key);
+// -0.0 is folded onto +0.0 first so the two compare equal.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  f = f + 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+// (value desc, index asc) as one 64-bit key: larger key ranks first.
+__device__ __forceinline__ uint64_t topk_key(float v, uint32_t idx) {
+  return ((uint64_t)float_key(v) << 32) | (uint64_t)(0xffffffffu - idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) { return 0xffffffffu - (uint32_t)(k & 0xffffffffu); }
+__device__ __forceinline__ float key_value(uint64_t k) { return key_float((uint32_t)(k >> 32)); }
+
+// Block reductions; `red` must hold blockDim.x/64 entries.  All threads get the result.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / WAVE; ++i) s += red[i];
+  return s;
+}
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float s = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NT / WAVE; ++i) s = fmaxf(s, red[i]);
+  return s;
+}

@@ -1,0 +1,94 @@
+// Internal launch interface between the C ABI (capi.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+struct RopeArgs {
+  const float* qkv;  // [n_rows, (hq + 2 hkv) hd] fp32
+  const int32_t* pos;
+  const int32_t* slot;
+  const int32_t* seq_of_row;
+  float* q_out;  // [n_rows, hq hd] rotated q
+  void* tree_k;
+  void* tree_v;
+  int n_rows, hq, hkv, hd;
+  float theta;
+};
+
+struct AttnArgs {
+  const float* q;  // rotated q [n_rows, hq hd]
+  const uint64_t* mask;
+  const int32_t* row_start;
+  const void* prefix_k;
+  const void* prefix_v;
+  const int64_t* prefix_off;
+  const int32_t* prefix_len;
+  const void* tree_k;
+  const void* tree_v;
+  float* part;  // [n_splits, n_rows, hq, hd + 2]
+  float* out;   // [n_rows, hq hd]
+  int n_rows, batch, hq, hkv, split_len, n_splits;
+};
+
+hipError_t launch_row_seq(const int32_t* row_start, int batch, int n_rows, int32_t* seq_of_row, hipStream_t s);
+hipError_t launch_rope_kv(const RopeArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, bool bf16, int hd, hipStream_t s);
+int attn_split_len(int max_prefix, int batch, int hkv);
+int attn_n_splits(int max_prefix, int split_len);
+
+// softmax + top-k
+size_t topk_workspace_bytes(int n_rows, int vocab);
+hipError_t launch_softmax_topk(int n_rows, int vocab, const float* logits, int k, float* lse, int32_t* idx,
+                               float* logq, void* ws, hipStream_t s);
+
+// tree builder
+struct PoolArgs {
+  int cap;
+  int32_t* parent;
+  int32_t* token;
+  int32_t* depth;
+  float* logv;
+  int32_t* feat_row;
+  int32_t* slot;
+  uint64_t* mask;
+  int32_t* count;
+  int32_t* frontier;
+};
+hipError_t launch_tree_init(int batch, const PoolArgs& p, const int32_t* root_token, int root_feat_row0,
+                            hipStream_t s);
+struct ExpandArgs {
+  PoolArgs pool;
+  int k, step, n_prev, topk, n_next, feat_row0;
+  const int32_t* nchild;  // NULL = EAGLE-2
+  const int32_t* topk_idx;
+  const float* topk_logq;
+  const int32_t* prefix_len;
+  int32_t *next_token, *next_parent, *next_pos, *next_slot, *next_row_start;
+  uint64_t* next_mask;
+  int batch;
+};
+hipError_t launch_tree_expand(const ExpandArgs& a, hipStream_t s);
+struct FinalizeArgs {
+  PoolArgs pool;
+  int m, n_nodes, batch;
+  const int32_t* prefix_len;
+  int32_t *tree_parent, *tree_token, *tree_depth, *tree_pool, *tree_qrow;
+  uint64_t* tree_mask;
+  int32_t *row_token, *row_parent, *row_pos, *row_slot, *row_start;
+  uint64_t* row_mask;
+};
+hipError_t launch_tree_finalize(const FinalizeArgs& a, hipStream_t s);
+
+// verification
+struct VerifyArgs {
+  int batch, n_nodes, vocab;
+  const int32_t* parent;
+  const int32_t* token;
+  const float* target;
+  const float* draft;
+  const int32_t* draft_row;
+  uint64_t seed, round;
+  int flags;
+  int32_t *path, *accept_len, *next_token, *out_flags;
+};
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);

@@ -1,0 +1,302 @@
+// Tree-structured recursive rejection sampling.
+//
+// Rule for one draft token x ~ q against the target p: accept with probability
+// min(1, p(x)/q(x)); else draw from norm(max(0, p - q)) ("EAGLE 推测解码为什么比
+// Medusa 快" section 6.2; "eagle feature-level speculative decoding", section
+// "随机采样验证").  On a tree it is applied from the root: a node's children are
+// tried in rank order; after a rejection p becomes the residual and (default)
+// the rejected token is removed from q, which is renormalised.  All children
+// rejected -> correction draw from the residual; accepted leaf -> bonus draw
+// from the leaf's p.  Greedy mode replaces p by the onehot of the argmax.
+//
+// Uniforms: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11), counter
+// (sequence, node, event, 0), key (seed, round), u = (word0 >> 40) * 2^-24;
+// event i = test of the i-th child, event 64 = correction / bonus draw.
+//
+// One 1024-thread workgroup walks one sequence.  Thread t owns the EPT
+// consecutive tokens [t*EPT, (t+1)*EPT): p and q live in registers, the walk
+// needs block reductions only, and the inverse-CDF draw is one block scan.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int VT = 1024;
+constexpr int NW = VT / WAVE;
+
+__device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t round, uint64_t c0, uint64_t c1, uint64_t c2) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+  uint64_t x0 = c0, x1 = c1, x2 = c2, x3 = 0;
+  uint64_t k0 = seed, k1 = round;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t hi0 = __umul64hi(M0, x0), lo0 = M0 * x0;
+    const uint64_t hi1 = __umul64hi(M1, x2), lo1 = M1 * x2;
+    const uint64_t y0 = hi1 ^ x1 ^ k0, y2 = hi0 ^ x3 ^ k1;
+    x0 = y0;
+    x1 = lo1;
+    x2 = y2;
+    x3 = lo0;
+  }
+  return (float)(x0 >> 40) * 5.9604644775390625e-08f;  // 2^-24
+}
+
+__device__ __forceinline__ float bsum(float v, float* red) { return block_sum<VT>(v, red); }
+__device__ __forceinline__ float bmax(float v, float* red) { return block_max<VT>(v, red); }
+
+__device__ __forceinline__ int bmin_int(int v, int* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, WAVE));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = min(r, red[i]);
+  return r;
+}
+
+// Exclusive block scan of one float per thread (fixed order).
+__device__ __forceinline__ float bscan_excl(float v, float* red, float* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(inc, o, WAVE);
+    if (lane >= o) inc += t;
+  }
+  __syncthreads();
+  if (lane == 63) red[w] = inc;
+  __syncthreads();
+  float before = 0.f, all = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    if (i < w) before += red[i];
+    all += red[i];
+  }
+  *total = all;
+  return before + inc - v;
+}
+
+// Inverse CDF in token order: smallest y with cum(y) > u * sum(w).
+template <int EPT>
+__device__ int draw_token(const float (&w)[EPT], int vocab, float u, float* fred, int* ired) {
+  float own = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) own += w[e];
+  float total;
+  const float excl = bscan_excl(own, fred, &total);
+  const float T = u * total;
+  int cand = 0x7fffffff, last = -1;
+  float c = excl;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int y = threadIdx.x * EPT + e;
+    if (y < vocab) {
+      c += w[e];
+      if (w[e] > 0.f) last = y;
+      if (c > T && cand == 0x7fffffff && w[e] > 0.f) cand = y;
+    }
+  }
+  const int y = bmin_int(cand, ired);
+  if (y != 0x7fffffff) return y;
+  return -bmin_int(-last, ired);  // rounding left no boundary above T: last positive token
+}
+
+template <int EPT>
+__global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
+  __shared__ float fred[NW];
+  __shared__ int ired[NW];
+  __shared__ int s_parent[64], s_token[64];
+  __shared__ int kids[64];
+  __shared__ int s_nk;
+  __shared__ float s_px, s_qx;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int N = a.n_nodes, V = a.vocab;
+  if (t < N) {
+    s_parent[t] = a.parent[(size_t)b * N + t];
+    s_token[t] = a.token[(size_t)b * N + t];
+  }
+  __syncthreads();
+  const bool greedy = a.flags & 1, iid = a.flags & 2;
+  int flags = 0, u = 0, nacc = 0, next_tok = 0;
+  float p[EPT], q[EPT];
+
+  for (int level = 0; level <= N; ++level) {
+    // target distribution at u
+    const float* trow = a.target + ((size_t)b * N + u) * V;
+    float tv[EPT];
+    bool bad = false;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int y = t * EPT + e;
+      tv[e] = (y < V) ? trow[y] : -INFINITY;
+      bad |= (tv[e] != tv[e]);
+    }
+    if (__syncthreads_or(bad)) flags |= 8;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) mx = fmaxf(mx, tv[e]);
+    mx = bmax(mx, fred);
+    if (greedy) {
+      int cand = 0x7fffffff;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+        if (tv[e] == mx && cand == 0x7fffffff) cand = t * EPT + e;
+      const int am = bmin_int(cand, ired);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) p[e] = (t * EPT + e == am) ? 1.f : 0.f;
+    } else {
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        p[e] = (tv[e] == -INFINITY) ? 0.f : __expf(tv[e] - mx);
+        ls += p[e];
+      }
+      const float Z = bsum(ls, fred);
+      const float inv = 1.f / Z;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) p[e] *= inv;
+    }
+    // children of u in rank (index) order
+    if (t == 0) {
+      int nk = 0;
+      for (int i = u + 1; i < N; ++i)
+        if (s_parent[i] == u) kids[nk++] = i;
+      s_nk = nk;
+    }
+    __syncthreads();
+    const int nk = s_nk;
+    if (nk == 0) {
+      next_tok = draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired);
+      break;
+    }
+    // draft distribution at u
+    const int drow_idx = a.draft_row[(size_t)b * N + u];
+    if (drow_idx < 0) {  // no draft row for a node with children: invalid input
+      flags |= 8;
+      next_tok = draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired);
+      break;
+    }
+    const float* drow = a.draft + (size_t)drow_idx * V;
+    float dmx = -INFINITY;
+    float dv[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int y = t * EPT + e;
+      dv[e] = (y < V) ? drow[y] : -INFINITY;
+      dmx = fmaxf(dmx, dv[e]);
+    }
+    dmx = bmax(dmx, fred);
+    float ds = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      q[e] = (dv[e] == -INFINITY) ? 0.f : __expf(dv[e] - dmx);
+      ds += q[e];
+    }
+    {
+      const float inv = 1.f / bsum(ds, fred);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) q[e] *= inv;
+    }
+    float qmass = 1.f;
+    int accepted = -1;
+    for (int i = 0; i < nk; ++i) {
+      if (!(qmass > 0.f)) {
+        flags |= 4;
+        break;
+      }
+      const int c = kids[i];
+      const int x = s_token[c];
+      const float r = philox_uniform(a.seed, a.round, b, u, i);
+      const bool x_ok = x >= 0 && x < V;
+      __syncthreads();
+      if (x_ok && t == x / EPT) {
+        float px = 0.f, qx = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+          if (e == x % EPT) {
+            px = p[e];
+            qx = q[e];
+          }
+        s_px = px;
+        s_qx = qx;
+      }
+      __syncthreads();
+      const float px = x_ok ? s_px : 0.f, qx = x_ok ? s_qx : 0.f;
+      bool ok;
+      if (qx > 0.f) {
+        ok = r < px / qx;
+      } else {
+        flags |= 2;
+        ok = px > 0.f;
+      }
+      if (ok) {
+        accepted = c;
+        break;
+      }
+      // residual target
+      float rs = 0.f, res[EPT];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        res[e] = fmaxf(0.f, p[e] - q[e]);
+        rs += res[e];
+      }
+      const float Z = bsum(rs, fred);
+      if (Z > 0.f) {
+        const float inv = 1.f / Z;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) p[e] = res[e] * inv;
+      } else {
+        flags |= 1;
+      }
+      if (!iid) {
+        float qs = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          if (t * EPT + e == x) q[e] = 0.f;
+          qs += q[e];
+        }
+        const float S = bsum(qs, fred);
+        qmass = S;
+        if (S > 0.f) {
+          const float inv = 1.f / S;
+#pragma unroll
+          for (int e = 0; e < EPT; ++e) q[e] *= inv;
+        }
+      }
+    }
+    if (accepted < 0) {
+      next_tok = draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired);
+      break;
+    }
+    if (t == 0) a.path[(size_t)b * N + nacc] = accepted;
+    ++nacc;
+    u = accepted;
+  }
+  if (t == 0) {
+    for (int j = nacc; j < N; ++j) a.path[(size_t)b * N + j] = -1;
+    a.accept_len[b] = nacc + 1;
+    a.next_token[b] = next_tok;
+    a.out_flags[b] = flags;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
+  if (a.vocab <= VT)
+    hipLaunchKernelGGL(verify_kernel<1>, dim3(a.batch), dim3(VT), 0, s, a);
+  else if (a.vocab <= 4 * VT)
+    hipLaunchKernelGGL(verify_kernel<4>, dim3(a.batch), dim3(VT), 0, s, a);
+  else if (a.vocab <= 32 * VT)
+    hipLaunchKernelGGL(verify_kernel<32>, dim3(a.batch), dim3(VT), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}

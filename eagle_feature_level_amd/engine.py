@@ -1,0 +1,193 @@
+"""Device buffers and call sequence of one EAGLE draft-and-verify round.
+
+Only sequences C-ABI calls; all arithmetic is in the HIP kernels.  The order
+follows the pages' draft loop ("EAGLE 推测解码为什么比 Medusa 快" section 6.1;
+"EAGLE 完全拆解", four-step pipeline): the root distribution from the true
+feature, then per depth an expansion step and one draft step over the new
+frontier, then rerank/flatten, an optional draft step over every drafted node
+of the flattened tree, and verification.
+
+Feature rows and logit rows share one index space: rows [0, B) are the root
+rows (true features, root logits); each depth step appends B * n rows.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import (EAGLE_HEAD_ONLY, eagle_draft_step, eagle_tree_expand, eagle_tree_finalize, eagle_tree_init,
+               eagle_verify, eagle_workspace_bytes, make_kv, make_out, make_pool, make_rows, make_shape,
+               make_weights)
+
+
+@dataclasses.dataclass
+class Step:
+    n_prev: int
+    n_next: int
+    feat_row0: int
+    token: torch.Tensor
+    parent: torch.Tensor
+    pos: torch.Tensor
+    slot: torch.Tensor
+    mask: torch.Tensor
+    row_start: torch.Tensor
+
+
+class EagleRound:
+    def __init__(self, shape: dict, weights: dict, batch: int, kind: str, k: int, depth: int, m: int = 0,
+                 template=None, prefix=None, device="cuda"):
+        """shape: d, n_heads, n_kv_heads, head_dim, ffn, vocab, rms_eps, rope_theta, dtype.
+        weights: name -> device tensor.  prefix: dict(k, v, off, len, max_len) device tensors."""
+        self.shape_d = shape
+        self.shape = make_shape(**shape)
+        self.weights_t = weights
+        self.weights = make_weights(weights)
+        self.B, self.kind, self.k, self.depth, self.m = batch, kind, k, depth, m
+        self.dev = device
+        d, V = shape["d"], shape["vocab"]
+        hkv, hd = shape["n_kv_heads"], shape["head_dim"]
+        kvdt = torch.bfloat16 if shape["dtype"] == "bf16" else torch.float32
+        i32 = dict(dtype=torch.int32, device=device)
+        B = batch
+        if kind == "dynamic":
+            self.cap = 1 + k + (depth - 1) * k * k
+            self.nchild = None
+            self.topk = k
+            ns = [k] * (depth - 1)
+            self.n_nodes = m + 1
+        else:
+            tmpl = list(template)
+            self.cap = len(tmpl)
+            nch = [0] * len(tmpl)
+            dep = [0] * len(tmpl)
+            for i in range(1, len(tmpl)):
+                nch[tmpl[i]] += 1
+                dep[i] = dep[tmpl[i]] + 1
+            self.nchild = torch.tensor(nch, **i32)
+            self.topk = max(1, max(nch))
+            ns = [sum(1 for i in range(len(tmpl)) if dep[i] == s + 1 and nch[i] > 0) for s in range(depth - 1)]
+            self.n_nodes = len(tmpl)
+        self.ns = ns
+        total = B + sum(B * n for n in ns)
+        self.total_rows = total
+        self.feat = torch.zeros(total, d, dtype=torch.float32, device=device)
+        self.logits = torch.zeros(total, V, dtype=torch.float32, device=device)
+        self.lse = torch.zeros(total, dtype=torch.float32, device=device)
+        self.topk_idx = torch.zeros(total, self.topk, **i32)
+        self.topk_logq = torch.zeros(total, self.topk, dtype=torch.float32, device=device)
+        self.root_rows = torch.arange(B, **i32)
+        self.root_start = torch.arange(B + 1, **i32)
+        # pool
+        cap = self.cap
+        self.pool_t = dict(parent=torch.zeros(B * cap, **i32), token=torch.zeros(B * cap, **i32),
+                           depth=torch.zeros(B * cap, **i32),
+                           logv=torch.zeros(B * cap, dtype=torch.float32, device=device),
+                           feat_row=torch.zeros(B * cap, **i32), slot=torch.zeros(B * cap, **i32),
+                           mask=torch.zeros(B * cap, dtype=torch.int64, device=device),
+                           count=torch.zeros(B, **i32), frontier=torch.zeros(B * 64, **i32))
+        self.pool = make_pool(cap, **self.pool_t)
+        # per-step rows
+        self.steps = []
+        row0 = B
+        n_prev = 1
+        for n in ns:
+            self.steps.append(Step(n_prev, n, row0, torch.zeros(B * n, **i32), torch.zeros(B * n, **i32),
+                                   torch.zeros(B * n, **i32), torch.zeros(B * n, **i32),
+                                   torch.zeros(B * n, dtype=torch.int64, device=device), torch.zeros(B + 1, **i32)))
+            row0 += B * n
+            n_prev = n
+        self.last_n = n_prev
+        # final tree and tree-wide rows
+        N = self.n_nodes
+        self.tree = dict(parent=torch.zeros(B * N, **i32), token=torch.zeros(B * N, **i32),
+                         depth=torch.zeros(B * N, **i32), pool=torch.zeros(B * N, **i32),
+                         mask=torch.zeros(B * N, dtype=torch.int64, device=device), qrow=torch.zeros(B * N, **i32))
+        nw = B * (N - 1)
+        self.tw = dict(token=torch.zeros(nw, **i32), parent=torch.zeros(nw, **i32), pos=torch.zeros(nw, **i32),
+                       slot=torch.zeros(nw, **i32), mask=torch.zeros(nw, dtype=torch.int64, device=device),
+                       row_start=torch.zeros(B + 1, **i32))
+        self.tw_feat = torch.zeros(max(nw, 1), d, dtype=torch.float32, device=device)
+        self.tw_logits = torch.zeros(max(nw, 1), V, dtype=torch.float32, device=device)
+        self.tw_lse = torch.zeros(max(nw, 1), dtype=torch.float32, device=device)
+        self.tw_idx = torch.zeros(max(nw, 1), 1, **i32)
+        self.tw_logq = torch.zeros(max(nw, 1), 1, dtype=torch.float32, device=device)
+        # KV
+        self.tree_k = torch.zeros(B, 64, hkv, hd, dtype=kvdt, device=device)
+        self.tree_v = torch.zeros(B, 64, hkv, hd, dtype=kvdt, device=device)
+        self.tw_tree_k = torch.zeros_like(self.tree_k)
+        self.tw_tree_v = torch.zeros_like(self.tree_v)
+        self.prefix = prefix
+        self.kv = make_kv(prefix["k"], prefix["v"], prefix["off"], prefix["len"], prefix["max_len"], self.tree_k,
+                          self.tree_v)
+        self.tw_kv = make_kv(prefix["k"], prefix["v"], prefix["off"], prefix["len"], prefix["max_len"],
+                             self.tw_tree_k, self.tw_tree_v)
+        max_rows = max([B] + [B * n for n in ns] + [nw])
+        ws = eagle_workspace_bytes(self.shape, max_rows, B, prefix["max_len"])
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        # verify outputs
+        self.v_path = torch.zeros(B * N, **i32)
+        self.v_len = torch.zeros(B, **i32)
+        self.v_next = torch.zeros(B, **i32)
+        self.v_flags = torch.zeros(B, **i32)
+
+    # ------------------------------------------------------------------ calls
+    def root_head(self, root_feat: torch.Tensor):
+        B = self.B
+        self.feat[:B].copy_(root_feat)
+        rows = make_rows(B, B, 1, self.root_start, None, self.root_rows)
+        out = make_out(None, self.logits, self.lse, self.topk, self.topk_idx, self.topk_logq)
+        eagle_draft_step(self.shape, self.weights, EAGLE_HEAD_ONLY, rows, self.feat, None, out, self.workspace)
+
+    def draft_phase(self, root_feat: torch.Tensor, root_token: torch.Tensor):
+        """Root head, then expand + draft step per depth, then rerank/flatten."""
+        B, k = self.B, self.k
+        self.root_head(root_feat)
+        eagle_tree_init(B, self.pool, root_token, 0)
+        prev_row0, n_prev = 0, 1
+        for s in range(self.depth):
+            last = s == self.depth - 1
+            if last:
+                # final expansion: create the deepest children; no further draft step
+                st = self._scratch_step()
+                n_next = 0
+            else:
+                st = self.steps[s]
+                n_next = st.n_next
+            eagle_tree_expand(B, k, s, self.nchild, self.pool, n_prev, self.topk, self.topk_idx[prev_row0:],
+                              self.topk_logq[prev_row0:], n_next, st.feat_row0, self.prefix["len"], st.token,
+                              st.parent, st.pos, st.slot, st.mask, st.row_start)
+            if last:
+                break
+            n = B * st.n_next
+            rows = make_rows(n, B, st.n_next, st.row_start, st.token, st.parent, st.pos, st.slot, st.mask)
+            out = make_out(self.feat[st.feat_row0:], self.logits[st.feat_row0:], self.lse[st.feat_row0:], self.topk,
+                           self.topk_idx[st.feat_row0:], self.topk_logq[st.feat_row0:])
+            eagle_draft_step(self.shape, self.weights, 0, rows, self.feat, self.kv, out, self.workspace)
+            prev_row0, n_prev = st.feat_row0, st.n_next
+        t = self.tree
+        eagle_tree_finalize(B, self.m, self.n_nodes, self.pool, self.prefix["len"], t["parent"], t["token"],
+                            t["depth"], t["pool"], t["mask"], t["qrow"], self.tw["token"], self.tw["parent"],
+                            self.tw["pos"], self.tw["slot"], self.tw["mask"], self.tw["row_start"])
+
+    def _scratch_step(self):
+        if not hasattr(self, "_scratch"):
+            B, k = self.B, max(self.k, 1)
+            i32 = dict(dtype=torch.int32, device=self.dev)
+            self._scratch = Step(0, k, self.total_rows, torch.zeros(B * k, **i32), torch.zeros(B * k, **i32),
+                                 torch.zeros(B * k, **i32), torch.zeros(B * k, **i32),
+                                 torch.zeros(B * k, dtype=torch.int64, device=self.dev), torch.zeros(B + 1, **i32))
+        return self._scratch
+
+    def tree_wide(self):
+        """One draft step over every drafted node of the flattened tree."""
+        nw = self.B * (self.n_nodes - 1)
+        rows = make_rows(nw, self.B, self.n_nodes - 1, self.tw["row_start"], self.tw["token"], self.tw["parent"],
+                         self.tw["pos"], self.tw["slot"], self.tw["mask"])
+        out = make_out(self.tw_feat, self.tw_logits, self.tw_lse, 1, self.tw_idx, self.tw_logq)
+        eagle_draft_step(self.shape, self.weights, 0, rows, self.feat, self.tw_kv, out, self.workspace)
+
+    def verify(self, target_logits: torch.Tensor, seed: int, round_: int, flags: int = 0):
+        t = self.tree
+        eagle_verify(self.B, self.n_nodes, self.shape_d["vocab"], t["parent"], t["token"], target_logits,
+                     self.logits, t["qrow"], seed, round_, flags, self.v_path, self.v_len, self.v_next, self.v_flags)

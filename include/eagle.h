@@ -1,0 +1,264 @@
+/*
+ * eagle.h - C ABI of the MI355X (gfx950) EAGLE draft-and-verify hot path.
+ *
+ * One round of EAGLE feature-level speculative decoding, as the pages describe
+ * it, is: a draft head (frozen target embedding, FC 2d->d over [f ; e(t)], one
+ * decoder layer, frozen shared LM head) grows a token tree from the last true
+ * target feature; EAGLE-2 chooses which nodes to expand and which to keep by
+ * the product of draft confidences along each path; the target's distributions
+ * over the tree are then checked by recursive rejection sampling, which keeps
+ * the output distribution equal to the target's.
+ *   - "EAGLE 推测解码为什么比 Medusa 快" (zzszmyf.github.io), sections 4.1, 6.1,
+ *     6.2, 7.1 and 10.3;
+ *   - "eagle feature-level speculative decoding" (charlestar.github.io),
+ *     sections on the draft head, tree attention, greedy and sampling
+ *     verification;
+ *   - "EAGLE 完全拆解" (pinghaoyang.com.cn), sections on the draft head and on
+ *     EAGLE-2.
+ *
+ * Conventions (all entry points):
+ *   - Every pointer argument is DEVICE memory owned by the caller, unless the
+ *     argument is a pointer to one of the small structs below, which are host
+ *     structs passed by pointer and read during the call only.  The library
+ *     never allocates or frees device memory in a call; scratch space comes in
+ *     through `workspace` (size from eagle_workspace_bytes).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Nothing synchronises with the host.  Calls on different streams
+ *     must not share a workspace.
+ *   - Return value: EAGLE_OK (0) or a negative EAGLE_E* code.  Argument errors
+ *     are detected on the host before any launch, so a failing call launches
+ *     nothing.  eagle_last_hip_error() gives the hipError_t behind EAGLE_EHIP.
+ *   - Matrices are row-major.  Weights are [out, in]: y = x W^T.
+ *   - Outputs are a pure function of the inputs (and of seed/round for
+ *     eagle_verify): reduction orders are fixed, no atomics decide values.
+ */
+#ifndef EAGLE_H
+#define EAGLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *eagle_stream_t; /* hipStream_t */
+
+enum {
+  EAGLE_OK = 0,
+  EAGLE_EINVAL = -1,       /* null pointer, bad size, inconsistent shape   */
+  EAGLE_EUNSUPPORTED = -2, /* dtype, top-k > 16, > 64 tree nodes, not gfx950 */
+  EAGLE_EWORKSPACE = -3,   /* workspace smaller than eagle_workspace_bytes */
+  EAGLE_EHIP = -4          /* a HIP launch or query failed                 */
+};
+
+enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 };
+
+/* Largest tree per sequence: node masks are 64-bit. */
+#define EAGLE_MAX_SLOTS 64
+/* Largest per-row top-k. */
+#define EAGLE_MAX_TOPK 16
+
+/* Draft-head shape.  d = hidden size (the feature width), n_heads query
+ * heads and n_kv_heads key/value heads of head_dim each (n_heads a multiple
+ * of n_kv_heads), ffn = SwiGLU width, vocab = shared vocabulary size.
+ * dtype EAGLE_BF16: weights, embedding, LM head and K/V are bf16, GEMMs run on
+ * bf16 matrix cores with fp32 accumulation (activations as split bf16 pairs);
+ * EAGLE_F32: everything fp32. */
+typedef struct {
+  int32_t d, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  float rms_eps;    /* RMSNorm epsilon, e.g. 1e-5                    */
+  float rope_theta; /* rotary base, e.g. 1e4                         */
+  int32_t dtype;    /* EAGLE_BF16 or EAGLE_F32                       */
+} eagle_shape;
+
+/* Draft-head weights (element type = shape.dtype), device pointers.
+ * embed/lm_head are the target's frozen embedding and LM head [vocab, d];
+ * fc_w [d, 2d] and fc_b [d] fuse [f ; e(t)]; the decoder layer is pre-norm
+ * (norm1/norm2 gains [d]), wq [Hq*hd, d], wk/wv [Hkv*hd, d], wo [d, Hq*hd],
+ * w_gate/w_up [ffn, d], w_down [d, ffn]. */
+typedef struct {
+  const void *embed, *fc_w, *fc_b, *norm1, *norm2, *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down, *lm_head;
+} eagle_weights;
+
+/* Rows of one draft step (device arrays of n_rows entries unless stated).
+ * A row is one expanded tree node: its input is the parent's feature and the
+ * node's own (advanced) token.  Rows of one sequence are contiguous:
+ * sequence b owns rows [row_start[b], row_start[b+1]). */
+typedef struct {
+  int32_t n_rows;           /* host: number of rows                            */
+  int32_t batch;            /* host: number of sequences                       */
+  int32_t max_rows_per_seq; /* host: max over b of row_start[b+1]-row_start[b] */
+  const int32_t *row_start; /* [batch+1]                                       */
+  const int32_t *token;     /* advanced token of the row, 0 <= t < vocab       */
+  const int32_t *parent;    /* row of feat_in holding the parent feature       */
+  const int32_t *pos;       /* rotary position (prefix_len + depth - 1)        */
+  const int32_t *slot;      /* tree slot (0..63) receiving this row's k, v     */
+  const uint64_t *mask;     /* tree slots visible to the row: ancestors + self */
+} eagle_rows;
+
+/* Draft-layer KV.  Prefix K (already rotated) and V are packed per sequence
+ * as [Hkv][L_b][hd] starting at element prefix_off[b].  Tree slots hold the
+ * k, v of drafted nodes: [batch][64][Hkv][hd].  Element type = shape.dtype. */
+typedef struct {
+  const void *prefix_k, *prefix_v;
+  const int64_t *prefix_off; /* [batch] element offsets         */
+  const int32_t *prefix_len; /* [batch] L_b >= 0                */
+  int32_t max_prefix_len;    /* host: max over b of L_b          */
+  void *tree_k, *tree_v;     /* written: the rows' slots         */
+} eagle_kv;
+
+/* Outputs of a draft step. */
+typedef struct {
+  float *feat;       /* [n_rows, d] predicted feature f^ (unused with HEAD_ONLY) */
+  float *logits;     /* [n_rows, vocab] LM-head logits                          */
+  float *lse;        /* [n_rows] log-sum-exp of each logits row                 */
+  int32_t topk;      /* 1..16                                                   */
+  int32_t *topk_idx; /* [n_rows, topk] ranked tokens, ties -> lower index        */
+  float *topk_logq;  /* [n_rows, topk] logit - lse of those tokens               */
+} eagle_draft_out;
+
+/* Flags of eagle_draft_step. */
+enum { EAGLE_HEAD_ONLY = 1 };
+
+/* Bytes of workspace needed by eagle_draft_step / eagle_softmax_topk for up
+ * to max_rows rows, max_batch sequences and prefixes up to max_prefix_len.
+ * Returns 0 for an invalid shape. */
+size_t eagle_workspace_bytes(const eagle_shape *shape, int32_t max_rows, int32_t max_batch, int32_t max_prefix_len);
+
+/* One draft step over a set of tree rows.
+ *
+ * Without flags, per row r (sequence b):
+ *   a   = [f ; e] with f = feat_in[parent[r]] and e = embed[token[r]]      (2d)
+ *   x   = a fc_w^T + fc_b
+ *   q,k,v = RMSNorm(x) * norm1 times wq, wk, wv; q and k rotated (RoPE,
+ *         rotate-half pairing i <-> i+hd/2, frequency theta^(-2i/hd)) at
+ *         pos[r]; k, v written to tree slot slot[r] of sequence b
+ *   att = per query head h (kv head h / (Hq/Hkv)): softmax over the prefix
+ *         keys 0..L_b-1 and the tree slots set in mask[r], scale 1/sqrt(hd)
+ *   h   = x + att wo^T
+ *   f^  = h + (silu(n2 w_gate^T) * (n2 w_up^T)) w_down^T, n2 = RMSNorm(h)*norm2
+ *   logits = f^ lm_head^T; lse; top-k of the row.
+ * With EAGLE_HEAD_ONLY: logits = feat_in[parent[r]] lm_head^T (the root
+ * distribution from the true feature; the decoder is skipped and kv, feat may
+ * be NULL).
+ *
+ * Precision (bf16 workloads): weights, embedding, LM head and the KV cache are
+ * bf16; activations (features, residuals, q, attention output, SwiGLU
+ * activation) are fp32 and enter the matrix units as a pair of bf16 values
+ * (hi, lo = x - hi) with fp32 accumulation, so the only activation rounding to
+ * bf16 is the store of k and v into the tree slots.  feat_in is fp32 [*, d].
+ * Rows that attend to each other's slots may share one call: every row's
+ * k, v is written before any row's attention runs. */
+int eagle_draft_step(const eagle_shape *shape, const eagle_weights *w, int32_t flags, const eagle_rows *rows,
+                     const float *feat_in, const eagle_kv *kv, const eagle_draft_out *out, void *workspace,
+                     size_t workspace_bytes, eagle_stream_t stream);
+
+/* Softmax normaliser and top-k of n_rows fp32 rows of `vocab` logits:
+ * lse[r] = log sum exp(logits[r]); topk_idx[r] = the `topk` largest entries
+ * by (value desc, index asc), -0.0 equal to +0.0; topk_logq = value - lse.
+ * Uses the workspace sized by eagle_workspace_bytes. */
+int eagle_softmax_topk(int32_t n_rows, int32_t vocab, const float *logits, int32_t topk, float *lse,
+                       int32_t *topk_idx, float *topk_logq, void *workspace, size_t workspace_bytes,
+                       eagle_stream_t stream);
+
+/* Candidate pool of the tree builder: per sequence b, entries
+ * [b*cap, (b+1)*cap) of each array; node 0 is the root. */
+typedef struct {
+  int32_t cap;          /* host: pool entries per sequence            */
+  int32_t *parent;      /* pool id of the parent (-1 for the root)    */
+  int32_t *token;       /* node token                                 */
+  int32_t *depth;       /* 0 for the root                             */
+  float *logv;          /* log value: fp32 sum of logq along the path */
+  int32_t *feat_row;    /* row of the node's feature once expanded    */
+  int32_t *slot;        /* tree slot of its decoder row               */
+  uint64_t *mask;       /* visible slots of its decoder row           */
+  int32_t *count;       /* [batch] pool size                          */
+  int32_t *frontier;    /* [batch*EAGLE_MAX_SLOTS] current frontier   */
+} eagle_pool;
+
+/* Reset each sequence's pool to its root: token root_token[b], feature row
+ * root_feat_row0 + b, log value 0, frontier = {root}. */
+int eagle_tree_init(int32_t batch, const eagle_pool *pool, const int32_t *root_token, int32_t root_feat_row0,
+                    eagle_stream_t stream);
+
+/* One expansion step.  The previous draft step ran n_prev rows per sequence
+ * (row b*n_prev + f = frontier position f of sequence b) and produced
+ * topk_idx/topk_logq [batch*n_prev, topk].
+ *   EAGLE-2 (static_nchild == NULL): every frontier node gets its top `k`
+ *     tokens as children, logv(child) = fl32(logv(parent) + logq); the next
+ *     frontier is the k children of largest logv (ties -> earlier creation;
+ *     creation order = (frontier position, rank)).  n_next must equal k, or
+ *     0 for the last expansion (children created, no next frontier or rows).
+ *   Static template (static_nchild = child count per template node, indexed
+ *     by pool id, which equals the template's BFS index): node u gets its
+ *     top static_nchild[u] tokens; the next frontier is every new child with
+ *     children of its own, in creation order.  n_next = their number.
+ * The next draft step's rows are written to next_rows (batch*n_next rows,
+ * row_start[b] = b*n_next): token, parent = the parent's feature row,
+ * pos = prefix_len[b] + depth - 1, slot = (EAGLE-2) step*k + f or (static)
+ * the pool id, mask = parent's mask | (1 << slot).  The frontier node at
+ * position f gets feature row feat_row0 + b*n_next + f.
+ * Limits: k <= topk <= 16, n_prev * k <= 256, slots < 64.  static_nchild must
+ * hold pool->cap entries.  If a sequence's pool would exceed pool->cap, its
+ * pool->count is set to -1 and nothing is added (its finalize then yields the
+ * root only). */
+int eagle_tree_expand(int32_t batch, int32_t k, int32_t step, const int32_t *static_nchild, const eagle_pool *pool,
+                      int32_t n_prev, int32_t topk, const int32_t *topk_idx, const float *topk_logq, int32_t n_next,
+                      int32_t feat_row0, const int32_t *prefix_len, int32_t *next_token, int32_t *next_parent,
+                      int32_t *next_pos, int32_t *next_slot, uint64_t *next_mask, int32_t *next_row_start,
+                      eagle_stream_t stream);
+
+/* Rerank and flatten.  Keeps the m pool nodes (root excluded) of largest logv,
+ * ties -> shallower, then earlier creation (m = 0: keep all), which is a
+ * connected tree; orders the root first and the rest by (depth, creation), so
+ * siblings stay in rank order.  Writes n_nodes = m+1 (or the pool size) nodes
+ * per sequence at [b*n_nodes, ...): tree_parent (tree index, -1 root),
+ * tree_token, tree_depth, tree_pool, tree_mask (bit t for node t and each
+ * non-root ancestor), tree_qrow (feature/logit row where the node was
+ * expanded, -1 if never).  Also writes the rows of a "tree-wide" draft step
+ * over the n_nodes-1 drafted nodes (row b*(n_nodes-1) + t-1 for node t):
+ * token, parent feature row, pos = prefix_len[b] + depth - 1, slot = t,
+ * mask = tree_mask. n_nodes <= 64. */
+int eagle_tree_finalize(int32_t batch, int32_t m, int32_t n_nodes, const eagle_pool *pool, const int32_t *prefix_len,
+                        int32_t *tree_parent, int32_t *tree_token, int32_t *tree_depth, int32_t *tree_pool,
+                        uint64_t *tree_mask, int32_t *tree_qrow, int32_t *row_token, int32_t *row_parent,
+                        int32_t *row_pos, int32_t *row_slot, uint64_t *row_mask, int32_t *row_start,
+                        eagle_stream_t stream);
+
+/* Flags of eagle_verify. */
+enum { EAGLE_VERIFY_GREEDY = 1, EAGLE_VERIFY_IID = 2 };
+/* Per-sequence status bits written to out_flags. */
+enum { EAGLE_F_ZRES = 1, EAGLE_F_QZERO = 2, EAGLE_F_QEMPTY = 4, EAGLE_F_NAN = 8 };
+
+/* Tree-structured recursive rejection sampling, one walk per sequence.
+ * Tree: n_nodes nodes per sequence (node 0 = root, tree_parent < own index,
+ * siblings in rank order).  target_logits [batch*n_nodes, vocab]: row
+ * b*n_nodes+i is the target's logits after node i.  q at node i is
+ * softmax(draft_logits[draft_row[b*n_nodes+i]]) (only read for nodes with
+ * children).  At node u with children c_1..c_m: p = softmax(target row u)
+ * (greedy: onehot of its argmax, ties -> lower index).  Child c_i is
+ * accepted iff u_i < p(x)/q(x) (x = its token; q(x) = 0: iff p(x) > 0),
+ * u_i = Philox4x64-10 uniform of counter (b, u, i, 0) and key (seed, round),
+ * (w0 >> 40) * 2^-24.  On rejection p <- norm(max(0, p - q)) (kept if that
+ * mass is 0) and, unless EAGLE_VERIFY_IID, q <- norm(q without x).  If all
+ * children are rejected the correction is drawn from p by inverse CDF in
+ * token order with uniform event 64; at an accepted leaf the bonus is drawn
+ * from that leaf's p the same way.
+ * Outputs: out_path[b*n_nodes + j] = j-th accepted node (-1 padded),
+ * out_accept_len[b] = accepted nodes + 1, out_next_token[b], out_flags[b].
+ * vocab <= 32768, n_nodes <= 64. */
+int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t *tree_parent, const int32_t *tree_token,
+                 const float *target_logits, const float *draft_logits, const int32_t *draft_row, uint64_t seed,
+                 uint64_t round, int32_t flags, int32_t *out_path, int32_t *out_accept_len, int32_t *out_next_token,
+                 int32_t *out_flags, eagle_stream_t stream);
+
+/* Message for an EAGLE_E* code. */
+const char *eagle_strerror(int code);
+/* hipError_t of the last EAGLE_EHIP on this thread. */
+int eagle_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE_H */

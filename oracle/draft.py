@@ -20,10 +20,10 @@ The first draft distribution of a round comes straight from the true feature
 (``head_only``): q = softmax(LM_Head(f_j)), which is the target's own p
 (study note sections 6.1 and 7.1).
 
-``mirror=True`` rounds to bf16 exactly the operands a bf16 GPU kernel feeds to
-its matrix units: the FC input [f ; e], RMSNorm outputs, rotated q, k and v,
-the attention output, the SwiGLU activation and f^ before the LM head.  All
-accumulation, normalisation and RoPE stay in fp64.
+Precision reading for bf16 workloads: weights, embedding, LM head and the KV
+cache are bf16 values; activations are carried at full precision.  So with
+``mirror=True`` the only rounding is of the rotated k and of v when they are
+stored into the bf16 tree slots (the cache format); everything else is fp64.
 """
 from __future__ import annotations
 
@@ -48,8 +48,7 @@ def new_tree_kv(shape, batch: int):
 def head_logits(shape, w, feats: np.ndarray, mirror: bool = True) -> np.ndarray:
     """Root distribution logits from true features: LM_Head(f) (no final norm,
     no bias: f is exactly the LM head's input)."""
-    on = mirror and shape.dtype == "bf16"
-    return matmul_t(_r(feats, on), w.lm_head)
+    return matmul_t(feats, w.lm_head)
 
 
 def tree_attention_row(q_heads, seq_prefix_k, seq_prefix_v, L, tree_k_seq, tree_v_seq, mask, n_heads,
@@ -63,10 +62,9 @@ def tree_attention_row(q_heads, seq_prefix_k, seq_prefix_v, L, tree_k_seq, tree_
     out = np.zeros((n_heads, hd))
     for h in range(n_heads):
         g = h // group
-        keys = [seq_prefix_k[g, j] for j in range(L)] + [tree_k_seq[s, g] for s in slots]
-        vals = [seq_prefix_v[g, j] for j in range(L)] + [tree_v_seq[s, g] for s in slots]
-        keys = np.asarray(keys, dtype=np.float64).reshape(-1, hd)
-        vals = np.asarray(vals, dtype=np.float64).reshape(-1, hd)
+        # visible keys: prefix positions 0..L-1, then the visible tree slots
+        keys = np.concatenate([seq_prefix_k[g, :L], tree_k_seq[slots, g]]).astype(np.float64).reshape(-1, hd)
+        vals = np.concatenate([seq_prefix_v[g, :L], tree_v_seq[slots, g]]).astype(np.float64).reshape(-1, hd)
         scores = keys @ q_heads[h] / np.sqrt(hd)
         p = softmax(scores)
         out[h] = p @ vals
@@ -102,10 +100,10 @@ def draft_step(shape, w, rows: dict, feat_buf: np.ndarray, prefix_k, prefix_v, p
 
     # a1, a2: [f_parent ; e(t)] -> FC 2d->d with bias
     a = np.concatenate([np.asarray(feat_buf, np.float64)[par], np.asarray(w.embed, np.float64)[tok]], axis=1)
-    x = matmul_t(_r(a, on), w.fc_w) + np.asarray(w.fc_b, np.float64)
+    x = matmul_t(a, w.fc_w) + np.asarray(w.fc_b, np.float64)
 
     # a3: RMSNorm -> q, k, v
-    n1 = _r(rmsnorm(x, w.norm1, shape.rms_eps), on)
+    n1 = rmsnorm(x, w.norm1, shape.rms_eps)
     q = matmul_t(n1, w.wq).reshape(M, hq, hd)
     k = matmul_t(n1, w.wk).reshape(M, hkv, hd)
     v = matmul_t(n1, w.wv).reshape(M, hkv, hd)
@@ -116,29 +114,32 @@ def draft_step(shape, w, rows: dict, feat_buf: np.ndarray, prefix_k, prefix_v, p
             q[r, h] = rope_rotate_half(q[r, h], int(pos[r]), shape.rope_theta)
         for h in range(hkv):
             k[r, h] = rope_rotate_half(k[r, h], int(pos[r]), shape.rope_theta)
-    q, k, v = _r(q, on), _r(k, on), _r(v, on)
+    k, v = _r(k, on), _r(v, on)  # the KV cache stores bf16
     for r in range(M):
         tree_k[seq[r], slot[r]] = k[r]
         tree_v[seq[r], slot[r]] = v[r]
 
     # a5: tree attention over prefix + visible tree slots
     attn = np.zeros((M, hq, hd))
+    pkv = {}
     for r in range(M):
         b = int(seq[r])
-        attn[r] = tree_attention_row(q[r], np.asarray(prefix_k[b], np.float64), np.asarray(prefix_v[b], np.float64),
-                                     int(prefix_len[b]), tree_k[b], tree_v[b], mask[r], hq, hkv)
-    attn = _r(attn.reshape(M, hq * hd), on)
+        if b not in pkv:
+            pkv[b] = (np.asarray(prefix_k[b], np.float64), np.asarray(prefix_v[b], np.float64))
+        attn[r] = tree_attention_row(q[r], pkv[b][0], pkv[b][1], int(prefix_len[b]), tree_k[b], tree_v[b], mask[r],
+                                     hq, hkv)
+    attn = attn.reshape(M, hq * hd)
 
     # a6: O projection + residual
     h_res = x + matmul_t(attn, w.wo)
 
     # a7: RMSNorm -> SwiGLU MLP + residual
-    n2 = _r(rmsnorm(h_res, w.norm2, shape.rms_eps), on)
-    act = _r(silu(matmul_t(n2, w.w_gate)) * matmul_t(n2, w.w_up), on)
+    n2 = rmsnorm(h_res, w.norm2, shape.rms_eps)
+    act = silu(matmul_t(n2, w.w_gate)) * matmul_t(n2, w.w_up)
     feat = h_res + matmul_t(act, w.w_down)
 
     out = {"x": x, "q": q, "k": k, "v": v, "attn": attn, "h": h_res, "feat": feat}
     # a8: frozen shared LM head
     if want_logits:
-        out["logits"] = matmul_t(_r(feat, on), w.lm_head)
+        out["logits"] = matmul_t(feat, w.lm_head)
     return out

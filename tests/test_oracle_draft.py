@@ -193,7 +193,7 @@ def test_chain_loop_equals_one_step_over_chain():
     assert np.allclose(o["feat"], np.array(feats), rtol=0, atol=1e-10)
 
 
-def test_bf16_mirror_rounds_only_gemm_operands():
+def test_bf16_mirror_rounds_only_the_kv_cache():
     cfg = CONFIGS[2]
     small = Shape(128, 2, 2, 64, 96, 300)
     shape, w, lens, pk, pv = _tiny_setup(small)
@@ -203,8 +203,8 @@ def test_bf16_mirror_rounds_only_gemm_operands():
     a = D.draft_step(shape, w, rows, f, pk, pv, lens, tk, tv, mirror=True)
     tk2, tv2 = D.new_tree_kv(shape, 1)
     b = D.draft_step(shape, w, rows, f, pk, pv, lens, tk2, tv2, mirror=False)
-    # k, v in the slots are bf16 values under the mirror
+    # k, v in the slots are bf16 values under the mirror; q and the residual stream are not rounded
     assert np.array_equal(round_bf16(tk[0, 1]), tk[0, 1])
-    # both readings agree to bf16 accuracy but are not identical
-    assert np.max(np.abs(a["feat"] - b["feat"])) < 0.1
-    assert np.max(np.abs(a["feat"] - b["feat"])) > 0
+    assert np.array_equal(a["x"], b["x"]) and np.array_equal(a["q"], b["q"])
+    # the readings differ only through the cache rounding, by a little
+    assert 0 < np.max(np.abs(a["feat"] - b["feat"])) < 0.05
