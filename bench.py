@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Throughput of the EAGLE draft-and-verify hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+the root distribution from the true feature, every depth's tree expansion and
+draft step (embedding gather, [f ; e] FC, one decoder layer with tree
+attention, LM head, softmax + top-k), the final expansion and rerank/flatten,
+and tree-structured recursive rejection sampling against target logits that
+sit in HBM before the timed region starts.
+
+Default workload: the LLaMA2-7B-shaped draft head (d=4096, 32 heads x 128,
+ffn 11008, vocab 32000, bf16), batch 1, prefix KV 1024, the static 26-node
+tree (depth 5, branching 4/3/2/1).  Weights ~N(0, 0.02), features and prefix
+KV ~N(0, 1), target logits = draft logits + N(0, 0.5) (root: exact copy).
+
+Prints one JSON line.  value = drafted tree nodes per second through draft +
+verify (whole job, one GPU).  `roofline` covers the dominant kernel, with its
+per-launch duration measured by HIP events around each launch on the stream
+it runs on; `cpu_baseline` times the fp64 CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+COUNTERS = os.path.join(ROOT, "profiles", "counters_gemm_lm_head_7b_static26.json")
+GEMM_SRC = os.path.join(ROOT, "eagle_feature_level_amd", "csrc", "gemm.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_engine(cid: int):
+    import torch
+    from eagle_feature_level_amd.engine import EagleRound
+    from workloads import (CONFIGS, TEMPLATES, make_prefix_kv, make_prefix_lens, make_root_features, make_root_tokens,
+                           make_weights)
+    from workloads import device as dev
+
+    cfg = CONFIGS[cid]
+    s = cfg.shape
+    t0 = time.time()
+    w = make_weights(cfg)
+    lens = make_prefix_lens(cfg)
+    ks, vs = make_prefix_kv(cfg, lens)
+    feat = make_root_features(cfg)
+    tok = make_root_tokens(cfg)
+    log(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s")
+    wt = dev.weights(w, s.dtype)
+    pf = dev.prefix(ks, vs, lens, s.dtype)
+    kind = "dynamic" if cfg.tree == "dynamic" else "static"
+    eng = EagleRound(dev.shape_dict(s), wt, cfg.batch, kind, cfg.topk, cfg.depth, cfg.rerank_m,
+                     TEMPLATES.get(cfg.tree), pf)
+    host = dict(w=w, lens=lens, ks=ks, vs=vs, feat=feat, tok=tok)
+    return cfg, eng, torch.from_numpy(feat).cuda(), dev.ints(tok), host
+
+
+def synth_target(cfg, eng):
+    """Target logits [B*N, V]: root row = the root draft row (q == p), other
+    nodes = tree-wide draft logits + N(0, 0.5) noise."""
+    import torch
+    from workloads import make_target_noise
+    B, N, V = cfg.batch, eng.n_nodes, cfg.shape.vocab
+    eng.tree_wide()
+    noise = torch.from_numpy(make_target_noise(cfg, B * N)).cuda()
+    tgt = torch.empty(B * N, V, device="cuda")
+    tw = eng.tw_logits[:B * (N - 1)].view(B, N - 1, V)
+    tgt.view(B, N, V)[:, 1:] = tw + noise.view(B, N, V)[:, 1:]
+    tgt.view(B, N, V)[:, 0] = eng.logits[:B]
+    torch.cuda.synchronize()
+    return tgt
+
+
+def run_steps(eng, feat, tok, tgt, steps, marks=None):
+    import torch
+    for i in range(steps):
+        if marks is not None:
+            marks[i][0].record()
+        eng.draft_phase(feat, tok)
+        if marks is not None:
+            marks[i][1].record()
+        eng.verify(tgt, 0, i)
+        if marks is not None:
+            marks[i][2].record()
+
+
+def cpu_baseline(cfg, host):
+    """The fp64 oracle on one full round of the same workload (root head, every
+    draft step, expansions, rerank, verify), on the host cores."""
+    import numpy as np
+    from oracle import pipeline as OP
+    from workloads import TEMPLATES, make_target_noise
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    s = cfg.shape
+    kind = "dynamic" if cfg.tree == "dynamic" else "static"
+    t0 = time.perf_counter()
+    res = OP.draft_phase(s, host["w"], host["feat"], host["tok"], host["ks"], host["vs"], host["lens"], kind, cfg.topk,
+                         cfg.depth, cfg.rerank_m, TEMPLATES.get(cfg.tree), tree_wide=False)
+    t_draft = time.perf_counter() - t0
+    # target logits from the oracle's own tree-wide step (not timed), then verify (timed)
+    from oracle import draft as OD
+    B = cfg.batch
+    rows = {k: [] for k in ("seq", "token", "parent", "pos", "slot", "mask")}
+    for b in range(B):
+        tr, pool = res["trees"][b], res["pools"][b]
+        for t in range(1, len(tr["parent"])):
+            pid = int(tr["pool_id"][t])
+            rows["seq"].append(b)
+            rows["token"].append(int(tr["token"][t]))
+            rows["parent"].append(pool.feat_row[pool.parent[pid]])
+            rows["pos"].append(int(host["lens"][b]) + int(tr["depth"][t]) - 1)
+            rows["slot"].append(t)
+            rows["mask"].append(int(tr["mask"][t]))
+    tk, tv = OD.new_tree_kv(s, B)
+    tw = OD.draft_step(s, host["w"], rows, res["feat_buf"], host["ks"], host["vs"], host["lens"], tk, tv)["logits"]
+    N = len(res["trees"][0]["parent"])
+    noise = make_target_noise(cfg, B * N).reshape(B, N, -1)
+    targets = [np.concatenate([res["logits"][b:b + 1], tw[b * (N - 1):(b + 1) * (N - 1)] + noise[b, 1:]])
+               for b in range(B)]
+    qrow = [OP.q_rows(res, b) for b in range(B)]
+    t1 = time.perf_counter()
+    OP.verify_all(res["trees"], targets, res["logits"], qrow, 0, 0)
+    t_verify = time.perf_counter() - t1
+    drafted = B * (N - 1)
+    total = t_draft + t_verify
+    return {"value": drafted / total, "unit": "draft-tree nodes/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one full round of the same workload ({B} x {N - 1} drafted nodes: root head, every draft "
+                      f"step, expansions, rerank, verify) in fp64 numpy; draft {t_draft:.2f}s + verify "
+                      f"{t_verify:.2f}s"}
+
+
+def traffic_for(kernel_role: str, launches_per_step: float):
+    """HBM bytes per launch of the LM-head GEMM from the committed rocprofv3
+    counter summary, or None if it is missing or the GEMM source changed since."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        c = json.load(f)
+    with open(GEMM_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if c.get("gemm_source_sha256") != sha or c.get("role") != kernel_role:
+        return None
+    return c["fetch_kib_per_dispatch"] * 1024 * c["fetch_factor"] + c["write_kib_per_dispatch"] * 1024 * c["write_factor"]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload id (2 = 7B static-26, the bench line)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path here is single-GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4, "launches": 3}))
+        return
+    import eagle_feature_level_amd as E
+
+    cfg, eng, feat, tok, host = build_engine(args.config)
+    B, N = cfg.batch, eng.n_nodes
+    drafted = B * (N - 1)
+    # target logits resident in HBM before timing
+    eng.draft_phase(feat, tok)
+    tgt = synth_target(cfg, eng)
+    run_steps(eng, feat, tok, tgt, args.warmup)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    run_steps(eng, feat, tok, tgt, args.steps, marks)
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    ms_draft = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps
+    ms_verify = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps
+
+    # per-kernel durations: HIP events around every draft-step launch, same K steps again
+    E.eagle_profile_enable(args.steps * 200)
+    run_steps(eng, feat, tok, tgt, args.steps)
+    torch.cuda.synchronize()
+    kernels = {}
+    for role in E._abi.ROLES:
+        r = E.eagle_profile_read(role)
+        if r["launches"]:
+            kernels[role] = dict(launches_per_step=r["launches"] / args.steps,
+                                 avg_us=1e3 * r["ms"] / r["launches"],
+                                 gbs=r["bytes"] / (r["ms"] * 1e-3) / 1e9 if r["ms"] > 0 else None,
+                                 tflops=r["flops"] / (r["ms"] * 1e-3) / 1e12 if r["ms"] > 0 else None,
+                                 bytes_per_launch=r["bytes"] / r["launches"],
+                                 ms_per_step=r["ms"] / args.steps)
+    E.eagle_profile_disable()
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    kd = kernels[dom]
+    achieved = kd["gbs"]
+    traffic = traffic_for(dom, kd["launches_per_step"])
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
+                "avg_launch_us": round(kd["avg_us"], 2), "bytes_per_launch": round(kd["bytes_per_launch"])}
+    gemm_roles = ["fc", "qkv", "o", "gate_up", "down", "lm_head"]
+    g_ms = sum(kernels[r]["ms_per_step"] for r in gemm_roles if r in kernels)
+    g_bytes = sum(kernels[r]["bytes_per_launch"] * kernels[r]["launches_per_step"] for r in gemm_roles if r in kernels)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on one round ...")
+        cpu = cpu_baseline(cfg, host)
+
+    s = cfg.shape
+    out = {
+        "metric": "draft-tree nodes/sec + verify nodes/sec at 7B shape; % of MFMA/HBM roofline",
+        "value": round(drafted / (ms_step * 1e-3), 1),
+        "unit": "draft-tree nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "d": s.d, "heads": f"{s.n_heads}q/{s.n_kv_heads}kv x {s.head_dim}",
+                   "ffn": s.ffn, "vocab": s.vocab, "batch": B, "prefix": cfg.prefix[1], "tree": cfg.tree,
+                   "drafted_nodes_per_seq": N - 1, "global_batch": B, "seq_len": cfg.prefix[1],
+                   "parallelism": "single GPU"},
+        "draft_nodes_per_s": round(drafted / (ms_draft * 1e-3), 1),
+        "verify_nodes_per_s": round(B * N / (ms_verify * 1e-3), 1),
+        "ms_draft_phase": round(ms_draft, 4),
+        "ms_verify": round(ms_verify, 4),
+        "wall_s_timed": round(t_wall, 4),
+        "gemm_stream_gbs": round(g_bytes / (g_ms * 1e-3) / 1e9, 1) if g_ms else None,
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -18,7 +18,8 @@ from ._abi import (EAGLE_BF16, EAGLE_F32, EAGLE_HEAD_ONLY, EAGLE_MAX_SLOTS, EAGL
 __all__ = ["eagle_workspace_bytes", "eagle_draft_step", "eagle_softmax_topk", "eagle_tree_init", "eagle_tree_expand",
            "eagle_tree_finalize", "eagle_verify", "make_shape", "make_weights", "make_rows", "make_kv", "make_out",
            "make_pool", "EagleError", "EAGLE_HEAD_ONLY", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
-           "EAGLE_F32", "EAGLE_MAX_SLOTS", "EAGLE_MAX_TOPK"]
+           "EAGLE_F32", "EAGLE_MAX_SLOTS", "EAGLE_MAX_TOPK", "eagle_profile_enable", "eagle_profile_reset",
+           "eagle_profile_disable", "eagle_profile_read"]
 
 WEIGHT_NAMES = [f[0] for f in eagle_weights._fields_]
 
@@ -131,3 +132,27 @@ def eagle_verify(batch, n_nodes, vocab, tree_parent, tree_token, target_logits, 
                           _ptr(draft_logits), _ptr(draft_row), seed, round_, flags, _ptr(out_path),
                           _ptr(out_accept_len), _ptr(out_next_token), _ptr(out_flags), _stream(stream))
     _abi.check("eagle_verify", rc)
+
+
+def eagle_profile_enable(max_launches: int):
+    _abi.check("eagle_profile_enable", _abi.load().eagle_profile_enable(max_launches))
+
+
+def eagle_profile_reset():
+    _abi.check("eagle_profile_reset", _abi.load().eagle_profile_reset())
+
+
+def eagle_profile_disable():
+    _abi.check("eagle_profile_disable", _abi.load().eagle_profile_disable())
+
+
+def eagle_profile_read(role) -> dict:
+    """Launch count, summed duration (ms), algorithmic bytes and flops of one
+    kernel role ('lm_head', 'gate_up', ... or its index) since the last reset."""
+    if isinstance(role, str):
+        role = _abi.ROLES.index(role)
+    n = ctypes.c_int32()
+    ms, by, fl = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _abi.check("eagle_profile_read", _abi.load().eagle_profile_read(role, ctypes.byref(n), ctypes.byref(ms),
+                                                                      ctypes.byref(by), ctypes.byref(fl)))
+    return dict(launches=n.value, ms=ms.value, bytes=by.value, flops=fl.value)

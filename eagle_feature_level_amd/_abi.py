@@ -19,6 +19,7 @@ EAGLE_F32, EAGLE_BF16 = 0, 1
 EAGLE_HEAD_ONLY = 1
 EAGLE_VERIFY_GREEDY, EAGLE_VERIFY_IID = 1, 2
 EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK = 64, 16
+ROLES = ("fc", "qkv", "rope", "attn", "o", "gate_up", "down", "lm_head", "topk")
 
 
 class eagle_shape(ctypes.Structure):
@@ -64,6 +65,10 @@ _SIGS = {
                                     c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "eagle_verify": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_u64, c_u64, c_i32, c_vp, c_vp,
                              c_vp, c_vp, c_vp]),
+    "eagle_profile_enable": (c_i32, [c_i32]),
+    "eagle_profile_reset": (c_i32, []),
+    "eagle_profile_disable": (c_i32, []),
+    "eagle_profile_read": (c_i32, [c_i32, P(c_i32), P(ctypes.c_double), P(ctypes.c_double), P(ctypes.c_double)]),
     "eagle_strerror": (ctypes.c_char_p, [c_i32]),
     "eagle_last_hip_error": (c_i32, []),
 }

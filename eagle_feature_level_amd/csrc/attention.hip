@@ -8,8 +8,8 @@
 // Layout of the work: one workgroup per (key split, kv head, sequence).  All
 // query rows of that sequence and all query heads sharing the kv head read the
 // same K/V tiles, so each prefix K/V tile is fetched from HBM once per call and
-// staged in LDS (64 keys per tile).  Split 0 also handles the 64 tree slots as
-// one extra masked tile.  Each split writes (max, sum, unnormalised output)
+// staged in LDS (64 keys per tile).  The last split handles the 64 tree slots
+// as one masked tile.  Each split writes (max, sum, unnormalised output)
 // per query; attn_combine merges the splits with the usual log-sum-exp rule.
 // Inside a workgroup, lane j of each wave owns key j of the tile for the
 // scores; a wave owns a quarter of the query chunk, so the softmax statistics
@@ -121,9 +121,10 @@ __global__ void __launch_bounds__(256) attn_partial_kernel(AttnArgs a) {
   const int r0 = a.row_start[b], nr = a.row_start[b + 1] - r0;
   const int nq = nr * G;
   const int L = a.prefix_len[b];
-  const int kbeg = s * a.split_len;
-  const int kend = min(L, kbeg + a.split_len);
-  const bool do_tree = (s == 0);
+  // splits 0 .. n_splits-2 cover the prefix; the last split is the tree block
+  const bool do_tree = (s == a.n_splits - 1);
+  const int kbeg = do_tree ? 0 : s * a.split_len;
+  const int kend = do_tree ? 0 : min(L, kbeg + a.split_len);
   const T* pk = (const T*)a.prefix_k + a.prefix_off[b] + (size_t)g * L * HD;
   const T* pv = (const T*)a.prefix_v + a.prefix_off[b] + (size_t)g * L * HD;
   const T* tk = (const T*)a.tree_k + ((size_t)b * 64 * a.hkv + g) * HD;  // slot stride hkv*HD
@@ -257,22 +258,32 @@ __global__ void __launch_bounds__(256) attn_partial_kernel(AttnArgs a) {
 }
 
 // Merge split partials: out[row, h*hd + d] (fp32) = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
-__global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a, int hd) {
-  const int row = blockIdx.x;
-  for (int i = threadIdx.x; i < a.hq * hd; i += 256) {
-    const int h = i / hd, dd = i % hd;
+// One workgroup per (row, head); the split weights are computed once in LDS.
+__global__ void __launch_bounds__(128) attn_combine_kernel(AttnArgs a, int hd) {
+  __shared__ float wsplit[1024];
+  __shared__ float s_inv;
+  const int row = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const size_t stride = (size_t)a.n_rows * a.hq * (hd + 2);
+  const float* base = a.part + ((size_t)row * a.hq + h) * (hd + 2);
+  if (t < WAVE) {
     float M = -INFINITY;
-    for (int s = 0; s < a.n_splits; ++s)
-      M = fmaxf(M, a.part[(((size_t)s * a.n_rows + row) * a.hq + h) * (hd + 2)]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < a.n_splits; ++s) {
-      const float* p = a.part + (((size_t)s * a.n_rows + row) * a.hq + h) * (hd + 2);
-      if (p[0] == -INFINITY) continue;
-      const float w = __expf(p[0] - M);
-      L += w * p[1];
-      acc += w * p[2 + dd];
+    for (int s = t; s < a.n_splits; s += WAVE) M = fmaxf(M, base[s * stride]);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int s = t; s < a.n_splits; s += WAVE) {
+      const float m = base[s * stride];
+      const float w = (m == -INFINITY) ? 0.f : __expf(m - M);
+      wsplit[s] = w;
+      L += w * base[s * stride + 1];
     }
-    a.out[(size_t)row * a.hq * hd + i] = acc / L;
+    L = wave_sum(L);
+    if (t == 0) s_inv = 1.f / L;
+  }
+  __syncthreads();
+  for (int dd = t; dd < hd; dd += 128) {
+    float acc = 0.f;
+    for (int s = 0; s < a.n_splits; ++s) acc += wsplit[s] * base[s * stride + 2 + dd];
+    a.out[((size_t)row * a.hq + h) * hd + dd] = acc * s_inv;
   }
 }
 
@@ -301,12 +312,11 @@ int attn_split_len(int max_prefix, int batch, int hkv) {
   return split_len;
 }
 
-int attn_n_splits(int max_prefix, int split_len) {
-  const int n = (max_prefix + split_len - 1) / split_len;
-  return n < 1 ? 1 : n;
-}
+// prefix splits plus one split for the tree block
+int attn_n_splits(int max_prefix, int split_len) { return (max_prefix + split_len - 1) / split_len + 1; }
 
 hipError_t launch_attention(const AttnArgs& a, bool bf16, int hd, hipStream_t s) {
+  if (a.n_splits > 1024) return hipErrorInvalidValue;  // combine keeps one weight per split in LDS
   dim3 grid(a.n_splits, a.hkv, a.batch), blk(256);
   if (bf16) {
     if (hd != 128) return hipErrorInvalidValue;
@@ -323,6 +333,6 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, int hd, hipStream_t s)
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.n_rows), blk, 0, s, a, hd);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.n_rows, a.hq), dim3(128), 0, s, a, hd);
   return hipGetLastError();
 }

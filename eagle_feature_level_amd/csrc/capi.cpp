@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <vector>
+
 #include "../../include/eagle.h"
 #include "gemm.h"
 #include "kernels.h"
@@ -57,6 +59,33 @@ int shape_supported(const eagle_shape* s) {
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Measurement hook state (see eagle_profile_enable).
+struct ProfRec {
+  int role;
+  double bytes, flops;
+};
+struct Prof {
+  bool on = false;
+  std::vector<hipEvent_t> ev;  // 2 per launch
+  std::vector<ProfRec> rec;
+  size_t used = 0;
+};
+Prof g_prof;
+
+// Brackets one launch; returns the launch's error.
+template <typename F>
+hipError_t timed(hipStream_t st, int role, double bytes, double flops, F&& launch) {
+  const bool rec = g_prof.on && g_prof.used < g_prof.rec.size();
+  if (rec) hipEventRecord(g_prof.ev[2 * g_prof.used], st);
+  hipError_t e = launch();
+  if (rec) {
+    hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st);
+    g_prof.rec[g_prof.used] = ProfRec{role, bytes, flops};
+    ++g_prof.used;
+  }
+  return e;
+}
 
 struct DraftWs {
   int32_t* seq_of_row;
@@ -195,11 +224,19 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
   rc = check_device();
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
-  auto gemm = [&](GemmArgs a, int load, int epi, int* np) -> hipError_t {
+  const double wbytes = bf16 ? 2.0 : 4.0;
+  // algorithmic bytes of a GEMM launch: weights once, fp32 activations in and out
+  auto gemm = [&](GemmArgs a, int load, int epi, int* np, int role) -> hipError_t {
     int dummy = 0;
     a.part = ws.gemm_part;  // split-K partials of the tiled kernel
-    return bf16 ? launch_gemm_bf16(a, load, epi, np ? np : &dummy, st)
-                : launch_gemm_f32(a, load, epi, np ? np : &dummy, st);
+    const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
+    const double bytes = wbytes * a.N * a.K + 4.0 * a.M * ((load == LOAD_GATHER ? a.d : a.K) + nout) +
+                         (load == LOAD_GATHER ? wbytes * a.M * a.d : 0.0);
+    const double flops = 2.0 * a.M * a.N * a.K;
+    return timed(st, role, bytes, flops, [&] {
+      return bf16 ? launch_gemm_bf16(a, load, epi, np ? np : &dummy, st)
+                  : launch_gemm_f32(a, load, epi, np ? np : &dummy, st);
+    });
   };
   hipError_t e;
   const int d = s.d, hq = s.n_heads * s.head_dim, hkv = s.n_kv_heads * s.head_dim, F = s.ffn;
@@ -221,7 +258,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.y = ws.x;
       a.ldy = d;
       a.sumsq_out = ws.sumsq1;
-      e = gemm(a, LOAD_GATHER, EPI_BIAS_SUMSQ, &np1);
+      e = gemm(a, LOAD_GATHER, EPI_BIAS_SUMSQ, &np1, EAGLE_ROLE_FC);
       if (e != hipSuccess) return hip_fail(e);
     }
     // a3: RMSNorm -> [q; k; v]
@@ -240,7 +277,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.eps = s.rms_eps;
       a.y = ws.qkv;
       a.ldy = hq + 2 * hkv;
-      e = gemm(a, LOAD_F32_NORM, EPI_STORE, nullptr);
+      e = gemm(a, LOAD_F32_NORM, EPI_STORE, nullptr, EAGLE_ROLE_QKV);
       if (e != hipSuccess) return hip_fail(e);
     }
     // a4: RoPE at each row's position; k, v into the rows' tree slots
@@ -258,7 +295,8 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       r.hkv = s.n_kv_heads;
       r.hd = s.head_dim;
       r.theta = s.rope_theta;
-      e = launch_rope_kv(r, bf16, st);
+      e = timed(st, EAGLE_ROLE_ROPE, 4.0 * M * (hq + 2 * hkv) + 4.0 * M * hq + 2.0 * wbytes * M * hkv, 0.0,
+                [&] { return launch_rope_kv(r, bf16, st); });
       if (e != hipSuccess) return hip_fail(e);
     }
     // a5: tree attention
@@ -281,7 +319,10 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       at.hkv = s.n_kv_heads;
       at.split_len = attn_split_len(maxL, rows->batch, s.n_kv_heads);
       at.n_splits = attn_n_splits(maxL, at.split_len);
-      e = launch_attention(at, bf16, s.head_dim, st);
+      // bytes: each sequence's prefix K and V once, tree slots, q in, output out; flops 4*hd per (query, key)
+      const double kv_bytes = 2.0 * wbytes * s.n_kv_heads * s.head_dim * ((double)kv->max_prefix_len * rows->batch);
+      e = timed(st, EAGLE_ROLE_ATTN, kv_bytes + 8.0 * M * hq, 4.0 * M * s.n_heads * s.head_dim * kv->max_prefix_len,
+                [&] { return launch_attention(at, bf16, s.head_dim, st); });
       if (e != hipSuccess) return hip_fail(e);
     }
     // a6: h = x + attn wo^T, sum of squares for RMSNorm 2
@@ -295,7 +336,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.y = ws.h;
       a.ldy = d;
       a.sumsq_out = ws.sumsq2;
-      e = gemm(a, LOAD_F32, EPI_RESID_SUMSQ, &np2);
+      e = gemm(a, LOAD_F32, EPI_RESID_SUMSQ, &np2, EAGLE_ROLE_O);
       if (e != hipSuccess) return hip_fail(e);
     }
     // a7: RMSNorm -> SwiGLU
@@ -315,7 +356,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.yb = ws.act;
       a.ldyb = F;
       a.part = ws.gemm_part;
-      e = gemm(a, LOAD_F32_NORM, EPI_SWIGLU, nullptr);
+      e = gemm(a, LOAD_F32_NORM, EPI_SWIGLU, nullptr, EAGLE_ROLE_GATE_UP);
       if (e != hipSuccess) return hip_fail(e);
     }
     // f^ = h + act w_down^T
@@ -329,7 +370,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.y = out->feat;
       a.ldy = d;
       a.part = ws.gemm_part;
-      e = gemm(a, LOAD_F32, EPI_RESID, nullptr);
+      e = gemm(a, LOAD_F32, EPI_RESID, nullptr, EAGLE_ROLE_DOWN);
       if (e != hipSuccess) return hip_fail(e);
     }
   }
@@ -343,12 +384,67 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     a.y = out->logits;
     a.ldy = s.vocab;
     a.part = ws.gemm_part;
-    e = gemm(a, LOAD_F32, EPI_STORE, nullptr);
+    e = gemm(a, LOAD_F32, EPI_STORE, nullptr, EAGLE_ROLE_LM_HEAD);
     if (e != hipSuccess) return hip_fail(e);
   }
   // a9: softmax normaliser + top-k
-  e = launch_softmax_topk(M, s.vocab, out->logits, out->topk, out->lse, out->topk_idx, out->topk_logq, ws.topk, st);
+  e = timed(st, EAGLE_ROLE_TOPK, 4.0 * M * s.vocab, 0.0, [&] {
+    return launch_softmax_topk(M, s.vocab, out->logits, out->topk, out->lse, out->topk_idx, out->topk_logq, ws.topk,
+                               st);
+  });
   if (e != hipSuccess) return hip_fail(e);
+  return EAGLE_OK;
+}
+
+int eagle_profile_enable(int32_t max_launches) {
+  if (max_launches <= 0) return EAGLE_EINVAL;
+  eagle_profile_disable();
+  g_prof.ev.resize(2 * (size_t)max_launches);
+  for (auto& e : g_prof.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) return hip_fail(r);
+  }
+  g_prof.rec.assign(max_launches, ProfRec{0, 0.0, 0.0});
+  g_prof.used = 0;
+  g_prof.on = true;
+  return EAGLE_OK;
+}
+
+int eagle_profile_reset(void) {
+  g_prof.used = 0;
+  return EAGLE_OK;
+}
+
+int eagle_profile_disable(void) {
+  for (auto& e : g_prof.ev)
+    if (e) hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.rec.clear();
+  g_prof.used = 0;
+  g_prof.on = false;
+  return EAGLE_OK;
+}
+
+int eagle_profile_read(int32_t role, int32_t* launches, double* total_ms, double* bytes, double* flops) {
+  if (role < 0 || role >= EAGLE_ROLE_COUNT || !launches || !total_ms || !bytes || !flops) return EAGLE_EINVAL;
+  int n = 0;
+  double ms = 0.0, by = 0.0, fl = 0.0;
+  for (size_t i = 0; i < g_prof.used; ++i) {
+    if (g_prof.rec[i].role != role) continue;
+    hipError_t r = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+    if (r != hipSuccess) return hip_fail(r);
+    float t = 0.f;
+    r = hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+    if (r != hipSuccess) return hip_fail(r);
+    ++n;
+    ms += t;
+    by += g_prof.rec[i].bytes;
+    fl += g_prof.rec[i].flops;
+  }
+  *launches = n;
+  *total_ms = ms;
+  *bytes = by;
+  *flops = fl;
   return EAGLE_OK;
 }
 

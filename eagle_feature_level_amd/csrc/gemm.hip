@@ -50,6 +50,25 @@ __device__ __forceinline__ float row_scale(const GemmArgs& a, int m) {
   return 1.0f / sqrtf(s / (float)a.K + a.eps);
 }
 
+// RMSNorm scales of rows m_base .. m_base+BM-1 into LDS, all threads of the
+// workgroup cooperating: 32 lanes per row, each summing every 32nd partial,
+// then a fixed butterfly across the 32 lanes.  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void row_scales_lds(const GemmArgs& a, int m_base, int BM, float* scale) {
+  constexpr int ROWS = NT / 32;
+  const int t = threadIdx.x, c = t & 31;
+  for (int m0 = 0; m0 < BM; m0 += ROWS) {
+    const int mm = m0 + t / 32, m = m_base + mm;
+    float s = 0.f;
+    if (mm < BM && m < a.M)
+      for (int p = c; p < a.n_part_in; p += 32) s += a.sumsq_in[(size_t)p * a.M + m];
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, WAVE);
+    if (c == 0 && mm < BM) scale[mm] = (m < a.M) ? 1.0f / sqrtf(s / (float)a.K + a.eps) : 1.f;
+  }
+  __syncthreads();
+}
+
 // Eight bf16 operand values as (hi, lo) pairs.
 struct B8 {
   u32x4 hi, lo;
@@ -146,15 +165,23 @@ __global__ void __launch_bounds__(512) gemm_skinny(GemmArgs a) {
     const int n = tile_row<AT, EPI>(a, tile, at, r, &ok);
     ap[at] = wrow<bf16_t>(a, n) + g * 32;
   }
-  float rs[MT];
+  const int nks = a.K / SK_KSTEP;
+  u32x4 A0[AT][4], A1[AT][4], A2[AT][4];
+  auto loadA = [&](u32x4 (&dst)[AT][4], int ks) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + r;
-    rs[mt] = 1.f;
-    if constexpr (LOAD == LOAD_F32_NORM) {
-      if (m < a.M) rs[mt] = row_scale(a, m);
-    }
-  }
+    for (int at = 0; at < AT; ++at)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[at][j] = *(const u32x4*)(ap[at] + (size_t)ks * SK_KSTEP + j * 8);
+  };
+  // weights for the first two k-steps are in flight while the row scales are summed
+  if (wv < nks) loadA(A0, wv);
+  if (wv + SK_NW < nks) loadA(A1, wv + SK_NW);
+
+  __shared__ float scale[16 * MT];
+  float rs[MT];
+  if constexpr (LOAD == LOAD_F32_NORM) row_scales_lds<512>(a, 0, 16 * MT, scale);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) rs[mt] = (LOAD == LOAD_F32_NORM) ? scale[mt * 16 + r] : 1.f;
 
   floatx4 acc[AT][MT];
 #pragma unroll
@@ -162,14 +189,6 @@ __global__ void __launch_bounds__(512) gemm_skinny(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[at][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int nks = a.K / SK_KSTEP;
-  u32x4 A0[AT][4], A1[AT][4];
-  auto loadA = [&](u32x4 (&dst)[AT][4], int ks) {
-#pragma unroll
-    for (int at = 0; at < AT; ++at)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[at][j] = *(const u32x4*)(ap[at] + (size_t)ks * SK_KSTEP + j * 8);
-  };
   auto step = [&](const u32x4 (&A)[AT][4], int ks) {
     B8 B[MT][4];
 #pragma unroll
@@ -197,16 +216,16 @@ __global__ void __launch_bounds__(512) gemm_skinny(GemmArgs a) {
         }
   };
 
-  int ks = wv;
-  if (ks < nks) loadA(A0, ks);
-  for (; ks < nks; ks += 2 * SK_NW) {
-    const int k1 = ks + SK_NW;
-    if (k1 < nks) loadA(A1, k1);
+  // three register stages: two k-steps of weights in flight during each MFMA step
+  for (int ks = wv; ks < nks; ks += 3 * SK_NW) {
+    if (ks + 2 * SK_NW < nks) loadA(A2, ks + 2 * SK_NW);
     step(A0, ks);
-    if (k1 >= nks) break;
-    const int k2 = k1 + SK_NW;
-    if (k2 < nks) loadA(A0, k2);
-    step(A1, k1);
+    if (ks + SK_NW >= nks) break;
+    if (ks + 3 * SK_NW < nks) loadA(A0, ks + 3 * SK_NW);
+    step(A1, ks + SK_NW);
+    if (ks + 2 * SK_NW >= nks) break;
+    if (ks + 4 * SK_NW < nks) loadA(A1, ks + 4 * SK_NW);
+    step(A2, ks + 2 * SK_NW);
   }
 
   // Cross-wave reduction in a fixed order.
@@ -282,13 +301,7 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a, int logical_swiglu
   const int k_begin = blockIdx.y * kper;
   const int nkb = kper / TL_BK;
 
-  if constexpr (LOAD == LOAD_F32_NORM) {
-    for (int t = threadIdx.x; t < BM; t += 256) {
-      const int m = m_base + t;
-      scale[t] = (m < a.M) ? row_scale(a, m) : 1.f;
-    }
-    __syncthreads();
-  }
+  if constexpr (LOAD == LOAD_F32_NORM) row_scales_lds<256>(a, m_base, BM, scale);
 
   const bf16_t* ap[AT];
 #pragma unroll

@@ -108,6 +108,26 @@ __device__ int draw_token(const float (&w)[EPT], int vocab, float u, float* fred
   return -bmin_int(-last, ired);  // rounding left no boundary above T: last positive token
 }
 
+// Thread t's EPT consecutive entries of a row; -inf beyond the vocabulary.
+template <int EPT>
+__device__ __forceinline__ bool load_row(const float* row, int V, float (&v)[EPT]) {
+  const int y0 = threadIdx.x * EPT;
+  bool bad = false;
+  if (EPT % 4 == 0 && y0 + EPT <= V) {
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4) {
+      const float4 f = *(const float4*)(row + y0 + e);
+      v[e] = f.x; v[e + 1] = f.y; v[e + 2] = f.z; v[e + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) v[e] = (y0 + e < V) ? row[y0 + e] : -INFINITY;
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) bad |= (v[e] != v[e]);
+  return bad;
+}
+
 template <int EPT>
 __global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
   __shared__ float fred[NW];
@@ -115,7 +135,10 @@ __global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
   __shared__ int s_parent[64], s_token[64];
   __shared__ int kids[64];
   __shared__ int s_nk;
-  __shared__ float s_px, s_qx;
+  __shared__ float s_px, s_dx;
+  // draft logits of the current node, element e of thread t at dl[e * VT + t]
+  // (lanes on consecutive banks); removed tokens are set to -inf
+  __shared__ float dl[EPT * VT];
   const int b = blockIdx.x, t = threadIdx.x;
   const int N = a.n_nodes, V = a.vocab;
   if (t < N) {
@@ -125,29 +148,21 @@ __global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
   __syncthreads();
   const bool greedy = a.flags & 1, iid = a.flags & 2;
   int flags = 0, u = 0, nacc = 0, next_tok = 0;
-  float p[EPT], q[EPT];
+  float p[EPT];  // current target distribution (normalised)
+#define D(e) dl[(e) * VT + t]
 
   for (int level = 0; level <= N; ++level) {
     // target distribution at u
-    const float* trow = a.target + ((size_t)b * N + u) * V;
-    float tv[EPT];
-    bool bad = false;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int y = t * EPT + e;
-      tv[e] = (y < V) ? trow[y] : -INFINITY;
-      bad |= (tv[e] != tv[e]);
-    }
-    if (__syncthreads_or(bad)) flags |= 8;
+    if (__syncthreads_or(load_row<EPT>(a.target + ((size_t)b * N + u) * V, V, p))) flags |= 8;
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) mx = fmaxf(mx, tv[e]);
+    for (int e = 0; e < EPT; ++e) mx = fmaxf(mx, p[e]);
     mx = bmax(mx, fred);
     if (greedy) {
       int cand = 0x7fffffff;
 #pragma unroll
       for (int e = 0; e < EPT; ++e)
-        if (tv[e] == mx && cand == 0x7fffffff) cand = t * EPT + e;
+        if (p[e] == mx && cand == 0x7fffffff) cand = t * EPT + e;
       const int am = bmin_int(cand, ired);
 #pragma unroll
       for (int e = 0; e < EPT; ++e) p[e] = (t * EPT + e == am) ? 1.f : 0.f;
@@ -155,11 +170,10 @@ __global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
       float ls = 0.f;
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
-        p[e] = (tv[e] == -INFINITY) ? 0.f : __expf(tv[e] - mx);
+        p[e] = (p[e] == -INFINITY) ? 0.f : __expf(p[e] - mx);
         ls += p[e];
       }
-      const float Z = bsum(ls, fred);
-      const float inv = 1.f / Z;
+      const float inv = 1.f / bsum(ls, fred);
 #pragma unroll
       for (int e = 0; e < EPT; ++e) p[e] *= inv;
     }
@@ -176,38 +190,34 @@ __global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
       next_tok = draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired);
       break;
     }
-    // draft distribution at u
+    // draft distribution at u: q(y) = exp(d_y - dmx) / S over the tokens not removed
     const int drow_idx = a.draft_row[(size_t)b * N + u];
     if (drow_idx < 0) {  // no draft row for a node with children: invalid input
       flags |= 8;
       next_tok = draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired);
       break;
     }
-    const float* drow = a.draft + (size_t)drow_idx * V;
     float dmx = -INFINITY;
-    float dv[EPT];
+    {
+      float dv[EPT];
+      load_row<EPT>(a.draft + (size_t)drow_idx * V, V, dv);
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int y = t * EPT + e;
-      dv[e] = (y < V) ? drow[y] : -INFINITY;
-      dmx = fmaxf(dmx, dv[e]);
+      for (int e = 0; e < EPT; ++e) {
+        dmx = fmaxf(dmx, dv[e]);
+        D(e) = dv[e];
+      }
     }
     dmx = bmax(dmx, fred);
-    float ds = 0.f;
+    auto qmass = [&]() {
+      float ds = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      q[e] = (dv[e] == -INFINITY) ? 0.f : __expf(dv[e] - dmx);
-      ds += q[e];
-    }
-    {
-      const float inv = 1.f / bsum(ds, fred);
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) q[e] *= inv;
-    }
-    float qmass = 1.f;
+      for (int e = 0; e < EPT; ++e) ds += (D(e) == -INFINITY) ? 0.f : __expf(D(e) - dmx);
+      return bsum(ds, fred);
+    };
+    float S = qmass();
     int accepted = -1;
     for (int i = 0; i < nk; ++i) {
-      if (!(qmass > 0.f)) {
+      if (!(S > 0.f)) {
         flags |= 4;
         break;
       }
@@ -217,18 +227,16 @@ __global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
       const bool x_ok = x >= 0 && x < V;
       __syncthreads();
       if (x_ok && t == x / EPT) {
-        float px = 0.f, qx = 0.f;
+        float px = 0.f;
 #pragma unroll
         for (int e = 0; e < EPT; ++e)
-          if (e == x % EPT) {
-            px = p[e];
-            qx = q[e];
-          }
+          if (e == x % EPT) px = p[e];
         s_px = px;
-        s_qx = qx;
+        s_dx = D(x % EPT);
       }
       __syncthreads();
-      const float px = x_ok ? s_px : 0.f, qx = x_ok ? s_qx : 0.f;
+      const float px = x_ok ? s_px : 0.f;
+      const float qx = (x_ok && s_dx != -INFINITY) ? __expf(s_dx - dmx) / S : 0.f;
       bool ok;
       if (qx > 0.f) {
         ok = r < px / qx;
@@ -240,35 +248,29 @@ __global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
         accepted = c;
         break;
       }
-      // residual target
-      float rs = 0.f, res[EPT];
+      // residual target norm(max(0, p - q))
+      // (mass first, then the update, so a zero mass leaves p untouched)
+      const float invS = 1.f / S;
+      float rs = 0.f;
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
-        res[e] = fmaxf(0.f, p[e] - q[e]);
-        rs += res[e];
+        const float qy = (D(e) == -INFINITY) ? 0.f : __expf(D(e) - dmx) * invS;
+        rs += fmaxf(0.f, p[e] - qy);
       }
       const float Z = bsum(rs, fred);
       if (Z > 0.f) {
         const float inv = 1.f / Z;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) p[e] = res[e] * inv;
+        for (int e = 0; e < EPT; ++e) {
+          const float qy = (D(e) == -INFINITY) ? 0.f : __expf(D(e) - dmx) * invS;
+          p[e] = fmaxf(0.f, p[e] - qy) * inv;
+        }
       } else {
-        flags |= 1;
+        flags |= 1;  // zero residual mass (reachable only through rounding): keep p
       }
       if (!iid) {
-        float qs = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-          if (t * EPT + e == x) q[e] = 0.f;
-          qs += q[e];
-        }
-        const float S = bsum(qs, fred);
-        qmass = S;
-        if (S > 0.f) {
-          const float inv = 1.f / S;
-#pragma unroll
-          for (int e = 0; e < EPT; ++e) q[e] *= inv;
-        }
+        if (x_ok && t == x / EPT) D(x % EPT) = -INFINITY;
+        S = qmass();
       }
     }
     if (accepted < 0) {
@@ -279,6 +281,7 @@ __global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
     ++nacc;
     u = accepted;
   }
+#undef D
   if (t == 0) {
     for (int j = nacc; j < N; ++j) a.path[(size_t)b * N + j] = -1;
     a.accept_len[b] = nacc + 1;

@@ -253,6 +253,25 @@ int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t *t
                  uint64_t round, int32_t flags, int32_t *out_path, int32_t *out_accept_len, int32_t *out_next_token,
                  int32_t *out_flags, eagle_stream_t stream);
 
+/* Measurement hook.  While enabled, each kernel launch of eagle_draft_step is
+ * bracketed by a pair of HIP events recorded on the call's stream, tagged
+ * with its role and with the algorithmic bytes it must move (weights once,
+ * activations in and out) and flops.  The events are created by
+ * eagle_profile_enable (not during a call); recording stops silently once
+ * max_launches pairs are used.  eagle_profile_read synchronises on the
+ * recorded events and returns, for one role, the number of launches, their
+ * summed duration in ms, bytes and flops; eagle_profile_reset rewinds the
+ * recording without destroying the events.  Not thread-safe: one measuring
+ * thread per process. */
+enum {
+  EAGLE_ROLE_FC = 0, EAGLE_ROLE_QKV, EAGLE_ROLE_ROPE, EAGLE_ROLE_ATTN, EAGLE_ROLE_O, EAGLE_ROLE_GATE_UP,
+  EAGLE_ROLE_DOWN, EAGLE_ROLE_LM_HEAD, EAGLE_ROLE_TOPK, EAGLE_ROLE_COUNT
+};
+int eagle_profile_enable(int32_t max_launches);
+int eagle_profile_reset(void);
+int eagle_profile_disable(void);
+int eagle_profile_read(int32_t role, int32_t *launches, double *total_ms, double *bytes, double *flops);
+
 /* Message for an EAGLE_E* code. */
 const char *eagle_strerror(int code);
 /* hipError_t of the last EAGLE_EHIP on this thread. */
