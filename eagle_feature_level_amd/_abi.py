@@ -19,7 +19,7 @@ EAGLE_F32, EAGLE_BF16 = 0, 1
 EAGLE_HEAD_ONLY = 1
 EAGLE_VERIFY_GREEDY, EAGLE_VERIFY_IID = 1, 2
 EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK = 64, 16
-ROLES = ("fc", "qkv", "rope", "attn", "o", "gate_up", "down", "lm_head", "topk")
+ROLES = ("fc", "qkv", "rope", "attn", "o", "gate_up", "down", "lm_head", "topk", "rows")
 
 
 class eagle_shape(ctypes.Structure):

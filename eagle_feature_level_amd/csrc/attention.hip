@@ -89,18 +89,6 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(RopeArgs a) {
   for (int i = threadIdx.x; i < a.hkv * hd; i += blockDim.x) st1<T>(tv + i, vs[i]);
 }
 
-// Per-row sequence index from row_start (rows of a sequence are contiguous).
-__global__ void row_seq_kernel(const int32_t* row_start, int batch, int n_rows, int32_t* seq_of_row) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= n_rows) return;
-  int lo = 0, hi = batch - 1;
-  while (lo < hi) {  // last b with row_start[b] <= r
-    const int mid = (lo + hi + 1) / 2;
-    if (row_start[mid] <= r) lo = mid; else hi = mid - 1;
-  }
-  seq_of_row[r] = lo;
-}
-
 constexpr int KT = 64;  // keys per tile
 constexpr int QC = 16;  // queries per chunk (4 per wave)
 constexpr int QPW = QC / 4;
@@ -288,12 +276,6 @@ __global__ void __launch_bounds__(128) attn_combine_kernel(AttnArgs a, int hd) {
 }
 
 }  // namespace
-
-hipError_t launch_row_seq(const int32_t* row_start, int batch, int n_rows, int32_t* seq_of_row, hipStream_t s) {
-  hipLaunchKernelGGL(row_seq_kernel, dim3((n_rows + 255) / 256), dim3(256), 0, s, row_start, batch, n_rows,
-                     seq_of_row);
-  return hipGetLastError();
-}
 
 hipError_t launch_rope_kv(const RopeArgs& a, bool bf16, hipStream_t s) {
   if (bf16)

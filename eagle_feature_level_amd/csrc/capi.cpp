@@ -89,6 +89,7 @@ hipError_t timed(hipStream_t st, int role, double bytes, double flops, F&& launc
 
 struct DraftWs {
   int32_t* seq_of_row;
+  float* xin;  // [f_parent ; e(token)], 2d per row
   float* x;
   float* sumsq1;
   float* qkv;
@@ -127,6 +128,7 @@ DraftWs carve(const eagle_shape* s, int M, int B, int max_prefix, char* base) {
     return (void*)p;
   };
   w.seq_of_row = (int32_t*)take((size_t)M * 4);
+  w.xin = (float*)take((size_t)M * 2 * s->d * 4);
   w.x = (float*)take((size_t)M * s->d * 4);
   w.sumsq1 = (float*)take((size_t)npart * M * 4);
   w.qkv = (float*)take((size_t)M * nqkv * 4);
@@ -230,8 +232,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     int dummy = 0;
     a.part = ws.gemm_part;  // split-K partials of the tiled kernel
     const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
-    const double bytes = wbytes * a.N * a.K + 4.0 * a.M * ((load == LOAD_GATHER ? a.d : a.K) + nout) +
-                         (load == LOAD_GATHER ? wbytes * a.M * a.d : 0.0);
+    const double bytes = wbytes * a.N * a.K + 4.0 * a.M * (a.K + nout);
     const double flops = 2.0 * a.M * a.N * a.K;
     return timed(st, role, bytes, flops, [&] {
       return bf16 ? launch_gemm_bf16(a, load, epi, np ? np : &dummy, st)
@@ -242,23 +243,36 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
   const int d = s.d, hq = s.n_heads * s.head_dim, hkv = s.n_kv_heads * s.head_dim, F = s.ffn;
 
   if (!head_only) {
-    e = launch_row_seq(rows->row_start, rows->batch, M, ws.seq_of_row, st);
-    if (e != hipSuccess) return hip_fail(e);
-    // a1, a2: [f_parent ; e(token)] -> FC (+bias) = x, sum of squares for RMSNorm 1
+    // a1: the rows' inputs [f_parent ; e(token)] and sequence indices
+    {
+      RowSetupArgs r;
+      r.row_start = rows->row_start;
+      r.batch = rows->batch;
+      r.n_rows = M;
+      r.seq_of_row = ws.seq_of_row;
+      r.parent = rows->parent;
+      r.token = rows->token;
+      r.feat = feat_in;
+      r.embed = w->embed;
+      r.d = d;
+      r.xin = ws.xin;
+      // bytes: the gathered feature and embedding rows in, the concatenation out
+      e = timed(st, EAGLE_ROLE_ROWS, 4.0 * M * d + wbytes * M * d + 8.0 * M * d, 0.0,
+                [&] { return launch_row_setup(r, bf16, st); });
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    // a2: FC (+bias) = x, sum of squares for RMSNorm 1
     int np1 = 0, np2 = 0;
     {
       GemmArgs a = gemm_base(M, d, 2 * d);
       a.w0 = w->fc_w;
-      a.feat = feat_in;
-      a.parent = rows->parent;
-      a.embed = w->embed;
-      a.token = rows->token;
-      a.d = d;
+      a.x = ws.xin;
+      a.ldx = 2 * d;
       a.bias = w->fc_b;
       a.y = ws.x;
       a.ldy = d;
       a.sumsq_out = ws.sumsq1;
-      e = gemm(a, LOAD_GATHER, EPI_BIAS_SUMSQ, &np1, EAGLE_ROLE_FC);
+      e = gemm(a, LOAD_F32, EPI_BIAS_SUMSQ, &np1, EAGLE_ROLE_FC);
       if (e != hipSuccess) return hip_fail(e);
     }
     // a3: RMSNorm -> [q; k; v]

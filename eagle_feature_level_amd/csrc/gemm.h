@@ -1,14 +1,13 @@
 // Internal interface of the draft-head GEMMs: y = x W^T with fused operand
-// loaders (gather/concat, RMSNorm, fp32->bf16) and epilogues (bias, residual,
-// SwiGLU, per-tile sums of squares for the next RMSNorm).
+// loaders (row gather, RMSNorm, fp32 -> bf16 hi/lo) and epilogues (bias,
+// residual, SwiGLU, per-tile sums of squares for the next RMSNorm).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 enum GemmLoad {
   LOAD_F32 = 1,       // x fp32 [M, K] (ldx), optional row gather xrows[m]
-  LOAD_F32_NORM = 2,  // x fp32 * rsqrt(mean(x^2)+eps) * gain[k]; mean from sumsq partials
-  LOAD_GATHER = 3     // [feat[parent[m]] ; embed[token[m]]], K = 2d
+  LOAD_F32_NORM = 2   // x fp32 * rsqrt(mean(x^2)+eps) * gain[k]; mean from sumsq partials
 };
 enum GemmEpi {
   EPI_STORE = 0,        // y = acc
@@ -29,11 +28,6 @@ struct GemmArgs {
   const void* x;
   int ldx;
   const int32_t* xrows;
-  const float* feat;
-  const int32_t* parent;
-  const void* embed;
-  const int32_t* token;
-  int d;
   const float* sumsq_in;  // [n_part_in][M]
   int n_part_in;
   const void* gain;
@@ -54,8 +48,9 @@ struct GemmArgs {
 };
 
 // Launch helpers (host).  Return hipSuccess or the launch error.
-// bf16 path: chooses the skinny (M <= 32) or tiled kernel.  `ws`/`ws_bytes`
-// holds split-K partials.  Sets args.n_part_out through *n_part_out.
+// bf16 path: chooses the skinny (M <= 16) or tiled kernel; args.part holds
+// the tiled kernel's split-K partials.  Sum-of-squares epilogues store their
+// number of partial tiles in *n_part_out.
 hipError_t launch_gemm_bf16(GemmArgs a, int load, int epi, int* n_part_out, hipStream_t s);
 hipError_t launch_gemm_f32(GemmArgs a, int load, int epi, int* n_part_out, hipStream_t s);
 size_t gemm_bf16_partial_bytes(int M, int N, int K);

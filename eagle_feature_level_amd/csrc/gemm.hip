@@ -6,15 +6,17 @@
 //  * W (bf16) is the MFMA "A" operand and goes straight from HBM to VGPRs, each
 //    lane pulling 32-64 contiguous bytes of a row per step; W is never staged
 //    through LDS because every W element is used by exactly one wave.
-//  * x is the MFMA "B" operand (M padded to 16).  The skinny kernel (M <= 32)
+//  * x is the MFMA "B" operand (M padded to 16).  The skinny kernel (M <= 16)
 //    reads it straight from L2; the tiled kernel stages it through LDS so the
 //    waves of a workgroup share it.
 //  * Activations are fp32 and enter the matrix units as a pair of bf16 values,
 //    hi = bf16(x) and lo = bf16(x - hi), two MFMAs into one fp32 accumulator:
 //    the product then carries ~16 significant bits of x instead of 8, which
 //    keeps a whole draft step within ~1e-3 of an fp64 evaluation.  Weights are
-//    exact bf16.  In the HBM-bound regime the second MFMA costs nothing; the
-//    embedding half of the FC input is exact bf16 and skips it.
+//    exact bf16.  In the HBM-bound regime the second MFMA costs nothing, so
+//    both MFMAs always run: no MFMA sits under a data-dependent branch (the
+//    compiler may drop the execz skip around a short block, and an MFMA does
+//    not honour an all-zero EXEC).
 //  * Since the MFMA sums over k, any permutation of k is fine as long as A and
 //    B agree: a lane's 8-element group for MFMA j is taken from a contiguous
 //    run of 32 (skinny) or 16 (tiled) elements, so the weight loads are wide.
@@ -93,40 +95,21 @@ __device__ __forceinline__ B8 split8(float4 v0, float4 v1) {
 // Eight operand values of row m at columns k..k+7 (k % 8 == 0) as (hi, lo).
 template <int LOAD>
 __device__ __forceinline__ B8 load_b8(const GemmArgs& a, int m, int k, float rs) {
-  if constexpr (LOAD == LOAD_GATHER) {
-    if (k < a.d) {
-      const float4* p = (const float4*)(a.feat + (size_t)a.parent[m] * a.d + k);
-      return split8(p[0], p[1]);
-    }
-    B8 r;
-    r.hi = *(const u32x4*)((const bf16_t*)a.embed + (size_t)a.token[m] * a.d + (k - a.d));
-    r.lo = u32x4{0, 0, 0, 0};
-    return r;
-  } else {
-    const int row = a.xrows ? a.xrows[m] : m;
-    const float4* p = (const float4*)((const float*)a.x + (size_t)row * a.ldx + k);
-    float4 v0 = p[0], v1 = p[1];
-    if constexpr (LOAD == LOAD_F32_NORM) {
-      u32x4 gv = *(const u32x4*)((const bf16_t*)a.gain + k);
-      float gs[8];
+  const int row = a.xrows ? a.xrows[m] : m;
+  const float4* p = (const float4*)((const float*)a.x + (size_t)row * a.ldx + k);
+  float4 v0 = p[0], v1 = p[1];
+  if constexpr (LOAD == LOAD_F32_NORM) {
+    u32x4 gv = *(const u32x4*)((const bf16_t*)a.gain + k);
+    float gs[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        gs[2 * i] = __uint_as_float(gv[i] << 16);
-        gs[2 * i + 1] = __uint_as_float(gv[i] & 0xffff0000u);
-      }
-      v0.x *= rs * gs[0]; v0.y *= rs * gs[1]; v0.z *= rs * gs[2]; v0.w *= rs * gs[3];
-      v1.x *= rs * gs[4]; v1.y *= rs * gs[5]; v1.z *= rs * gs[6]; v1.w *= rs * gs[7];
+    for (int i = 0; i < 4; ++i) {
+      gs[2 * i] = __uint_as_float(gv[i] << 16);
+      gs[2 * i + 1] = __uint_as_float(gv[i] & 0xffff0000u);
     }
-    return split8(v0, v1);
+    v0.x *= rs * gs[0]; v0.y *= rs * gs[1]; v0.z *= rs * gs[2]; v0.w *= rs * gs[3];
+    v1.x *= rs * gs[4]; v1.y *= rs * gs[5]; v1.z *= rs * gs[6]; v1.w *= rs * gs[7];
   }
-}
-
-// Does the k-block starting at k carry a nonzero lo half?  Only the embedding
-// half of the gathered FC input is exact bf16.
-template <int LOAD>
-__device__ __forceinline__ bool has_lo(const GemmArgs& a, int k) {
-  if constexpr (LOAD == LOAD_GATHER) return k < a.d;
-  return true;
+  return split8(v0, v1);
 }
 
 __device__ __forceinline__ floatx4 mfma16(u32x4 a, u32x4 b, floatx4 c) {
@@ -150,10 +133,23 @@ __device__ __forceinline__ int tile_row(const GemmArgs& a, int tile, int at, int
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel: M <= 16*MT, one workgroup = 16*AT weight rows, 8 waves split K.
+// Skinny kernel: M <= 16*MT, one workgroup = 16*AT weight rows, NW waves split K.
+// Vector-memory loads complete in issue order, so the activations of a k-step
+// are loaded in the same register stage as its weights: waiting for a stage
+// never waits for a later prefetch.  Three stages, two in flight.
 // ---------------------------------------------------------------------------
-template <int AT, int MT, int LOAD, int EPI>
-__global__ void __launch_bounds__(512) gemm_skinny(GemmArgs a) {
+template <int AT, int MT, int LOAD>
+struct SkStage {
+  u32x4 A[AT][4];    // weight fragments
+  u32x4 X[MT][8];    // raw fp32 activation bits
+};
+
+__device__ __forceinline__ float4 as_f4(u32x4 v) {
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+
+template <int AT, int MT, int NW, int LOAD, int EPI>
+__global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int tile = blockIdx.x;
@@ -165,21 +161,41 @@ __global__ void __launch_bounds__(512) gemm_skinny(GemmArgs a) {
     const int n = tile_row<AT, EPI>(a, tile, at, r, &ok);
     ap[at] = wrow<bf16_t>(a, n) + g * 32;
   }
+  // per-lane activation rows (rows >= M clamped to a valid row, zeroed at use)
+  const float* xp[MT];
+  bool mv[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + r;
+    mv[mt] = m < a.M;
+    const int mm = mv[mt] ? m : 0;
+    const int row = a.xrows ? a.xrows[mm] : mm;
+    xp[mt] = (const float*)a.x + (size_t)row * a.ldx + g * 32;
+  }
   const int nks = a.K / SK_KSTEP;
-  u32x4 A0[AT][4], A1[AT][4], A2[AT][4];
-  auto loadA = [&](u32x4 (&dst)[AT][4], int ks) {
+  SkStage<AT, MT, LOAD> S0, S1, S2;
+  auto issue = [&](SkStage<AT, MT, LOAD>& st, int ks) {
 #pragma unroll
     for (int at = 0; at < AT; ++at)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[at][j] = *(const u32x4*)(ap[at] + (size_t)ks * SK_KSTEP + j * 8);
+      for (int j = 0; j < 4; ++j) st.A[at][j] = *(const u32x4*)(ap[at] + (size_t)ks * SK_KSTEP + j * 8);
+    const int k0 = ks * SK_KSTEP;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) st.X[mt][q] = *(const u32x4*)(xp[mt] + k0 + q * 4);
   };
-  // weights for the first two k-steps are in flight while the row scales are summed
-  if (wv < nks) loadA(A0, wv);
-  if (wv + SK_NW < nks) loadA(A1, wv + SK_NW);
+  if (wv < nks) issue(S0, wv);
+  if (wv + NW < nks) issue(S1, wv + NW);
 
+  // RMSNorm row scales and gains (LDS), summed while the first stages are in flight
   __shared__ float scale[16 * MT];
+  __shared__ float gain_s[LOAD == LOAD_F32_NORM ? 8192 : 1];
   float rs[MT];
-  if constexpr (LOAD == LOAD_F32_NORM) row_scales_lds<512>(a, 0, 16 * MT, scale);
+  if constexpr (LOAD == LOAD_F32_NORM) {
+    for (int k = threadIdx.x; k < a.K; k += NW * 64) gain_s[k] = bf2f(((const bf16_t*)a.gain)[k]);
+    row_scales_lds<NW * 64>(a, 0, 16 * MT, scale);
+  }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) rs[mt] = (LOAD == LOAD_F32_NORM) ? scale[mt * 16 + r] : 1.f;
 
@@ -189,49 +205,51 @@ __global__ void __launch_bounds__(512) gemm_skinny(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[at][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](const u32x4 (&A)[AT][4], int ks) {
-    B8 B[MT][4];
+  auto step = [&](const SkStage<AT, MT, LOAD>& st, int ks) {
+    const int k0 = ks * SK_KSTEP;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + r;
+    for (int j = 0; j < 4; ++j) {
+      B8 B[MT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (m < a.M) {
-          B[mt][j] = load_b8<LOAD>(a, m, ks * SK_KSTEP + g * 32 + j * 8, rs[mt]);
-        } else {
-          B[mt][j].hi = u32x4{0, 0, 0, 0};
-          B[mt][j].lo = u32x4{0, 0, 0, 0};
+      for (int mt = 0; mt < MT; ++mt) {
+        float4 v0 = as_f4(st.X[mt][2 * j]), v1 = as_f4(st.X[mt][2 * j + 1]);
+        if constexpr (LOAD == LOAD_F32_NORM) {
+          const float* gs = &gain_s[k0 + g * 32 + j * 8];
+          const float s0 = rs[mt];
+          v0.x *= s0 * gs[0]; v0.y *= s0 * gs[1]; v0.z *= s0 * gs[2]; v0.w *= s0 * gs[3];
+          v1.x *= s0 * gs[4]; v1.y *= s0 * gs[5]; v1.z *= s0 * gs[6]; v1.w *= s0 * gs[7];
+        }
+        B[mt] = split8(v0, v1);
+        if (!mv[mt]) {
+          B[mt].hi = u32x4{0, 0, 0, 0};
+          B[mt].lo = u32x4{0, 0, 0, 0};
         }
       }
-    }
-    const bool lo = has_lo<LOAD>(a, ks * SK_KSTEP);  // uniform across the wave
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int at = 0; at < AT; ++at)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          acc[at][mt] = mfma16(A[at][j], B[mt][j].hi, acc[at][mt]);
-          if (lo) acc[at][mt] = mfma16(A[at][j], B[mt][j].lo, acc[at][mt]);
+          acc[at][mt] = mfma16(st.A[at][j], B[mt].hi, acc[at][mt]);
+          acc[at][mt] = mfma16(st.A[at][j], B[mt].lo, acc[at][mt]);
         }
+    }
   };
 
-  // three register stages: two k-steps of weights in flight during each MFMA step
-  for (int ks = wv; ks < nks; ks += 3 * SK_NW) {
-    if (ks + 2 * SK_NW < nks) loadA(A2, ks + 2 * SK_NW);
-    step(A0, ks);
-    if (ks + SK_NW >= nks) break;
-    if (ks + 3 * SK_NW < nks) loadA(A0, ks + 3 * SK_NW);
-    step(A1, ks + SK_NW);
-    if (ks + 2 * SK_NW >= nks) break;
-    if (ks + 4 * SK_NW < nks) loadA(A1, ks + 4 * SK_NW);
-    step(A2, ks + 2 * SK_NW);
+  for (int ks = wv; ks < nks; ks += 3 * NW) {
+    if (ks + 2 * NW < nks) issue(S2, ks + 2 * NW);
+    step(S0, ks);
+    if (ks + NW >= nks) break;
+    if (ks + 3 * NW < nks) issue(S0, ks + 3 * NW);
+    step(S1, ks + NW);
+    if (ks + 2 * NW >= nks) break;
+    if (ks + 4 * NW < nks) issue(S1, ks + 4 * NW);
+    step(S2, ks + 2 * NW);
   }
 
   // Cross-wave reduction in a fixed order.
   constexpr int BN = 16 * AT;
   constexpr int BM = 16 * MT;
-  __shared__ float red[SK_NW][BM][BN + 4];
+  __shared__ float red[NW][BM][BN + 4];
 #pragma unroll
   for (int at = 0; at < AT; ++at)
 #pragma unroll
@@ -242,13 +260,13 @@ __global__ void __launch_bounds__(512) gemm_skinny(GemmArgs a) {
 
   if constexpr (EPI == EPI_SWIGLU) {
     constexpr int H = BN / 2;
-    for (int e = threadIdx.x; e < BM * H; e += 512) {
+    for (int e = threadIdx.x; e < BM * H; e += NW * 64) {
       const int m = e / H, jl = e % H;
       const int j = tile * H + jl;
       if (m < a.M && j < a.ffn) {
         float gs = 0.f, us = 0.f;
 #pragma unroll
-        for (int w = 0; w < SK_NW; ++w) {
+        for (int w = 0; w < NW; ++w) {
           gs += red[w][m][jl];
           us += red[w][m][jl + H];
         }
@@ -257,7 +275,7 @@ __global__ void __launch_bounds__(512) gemm_skinny(GemmArgs a) {
     }
   } else {
     constexpr int ELEMS = BM * BN;
-    for (int e0 = 0; e0 < ELEMS; e0 += 512) {
+    for (int e0 = 0; e0 < ELEMS; e0 += NW * 64) {
       const int e = e0 + threadIdx.x;
       const bool act = e < ELEMS;
       const int m = act ? e / BN : 0, nl = act ? e % BN : 0;
@@ -266,7 +284,7 @@ __global__ void __launch_bounds__(512) gemm_skinny(GemmArgs a) {
       float y = 0.f;
       if (live) {
 #pragma unroll
-        for (int w = 0; w < SK_NW; ++w) y += red[w][m][nl];
+        for (int w = 0; w < NW; ++w) y += red[w][m][nl];
         if constexpr (EPI == EPI_BIAS_SUMSQ) y += bf2f(((const bf16_t*)a.bias)[n]);
         if constexpr (EPI == EPI_RESID || EPI == EPI_RESID_SUMSQ) y += a.resid[(size_t)m * a.ldr + n];
         a.y[(size_t)m * a.ldy + n] = y;
@@ -352,7 +370,7 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a, int logical_swiglu
 #pragma unroll
       for (int j = 0; j < 2; ++j) dst[at][j] = *(const u32x4*)(ap[at] + (size_t)kb * TL_BK + j * 8);
   };
-  auto compute = [&](const u32x4 (&A)[AT][2], int buf, bool lo) {
+  auto compute = [&](const u32x4 (&A)[AT][2], int buf) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       u32x4 B[MT];
@@ -362,14 +380,12 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a, int logical_swiglu
       for (int at = 0; at < AT; ++at)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[at][mt] = mfma16(A[at][j], B[mt], acc[at][mt]);
-      if (lo) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) B[mt] = *(const u32x4*)&xl[buf][mt * 16 + r][g * 16 + j * 8];
+      for (int mt = 0; mt < MT; ++mt) B[mt] = *(const u32x4*)&xl[buf][mt * 16 + r][g * 16 + j * 8];
 #pragma unroll
-        for (int at = 0; at < AT; ++at)
+      for (int at = 0; at < AT; ++at)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[at][mt] = mfma16(A[at][j], B[mt], acc[at][mt]);
-      }
+        for (int mt = 0; mt < MT; ++mt) acc[at][mt] = mfma16(A[at][j], B[mt], acc[at][mt]);
     }
   };
 
@@ -382,7 +398,7 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a, int logical_swiglu
       loadA(A1, kb + 1);
       load_x(kb + 1);
     }
-    compute(A0, 0, has_lo<LOAD>(a, k_begin + kb * TL_BK));
+    compute(A0, 0);
     if (kb + 1 < nkb) store_x(1);
     __syncthreads();
     if (kb + 1 >= nkb) break;
@@ -390,7 +406,7 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a, int logical_swiglu
       loadA(A0, kb + 2);
       load_x(kb + 2);
     }
-    compute(A1, 1, has_lo<LOAD>(a, k_begin + (kb + 1) * TL_BK));
+    compute(A1, 1);
     if (kb + 2 < nkb) store_x(0);
     __syncthreads();
   }
@@ -455,15 +471,10 @@ __global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a) {
 // ---------------------------------------------------------------------------
 template <int LOAD>
 __device__ __forceinline__ float load_x1(const GemmArgs& a, int m, int k, float rs) {
-  if constexpr (LOAD == LOAD_GATHER) {
-    if (k < a.d) return a.feat[(size_t)a.parent[m] * a.d + k];
-    return ((const float*)a.embed)[(size_t)a.token[m] * a.d + (k - a.d)];
-  } else {
-    const int row = (LOAD == LOAD_F32 && a.xrows) ? a.xrows[m] : m;
-    float v = ((const float*)a.x)[(size_t)row * a.ldx + k];
-    if constexpr (LOAD == LOAD_F32_NORM) v *= rs * ((const float*)a.gain)[k];
-    return v;
-  }
+  const int row = (LOAD == LOAD_F32 && a.xrows) ? a.xrows[m] : m;
+  float v = ((const float*)a.x)[(size_t)row * a.ldx + k];
+  if constexpr (LOAD == LOAD_F32_NORM) v *= rs * ((const float*)a.gain)[k];
+  return v;
 }
 
 template <int LOAD, int EPI>
@@ -503,45 +514,52 @@ __global__ void __launch_bounds__(64) gemm_f32(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
-template <int AT, int MT, int LOAD>
+template <int AT, int MT, int NW, int LOAD>
 hipError_t skinny_epi(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
   const int BN = 16 * AT;
-  dim3 blk(512);
+  dim3 blk(NW * 64);
+  const dim3 grid((a.N + BN - 1) / BN);
   switch (epi) {
-    case EPI_STORE:
-      hipLaunchKernelGGL((gemm_skinny<AT, MT, LOAD, EPI_STORE>), dim3((a.N + BN - 1) / BN), blk, 0, s, a);
-      break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<AT, MT, NW, LOAD, EPI_STORE>), grid, blk, 0, s, a); break;
     case EPI_BIAS_SUMSQ:
-      hipLaunchKernelGGL((gemm_skinny<AT, MT, LOAD, EPI_BIAS_SUMSQ>), dim3((a.N + BN - 1) / BN), blk, 0, s, a);
-      *n_part = (a.N + BN - 1) / BN;
+      hipLaunchKernelGGL((gemm_skinny<AT, MT, NW, LOAD, EPI_BIAS_SUMSQ>), grid, blk, 0, s, a);
+      *n_part = grid.x;
       break;
-    case EPI_RESID:
-      hipLaunchKernelGGL((gemm_skinny<AT, MT, LOAD, EPI_RESID>), dim3((a.N + BN - 1) / BN), blk, 0, s, a);
-      break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<AT, MT, NW, LOAD, EPI_RESID>), grid, blk, 0, s, a); break;
     case EPI_RESID_SUMSQ:
-      hipLaunchKernelGGL((gemm_skinny<AT, MT, LOAD, EPI_RESID_SUMSQ>), dim3((a.N + BN - 1) / BN), blk, 0, s, a);
-      *n_part = (a.N + BN - 1) / BN;
+      hipLaunchKernelGGL((gemm_skinny<AT, MT, NW, LOAD, EPI_RESID_SUMSQ>), grid, blk, 0, s, a);
+      *n_part = grid.x;
       break;
-    case EPI_SWIGLU: {
-      const int H = BN / 2;
-      hipLaunchKernelGGL((gemm_skinny<AT, MT, LOAD, EPI_SWIGLU>), dim3((a.ffn + H - 1) / H), blk, 0, s, a);
-      break;
-    }
+    case EPI_SWIGLU:
+      if constexpr (AT >= 2) {  // gate and up tiles pair up inside a workgroup
+        const int H = BN / 2;
+        hipLaunchKernelGGL((gemm_skinny<AT, MT, NW, LOAD, EPI_SWIGLU>), dim3((a.ffn + H - 1) / H), blk, 0, s, a);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// Four weight tiles x four waves when that still gives >= ~500 workgroups,
+// else one tile x eight waves (K split 8 ways inside the workgroup).
+template <int MT, int LOAD>
+hipError_t skinny_shape(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
+  const int rows = (epi == EPI_SWIGLU) ? 2 * a.ffn : a.N;
+  if (rows / 64 >= 384) return skinny_epi<4, MT, 4, LOAD>(a, epi, n_part, s);
+  if (epi == EPI_SWIGLU) return skinny_epi<2, MT, 8, LOAD>(a, epi, n_part, s);
+  return skinny_epi<1, MT, 8, LOAD>(a, epi, n_part, s);
+}
+
 template <int MT>
 hipError_t skinny_load(const GemmArgs& a, int load, int epi, int* n_part, hipStream_t s) {
-  // Two weight tiles per workgroup when that still gives >= ~2 workgroups per CU.
-  const int nt2 = (epi == EPI_SWIGLU) ? a.ffn / 16 : a.N / 32;
-  const bool at2 = nt2 >= 512 || epi == EPI_SWIGLU;
+  if (load == LOAD_F32_NORM && a.K > 8192) return hipErrorInvalidValue;  // gains staged in LDS
   switch (load) {
-    case LOAD_F32: return at2 ? skinny_epi<2, MT, LOAD_F32>(a, epi, n_part, s) : skinny_epi<1, MT, LOAD_F32>(a, epi, n_part, s);
-    case LOAD_F32_NORM: return at2 ? skinny_epi<2, MT, LOAD_F32_NORM>(a, epi, n_part, s) : skinny_epi<1, MT, LOAD_F32_NORM>(a, epi, n_part, s);
-    case LOAD_GATHER: return at2 ? skinny_epi<2, MT, LOAD_GATHER>(a, epi, n_part, s) : skinny_epi<1, MT, LOAD_GATHER>(a, epi, n_part, s);
+    case LOAD_F32: return skinny_shape<MT, LOAD_F32>(a, epi, n_part, s);
+    case LOAD_F32_NORM: return skinny_shape<MT, LOAD_F32_NORM>(a, epi, n_part, s);
   }
   return hipErrorInvalidValue;
 }
@@ -575,7 +593,6 @@ hipError_t tiled_launch(const GemmArgs& a, int load, const TiledPlan& p, hipStre
   switch (load) {
     case LOAD_F32: hipLaunchKernelGGL((gemm_tiled<2, MT, LOAD_F32>), grid, blk, 0, s, a, 0); break;
     case LOAD_F32_NORM: hipLaunchKernelGGL((gemm_tiled<2, MT, LOAD_F32_NORM>), grid, blk, 0, s, a, 0); break;
-    case LOAD_GATHER: hipLaunchKernelGGL((gemm_tiled<2, MT, LOAD_GATHER>), grid, blk, 0, s, a, 0); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -584,7 +601,7 @@ hipError_t tiled_launch(const GemmArgs& a, int load, const TiledPlan& p, hipStre
 }  // namespace
 
 size_t gemm_bf16_partial_bytes(int M, int N, int K) {
-  if (M <= 32) return 0;
+  if (M <= 16) return 0;
   TiledPlan p = plan_tiled(M, N, K);
   return (size_t)p.splits * M * N * sizeof(float);
 }
@@ -592,7 +609,6 @@ size_t gemm_bf16_partial_bytes(int M, int N, int K) {
 hipError_t launch_gemm_bf16(GemmArgs a, int load, int epi, int* n_part_out, hipStream_t s) {
   if (a.K % SK_KSTEP) return hipErrorInvalidValue;  // both kernels step K in whole 128-element blocks
   if (a.M <= 16) return skinny_load<1>(a, load, epi, n_part_out, s);
-  if (a.M <= 32) return skinny_load<2>(a, load, epi, n_part_out, s);
   // tiled path; for SwiGLU the logical matrix is [gate; up] with N = 2*ffn
   if (a.part == nullptr) return hipErrorInvalidValue;  // partial buffer is mandatory here
   if (a.K % TL_BK) return hipErrorInvalidValue;
@@ -634,7 +650,6 @@ hipError_t launch_gemm_f32(GemmArgs a, int load, int epi, int* n_part_out, hipSt
   switch (load) {
     case LOAD_F32: F32_EPI(LOAD_F32); break;
     case LOAD_F32_NORM: F32_EPI(LOAD_F32_NORM); break;
-    case LOAD_GATHER: F32_EPI(LOAD_GATHER); break;
     default: return hipErrorInvalidValue;
   }
 #undef F32_EPI

@@ -30,7 +30,19 @@ struct AttnArgs {
   int n_rows, batch, hq, hkv, split_len, n_splits;
 };
 
-hipError_t launch_row_seq(const int32_t* row_start, int batch, int n_rows, int32_t* seq_of_row, hipStream_t s);
+// Row set-up: seq_of_row[m]; when xin is set, also xin[m] = [feat[parent[m]] ; embed[token[m]]] (fp32, 2d).
+struct RowSetupArgs {
+  const int32_t* row_start;
+  int batch, n_rows;
+  int32_t* seq_of_row;
+  const int32_t* parent;
+  const int32_t* token;
+  const float* feat;  // [*, d] fp32
+  const void* embed;  // [vocab, d] bf16 or fp32
+  int d;
+  float* xin;  // [n_rows, 2d]
+};
+hipError_t launch_row_setup(const RowSetupArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_rope_kv(const RopeArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, bool bf16, int hd, hipStream_t s);
 int attn_split_len(int max_prefix, int batch, int hkv);

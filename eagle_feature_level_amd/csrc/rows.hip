@@ -1,0 +1,67 @@
+// Per-call row set-up of a draft step: each row's sequence index and the
+// draft layer's input [f_parent ; e(token)] as one fp32 row of 2d values.
+//
+// The draft head concatenates the parent's feature vector with the embedding
+// of the token sampled after it, then reduces the 2d values to d with a fully
+// connected layer ("eagle feature-level speculative decoding", the drafting
+// section: the shifted token sequence is appended to the feature sequence).
+// Writing the concatenation once here keeps the FC GEMM a plain fp32 loader;
+// the embedding half converts exactly (bf16 -> fp32), so its lo half is zero.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+// One workgroup per row.  Thread 0 finds the row's sequence (rows of a
+// sequence are contiguous, row_start ascending).
+template <typename T>
+__global__ void __launch_bounds__(256) row_setup_kernel(RowSetupArgs a) {
+  const int m = blockIdx.x;
+  if (threadIdx.x == 0) {
+    int lo = 0, hi = a.batch - 1;
+    while (lo < hi) {  // last b with row_start[b] <= m
+      const int mid = (lo + hi + 1) / 2;
+      if (a.row_start[mid] <= m) lo = mid; else hi = mid - 1;
+    }
+    a.seq_of_row[m] = lo;
+  }
+  if (a.xin == nullptr) return;
+  const int d = a.d;
+  float* out = a.xin + (size_t)m * 2 * d;
+  const float* fr = a.feat + (size_t)a.parent[m] * d;
+  const T* e = (const T*)a.embed + (size_t)a.token[m] * d;
+  if (d % 8) {  // unaligned widths: element by element
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+      out[i] = fr[i];
+      if constexpr (sizeof(T) == 2) out[d + i] = bf2f(e[i]); else out[d + i] = e[i];
+    }
+    return;
+  }
+  for (int i = threadIdx.x; i < d / 4; i += blockDim.x) ((float4*)out)[i] = ((const float4*)fr)[i];
+  if constexpr (sizeof(T) == 2) {
+    // eight bf16 per 16-byte load
+    for (int i = threadIdx.x; i < d / 8; i += blockDim.x) {
+      const u32x4 v = *(const u32x4*)(e + i * 8);
+      float4 lo4, hi4;
+      lo4.x = __uint_as_float(v[0] << 16); lo4.y = __uint_as_float(v[0] & 0xffff0000u);
+      lo4.z = __uint_as_float(v[1] << 16); lo4.w = __uint_as_float(v[1] & 0xffff0000u);
+      hi4.x = __uint_as_float(v[2] << 16); hi4.y = __uint_as_float(v[2] & 0xffff0000u);
+      hi4.z = __uint_as_float(v[3] << 16); hi4.w = __uint_as_float(v[3] & 0xffff0000u);
+      ((float4*)(out + d))[2 * i] = lo4;
+      ((float4*)(out + d))[2 * i + 1] = hi4;
+    }
+  } else {
+    for (int i = threadIdx.x; i < d / 4; i += blockDim.x) ((float4*)(out + d))[i] = ((const float4*)e)[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_row_setup(const RowSetupArgs& a, bool bf16, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(row_setup_kernel<bf16_t>, dim3(a.n_rows), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(row_setup_kernel<float>, dim3(a.n_rows), dim3(256), 0, s, a);
+  return hipGetLastError();
+}

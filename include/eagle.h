@@ -265,8 +265,8 @@ int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t *t
  * thread per process. */
 enum {
   EAGLE_ROLE_FC = 0, EAGLE_ROLE_QKV, EAGLE_ROLE_ROPE, EAGLE_ROLE_ATTN, EAGLE_ROLE_O, EAGLE_ROLE_GATE_UP,
-  EAGLE_ROLE_DOWN, EAGLE_ROLE_LM_HEAD, EAGLE_ROLE_TOPK, EAGLE_ROLE_COUNT
-};
+  EAGLE_ROLE_DOWN, EAGLE_ROLE_LM_HEAD, EAGLE_ROLE_TOPK, EAGLE_ROLE_ROWS, EAGLE_ROLE_COUNT
+};  /* EAGLE_ROLE_ROWS: per-row set-up (sequence index, [f ; e] concatenation) */
 int eagle_profile_enable(int32_t max_launches);
 int eagle_profile_reset(void);
 int eagle_profile_disable(void);
