@@ -91,6 +91,7 @@ struct DraftWs {
   int32_t* seq_of_row;
   float* xin;  // [f_parent ; e(token)], 2d per row
   float* x;
+  float* xg;  // x * gain of the next RMSNorm (first x * g1, then h * g2)
   float* sumsq1;
   float* qkv;
   void* qrot;
@@ -130,6 +131,7 @@ DraftWs carve(const eagle_shape* s, int M, int B, int max_prefix, char* base) {
   w.seq_of_row = (int32_t*)take((size_t)M * 4);
   w.xin = (float*)take((size_t)M * 2 * s->d * 4);
   w.x = (float*)take((size_t)M * s->d * 4);
+  w.xg = (float*)take((size_t)M * s->d * 4);
   w.sumsq1 = (float*)take((size_t)npart * M * 4);
   w.qkv = (float*)take((size_t)M * nqkv * 4);
   w.qrot = take((size_t)M * hq * 4);
@@ -228,15 +230,14 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
   hipStream_t st = (hipStream_t)stream;
   const double wbytes = bf16 ? 2.0 : 4.0;
   // algorithmic bytes of a GEMM launch: weights once, fp32 activations in and out
-  auto gemm = [&](GemmArgs a, int load, int epi, int* np, int role) -> hipError_t {
+  auto gemm = [&](GemmArgs a, int epi, int* np, int role) -> hipError_t {
     int dummy = 0;
     a.part = ws.gemm_part;  // split-K partials of the tiled kernel
     const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
-    const double bytes = wbytes * a.N * a.K + 4.0 * a.M * (a.K + nout);
+    const double bytes = wbytes * a.N * a.K + 4.0 * a.M * (a.K + nout) + (a.y2 ? 4.0 * a.M * a.N : 0.0);
     const double flops = 2.0 * a.M * a.N * a.K;
     return timed(st, role, bytes, flops, [&] {
-      return bf16 ? launch_gemm_bf16(a, load, epi, np ? np : &dummy, st)
-                  : launch_gemm_f32(a, load, epi, np ? np : &dummy, st);
+      return bf16 ? launch_gemm_bf16(a, epi, np ? np : &dummy, st) : launch_gemm_f32(a, epi, np ? np : &dummy, st);
     });
   };
   hipError_t e;
@@ -261,7 +262,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
                 [&] { return launch_row_setup(r, bf16, st); });
       if (e != hipSuccess) return hip_fail(e);
     }
-    // a2: FC (+bias) = x, sum of squares for RMSNorm 1
+    // a2: FC (+bias) = x; sums of squares and x * g1 for RMSNorm 1
     int np1 = 0, np2 = 0;
     {
       GemmArgs a = gemm_base(M, d, 2 * d);
@@ -272,10 +273,12 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.y = ws.x;
       a.ldy = d;
       a.sumsq_out = ws.sumsq1;
-      e = gemm(a, LOAD_F32, EPI_BIAS_SUMSQ, &np1, EAGLE_ROLE_FC);
+      a.gain_out = w->norm1;
+      a.y2 = ws.xg;
+      e = gemm(a, EPI_BIAS_SUMSQ, &np1, EAGLE_ROLE_FC);
       if (e != hipSuccess) return hip_fail(e);
     }
-    // a3: RMSNorm -> [q; k; v]
+    // a3: RMSNorm -> [q; k; v]: (x * g1) [wq; wk; wv]^T, row scale in the epilogue
     {
       GemmArgs a = gemm_base(M, hq + 2 * hkv, d);
       a.w0 = w->wq;
@@ -283,15 +286,14 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.w1 = w->wk;
       a.n_seg1 = hkv;
       a.w2 = w->wv;
-      a.x = ws.x;
+      a.x = ws.xg;
       a.ldx = d;
       a.sumsq_in = ws.sumsq1;
       a.n_part_in = np1;
-      a.gain = w->norm1;
       a.eps = s.rms_eps;
       a.y = ws.qkv;
       a.ldy = hq + 2 * hkv;
-      e = gemm(a, LOAD_F32_NORM, EPI_STORE, nullptr, EAGLE_ROLE_QKV);
+      e = gemm(a, EPI_STORE, nullptr, EAGLE_ROLE_QKV);
       if (e != hipSuccess) return hip_fail(e);
     }
     // a4: RoPE at each row's position; k, v into the rows' tree slots
@@ -339,21 +341,23 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
                 [&] { return launch_attention(at, bf16, s.head_dim, st); });
       if (e != hipSuccess) return hip_fail(e);
     }
-    // a6: h = x + attn wo^T, sum of squares for RMSNorm 2
+    // a6: h = x + attn wo^T; sums of squares and h * g2 for RMSNorm 2
     {
       GemmArgs a = gemm_base(M, d, hq);
       a.w0 = w->wo;
-      a.x = ws.attn;
+      a.x = (const float*)ws.attn;
       a.ldx = hq;
       a.resid = ws.x;
       a.ldr = d;
       a.y = ws.h;
       a.ldy = d;
       a.sumsq_out = ws.sumsq2;
-      e = gemm(a, LOAD_F32, EPI_RESID_SUMSQ, &np2, EAGLE_ROLE_O);
+      a.gain_out = w->norm2;
+      a.y2 = ws.xg;
+      e = gemm(a, EPI_RESID_SUMSQ, &np2, EAGLE_ROLE_O);
       if (e != hipSuccess) return hip_fail(e);
     }
-    // a7: RMSNorm -> SwiGLU
+    // a7: RMSNorm -> SwiGLU: (h * g2) [w_gate; w_up]^T, row scale in the epilogue
     {
       GemmArgs a = gemm_base(M, 2 * F, d);
       a.w0 = w->w_gate;
@@ -361,30 +365,29 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.w1 = w->w_up;
       a.n_seg1 = F;
       a.ffn = F;
-      a.x = ws.h;
+      a.x = ws.xg;
       a.ldx = d;
       a.sumsq_in = ws.sumsq2;
       a.n_part_in = np2;
-      a.gain = w->norm2;
       a.eps = s.rms_eps;
-      a.yb = ws.act;
+      a.yb = (float*)ws.act;
       a.ldyb = F;
       a.part = ws.gemm_part;
-      e = gemm(a, LOAD_F32_NORM, EPI_SWIGLU, nullptr, EAGLE_ROLE_GATE_UP);
+      e = gemm(a, EPI_SWIGLU, nullptr, EAGLE_ROLE_GATE_UP);
       if (e != hipSuccess) return hip_fail(e);
     }
     // f^ = h + act w_down^T
     {
       GemmArgs a = gemm_base(M, d, F);
       a.w0 = w->w_down;
-      a.x = ws.act;
+      a.x = (const float*)ws.act;
       a.ldx = F;
       a.resid = ws.h;
       a.ldr = d;
       a.y = out->feat;
       a.ldy = d;
       a.part = ws.gemm_part;
-      e = gemm(a, LOAD_F32, EPI_RESID, nullptr, EAGLE_ROLE_DOWN);
+      e = gemm(a, EPI_RESID, nullptr, EAGLE_ROLE_DOWN);
       if (e != hipSuccess) return hip_fail(e);
     }
   }
@@ -398,7 +401,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     a.y = out->logits;
     a.ldy = s.vocab;
     a.part = ws.gemm_part;
-    e = gemm(a, LOAD_F32, EPI_STORE, nullptr, EAGLE_ROLE_LM_HEAD);
+    e = gemm(a, EPI_STORE, nullptr, EAGLE_ROLE_LM_HEAD);
     if (e != hipSuccess) return hip_fail(e);
   }
   // a9: softmax normaliser + top-k

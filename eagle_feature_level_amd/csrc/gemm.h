@@ -1,20 +1,17 @@
-// Internal interface of the draft-head GEMMs: y = x W^T with fused operand
-// loaders (row gather, RMSNorm, fp32 -> bf16 hi/lo) and epilogues (bias,
-// residual, SwiGLU, per-tile sums of squares for the next RMSNorm).
+// Internal interface of the draft-head GEMMs: y = x W^T with an fp32 operand
+// stream (optional row gather) and fused epilogues (RMSNorm row scale, bias,
+// residual, SwiGLU, per-tile sums of squares and gain product for the next
+// RMSNorm).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-enum GemmLoad {
-  LOAD_F32 = 1,       // x fp32 [M, K] (ldx), optional row gather xrows[m]
-  LOAD_F32_NORM = 2   // x fp32 * rsqrt(mean(x^2)+eps) * gain[k]; mean from sumsq partials
-};
 enum GemmEpi {
   EPI_STORE = 0,        // y = acc
-  EPI_BIAS_SUMSQ = 1,   // y = acc + bias[n]; sum of squares partials
+  EPI_BIAS_SUMSQ = 1,   // y = acc + bias[n]; sum of squares partials; y2 = y * gain_out[n] if y2
   EPI_RESID = 2,        // y = acc + resid[m, n]
-  EPI_RESID_SUMSQ = 3,  // y = acc + resid[m, n]; sum of squares partials
-  EPI_SWIGLU = 4        // yb[m, j] = silu(gate) * up (fp32), gate row j, up row ffn + j
+  EPI_RESID_SUMSQ = 3,  // y = acc + resid[m, n]; sum of squares partials; y2 = y * gain_out[n] if y2
+  EPI_SWIGLU = 4        // yb[m, j] = silu(gate) * up, gate row j, up row ffn + j
 };
 
 struct GemmArgs {
@@ -24,23 +21,26 @@ struct GemmArgs {
   const void* w2;
   int n_seg0, n_seg1;
   int N, K, M;
-  // operand loaders
-  const void* x;
+  // activations: x fp32 [M, K] (ldx), row m read from row xrows[m] if xrows is set
+  const float* x;
   int ldx;
   const int32_t* xrows;
+  // RMSNorm of the input rows, when sumsq_in is set: acc[m, :] *= rsqrt(sum_p sumsq_in[p][m] / K + eps)
+  // (x then already carries the gain)
   const float* sumsq_in;  // [n_part_in][M]
   int n_part_in;
-  const void* gain;
   float eps;
   // epilogue
   float* y;
   int ldy;
-  void* yb;  // SwiGLU output (fp32)
+  float* yb;  // SwiGLU output
   int ldyb;
   const void* bias;
   const float* resid;
   int ldr;
   float* sumsq_out;  // [n_part_out][M]
+  const void* gain_out;  // next RMSNorm's gain (bf16 or fp32 like the weights)
+  float* y2;             // y * gain_out, same layout as y
   int ffn;
   // split-K partials for the tiled kernel
   float* part;
@@ -51,6 +51,6 @@ struct GemmArgs {
 // bf16 path: chooses the skinny (M <= 16) or tiled kernel; args.part holds
 // the tiled kernel's split-K partials.  Sum-of-squares epilogues store their
 // number of partial tiles in *n_part_out.
-hipError_t launch_gemm_bf16(GemmArgs a, int load, int epi, int* n_part_out, hipStream_t s);
-hipError_t launch_gemm_f32(GemmArgs a, int load, int epi, int* n_part_out, hipStream_t s);
+hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s);
+hipError_t launch_gemm_f32(GemmArgs a, int epi, int* n_part_out, hipStream_t s);
 size_t gemm_bf16_partial_bytes(int M, int N, int K);

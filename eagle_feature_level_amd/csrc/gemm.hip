@@ -4,23 +4,29 @@
 // call; with M <= 160 rows they are bound by HBM, not by the matrix units
 // (arithmetic intensity ~M flop/byte against a ridge of ~315).  So:
 //  * W (bf16) is the MFMA "A" operand and goes straight from HBM to VGPRs, each
-//    lane pulling 32-64 contiguous bytes of a row per step; W is never staged
+//    lane pulling 64 contiguous bytes of a row per step; W is never staged
 //    through LDS because every W element is used by exactly one wave.
-//  * x is the MFMA "B" operand (M padded to 16).  The skinny kernel (M <= 16)
-//    reads it straight from L2; the tiled kernel stages it through LDS so the
-//    waves of a workgroup share it.
-//  * Activations are fp32 and enter the matrix units as a pair of bf16 values,
-//    hi = bf16(x) and lo = bf16(x - hi), two MFMAs into one fp32 accumulator:
-//    the product then carries ~16 significant bits of x instead of 8, which
-//    keeps a whole draft step within ~1e-3 of an fp64 evaluation.  Weights are
-//    exact bf16.  In the HBM-bound regime the second MFMA costs nothing, so
-//    both MFMAs always run: no MFMA sits under a data-dependent branch (the
-//    compiler may drop the execz skip around a short block, and an MFMA does
-//    not honour an all-zero EXEC).
+//  * x (fp32) is the MFMA "B" operand (M padded to 16).  The skinny kernel
+//    (M <= 16) loads each k-step's rows of x coalesced and re-reads them in the
+//    B layout from the wave's own LDS slice; the tiled kernel stages x through
+//    LDS so the waves of a workgroup share it.
+//  * Activations enter the matrix units as a pair of bf16 values, hi = x cut
+//    to bf16 and lo = bf16(x - hi), two MFMAs into one fp32 accumulator: the
+//    product then carries ~16 significant bits of x instead of 8, which keeps a
+//    whole draft step within ~1e-3 of an fp64 evaluation.  Weights are exact
+//    bf16.
+//    In the HBM-bound regime the second MFMA costs nothing, so both MFMAs always
+//    run: no MFMA sits under a data-dependent branch (the compiler may drop the
+//    execz skip around a short block, and an MFMA does not honour an all-zero
+//    EXEC).
+//  * RMSNorm(x) * g feeds the next GEMM as (x * g) W^T scaled per row by
+//    rsqrt(mean(x^2) + eps): the producing GEMM's epilogue writes x * g next to
+//    x and per-tile sums of squares of x; the consuming GEMM applies the row
+//    scale in its epilogue.  Its main loop is a plain fp32 stream.
 //  * Since the MFMA sums over k, any permutation of k is fine as long as A and
 //    B agree: a lane's 8-element group for MFMA j is taken from a contiguous
 //    run of 32 (skinny) or 16 (tiled) elements, so the weight loads are wide.
-//  * The skinny kernel splits K across the 8 waves of a workgroup and reduces
+//  * The skinny kernel splits K across the waves of a workgroup and reduces
 //    through LDS in a fixed order, then runs the fused epilogue: results are
 //    deterministic and need no global atomics.
 // MFMA v_mfma_f32_16x16x32_bf16 lane layout (lane l, r = l%16, g = l/16):
@@ -30,7 +36,6 @@
 
 namespace {
 
-constexpr int SK_NW = 8;       // waves per skinny workgroup
 constexpr int SK_KSTEP = 128;  // K covered by one wave iteration (4 lane groups x 32)
 constexpr int TL_BK = 64;      // K per tiled-kernel stage
 
@@ -45,30 +50,33 @@ __device__ __forceinline__ const T* wrow(const GemmArgs& a, int n) {
   return (const T*)a.w2 + (size_t)n * a.K;
 }
 
+__device__ __forceinline__ float rms_scale(float sumsq, const GemmArgs& a) {
+  return 1.0f / sqrtf(sumsq / (float)a.K + a.eps);
+}
+
 // Row scale of RMSNorm from per-tile sums of squares (fixed summation order).
 __device__ __forceinline__ float row_scale(const GemmArgs& a, int m) {
   float s = 0.f;
   for (int t = 0; t < a.n_part_in; ++t) s += a.sumsq_in[(size_t)t * a.M + m];
-  return 1.0f / sqrtf(s / (float)a.K + a.eps);
+  return rms_scale(s, a);
 }
 
-// RMSNorm scales of rows m_base .. m_base+BM-1 into LDS, all threads of the
-// workgroup cooperating: 32 lanes per row, each summing every 32nd partial,
-// then a fixed butterfly across the 32 lanes.  Ends with a barrier.
+// RMSNorm scales of rows 0 .. BM-1 into LDS, all threads of the workgroup
+// cooperating: 32 lanes per row, each summing every 32nd partial, then a fixed
+// butterfly across the 32 lanes.  No barrier: readers sync first.
 template <int NT>
-__device__ __forceinline__ void row_scales_lds(const GemmArgs& a, int m_base, int BM, float* scale) {
+__device__ __forceinline__ void row_scales_lds(const GemmArgs& a, int BM, float* scale) {
   constexpr int ROWS = NT / 32;
   const int t = threadIdx.x, c = t & 31;
   for (int m0 = 0; m0 < BM; m0 += ROWS) {
-    const int mm = m0 + t / 32, m = m_base + mm;
+    const int m = m0 + t / 32;
     float s = 0.f;
-    if (mm < BM && m < a.M)
+    if (m < BM && m < a.M)
       for (int p = c; p < a.n_part_in; p += 32) s += a.sumsq_in[(size_t)p * a.M + m];
 #pragma unroll
     for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, WAVE);
-    if (c == 0 && mm < BM) scale[mm] = (m < a.M) ? 1.0f / sqrtf(s / (float)a.K + a.eps) : 1.f;
+    if (c == 0 && m < BM) scale[m] = (m < a.M) ? rms_scale(s, a) : 1.f;
   }
-  __syncthreads();
 }
 
 // Eight bf16 operand values as (hi, lo) pairs.
@@ -76,10 +84,16 @@ struct B8 {
   u32x4 hi, lo;
 };
 
+// Two fp32 values as packed bf16 pairs (value a in the low half): hi = x with
+// its low 16 bits dropped (so x - hi is exact in fp32), lo = x - hi rounded to
+// bf16, ties away from zero.  |x - hi - lo| <= 2^-15 |x|.  Byte permutes and
+// three integer/float ops per value: this runs once per operand element per
+// wave, so it must stay cheap next to the weight stream.
 __device__ __forceinline__ uint32_t split2(float a, float b, uint32_t* lo) {
-  const bf16_t ha = f2bf(a), hb = f2bf(b);
-  *lo = pack_bf16x2(a - bf2f(ha), b - bf2f(hb));
-  return (uint32_t)ha | ((uint32_t)hb << 16);
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  const float ra = a - __uint_as_float(ua & 0xffff0000u), rb = b - __uint_as_float(ub & 0xffff0000u);
+  *lo = __builtin_amdgcn_perm(__float_as_uint(rb) + 0x8000u, __float_as_uint(ra) + 0x8000u, 0x07060302u);
+  return __builtin_amdgcn_perm(ub, ua, 0x07060302u);
 }
 
 __device__ __forceinline__ B8 split8(float4 v0, float4 v1) {
@@ -92,24 +106,15 @@ __device__ __forceinline__ B8 split8(float4 v0, float4 v1) {
   return r;
 }
 
+__device__ __forceinline__ float4 as_f4(u32x4 v) {
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+
 // Eight operand values of row m at columns k..k+7 (k % 8 == 0) as (hi, lo).
-template <int LOAD>
-__device__ __forceinline__ B8 load_b8(const GemmArgs& a, int m, int k, float rs) {
+__device__ __forceinline__ B8 load_b8(const GemmArgs& a, int m, int k) {
   const int row = a.xrows ? a.xrows[m] : m;
   const float4* p = (const float4*)((const float*)a.x + (size_t)row * a.ldx + k);
-  float4 v0 = p[0], v1 = p[1];
-  if constexpr (LOAD == LOAD_F32_NORM) {
-    u32x4 gv = *(const u32x4*)((const bf16_t*)a.gain + k);
-    float gs[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gs[2 * i] = __uint_as_float(gv[i] << 16);
-      gs[2 * i + 1] = __uint_as_float(gv[i] & 0xffff0000u);
-    }
-    v0.x *= rs * gs[0]; v0.y *= rs * gs[1]; v0.z *= rs * gs[2]; v0.w *= rs * gs[3];
-    v1.x *= rs * gs[4]; v1.y *= rs * gs[5]; v1.z *= rs * gs[6]; v1.w *= rs * gs[7];
-  }
-  return split8(v0, v1);
+  return split8(p[0], p[1]);
 }
 
 __device__ __forceinline__ floatx4 mfma16(u32x4 a, u32x4 b, floatx4 c) {
@@ -133,23 +138,34 @@ __device__ __forceinline__ int tile_row(const GemmArgs& a, int tile, int at, int
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel: M <= 16*MT, one workgroup = 16*AT weight rows, NW waves split K.
+// Skinny kernel: M <= 16, one workgroup = 16*AT weight rows, NW waves split K.
 // Vector-memory loads complete in issue order, so the activations of a k-step
 // are loaded in the same register stage as its weights: waiting for a stage
 // never waits for a later prefetch.  Three stages, two in flight.
+//
+// Activations: a k-step needs 128 fp32 values of each of the M rows, but in
+// the MFMA B layout only the 4*M lanes of real rows hold data, 32 values each,
+// so loading them in that layout costs 8 load instructions per k-step however
+// small M is.  Instead the chunk [M][128] is loaded coalesced, 16 bytes per
+// lane (MQ = ceil(M/2) instructions), written to this wave's own LDS slice and
+// read back in the B layout: one instruction per two rows in the weight stream.
+// A wave's LDS traffic is ordered, so no barrier is involved.
 // ---------------------------------------------------------------------------
-template <int AT, int MT, int LOAD>
+constexpr int SK_XROW = SK_KSTEP + 4;  // padded LDS row (floats): rows fall in different banks
+
+template <int AT, int MQ>
 struct SkStage {
-  u32x4 A[AT][4];    // weight fragments
-  u32x4 X[MT][8];    // raw fp32 activation bits
+  u32x4 A[AT][4];  // weight fragments
+  u32x4 X[MQ];     // coalesced activation chunk: lane l, quad q -> row (q*64+l)/32, 4 floats
 };
 
-__device__ __forceinline__ float4 as_f4(u32x4 v) {
-  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
-}
-
-template <int AT, int MT, int NW, int LOAD, int EPI>
+template <int AT, int NW, int MQ, int EPI>
 __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
+  constexpr int XR = 2 * MQ;  // activation rows this instance can hold
+  constexpr int BN = 16 * AT;
+  constexpr int XL = NW * XR * SK_XROW, RED = NW * 16 * (BN + 4);
+  // per-wave activation slices during the main loop, then the cross-wave reduction
+  __shared__ float smem[XL > RED ? XL : RED];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int tile = blockIdx.x;
@@ -161,106 +177,87 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
     const int n = tile_row<AT, EPI>(a, tile, at, r, &ok);
     ap[at] = wrow<bf16_t>(a, n) + g * 32;
   }
-  // per-lane activation rows (rows >= M clamped to a valid row, zeroed at use)
-  const float* xp[MT];
-  bool mv[MT];
+  // coalesced chunk: quad q of lane l covers row xm[q], columns xc..xc+3 of the k-step
+  const int xc = (lane & 31) * 4;
+  const float* xq[MQ];
+  bool xv[MQ];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + r;
-    mv[mt] = m < a.M;
-    const int mm = mv[mt] ? m : 0;
-    const int row = a.xrows ? a.xrows[mm] : mm;
-    xp[mt] = (const float*)a.x + (size_t)row * a.ldx + g * 32;
+  for (int q = 0; q < MQ; ++q) {
+    const int m = 2 * q + (lane >> 5);
+    xv[q] = m < a.M;
+    const int row = xv[q] ? (a.xrows ? a.xrows[m] : m) : 0;
+    xq[q] = a.x + (size_t)row * a.ldx + xc;
   }
+  float* xw = &smem[wv * XR * SK_XROW];
+  const bool mv = r < a.M;
+
   const int nks = a.K / SK_KSTEP;
-  SkStage<AT, MT, LOAD> S0, S1, S2;
-  auto issue = [&](SkStage<AT, MT, LOAD>& st, int ks) {
+  SkStage<AT, MQ> S0, S1, S2;
+  auto issue = [&](SkStage<AT, MQ>& st, int ks) {
 #pragma unroll
     for (int at = 0; at < AT; ++at)
 #pragma unroll
       for (int j = 0; j < 4; ++j) st.A[at][j] = *(const u32x4*)(ap[at] + (size_t)ks * SK_KSTEP + j * 8);
-    const int k0 = ks * SK_KSTEP;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) st.X[mt][q] = *(const u32x4*)(xp[mt] + k0 + q * 4);
+    for (int q = 0; q < MQ; ++q)
+      st.X[q] = xv[q] ? *(const u32x4*)(xq[q] + (size_t)ks * SK_KSTEP) : u32x4{0, 0, 0, 0};
   };
   if (wv < nks) issue(S0, wv);
   if (wv + NW < nks) issue(S1, wv + NW);
 
-  // RMSNorm row scales and gains (LDS), summed while the first stages are in flight
-  __shared__ float scale[16 * MT];
-  __shared__ float gain_s[LOAD == LOAD_F32_NORM ? 8192 : 1];
-  float rs[MT];
-  if constexpr (LOAD == LOAD_F32_NORM) {
-    for (int k = threadIdx.x; k < a.K; k += NW * 64) gain_s[k] = bf2f(((const bf16_t*)a.gain)[k]);
-    row_scales_lds<NW * 64>(a, 0, 16 * MT, scale);
-  }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) rs[mt] = (LOAD == LOAD_F32_NORM) ? scale[mt * 16 + r] : 1.f;
+  // RMSNorm row scales of the input rows (applied in the epilogue), summed
+  // while the first stages are in flight; visible after the reduction barrier
+  __shared__ float scale[16];
+  if (a.sumsq_in) row_scales_lds<NW * 64>(a, 16, scale);
 
-  floatx4 acc[AT][MT];
+  floatx4 acc[AT];
 #pragma unroll
-  for (int at = 0; at < AT; ++at)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[at][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int at = 0; at < AT; ++at) acc[at] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](const SkStage<AT, MT, LOAD>& st, int ks) {
-    const int k0 = ks * SK_KSTEP;
+  auto step = [&](const SkStage<AT, MQ>& st) {
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) *(u32x4*)&xw[(2 * q + (lane >> 5)) * SK_XROW + xc] = st.X[q];
+    const float* xr = &xw[(mv && r < XR ? r : 0) * SK_XROW + g * 32];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      B8 B[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        float4 v0 = as_f4(st.X[mt][2 * j]), v1 = as_f4(st.X[mt][2 * j + 1]);
-        if constexpr (LOAD == LOAD_F32_NORM) {
-          const float* gs = &gain_s[k0 + g * 32 + j * 8];
-          const float s0 = rs[mt];
-          v0.x *= s0 * gs[0]; v0.y *= s0 * gs[1]; v0.z *= s0 * gs[2]; v0.w *= s0 * gs[3];
-          v1.x *= s0 * gs[4]; v1.y *= s0 * gs[5]; v1.z *= s0 * gs[6]; v1.w *= s0 * gs[7];
-        }
-        B[mt] = split8(v0, v1);
-        if (!mv[mt]) {
-          B[mt].hi = u32x4{0, 0, 0, 0};
-          B[mt].lo = u32x4{0, 0, 0, 0};
-        }
+      float4 v0 = *(const float4*)(xr + j * 8), v1 = *(const float4*)(xr + j * 8 + 4);
+      if (!mv) {
+        v0 = make_float4(0.f, 0.f, 0.f, 0.f);
+        v1 = v0;
       }
+      const B8 B = split8(v0, v1);
 #pragma unroll
-      for (int at = 0; at < AT; ++at)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[at][mt] = mfma16(st.A[at][j], B[mt].hi, acc[at][mt]);
-          acc[at][mt] = mfma16(st.A[at][j], B[mt].lo, acc[at][mt]);
-        }
+      for (int at = 0; at < AT; ++at) {
+        acc[at] = mfma16(st.A[at][j], B.hi, acc[at]);
+        acc[at] = mfma16(st.A[at][j], B.lo, acc[at]);
+      }
     }
   };
 
   for (int ks = wv; ks < nks; ks += 3 * NW) {
     if (ks + 2 * NW < nks) issue(S2, ks + 2 * NW);
-    step(S0, ks);
+    step(S0);
     if (ks + NW >= nks) break;
     if (ks + 3 * NW < nks) issue(S0, ks + 3 * NW);
-    step(S1, ks + NW);
+    step(S1);
     if (ks + 2 * NW >= nks) break;
     if (ks + 4 * NW < nks) issue(S1, ks + 4 * NW);
-    step(S2, ks + 2 * NW);
+    step(S2);
   }
 
-  // Cross-wave reduction in a fixed order.
-  constexpr int BN = 16 * AT;
-  constexpr int BM = 16 * MT;
-  __shared__ float red[NW][BM][BN + 4];
+  // Cross-wave reduction in a fixed order (over the activation slices: all
+  // waves must be done with them first).
+  __syncthreads();
+  float(*red)[16][BN + 4] = reinterpret_cast<float(*)[16][BN + 4]>(smem);
 #pragma unroll
   for (int at = 0; at < AT; ++at)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) red[wv][mt * 16 + r][at * 16 + g * 4 + v] = acc[at][mt][v];
+    for (int v = 0; v < 4; ++v) red[wv][r][at * 16 + g * 4 + v] = acc[at][v];
   __syncthreads();
 
   if constexpr (EPI == EPI_SWIGLU) {
     constexpr int H = BN / 2;
-    for (int e = threadIdx.x; e < BM * H; e += NW * 64) {
+    for (int e = threadIdx.x; e < 16 * H; e += NW * 64) {
       const int m = e / H, jl = e % H;
       const int j = tile * H + jl;
       if (m < a.M && j < a.ffn) {
@@ -270,11 +267,15 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
           gs += red[w][m][jl];
           us += red[w][m][jl + H];
         }
-        ((float*)a.yb)[(size_t)m * a.ldyb + j] = silu_f(gs) * us;
+        if (a.sumsq_in) {
+          gs *= scale[m];
+          us *= scale[m];
+        }
+        a.yb[(size_t)m * a.ldyb + j] = silu_f(gs) * us;
       }
     }
   } else {
-    constexpr int ELEMS = BM * BN;
+    constexpr int ELEMS = 16 * BN;
     for (int e0 = 0; e0 < ELEMS; e0 += NW * 64) {
       const int e = e0 + threadIdx.x;
       const bool act = e < ELEMS;
@@ -285,9 +286,12 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
       if (live) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) y += red[w][m][nl];
+        if (a.sumsq_in) y *= scale[m];
         if constexpr (EPI == EPI_BIAS_SUMSQ) y += bf2f(((const bf16_t*)a.bias)[n]);
         if constexpr (EPI == EPI_RESID || EPI == EPI_RESID_SUMSQ) y += a.resid[(size_t)m * a.ldr + n];
         a.y[(size_t)m * a.ldy + n] = y;
+        if (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ)
+          if (a.y2) a.y2[(size_t)m * a.ldy + n] = y * bf2f(((const bf16_t*)a.gain_out)[n]);
       }
       if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
         float s = live ? y * y : 0.f;
@@ -304,13 +308,12 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
 // LDS; split-K over gridDim.y, M blocks over gridDim.z.  Writes fp32 partials;
 // gemm_reduce applies the epilogue.
 // ---------------------------------------------------------------------------
-template <int AT, int MT, int LOAD>
-__global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a, int logical_swiglu) {
+template <int AT, int MT>
+__global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a) {
   constexpr int BM = 16 * MT;
   constexpr int LDSW = TL_BK + 8;  // padded row (bf16 elements)
   __shared__ bf16_t xs[2][BM][LDSW];  // hi halves
   __shared__ bf16_t xl[2][BM][LDSW];  // lo halves
-  __shared__ float scale[BM];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int m_base = blockIdx.z * BM;
@@ -318,8 +321,6 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a, int logical_swiglu
   const int kper = a.K / a.splits;  // multiple of TL_BK
   const int k_begin = blockIdx.y * kper;
   const int nkb = kper / TL_BK;
-
-  if constexpr (LOAD == LOAD_F32_NORM) row_scales_lds<256>(a, m_base, BM, scale);
 
   const bf16_t* ap[AT];
 #pragma unroll
@@ -339,10 +340,7 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a, int logical_swiglu
       const int m = m_base + mm;
       xr[i].hi = u32x4{0, 0, 0, 0};
       xr[i].lo = u32x4{0, 0, 0, 0};
-      if (idx < GROUPS && m < a.M) {
-        const float rs = (LOAD == LOAD_F32_NORM) ? scale[mm] : 1.f;
-        xr[i] = load_b8<LOAD>(a, m, k_begin + kb * TL_BK + kg * 8, rs);
-      }
+      if (idx < GROUPS && m < a.M) xr[i] = load_b8(a, m, k_begin + kb * TL_BK + kg * 8);
     }
   };
   auto store_x = [&](int buf) {
@@ -432,6 +430,12 @@ __global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a) {
   const int n = blockIdx.x * 1024 + threadIdx.x * 4;
   const int nout = (EPI == EPI_SWIGLU) ? a.ffn : a.N;
   const size_t stride = (size_t)a.M * a.N;
+  float rs = 1.f;
+  if (a.sumsq_in) {
+    float s = 0.f;
+    for (int p = threadIdx.x; p < a.n_part_in; p += 256) s += a.sumsq_in[(size_t)p * a.M + m];
+    rs = rms_scale(block_sum<256>(s, red), a);
+  }
   float ss = 0.f;
   if (n < nout) {
     float4 s = {0.f, 0.f, 0.f, 0.f};
@@ -439,14 +443,16 @@ __global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a) {
       const float4 v = *(const float4*)(a.part + sp * stride + (size_t)m * a.N + n);
       s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
+    s.x *= rs; s.y *= rs; s.z *= rs; s.w *= rs;
     if constexpr (EPI == EPI_SWIGLU) {
       float4 u = {0.f, 0.f, 0.f, 0.f};
       for (int sp = 0; sp < a.splits; ++sp) {
         const float4 v = *(const float4*)(a.part + sp * stride + (size_t)m * a.N + a.ffn + n);
         u.x += v.x; u.y += v.y; u.z += v.z; u.w += v.w;
       }
+      u.x *= rs; u.y *= rs; u.z *= rs; u.w *= rs;
       const float4 o = {silu_f(s.x) * u.x, silu_f(s.y) * u.y, silu_f(s.z) * u.z, silu_f(s.w) * u.w};
-      *(float4*)((float*)a.yb + (size_t)m * a.ldyb + n) = o;
+      *(float4*)(a.yb + (size_t)m * a.ldyb + n) = o;
     } else {
       if constexpr (EPI == EPI_BIAS_SUMSQ) {
         const bf16_t* b = (const bf16_t*)a.bias + n;
@@ -457,6 +463,13 @@ __global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a) {
         s.x += rr.x; s.y += rr.y; s.z += rr.z; s.w += rr.w;
       }
       *(float4*)(a.y + (size_t)m * a.ldy + n) = s;
+      if (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
+        if (a.y2) {
+          const bf16_t* gn = (const bf16_t*)a.gain_out + n;
+          const float4 o = {s.x * bf2f(gn[0]), s.y * bf2f(gn[1]), s.z * bf2f(gn[2]), s.w * bf2f(gn[3])};
+          *(float4*)(a.y2 + (size_t)m * a.ldy + n) = o;
+        }
+      }
       ss = s.x * s.x + s.y * s.y + s.z * s.z + s.w * s.w;
     }
   }
@@ -468,22 +481,19 @@ __global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // fp32 path (tiny fp32 workloads): one thread per output, 64 outputs per block.
+// Same interface as the bf16 path; gains and bias are fp32 here.
 // ---------------------------------------------------------------------------
-template <int LOAD>
-__device__ __forceinline__ float load_x1(const GemmArgs& a, int m, int k, float rs) {
-  const int row = (LOAD == LOAD_F32 && a.xrows) ? a.xrows[m] : m;
-  float v = ((const float*)a.x)[(size_t)row * a.ldx + k];
-  if constexpr (LOAD == LOAD_F32_NORM) v *= rs * ((const float*)a.gain)[k];
-  return v;
+__device__ __forceinline__ float load_x1(const GemmArgs& a, int m, int k) {
+  const int row = a.xrows ? a.xrows[m] : m;
+  return a.x[(size_t)row * a.ldx + k];
 }
 
-template <int LOAD, int EPI>
+template <int EPI>
 __global__ void __launch_bounds__(64) gemm_f32(GemmArgs a) {
   const int m = blockIdx.y;
   const int n = blockIdx.x * 64 + threadIdx.x;
   const int nout = (EPI == EPI_SWIGLU) ? a.ffn : a.N;
-  float rs = 1.f;
-  if constexpr (LOAD == LOAD_F32_NORM) rs = row_scale(a, m);
+  const float rs = a.sumsq_in ? row_scale(a, m) : 1.f;
   float y = 0.f;
   const bool live = n < nout;
   if (live) {
@@ -492,17 +502,20 @@ __global__ void __launch_bounds__(64) gemm_f32(GemmArgs a) {
       const float* wu = wrow<float>(a, a.ffn + n);
       float gs = 0.f, us = 0.f;
       for (int k = 0; k < a.K; ++k) {
-        const float xv = load_x1<LOAD>(a, m, k, rs);
+        const float xv = load_x1(a, m, k);
         gs += wg[k] * xv;
         us += wu[k] * xv;
       }
-      ((float*)a.yb)[(size_t)m * a.ldyb + n] = silu_f(gs) * us;
+      a.yb[(size_t)m * a.ldyb + n] = silu_f(gs * rs) * (us * rs);
     } else {
       const float* w = wrow<float>(a, n);
-      for (int k = 0; k < a.K; ++k) y += w[k] * load_x1<LOAD>(a, m, k, rs);
+      for (int k = 0; k < a.K; ++k) y += w[k] * load_x1(a, m, k);
+      y *= rs;
       if constexpr (EPI == EPI_BIAS_SUMSQ) y += ((const float*)a.bias)[n];
       if constexpr (EPI == EPI_RESID || EPI == EPI_RESID_SUMSQ) y += a.resid[(size_t)m * a.ldr + n];
       a.y[(size_t)m * a.ldy + n] = y;
+      if (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ)
+        if (a.y2) a.y2[(size_t)m * a.ldy + n] = y * ((const float*)a.gain_out)[n];
     }
   }
   if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
@@ -514,26 +527,26 @@ __global__ void __launch_bounds__(64) gemm_f32(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
-template <int AT, int MT, int NW, int LOAD>
+template <int AT, int NW, int MQ>
 hipError_t skinny_epi(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
   const int BN = 16 * AT;
   dim3 blk(NW * 64);
   const dim3 grid((a.N + BN - 1) / BN);
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<AT, MT, NW, LOAD, EPI_STORE>), grid, blk, 0, s, a); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, EPI_STORE>), grid, blk, 0, s, a); break;
     case EPI_BIAS_SUMSQ:
-      hipLaunchKernelGGL((gemm_skinny<AT, MT, NW, LOAD, EPI_BIAS_SUMSQ>), grid, blk, 0, s, a);
+      hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, EPI_BIAS_SUMSQ>), grid, blk, 0, s, a);
       *n_part = grid.x;
       break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<AT, MT, NW, LOAD, EPI_RESID>), grid, blk, 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, EPI_RESID>), grid, blk, 0, s, a); break;
     case EPI_RESID_SUMSQ:
-      hipLaunchKernelGGL((gemm_skinny<AT, MT, NW, LOAD, EPI_RESID_SUMSQ>), grid, blk, 0, s, a);
+      hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, EPI_RESID_SUMSQ>), grid, blk, 0, s, a);
       *n_part = grid.x;
       break;
     case EPI_SWIGLU:
       if constexpr (AT >= 2) {  // gate and up tiles pair up inside a workgroup
         const int H = BN / 2;
-        hipLaunchKernelGGL((gemm_skinny<AT, MT, NW, LOAD, EPI_SWIGLU>), dim3((a.ffn + H - 1) / H), blk, 0, s, a);
+        hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, EPI_SWIGLU>), dim3((a.ffn + H - 1) / H), blk, 0, s, a);
         break;
       } else {
         return hipErrorInvalidValue;
@@ -544,24 +557,23 @@ hipError_t skinny_epi(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Four weight tiles x four waves when that still gives >= ~500 workgroups,
-// else one tile x eight waves (K split 8 ways inside the workgroup).
-template <int MT, int LOAD>
-hipError_t skinny_shape(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
-  const int rows = (epi == EPI_SWIGLU) ? 2 * a.ffn : a.N;
-  if (rows / 64 >= 384) return skinny_epi<4, MT, 4, LOAD>(a, epi, n_part, s);
-  if (epi == EPI_SWIGLU) return skinny_epi<2, MT, 8, LOAD>(a, epi, n_part, s);
-  return skinny_epi<1, MT, 8, LOAD>(a, epi, n_part, s);
+template <int AT, int NW>
+hipError_t skinny_mq(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
+  if (a.M <= 2) return skinny_epi<AT, NW, 1>(a, epi, n_part, s);
+  if (a.M <= 4) return skinny_epi<AT, NW, 2>(a, epi, n_part, s);
+  if (a.M <= 8) return skinny_epi<AT, NW, 4>(a, epi, n_part, s);
+  return skinny_epi<AT, NW, 8>(a, epi, n_part, s);
 }
 
-template <int MT>
-hipError_t skinny_load(const GemmArgs& a, int load, int epi, int* n_part, hipStream_t s) {
-  if (load == LOAD_F32_NORM && a.K > 8192) return hipErrorInvalidValue;  // gains staged in LDS
-  switch (load) {
-    case LOAD_F32: return skinny_shape<MT, LOAD_F32>(a, epi, n_part, s);
-    case LOAD_F32_NORM: return skinny_shape<MT, LOAD_F32_NORM>(a, epi, n_part, s);
-  }
-  return hipErrorInvalidValue;
+// One weight tile (16 rows) per workgroup keeps the operand split cheapest per
+// weight byte.  Waves per workgroup: 4 when there are >= 512 row tiles, else 8,
+// so that a launch has ~2000-8000 waves in flight; SwiGLU pairs a gate and an
+// up tile.  (Measured on the 7B shapes with M = 1..16.)
+hipError_t skinny_launch(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
+  if (epi == EPI_SWIGLU)  // 8 waves of 2 tiles would spill registers at M > 8
+    return a.M > 8 ? skinny_mq<2, 4>(a, epi, n_part, s) : skinny_mq<2, 8>(a, epi, n_part, s);
+  if (a.N / 16 >= 512) return skinny_mq<1, 4>(a, epi, n_part, s);
+  return skinny_mq<1, 8>(a, epi, n_part, s);
 }
 
 struct TiledPlan {
@@ -588,13 +600,9 @@ TiledPlan plan_tiled(int M, int N, int K) {
 }
 
 template <int MT>
-hipError_t tiled_launch(const GemmArgs& a, int load, const TiledPlan& p, hipStream_t s) {
+hipError_t tiled_launch(const GemmArgs& a, const TiledPlan& p, hipStream_t s) {
   dim3 grid(p.ntiles, p.splits, p.mblocks), blk(256);
-  switch (load) {
-    case LOAD_F32: hipLaunchKernelGGL((gemm_tiled<2, MT, LOAD_F32>), grid, blk, 0, s, a, 0); break;
-    case LOAD_F32_NORM: hipLaunchKernelGGL((gemm_tiled<2, MT, LOAD_F32_NORM>), grid, blk, 0, s, a, 0); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL((gemm_tiled<2, MT>), grid, blk, 0, s, a);
   return hipGetLastError();
 }
 
@@ -606,9 +614,10 @@ size_t gemm_bf16_partial_bytes(int M, int N, int K) {
   return (size_t)p.splits * M * N * sizeof(float);
 }
 
-hipError_t launch_gemm_bf16(GemmArgs a, int load, int epi, int* n_part_out, hipStream_t s) {
+hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s) {
   if (a.K % SK_KSTEP) return hipErrorInvalidValue;  // both kernels step K in whole 128-element blocks
-  if (a.M <= 16) return skinny_load<1>(a, load, epi, n_part_out, s);
+  if ((epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) && a.y2 && !a.gain_out) return hipErrorInvalidValue;
+  if (a.M <= 16) return skinny_launch(a, epi, n_part_out, s);
   // tiled path; for SwiGLU the logical matrix is [gate; up] with N = 2*ffn
   if (a.part == nullptr) return hipErrorInvalidValue;  // partial buffer is mandatory here
   if (a.K % TL_BK) return hipErrorInvalidValue;
@@ -616,10 +625,10 @@ hipError_t launch_gemm_bf16(GemmArgs a, int load, int epi, int* n_part_out, hipS
   a.splits = p.splits;
   hipError_t e;
   switch (p.mt) {
-    case 4: e = tiled_launch<4>(a, load, p, s); break;
-    case 6: e = tiled_launch<6>(a, load, p, s); break;
-    case 8: e = tiled_launch<8>(a, load, p, s); break;
-    default: e = tiled_launch<10>(a, load, p, s); break;
+    case 4: e = tiled_launch<4>(a, p, s); break;
+    case 6: e = tiled_launch<6>(a, p, s); break;
+    case 8: e = tiled_launch<8>(a, p, s); break;
+    default: e = tiled_launch<10>(a, p, s); break;
   }
   if (e != hipSuccess) return e;
   const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
@@ -635,24 +644,18 @@ hipError_t launch_gemm_bf16(GemmArgs a, int load, int epi, int* n_part_out, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_f32(GemmArgs a, int load, int epi, int* n_part_out, hipStream_t s) {
+hipError_t launch_gemm_f32(GemmArgs a, int epi, int* n_part_out, hipStream_t s) {
+  if ((epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) && a.y2 && !a.gain_out) return hipErrorInvalidValue;
   const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
   dim3 grid((nout + 63) / 64, a.M), blk(64);
-#define F32_EPI(L)                                                                                   \
-  switch (epi) {                                                                                     \
-    case EPI_STORE: hipLaunchKernelGGL((gemm_f32<L, EPI_STORE>), grid, blk, 0, s, a); break;         \
-    case EPI_BIAS_SUMSQ: hipLaunchKernelGGL((gemm_f32<L, EPI_BIAS_SUMSQ>), grid, blk, 0, s, a); break; \
-    case EPI_RESID: hipLaunchKernelGGL((gemm_f32<L, EPI_RESID>), grid, blk, 0, s, a); break;         \
-    case EPI_RESID_SUMSQ: hipLaunchKernelGGL((gemm_f32<L, EPI_RESID_SUMSQ>), grid, blk, 0, s, a); break; \
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_f32<L, EPI_SWIGLU>), grid, blk, 0, s, a); break;       \
-    default: return hipErrorInvalidValue;                                                            \
-  }
-  switch (load) {
-    case LOAD_F32: F32_EPI(LOAD_F32); break;
-    case LOAD_F32_NORM: F32_EPI(LOAD_F32_NORM); break;
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL(gemm_f32<EPI_STORE>, grid, blk, 0, s, a); break;
+    case EPI_BIAS_SUMSQ: hipLaunchKernelGGL(gemm_f32<EPI_BIAS_SUMSQ>, grid, blk, 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL(gemm_f32<EPI_RESID>, grid, blk, 0, s, a); break;
+    case EPI_RESID_SUMSQ: hipLaunchKernelGGL(gemm_f32<EPI_RESID_SUMSQ>, grid, blk, 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_f32<EPI_SWIGLU>, grid, blk, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
-#undef F32_EPI
   if (epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) *n_part_out = grid.x;
   return hipGetLastError();
 }
