@@ -212,6 +212,7 @@ def main():
     start.record()
     run_steps(eng, feat, tok, tgt, args.steps, marks)
     end.record()
+    t_submit = time.perf_counter() - t_wall
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(end)
@@ -273,6 +274,7 @@ def main():
         "ms_draft_phase": round(ms_draft, 4),
         "ms_verify": round(ms_verify, 4),
         "wall_s_timed": round(t_wall, 4),
+        "host_submit_ms_per_step": round(1e3 * t_submit / args.steps, 4),
         "gemm_stream_gbs": round(g_bytes / (g_ms * 1e-3) / 1e9, 1) if g_ms else None,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},

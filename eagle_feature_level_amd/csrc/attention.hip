@@ -53,40 +53,59 @@ template <>
 __device__ __forceinline__ void st1<bf16_t>(bf16_t* p, float v) { *p = f2bf(v); }
 
 // qkv fp32 [M, (Hq + 2 Hkv) hd] -> rotated q (fp32) [M, Hq hd]; rotated k and v
-// into tree slots in the KV cache's element type T.
+// into tree slots in the KV cache's element type T.  grid (rows, ceil((Hq +
+// 2 Hkv) / 4)): a block takes four heads of one row from the list [q heads, k
+// heads, v heads].  The rotation angles pos * theta^(-2e/hd) depend only on
+// the row's position and the pair index e: computed once per block (fp64, so a
+// position in the thousands keeps its phase exact to fp32), then shared.
+constexpr int ROPE_HPB = 4;
+
 template <typename T>
 __global__ void __launch_bounds__(256) rope_kv_kernel(RopeArgs a) {
+  __shared__ float cs[64], sn[64];
   const int r = blockIdx.x;
   const int hd = a.hd, half = hd / 2;
-  const int nqkv = (a.hq + 2 * a.hkv) * hd;
-  const float* src = a.qkv + (size_t)r * nqkv;
-  const int pos = a.pos[r];
+  const int nheads = a.hq + 2 * a.hkv;
+  const int h0 = blockIdx.y * ROPE_HPB;
+  const float* src = a.qkv + (size_t)r * nheads * hd;
   const int b = a.seq_of_row ? a.seq_of_row[r] : 0;
   const int slot = a.slot[r];
   T* tk = (T*)a.tree_k + (((size_t)b * 64 + slot) * a.hkv) * hd;
   T* tv = (T*)a.tree_v + (((size_t)b * 64 + slot) * a.hkv) * hd;
   float* qo = a.q_out + (size_t)r * a.hq * hd;
-  const int npairs = (a.hq + a.hkv) * half;
-  for (int i = threadIdx.x; i < npairs; i += blockDim.x) {
-    const int h = i / half, e = i % half;
-    const double inv = exp2(-2.0 * (double)e / (double)hd * log2((double)a.theta));
-    double sd, cd;
-    sincos((double)pos * inv, &sd, &cd);
-    const float c = (float)cd, s = (float)sd;
-    const float* v = src + h * hd;
-    const float x0 = v[e], x1 = v[e + half];
-    const float y0 = x0 * c - x1 * s, y1 = x1 * c + x0 * s;
-    if (h < a.hq) {
-      qo[h * hd + e] = y0;
-      qo[h * hd + e + half] = y1;
+  if (h0 < a.hq + a.hkv) {  // this block rotates something
+    const int pos = a.pos[r];
+    for (int e = threadIdx.x; e < half; e += blockDim.x) {
+      const double inv = exp2(-2.0 * (double)e / (double)hd * log2((double)a.theta));
+      double sd, cd;
+      sincos((double)pos * inv, &sd, &cd);
+      cs[e] = (float)cd;
+      sn[e] = (float)sd;
+    }
+    __syncthreads();
+  }
+  const int hend = min(h0 + ROPE_HPB, nheads);
+  for (int i = threadIdx.x; i < (hend - h0) * half; i += blockDim.x) {
+    const int h = h0 + i / half, e = i % half;
+    const float* v = src + (size_t)h * hd;
+    if (h < a.hq + a.hkv) {
+      const float c = cs[e], sv = sn[e];
+      const float x0 = v[e], x1 = v[e + half];
+      const float y0 = x0 * c - x1 * sv, y1 = x1 * c + x0 * sv;
+      if (h < a.hq) {
+        qo[h * hd + e] = y0;
+        qo[h * hd + e + half] = y1;
+      } else {
+        const int g = h - a.hq;
+        st1<T>(tk + g * hd + e, y0);
+        st1<T>(tk + g * hd + e + half, y1);
+      }
     } else {
-      const int g = h - a.hq;
-      st1<T>(tk + g * hd + e, y0);
-      st1<T>(tk + g * hd + e + half, y1);
+      const int g = h - a.hq - a.hkv;
+      st1<T>(tv + g * hd + e, v[e]);
+      st1<T>(tv + g * hd + e + half, v[e + half]);
     }
   }
-  const float* vs = src + (a.hq + a.hkv) * hd;
-  for (int i = threadIdx.x; i < a.hkv * hd; i += blockDim.x) st1<T>(tv + i, vs[i]);
 }
 
 constexpr int KT = 64;  // keys per tile
@@ -121,18 +140,35 @@ __global__ void __launch_bounds__(256) attn_partial_kernel(AttnArgs a) {
   constexpr int DPL = HD / 64 > 0 ? HD / 64 : 1;  // output dims per lane
   const bool lane_dims = lane * DPL < HD;
 
+  // K/V tile staging: every load of a tile is issued before any LDS store, and
+  // the next tile's loads are in flight while the current tile is used.
+  constexpr int EPV = 16 / sizeof(T);            // elements per 16-byte vector
+  constexpr int KVI = KT * (HD / EPV) / 256;     // vectors per thread per tile
+  constexpr int QE = QC * HD / 256;              // query elements per thread
+  static_assert(KVI >= 1 && QE >= 1, "tile shapes");
+  u32x4 kr[KVI], vr[KVI];
+
   for (int qc0 = 0; qc0 < nq; qc0 += QC) {
     // queries of this chunk: q index qi -> row r0 + qi / G, head g*G + qi % G
     __syncthreads();
-    for (int i = threadIdx.x; i < QC * HD; i += 256) {
-      const int qq = i / HD, dd = i % HD;
-      const int qi = qc0 + qq;
-      float v = 0.f;
-      if (qi < nq) {
-        const int row = r0 + qi / G, h = g * G + qi % G;
-        v = a.q[((size_t)row * a.hq + h) * HD + dd] * scale;
+    {
+      float qv[QE];
+#pragma unroll
+      for (int j = 0; j < QE; ++j) {
+        const int i = threadIdx.x + j * 256;
+        const int qq = i / HD, dd = i % HD;
+        const int qi = qc0 + qq;
+        qv[j] = 0.f;
+        if (qi < nq) {
+          const int row = r0 + qi / G, h = g * G + qi % G;
+          qv[j] = a.q[((size_t)row * a.hq + h) * HD + dd] * scale;
+        }
       }
-      qs[qq][dd] = v;
+#pragma unroll
+      for (int j = 0; j < QE; ++j) {
+        const int i = threadIdx.x + j * 256;
+        qs[i / HD][i % HD] = qv[j];
+      }
     }
     if (threadIdx.x < QC) {
       const int qi = qc0 + threadIdx.x;
@@ -154,29 +190,43 @@ __global__ void __launch_bounds__(256) attn_partial_kernel(AttnArgs a) {
 
     const int n_prefix_tiles = (kend > kbeg) ? (kend - kbeg + KT - 1) / KT : 0;
     const int n_tiles = n_prefix_tiles + (do_tree ? 1 : 0);
+    // K and V of tile t into registers (zeros where no key)
+    auto load_tile = [&](int t) {
+      const bool tree_tile = (t == n_prefix_tiles);
+      const int k0 = kbeg + t * KT;
+      const int tlen = tree_tile ? KT : min(KT, kend - k0);
+#pragma unroll
+      for (int u = 0; u < KVI; ++u) {
+        const int i = threadIdx.x + u * 256;
+        const int j = i / (HD / EPV), dd = (i % (HD / EPV)) * EPV;
+        kr[u] = u32x4{0, 0, 0, 0};
+        vr[u] = u32x4{0, 0, 0, 0};
+        if (tree_tile) {
+          if ((umask >> j) & 1ull) {
+            kr[u] = *(const u32x4*)(tk + (size_t)j * a.hkv * HD + dd);
+            vr[u] = *(const u32x4*)(tv + (size_t)j * a.hkv * HD + dd);
+          }
+        } else if (j < tlen) {
+          kr[u] = *(const u32x4*)(pk + (size_t)(k0 + j) * HD + dd);
+          vr[u] = *(const u32x4*)(pv + (size_t)(k0 + j) * HD + dd);
+        }
+      }
+    };
+    if (n_tiles > 0) load_tile(0);
     for (int t = 0; t < n_tiles; ++t) {
       const bool tree_tile = (t == n_prefix_tiles);
       const int k0 = kbeg + t * KT;
       const int tlen = tree_tile ? KT : min(KT, kend - k0);
       __syncthreads();
-      // stage K and V of the tile (zeros where no key)
-      constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
-      for (int i = threadIdx.x; i < KT * (HD / EPV); i += 256) {
+#pragma unroll
+      for (int u = 0; u < KVI; ++u) {
+        const int i = threadIdx.x + u * 256;
         const int j = i / (HD / EPV), dd = (i % (HD / EPV)) * EPV;
-        u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-        if (tree_tile) {
-          if ((umask >> j) & 1ull) {
-            kv = *(const u32x4*)(tk + (size_t)j * a.hkv * HD + dd);
-            vv = *(const u32x4*)(tv + (size_t)j * a.hkv * HD + dd);
-          }
-        } else if (j < tlen) {
-          kv = *(const u32x4*)(pk + (size_t)(k0 + j) * HD + dd);
-          vv = *(const u32x4*)(pv + (size_t)(k0 + j) * HD + dd);
-        }
-        *(u32x4*)&ks[j][dd] = kv;
-        *(u32x4*)&vsm[j][dd] = vv;
+        *(u32x4*)&ks[j][dd] = kr[u];
+        *(u32x4*)&vsm[j][dd] = vr[u];
       }
       __syncthreads();
+      if (t + 1 < n_tiles) load_tile(t + 1);
       // scores: lane j = key, this wave's queries wv, wv+4, ...
       float sc[QPW];
 #pragma unroll
@@ -275,35 +325,290 @@ __global__ void __launch_bounds__(128) attn_combine_kernel(AttnArgs a, int hd) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Tree attention on the matrix units: bf16 K/V cache, head_dim 128.
+//
+// One workgroup = (key split, kv head and query block, sequence); 4 waves x 16
+// queries.  Per 64-key tile:
+//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; A = K rows from LDS, B = the
+//                  wave's queries, held in registers as bf16 hi/lo pairs)
+//   online softmax per query over the tile (fp32, exp of s - running max)
+//   O^T += V^T P^T  (A = V^T from a transposed LDS tile, B = P^T straight from
+//                  the S^T accumulators: the MFMA sums over keys, so the keys of
+//                  a lane's accumulator block may stand in any order as long as
+//                  the V^T rows use the same order)
+// The next tile's K and V are loaded into registers while the current one is
+// used.  The 64 tree slots ride with the last split as one more tile, masked
+// per query by its row's ancestor bitmask.  With one split the normalised
+// output is written directly; otherwise (max, sum, unnormalised output) per
+// split goes to attn_combine_kernel.
+// ---------------------------------------------------------------------------
+constexpr int AQ = 64;          // queries per workgroup
+constexpr int AKROW = 128 + 8;  // K tile row (bf16): 272 B, rows land 4 banks apart
+constexpr int AVROW = KT + 4;   // transposed V tile row (bf16): 136 B, 8-byte aligned
+
+__device__ __forceinline__ floatx4 mfma16a(u32x4 a, u32x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// Two fp32 values as packed bf16 (a in the low half): hi = cut to bf16 (exact
+// remainder), lo = remainder rounded, ties away from zero.
+__device__ __forceinline__ uint32_t asplit2(float a, float b, uint32_t* lo) {
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  const float ra = a - __uint_as_float(ua & 0xffff0000u), rb = b - __uint_as_float(ub & 0xffff0000u);
+  *lo = __builtin_amdgcn_perm(__float_as_uint(rb) + 0x8000u, __float_as_uint(ra) + 0x8000u, 0x07060302u);
+  return __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+}
+
+__global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t ks[KT][AKROW];
+  __shared__ __attribute__((aligned(16))) bf16_t vt[128][AVROW];
+  __shared__ unsigned long long umask_s;
+  const int s = blockIdx.x;
+  const int g = blockIdx.y % a.hkv, qb = blockIdx.y / a.hkv;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c = lane & 15, gq = lane >> 4;
+  const int G = a.hq / a.hkv;
+  const int r0 = a.row_start[b], nr = a.row_start[b + 1] - r0;
+  const int nq = nr * G;
+  if (qb * AQ >= nq) return;  // whole workgroup: no queries in this block
+  const int L = a.prefix_len[b];
+  const int kbeg = s * a.split_len;
+  const int kend = min(L, kbeg + a.split_len);
+  const bool with_tree = (s == a.n_splits - 1);
+  const int n_prefix_tiles = (kend > kbeg) ? (kend - kbeg + KT - 1) / KT : 0;
+  const int n_tiles = n_prefix_tiles + (with_tree ? 1 : 0);
+  const bf16_t* pk = (const bf16_t*)a.prefix_k + a.prefix_off[b] + (size_t)g * L * 128;
+  const bf16_t* pv = (const bf16_t*)a.prefix_v + a.prefix_off[b] + (size_t)g * L * 128;
+  const bf16_t* tk = (const bf16_t*)a.tree_k + ((size_t)b * 64 * a.hkv + g) * 128;  // slot stride hkv*128
+  const bf16_t* tv = (const bf16_t*)a.tree_v + ((size_t)b * 64 * a.hkv + g) * 128;
+
+  // tree slots any row of this sequence may see (only those are loaded)
+  if (threadIdx.x == 0) umask_s = 0ull;
+  __syncthreads();
+  if (with_tree)
+    for (int t = threadIdx.x; t < nr; t += 256) atomicOr(&umask_s, (unsigned long long)a.mask[r0 + t]);
+
+  // this lane's query: q = qb*64 + wv*16 + c -> row r0 + q/G, head g*G + q%G
+  const int qi = qb * AQ + wv * 16 + c;
+  const bool qv = qi < nq;
+  const int row = r0 + (qv ? qi / G : 0);
+  const int h = g * G + (qv ? qi % G : 0);
+  const uint64_t qmask = qv ? a.mask[row] : 0ull;
+  u32x4 qh[4], ql[4];  // B operand: lane (query c, group gq) holds dims dc*32 + gq*8 + i
+  {
+    const float* qp = a.q + ((size_t)row * a.hq + h) * 128;
+    const float sc = rsqrtf(128.f);
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) {
+      float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+      if (qv) {
+        v0 = *(const float4*)(qp + dc * 32 + gq * 8);
+        v1 = *(const float4*)(qp + dc * 32 + gq * 8 + 4);
+      }
+      uint32_t l;
+      qh[dc][0] = asplit2(v0.x * sc, v0.y * sc, &l); ql[dc][0] = l;
+      qh[dc][1] = asplit2(v0.z * sc, v0.w * sc, &l); ql[dc][1] = l;
+      qh[dc][2] = asplit2(v1.x * sc, v1.y * sc, &l); ql[dc][2] = l;
+      qh[dc][3] = asplit2(v1.z * sc, v1.w * sc, &l); ql[dc][3] = l;
+    }
+  }
+  __syncthreads();  // umask_s complete
+  const uint64_t umask = umask_s;
+
+  // tile staging: thread t, part u: key (t + 256u) / 16, dims 8 * ((t + 256u) % 16) .. +7
+  u32x4 kr[4], vr[4];
+  auto load_tile = [&](int t) {
+    const bool tree_tile = (t == n_prefix_tiles);
+    const int k0 = kbeg + t * KT;
+    const int tlen = tree_tile ? KT : min(KT, kend - k0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = threadIdx.x + u * 256;
+      const int j = i >> 4, dd = (i & 15) * 8;
+      kr[u] = u32x4{0, 0, 0, 0};
+      vr[u] = u32x4{0, 0, 0, 0};
+      if (tree_tile) {
+        if ((umask >> j) & 1ull) {
+          kr[u] = *(const u32x4*)(tk + (size_t)j * a.hkv * 128 + dd);
+          vr[u] = *(const u32x4*)(tv + (size_t)j * a.hkv * 128 + dd);
+        }
+      } else if (j < tlen) {
+        kr[u] = *(const u32x4*)(pk + (size_t)(k0 + j) * 128 + dd);
+        vr[u] = *(const u32x4*)(pv + (size_t)(k0 + j) * 128 + dd);
+      }
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  floatx4 oacc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (n_tiles > 0) load_tile(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const bool tree_tile = (t == n_prefix_tiles);
+    const int tlen = tree_tile ? KT : min(KT, kend - (kbeg + t * KT));
+    __syncthreads();  // previous tile fully used
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = threadIdx.x + u * 256;
+      const int j = i >> 4, dd = (i & 15) * 8;
+      *(u32x4*)&ks[j][dd] = kr[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[dd + 2 * e][j] = (bf16_t)(vr[u][e] & 0xffffu);
+        vt[dd + 2 * e + 1][j] = (bf16_t)(vr[u][e] >> 16);
+      }
+    }
+    __syncthreads();
+    if (t + 1 < n_tiles) load_tile(t + 1);
+
+    // S^T: lane (query c, gq) gets keys kb*16 + 4*gq + v, v < 4
+    floatx4 sacc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < 4; ++dc) {
+        const u32x4 A = *(const u32x4*)&ks[kb * 16 + c][dc * 32 + gq * 8];
+        sacc[kb] = mfma16a(A, qh[dc], sacc[kb]);
+        sacc[kb] = mfma16a(A, ql[dc], sacc[kb]);
+      }
+    }
+    float sv[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int kk = kb * 16 + gq * 4 + v;
+        const bool ok = tree_tile ? ((qmask >> kk) & 1ull) != 0 : (kk < tlen && qv);
+        sv[kb][v] = ok ? sacc[kb][v] : -INFINITY;
+        mx = fmaxf(mx, sv[kb][v]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+    const float mnew = fmaxf(m_run, mx);
+    const float alpha = (m_run > -INFINITY) ? __expf(m_run - mnew) : 0.f;
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = (sv[kb][v] > -INFINITY) ? __expf(sv[kb][v] - mnew) : 0.f;
+        sv[kb][v] = p;
+        ps += p;
+      }
+    ps += __shfl_xor(ps, 16, WAVE);
+    ps += __shfl_xor(ps, 32, WAVE);
+    l_run = l_run * alpha + ps;
+    m_run = mnew;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      oacc[db][0] *= alpha; oacc[db][1] *= alpha; oacc[db][2] *= alpha; oacc[db][3] *= alpha;
+    }
+    // O^T += V^T P^T over two 32-key chunks: chunk kc uses key blocks 2kc, 2kc+1
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      u32x4 Bh, Bl;
+      uint32_t l;
+      Bh[0] = asplit2(sv[2 * kc][0], sv[2 * kc][1], &l); Bl[0] = l;
+      Bh[1] = asplit2(sv[2 * kc][2], sv[2 * kc][3], &l); Bl[1] = l;
+      Bh[2] = asplit2(sv[2 * kc + 1][0], sv[2 * kc + 1][1], &l); Bl[2] = l;
+      Bh[3] = asplit2(sv[2 * kc + 1][2], sv[2 * kc + 1][3], &l); Bl[3] = l;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16_t* vr0 = &vt[db * 16 + c][kc * 32 + gq * 4];
+        const uint2 x0 = *(const uint2*)vr0;
+        const uint2 x1 = *(const uint2*)(vr0 + 16);
+        const u32x4 A = u32x4{x0.x, x0.y, x1.x, x1.y};
+        oacc[db] = mfma16a(A, Bh, oacc[db]);
+        oacc[db] = mfma16a(A, Bl, oacc[db]);
+      }
+    }
+  }
+
+  if (!qv) return;
+  // lane (query c, gq) holds dims db*16 + 4*gq + v
+  if (a.n_splits == 1) {
+    const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+    float* dst = a.out + ((size_t)row * a.hq + h) * 128;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      *(float4*)(dst + db * 16 + gq * 4) =
+          make_float4(oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv);
+  } else {
+    float* dst = a.part + (((size_t)s * a.n_rows + row) * a.hq + h) * (128 + 2);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      float* d4 = dst + 2 + db * 16 + gq * 4;
+      d4[0] = oacc[db][0]; d4[1] = oacc[db][1]; d4[2] = oacc[db][2]; d4[3] = oacc[db][3];
+    }
+    if (gq == 0) {
+      dst[0] = m_run;
+      dst[1] = l_run;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rope_kv(const RopeArgs& a, bool bf16, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  if (a.hd > 128 || a.hd % 2) return hipErrorInvalidValue;  // angle table holds 64 pairs
+  const dim3 grid(a.n_rows, (a.hq + 2 * a.hkv + ROPE_HPB - 1) / ROPE_HPB);
   if (bf16)
-    hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(a.n_rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(a.n_rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(rope_kv_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-int attn_split_len(int max_prefix, int batch, int hkv) {
-  // aim for ~2048 workgroups; splits are multiples of the 64-key tile
+// fp32 scalar kernel: prefix splits of a multiple of the 64-key tile aiming at
+// ~2048 workgroups, plus one split for the tree block.
+static AttnPlan plan_scalar(int max_prefix, int batch, int hkv) {
   const long want = 2048;
-  long per = (long)batch * hkv;
+  const long per = (long)batch * hkv;
   int split_len = KT;
   while ((long)((max_prefix + split_len - 1) / split_len) * per > want && split_len < (1 << 20)) split_len *= 2;
-  return split_len;
+  return AttnPlan{split_len, (max_prefix + split_len - 1) / split_len + 1};
 }
 
-// prefix splits plus one split for the tree block
-int attn_n_splits(int max_prefix, int split_len) { return (max_prefix + split_len - 1) / split_len + 1; }
+// bf16 matrix-core kernel: splits of whole tiles aiming at ~1024 workgroups
+// counting the query blocks; the tree slots ride with the last split.
+static AttnPlan plan_mfma(int max_prefix, int batch, int hkv, int max_queries) {
+  const long qblocks = (max_queries + AQ - 1) / AQ;
+  const long per = (long)batch * hkv * (qblocks > 0 ? qblocks : 1);
+  const int tiles = (max_prefix + KT - 1) / KT;
+  int splits = (int)((1024 + per - 1) / per);
+  if (splits > tiles) splits = tiles;
+  if (splits < 1) splits = 1;
+  const int tiles_per = (tiles + splits - 1) / splits;
+  const int split_len = (tiles_per > 0 ? tiles_per : 1) * KT;
+  const int n = (max_prefix + split_len - 1) / split_len;
+  return AttnPlan{split_len, n > 0 ? n : 1};
+}
 
-hipError_t launch_attention(const AttnArgs& a, bool bf16, int hd, hipStream_t s) {
-  if (a.n_splits > 1024) return hipErrorInvalidValue;  // combine keeps one weight per split in LDS
-  dim3 grid(a.n_splits, a.hkv, a.batch), blk(256);
+AttnPlan attn_plan(bool bf16, int max_prefix, int batch, int hkv, int max_queries) {
+  return bf16 ? plan_mfma(max_prefix, batch, hkv, max_queries) : plan_scalar(max_prefix, batch, hkv);
+}
+
+hipError_t launch_attention(const AttnArgs& a, bool bf16, int hd, int max_queries, hipStream_t s) {
+  if (a.n_splits > 1024 || a.n_splits < 1) return hipErrorInvalidValue;  // combine keeps a weight per split in LDS
   if (bf16) {
     if (hd != 128) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_partial_kernel<bf16_t, 128>), grid, blk, 0, s, a);
+    const int qblocks = (max_queries + AQ - 1) / AQ;
+    if (qblocks < 1) return hipSuccess;
+    if ((long)qblocks * a.hkv > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_mfma_kernel, dim3(a.n_splits, a.hkv * qblocks, a.batch), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.n_splits == 1) return e;
   } else {
+    dim3 grid(a.n_splits, a.hkv, a.batch), blk(256);
     if (hd == 16)
       hipLaunchKernelGGL((attn_partial_kernel<float, 16>), grid, blk, 0, s, a);
     else if (hd == 64)
@@ -312,9 +617,9 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, int hd, hipStream_t s)
       hipLaunchKernelGGL((attn_partial_kernel<float, 128>), grid, blk, 0, s, a);
     else
       return hipErrorInvalidValue;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(a.n_rows, a.hq), dim3(128), 0, s, a, hd);
   return hipGetLastError();
 }

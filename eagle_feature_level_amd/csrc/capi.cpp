@@ -111,8 +111,8 @@ DraftWs carve(const eagle_shape* s, int M, int B, int max_prefix, char* base) {
   const int hq = s->n_heads * s->head_dim, hkv = s->n_kv_heads * s->head_dim;
   const int nqkv = hq + 2 * hkv;
   const int npart = s->d / 16 + 2;  // >= partial tiles of any GEMM producing a d-wide output
-  const int split_len = attn_split_len(max_prefix, B, s->n_kv_heads);
-  const int nsplit = attn_n_splits(max_prefix, split_len);
+  // most splits an attention call can use: one query block per (sequence, kv head)
+  const int nsplit = attn_plan(s->dtype == EAGLE_BF16, max_prefix, B, s->n_kv_heads, 1).n_splits;
   size_t gp = 0;
   if (s->dtype == EAGLE_BF16) {
     const int Ns[6] = {s->d, nqkv, s->d, 2 * s->ffn, s->d, s->vocab};
@@ -333,12 +333,14 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       at.batch = rows->batch;
       at.hq = s.n_heads;
       at.hkv = s.n_kv_heads;
-      at.split_len = attn_split_len(maxL, rows->batch, s.n_kv_heads);
-      at.n_splits = attn_n_splits(maxL, at.split_len);
+      const int max_q = rows->max_rows_per_seq * (s.n_heads / s.n_kv_heads);
+      const AttnPlan plan = attn_plan(bf16, maxL, rows->batch, s.n_kv_heads, max_q);
+      at.split_len = plan.split_len;
+      at.n_splits = plan.n_splits;
       // bytes: each sequence's prefix K and V once, tree slots, q in, output out; flops 4*hd per (query, key)
       const double kv_bytes = 2.0 * wbytes * s.n_kv_heads * s.head_dim * ((double)kv->max_prefix_len * rows->batch);
       e = timed(st, EAGLE_ROLE_ATTN, kv_bytes + 8.0 * M * hq, 4.0 * M * s.n_heads * s.head_dim * kv->max_prefix_len,
-                [&] { return launch_attention(at, bf16, s.head_dim, st); });
+                [&] { return launch_attention(at, bf16, s.head_dim, max_q, st); });
       if (e != hipSuccess) return hip_fail(e);
     }
     // a6: h = x + attn wo^T; sums of squares and h * g2 for RMSNorm 2

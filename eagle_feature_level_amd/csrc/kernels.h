@@ -44,9 +44,15 @@ struct RowSetupArgs {
 };
 hipError_t launch_row_setup(const RowSetupArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_rope_kv(const RopeArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_attention(const AttnArgs& a, bool bf16, int hd, hipStream_t s);
-int attn_split_len(int max_prefix, int batch, int hkv);
-int attn_n_splits(int max_prefix, int split_len);
+// Key splits of one attention call: split s covers prefix keys [s*split_len,
+// (s+1)*split_len).  bf16: the tree slots go with the last split; fp32: they
+// are one more split of their own.  max_queries = most rows of one sequence
+// times query heads per kv head.
+struct AttnPlan {
+  int split_len, n_splits;
+};
+AttnPlan attn_plan(bool bf16, int max_prefix, int batch, int hkv, int max_queries);
+hipError_t launch_attention(const AttnArgs& a, bool bf16, int hd, int max_queries, hipStream_t s);
 
 // softmax + top-k
 size_t topk_workspace_bytes(int n_rows, int vocab);
