@@ -346,7 +346,14 @@ __global__ void __launch_bounds__(128) attn_combine_kernel(AttnArgs a, int hd) {
 // ---------------------------------------------------------------------------
 constexpr int AQ = 64;          // queries per workgroup
 constexpr int AKROW = 128 + 8;  // K tile row (bf16): 272 B, rows land 4 banks apart
-constexpr int AVROW = KT + 4;   // transposed V tile row (bf16): 136 B, 8-byte aligned
+constexpr int AVROW = KT + 8;   // transposed V tile row (bf16): 144 B, 16-byte aligned
+
+// Transposed V tile, row d = one dim.  Keys are stored in the order the PV
+// MFMA consumes them: lane group gq of 32-key chunk kc takes keys
+// kc*32 + 4gq + {0..3} and kc*32 + 16 + 4gq + {0..3}, so 4-key group k' (keys
+// 4k'..4k'+3) sits at slot (k'/8)*8 + (k'%4)*2 + (k'/4)%2 (4 keys per slot)
+// and a lane's 8 keys are one 16-byte read.
+__device__ __forceinline__ int vt_col(int key4) { return ((key4 >> 3) * 8 + (key4 & 3) * 2 + ((key4 >> 2) & 1)) << 2; }
 
 __device__ __forceinline__ floatx4 mfma16a(u32x4 a, u32x4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -362,7 +369,7 @@ __device__ __forceinline__ uint32_t asplit2(float a, float b, uint32_t* lo) {
   return __builtin_amdgcn_perm(ub, ua, 0x07060302u);
 }
 
-__global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t ks[KT][AKROW];
   __shared__ __attribute__((aligned(16))) bf16_t vt[128][AVROW];
   __shared__ unsigned long long umask_s;
@@ -386,6 +393,44 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
   const bf16_t* tk = (const bf16_t*)a.tree_k + ((size_t)b * 64 * a.hkv + g) * 128;  // slot stride hkv*128
   const bf16_t* tv = (const bf16_t*)a.tree_v + ((size_t)b * 64 * a.hkv + g) * 128;
 
+  // tile staging: thread t holds keys skey..skey+3, dims sdim..sdim+7 of K (16
+  // lanes cover a key row) and keys vkey..vkey+3, dims vdim..vdim+7 of V (16
+  // lanes cover one dim of 64 keys, so each transposed V row is written as one
+  // contiguous 128-byte span)
+  const int skey = (threadIdx.x >> 4) * 4, sdim = (threadIdx.x & 15) * 8;
+  const int vkey = (threadIdx.x & 15) * 4, vdim = (threadIdx.x >> 4) * 8;
+  u32x4 kr[4], vr[4];
+  const bf16_t* pk0 = pk + (size_t)(kbeg + skey) * 128 + sdim;  // this thread's first key row
+  const bf16_t* pv0 = pv + (size_t)(kbeg + vkey) * 128 + vdim;
+  auto load_prefix_tile = [&](int t) {
+    const int tlen = min(KT, kend - (kbeg + t * KT));
+    const bf16_t* k1 = pk0 + (size_t)t * KT * 128;
+    const bf16_t* v1 = pv0 + (size_t)t * KT * 128;
+    if (tlen == KT) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        kr[u] = *(const u32x4*)(k1 + u * 128);
+        vr[u] = *(const u32x4*)(v1 + u * 128);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        kr[u] = (skey + u < tlen) ? *(const u32x4*)(k1 + u * 128) : u32x4{0, 0, 0, 0};
+        vr[u] = (vkey + u < tlen) ? *(const u32x4*)(v1 + u * 128) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto load_tree_tile = [&](uint64_t um) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = skey + u, jv = vkey + u;
+      kr[u] = ((um >> j) & 1ull) ? *(const u32x4*)(tk + (size_t)j * a.hkv * 128 + sdim) : u32x4{0, 0, 0, 0};
+      vr[u] = ((um >> jv) & 1ull) ? *(const u32x4*)(tv + (size_t)jv * a.hkv * 128 + vdim) : u32x4{0, 0, 0, 0};
+    }
+  };
+  // the first prefix tile does not depend on anything below: start it now
+  if (n_prefix_tiles > 0) load_prefix_tile(0);
+
   // tree slots any row of this sequence may see (only those are loaded)
   if (threadIdx.x == 0) umask_s = 0ull;
   __syncthreads();
@@ -401,7 +446,8 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
   u32x4 qh[4], ql[4];  // B operand: lane (query c, group gq) holds dims dc*32 + gq*8 + i
   {
     const float* qp = a.q + ((size_t)row * a.hq + h) * 128;
-    const float sc = rsqrtf(128.f);
+    // scores come out in log2 units: softmax weights are then plain 2^x
+    const float sc = rsqrtf(128.f) * 1.4426950408889634f;
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
       float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
@@ -419,53 +465,34 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
   __syncthreads();  // umask_s complete
   const uint64_t umask = umask_s;
 
-  // tile staging: thread t, part u: key (t + 256u) / 16, dims 8 * ((t + 256u) % 16) .. +7
-  u32x4 kr[4], vr[4];
-  auto load_tile = [&](int t) {
-    const bool tree_tile = (t == n_prefix_tiles);
-    const int k0 = kbeg + t * KT;
-    const int tlen = tree_tile ? KT : min(KT, kend - k0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = threadIdx.x + u * 256;
-      const int j = i >> 4, dd = (i & 15) * 8;
-      kr[u] = u32x4{0, 0, 0, 0};
-      vr[u] = u32x4{0, 0, 0, 0};
-      if (tree_tile) {
-        if ((umask >> j) & 1ull) {
-          kr[u] = *(const u32x4*)(tk + (size_t)j * a.hkv * 128 + dd);
-          vr[u] = *(const u32x4*)(tv + (size_t)j * a.hkv * 128 + dd);
-        }
-      } else if (j < tlen) {
-        kr[u] = *(const u32x4*)(pk + (size_t)(k0 + j) * 128 + dd);
-        vr[u] = *(const u32x4*)(pv + (size_t)(k0 + j) * 128 + dd);
-      }
-    }
-  };
 
   float m_run = -INFINITY, l_run = 0.f;
   floatx4 oacc[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if (n_tiles > 0) load_tile(0);
+  if (n_prefix_tiles == 0 && n_tiles > 0) load_tree_tile(umask);
   for (int t = 0; t < n_tiles; ++t) {
     const bool tree_tile = (t == n_prefix_tiles);
     const int tlen = tree_tile ? KT : min(KT, kend - (kbeg + t * KT));
     __syncthreads();  // previous tile fully used
+    // K rows as loaded; V transposed in registers: dim vdim+d gets keys vkey..vkey+3
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = threadIdx.x + u * 256;
-      const int j = i >> 4, dd = (i & 15) * 8;
-      *(u32x4*)&ks[j][dd] = kr[u];
+    for (int u = 0; u < 4; ++u) *(u32x4*)&ks[skey + u][sdim] = kr[u];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[dd + 2 * e][j] = (bf16_t)(vr[u][e] & 0xffffu);
-        vt[dd + 2 * e + 1][j] = (bf16_t)(vr[u][e] >> 16);
-      }
+    for (int e = 0; e < 4; ++e) {
+      // even dim 2e: low halves; odd dim 2e+1: high halves
+      const uint32_t lo01 = __builtin_amdgcn_perm(vr[1][e], vr[0][e], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(vr[3][e], vr[2][e], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(vr[1][e], vr[0][e], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(vr[3][e], vr[2][e], 0x07060302u);
+      const int col = vt_col(vkey >> 2);
+      *(uint2*)&vt[vdim + 2 * e][col] = make_uint2(lo01, lo23);
+      *(uint2*)&vt[vdim + 2 * e + 1][col] = make_uint2(hi01, hi23);
     }
     __syncthreads();
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    if (t + 1 < n_prefix_tiles) load_prefix_tile(t + 1);
+    else if (t + 1 == n_prefix_tiles && with_tree) load_tree_tile(umask);
 
     // S^T: lane (query c, gq) gets keys kb*16 + 4*gq + v, v < 4
     floatx4 sacc[4];
@@ -480,37 +507,50 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
       }
     }
     float sv[4][4];
-    float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int kk = kb * 16 + gq * 4 + v;
-        const bool ok = tree_tile ? ((qmask >> kk) & 1ull) != 0 : (kk < tlen && qv);
-        sv[kb][v] = ok ? sacc[kb][v] : -INFINITY;
-        mx = fmaxf(mx, sv[kb][v]);
-      }
+      for (int v = 0; v < 4; ++v) sv[kb][v] = sacc[kb][v];
+    if (tree_tile || tlen < KT) {  // uniform: only the tree tile and a ragged last tile mask keys
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int kk = kb * 16 + gq * 4 + v;
+          const bool ok = tree_tile ? ((qmask >> kk) & 1ull) != 0 : kk < tlen;
+          if (!ok) sv[kb][v] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mx = fmaxf(fmaxf(mx, fmaxf(sv[kb][0], sv[kb][1])), fmaxf(sv[kb][2], sv[kb][3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
     mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
     const float mnew = fmaxf(m_run, mx);
-    const float alpha = (m_run > -INFINITY) ? __expf(m_run - mnew) : 0.f;
+    // rows whose keys so far are all masked keep mnew = -inf: their weights are 0
+    const float mref = (mnew > -INFINITY) ? mnew : 0.f;
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float p = (sv[kb][v] > -INFINITY) ? __expf(sv[kb][v] - mnew) : 0.f;
+        const float p = __builtin_amdgcn_exp2f(sv[kb][v] - mref);  // 2^-inf = 0
         sv[kb][v] = p;
         ps += p;
       }
     ps += __shfl_xor(ps, 16, WAVE);
     ps += __shfl_xor(ps, 32, WAVE);
-    l_run = l_run * alpha + ps;
-    m_run = mnew;
+    if (mnew != m_run) {
+      // rescale only when a running max moved (exact: otherwise the factor is 1)
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mref);  // m_run = -inf -> 0
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      oacc[db][0] *= alpha; oacc[db][1] *= alpha; oacc[db][2] *= alpha; oacc[db][3] *= alpha;
+      for (int db = 0; db < 8; ++db) {
+        oacc[db][0] *= alpha; oacc[db][1] *= alpha; oacc[db][2] *= alpha; oacc[db][3] *= alpha;
+      }
     }
+    l_run += ps;
+    m_run = mnew;
     // O^T += V^T P^T over two 32-key chunks: chunk kc uses key blocks 2kc, 2kc+1
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
@@ -522,10 +562,8 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
       Bh[3] = asplit2(sv[2 * kc + 1][2], sv[2 * kc + 1][3], &l); Bl[3] = l;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const bf16_t* vr0 = &vt[db * 16 + c][kc * 32 + gq * 4];
-        const uint2 x0 = *(const uint2*)vr0;
-        const uint2 x1 = *(const uint2*)(vr0 + 16);
-        const u32x4 A = u32x4{x0.x, x0.y, x1.x, x1.y};
+        const int d = db * 16 + c;
+        const u32x4 A = *(const u32x4*)&vt[d][(kc * 8 + gq * 2) * 4];
         oacc[db] = mfma16a(A, Bh, oacc[db]);
         oacc[db] = mfma16a(A, Bl, oacc[db]);
       }
@@ -549,7 +587,7 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
       d4[0] = oacc[db][0]; d4[1] = oacc[db][1]; d4[2] = oacc[db][2]; d4[3] = oacc[db][3];
     }
     if (gq == 0) {
-      dst[0] = m_run;
+      dst[0] = m_run * 0.6931471805599453f;  // back to natural-log units for the combine
       dst[1] = l_run;
     }
   }
