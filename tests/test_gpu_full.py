@@ -1,0 +1,217 @@
+"""Full-size staged parity of a whole round on the EAGLE-2 workloads.
+
+The 7B EAGLE-2 (prefix 2048, k 10, depth 6, 60 nodes), 13B batched (8
+sequences, ragged prefixes 512..4096) and 70B GQA (16 sequences, 64/8 heads,
+prefix 4096) workloads each run one round on the GPU at full size, in the
+launch configuration the benchmark uses; the oracle then checks every stage
+from the GPU's own inputs to that stage:
+
+* floats (root head, one per-depth draft step, the tree-wide step): sampled
+  rows recomputed by the fp64 oracle from the same parent features, tokens,
+  positions, masks and tree K/V (ancestor slots as the GPU wrote them), within
+  2e-2 max-abs;
+* top-k of every draft row: bit-exact indices on the GPU's fp32 logits;
+* tree: the oracle's expand / rerank / flatten driven by the GPU's top-k
+  reproduces every step's rows, the flattened tree and the tree-wide rows
+  bit-exactly;
+* verify: bit-exact paths, lengths, next tokens and flags on the GPU's fp32
+  logits, except near-ties flagged by the oracle's margins (at most 2).
+"""
+import numpy as np
+import pytest
+import torch
+
+from eagle_feature_level_amd.engine import EagleRound
+from oracle import draft as OD
+from oracle import pipeline as OP
+from oracle import tree as OT
+from oracle.topk import softmax_topk as o_topk
+from workloads import (CONFIGS, TEMPLATES, make_prefix_kv, make_prefix_lens, make_root_features, make_root_tokens,
+                       make_target_noise, make_weights)
+from workloads import device as dev
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+AMBIG = 1e-5
+AMBIG_DRAW = 3e-6
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _run_round(cid):
+    cfg = CONFIGS[cid]
+    s = cfg.shape
+    w = make_weights(cfg)
+    lens = make_prefix_lens(cfg)
+    ks, vs = make_prefix_kv(cfg, lens)
+    feat = make_root_features(cfg)
+    tok = make_root_tokens(cfg)
+    kind = "dynamic" if cfg.tree == "dynamic" else "static"
+    eng = EagleRound(dev.shape_dict(s), dev.weights(w, s.dtype), cfg.batch, kind, cfg.topk, cfg.depth, cfg.rerank_m,
+                     TEMPLATES.get(cfg.tree), dev.prefix(ks, vs, lens, s.dtype))
+    eng.draft_phase(torch.from_numpy(feat).cuda(), dev.ints(tok))
+    eng.tree_wide()
+    torch.cuda.synchronize()
+    return cfg, eng, w, lens, ks, vs, feat, tok
+
+
+def _step_rows(st, B):
+    """The GPU's rows of one draft step as the oracle's row dict."""
+    rs = _np(st.row_start)
+    seq = np.zeros(int(rs[B]), np.int64)
+    for b in range(B):
+        seq[rs[b]:rs[b + 1]] = b
+    return dict(seq=seq, token=_np(st.token).astype(np.int64), parent=_np(st.parent).astype(np.int64),
+                pos=_np(st.pos).astype(np.int64), slot=_np(st.slot).astype(np.int64),
+                mask=_np(st.mask).view(np.uint64))
+
+
+def _sample(rows, idx):
+    return {k: [v[i] for i in idx] for k, v in rows.items()}
+
+
+def _check_floats(cfg, w, rows, sample, feat_buf, ks, vs, lens, tk, tv, got_feat, got_logits):
+    ref = OD.draft_step(cfg.shape, w, _sample(rows, sample), feat_buf, ks, vs, lens, tk.copy(), tv.copy(), mirror=True)
+    ef = float(np.max(np.abs(got_feat[sample] - ref["feat"])))
+    el = float(np.max(np.abs(got_logits[sample] - ref["logits"])))
+    assert ef < TOL_BF16 and el < TOL_BF16, (ef, el)
+    return ef, el
+
+
+def _staged_parity(cid, n_sample=3):
+    cfg, eng, w, lens, ks, vs, feat, tok = _run_round(cid)
+    s, B, k = cfg.shape, cfg.batch, cfg.topk
+    g = np.random.default_rng(100 + cid)
+    feat_buf = _np(eng.feat).astype(np.float64)
+    logits = _np(eng.logits)
+    gidx, glogq = _np(eng.topk_idx), _np(eng.topk_logq)
+
+    # root head on two sequences
+    for b in sorted(set([0, B - 1])):
+        ref = OD.head_logits(s, w, feat[b:b + 1])
+        assert np.max(np.abs(logits[b] - ref[0])) < TOL_BF16
+
+    # top-k of every draft row, on the GPU's logits
+    lse_o, idx_o, logq_o = o_topk(logits, k)
+    assert np.array_equal(gidx[:, :k], idx_o), "top-k indices"
+    # fp32 logit - lse against fp64 from the same fp32 logits: a few ulps of the
+    # operands (peaked rows have lse in the hundreds and logq near 0)
+    big = np.abs(lse_o)[:, None] + np.abs(logq_o + lse_o[:, None])
+    assert np.all(np.abs(glogq[:, :k] - logq_o) <= 4e-7 * big + 4e-6)
+    assert np.all(np.abs(_np(eng.lse) - lse_o) <= 4e-7 * np.abs(lse_o) + 4e-6)
+
+    # tree construction driven by the GPU's top-k
+    pools = [OT.Pool(int(tok[b]), b) for b in range(B)]
+    frontier = [[0] for _ in range(B)]
+    sel = [([gidx[b]], [glogq[b]]) for b in range(B)]
+    for d in range(cfg.depth):
+        for b in range(B):
+            frontier[b] = OT.expand(pools[b], frontier[b], sel[b][0], sel[b][1], k, None)
+        if d == cfg.depth - 1:
+            break
+        st = eng.steps[d]
+        rows = _step_rows(st, B)
+        want = {key: [] for key in ("token", "parent", "pos", "slot", "mask")}
+        base = st.feat_row0
+        for b in range(B):
+            for (t_, p_, pos_, sl_, m_) in OT.assign_rows(pools[b], frontier[b], d, k, False, base + len(want["token"]),
+                                                          int(lens[b])):
+                want["token"].append(t_)
+                want["parent"].append(p_)
+                want["pos"].append(pos_)
+                want["slot"].append(sl_)
+                want["mask"].append(m_)
+        for key in want:
+            assert [int(x) for x in rows[key]] == [int(x) for x in want[key]], (d, key)
+        o = 0
+        for b in range(B):
+            nf = len(frontier[b])
+            r0 = base + o
+            sel[b] = ([gidx[r0 + f] for f in range(nf)], [glogq[r0 + f] for f in range(nf)])
+            o += nf
+    N = eng.n_nodes
+    tree = {key: _np(v) for key, v in eng.tree.items()}
+    trees = []
+    for b in range(B):
+        tr = OT.finalize(pools[b], cfg.rerank_m)
+        trees.append(tr)
+        sl = slice(b * N, (b + 1) * N)
+        assert list(tree["parent"][sl]) == list(tr["parent"]), b
+        assert list(tree["token"][sl]) == list(tr["token"]), b
+        assert list(tree["depth"][sl]) == list(tr["depth"]), b
+        assert list(tree["mask"][sl].view(np.uint64)) == list(tr["mask"]), b
+        qrow = [pools[b].feat_row[int(pid)] for pid in tr["pool_id"]]
+        assert list(tree["qrow"][sl]) == qrow, b
+
+    # floats of one per-depth step (the second, so ancestors come from an earlier step)
+    tk = _np(eng.tree_k.float()).astype(np.float64)
+    tv = _np(eng.tree_v.float()).astype(np.float64)
+    d = min(1, len(eng.steps) - 1)
+    st = eng.steps[d]
+    rows = _step_rows(st, B)
+    n = len(rows["seq"])
+    smp = sorted(set([0, n - 1] + list(g.integers(0, n, n_sample - 2))))
+    gf = _np(eng.feat[st.feat_row0:st.feat_row0 + n])
+    gl = logits[st.feat_row0:st.feat_row0 + n]
+    _check_floats(cfg, w, rows, smp, feat_buf, ks, vs, lens, tk, tv, gf, gl)
+
+    # tree-wide rows: the flattened tree's nodes with their parents' feature rows
+    tw = {key: _np(v) for key, v in eng.tw.items()}
+    tw_rows = dict(seq=np.repeat(np.arange(B), N - 1), token=tw["token"].astype(np.int64),
+                   parent=tw["parent"].astype(np.int64), pos=tw["pos"].astype(np.int64),
+                   slot=tw["slot"].astype(np.int64), mask=tw["mask"].view(np.uint64))
+    for b in range(B):
+        tr, pool = trees[b], pools[b]
+        for t in range(1, N):
+            i = b * (N - 1) + t - 1
+            pid = int(tr["pool_id"][t])
+            assert tw_rows["token"][i] == tr["token"][t]
+            assert tw_rows["parent"][i] == pool.feat_row[pool.parent[pid]]
+            assert tw_rows["pos"][i] == int(lens[b]) + int(tr["depth"][t]) - 1
+            assert tw_rows["slot"][i] == t and int(tw_rows["mask"][i]) == int(tr["mask"][t])
+    ttk = _np(eng.tw_tree_k.float()).astype(np.float64)
+    ttv = _np(eng.tw_tree_v.float()).astype(np.float64)
+    nw = B * (N - 1)
+    smp = sorted(set([0, nw - 1] + list(g.integers(0, nw, n_sample - 2))))
+    _check_floats(cfg, w, tw_rows, smp, feat_buf, ks, vs, lens, ttk, ttv, _np(eng.tw_feat), _np(eng.tw_logits))
+
+    # verification on the GPU's fp32 logits (root target = root draft row)
+    V = s.vocab
+    noise = make_target_noise(cfg, B * N)
+    twl = _np(eng.tw_logits)
+    tgt = np.empty((B * N, V), np.float32)
+    for b in range(B):
+        tgt[b * N] = logits[b]
+        tgt[b * N + 1:(b + 1) * N] = twl[b * (N - 1):(b + 1) * (N - 1)] + noise[b * N + 1:(b + 1) * N]
+    qrows = [tree["qrow"][b * N:(b + 1) * N].astype(np.int64) for b in range(B)]
+    ambiguous = 0
+    for rnd in range(2):
+        eng.verify(torch.from_numpy(tgt).cuda(), 0, rnd)
+        torch.cuda.synchronize()
+        path, vlen, vnext, vflags = _np(eng.v_path), _np(eng.v_len), _np(eng.v_next), _np(eng.v_flags)
+        want = OP.verify_all(trees, [tgt[b * N:(b + 1) * N] for b in range(B)], logits, qrows, 0, rnd)
+        for b in range(B):
+            ref = want[b]
+            if (ref["margins"] and min(ref["margins"]) < AMBIG) or ref["draw_margin"] < AMBIG_DRAW:
+                ambiguous += 1
+                continue
+            assert vlen[b] == ref["accept_len"], (rnd, b)
+            assert list(path[b * N:b * N + len(ref["path"])]) == ref["path"], (rnd, b)
+            assert vnext[b] == ref["next_token"], (rnd, b)
+            assert vflags[b] == ref["flags"], (rnd, b)
+    assert ambiguous <= 2, ambiguous
+
+
+def test_7b_eagle2_round_staged_parity():
+    _staged_parity(3)
+
+
+def test_13b_batched_ragged_round_staged_parity():
+    _staged_parity(4)
+
+
+def test_70b_gqa_batched_round_staged_parity():
+    _staged_parity(5)
