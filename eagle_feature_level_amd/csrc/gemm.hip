@@ -1,15 +1,16 @@
 // Draft-head GEMMs on gfx950: y[M, N] = x[M, K] W[N, K]^T.
 //
 // The draft step's GEMMs stream the whole draft head and the LM head once per
-// call; with M <= 160 rows they are bound by HBM, not by the matrix units
-// (arithmetic intensity ~M flop/byte against a ridge of ~315).  So:
+// call; with a few rows they are bound by HBM, not by the matrix units
+// (arithmetic intensity ~M flop/byte against a ridge of ~315); the tree-wide
+// step over hundreds of rows is bound by the matrix units.  So:
 //  * W (bf16) is the MFMA "A" operand and goes straight from HBM to VGPRs, each
 //    lane pulling 64 contiguous bytes of a row per step; W is never staged
 //    through LDS because every W element is used by exactly one wave.
 //  * x (fp32) is the MFMA "B" operand (M padded to 16).  The skinny kernel
 //    (M <= 16) loads each k-step's rows of x coalesced and re-reads them in the
-//    B layout from the wave's own LDS slice; the tiled kernel stages x through
-//    LDS so the waves of a workgroup share it.
+//    B layout from the wave's own LDS slice; the large-M kernel stages weight
+//    and x tiles through LDS so the waves of a workgroup share both.
 //  * Activations enter the matrix units as a pair of bf16 values, hi = x cut
 //    to bf16 and lo = bf16(x - hi), two MFMAs into one fp32 accumulator: the
 //    product then carries ~16 significant bits of x instead of 8, which keeps a
@@ -37,7 +38,6 @@
 namespace {
 
 constexpr int SK_KSTEP = 128;  // K covered by one wave iteration (4 lane groups x 32)
-constexpr int TL_BK = 64;      // K per tiled-kernel stage
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -108,13 +108,6 @@ __device__ __forceinline__ B8 split8(float4 v0, float4 v1) {
 
 __device__ __forceinline__ float4 as_f4(u32x4 v) {
   return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
-}
-
-// Eight operand values of row m at columns k..k+7 (k % 8 == 0) as (hi, lo).
-__device__ __forceinline__ B8 load_b8(const GemmArgs& a, int m, int k) {
-  const int row = a.xrows ? a.xrows[m] : m;
-  const float4* p = (const float4*)((const float*)a.x + (size_t)row * a.ldx + k);
-  return split8(p[0], p[1]);
 }
 
 __device__ __forceinline__ floatx4 mfma16(u32x4 a, u32x4 b, floatx4 c) {
@@ -304,120 +297,197 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: 4 waves, each 16*AT weight rows x all 16*MT rows of x staged in
-// LDS; split-K over gridDim.y, M blocks over gridDim.z.  Writes fp32 partials;
-// gemm_reduce applies the epilogue.
+// Large-M kernel (M > 16): the matrix units are the bound once M reaches a few
+// hundred rows.  A workgroup of 8 waves computes 256 weight rows x 128 rows of
+// x (64 x 64 per wave, 4 x 4 blocks of v_mfma_f32_16x16x32_bf16, hi and lo).
+// Per 64-wide K step the weight tile and the hi/lo split of the x tile are
+// staged in LDS (two buffers); the next step's global loads sit in registers
+// while the current step is multiplied.  Row blocks of x vary fastest over the
+// grid, and consecutive tiles are kept on one XCD, so the workgroups sharing
+// a weight tile run together and share an L2.  With a K split the raw
+// partial sums go to a.part and gemm_reduce applies the epilogue; otherwise
+// the epilogue runs here on the accumulators.
+// SwiGLU: the 256 rows of a tile are, per wave quarter, 32 gate rows and the
+// 32 up rows of the same ffn columns, so gate and up meet in one lane.
 // ---------------------------------------------------------------------------
-template <int AT, int MT>
-__global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a) {
-  constexpr int BM = 16 * MT;
-  constexpr int LDSW = TL_BK + 8;  // padded row (bf16 elements)
-  __shared__ bf16_t xs[2][BM][LDSW];  // hi halves
-  __shared__ bf16_t xl[2][BM][LDSW];  // lo halves
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+constexpr int BG_BN = 256, BG_BM = 128, BG_BK = 64;
+constexpr int BG_LD = BG_BK + 8;  // LDS row (bf16): 144 B, rows 4 banks apart
+
+struct BigPlan {
+  int tiles_n, tiles_m, splits;
+};
+
+template <int EPI>
+__global__ void __launch_bounds__(512) gemm_big(GemmArgs a, BigPlan p) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BG_BN][BG_LD];
+  __shared__ __attribute__((aligned(16))) bf16_t Bh[2][BG_BM][BG_LD];
+  __shared__ __attribute__((aligned(16))) bf16_t Bl[2][BG_BM][BG_LD];
+  __shared__ float rs_s[BG_BM];
+  __shared__ float ssq_s[4][BG_BM];
+  const int nwg = gridDim.x, bid = blockIdx.x;
+  const int lid = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;  // consecutive tiles on one XCD
+  const int mt = lid % p.tiles_m, rest = lid / p.tiles_m;
+  const int nt = rest % p.tiles_n, sp = rest / p.tiles_n;
+  const int m0 = mt * BG_BM;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int wn = wv & 3, wm = wv >> 2;
   const int r = lane & 15, g = lane >> 4;
-  const int m_base = blockIdx.z * BM;
-  const int n_base = blockIdx.x * (64 * AT) + wv * 16 * AT;
-  const int kper = a.K / a.splits;  // multiple of TL_BK
-  const int k_begin = blockIdx.y * kper;
-  const int nkb = kper / TL_BK;
+  const int kper = a.K / p.splits, kbeg = sp * kper, nkb = kper / BG_BK;
 
-  const bf16_t* ap[AT];
-#pragma unroll
-  for (int at = 0; at < AT; ++at) {
-    const int n = n_base + at * 16 + r;
-    ap[at] = wrow<bf16_t>(a, n < a.N ? n : 0) + k_begin + g * 16;
-  }
-
-  constexpr int GROUPS = BM * (TL_BK / 8);  // 8-element groups per x tile
-  constexpr int GPT = (GROUPS + 255) / 256;
-  B8 xr[GPT];
-  auto load_x = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-      const int idx = threadIdx.x + i * 256;
-      const int mm = idx / (TL_BK / 8), kg = idx % (TL_BK / 8);
-      const int m = m_base + mm;
-      xr[i].hi = u32x4{0, 0, 0, 0};
-      xr[i].lo = u32x4{0, 0, 0, 0};
-      if (idx < GROUPS && m < a.M) xr[i] = load_b8(a, m, k_begin + kb * TL_BK + kg * 8);
+  // logical weight row of tile row i (-1 past the end)
+  auto wrow_of = [&](int i) -> int {
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int q = i >> 6, w = i & 63;
+      const int j = nt * 128 + q * 32 + (w & 31);
+      if (j >= a.ffn) return -1;
+      return (w < 32) ? j : a.ffn + j;
+    } else {
+      const int n = nt * BG_BN + i;
+      return n < a.N ? n : -1;
     }
   };
-  auto store_x = [&](int buf) {
+  // staging: weights rows t/8 + 64u, 8 columns at 8*(t%8); x rows t/16 + 32u, 4 columns at 4*(t%16)
+  const int ac = (t & 7) * 8, xc = (t & 15) * 4;
+  const bf16_t* ap[4];
+  const float* xp[4];
 #pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-      const int idx = threadIdx.x + i * 256;
-      if (idx < GROUPS) {
-        const int mm = idx / (TL_BK / 8), kg = idx % (TL_BK / 8);
-        *(u32x4*)&xs[buf][mm][kg * 8] = xr[i].hi;
-        *(u32x4*)&xl[buf][mm][kg * 8] = xr[i].lo;
+  for (int u = 0; u < 4; ++u) {
+    const int n = wrow_of((t >> 3) + 64 * u);
+    ap[u] = (n >= 0) ? wrow<bf16_t>(a, n) + kbeg + ac : nullptr;
+    const int m = m0 + (t >> 4) + 32 * u;
+    xp[u] = (m < a.M) ? a.x + (size_t)(a.xrows ? a.xrows[m] : m) * a.ldx + kbeg + xc : nullptr;
+  }
+  u32x4 areg[4];
+  float4 xreg[4];
+  auto load_global = [&](int kb) {
+    const int k0 = kb * BG_BK;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      areg[u] = ap[u] ? *(const u32x4*)(ap[u] + k0) : u32x4{0, 0, 0, 0};
+      xreg[u] = xp[u] ? *(const float4*)(xp[u] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store_lds = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      *(u32x4*)&As[buf][(t >> 3) + 64 * u][ac] = areg[u];
+      uint32_t l0, l1;
+      const uint32_t h0 = split2(xreg[u].x, xreg[u].y, &l0), h1 = split2(xreg[u].z, xreg[u].w, &l1);
+      *(uint2*)&Bh[buf][(t >> 4) + 32 * u][xc] = make_uint2(h0, h1);
+      *(uint2*)&Bl[buf][(t >> 4) + 32 * u][xc] = make_uint2(l0, l1);
+    }
+  };
+
+  const bool fused = (p.splits == 1);
+  if (fused && a.sumsq_in && t < BG_BM) rs_s[t] = (m0 + t < a.M) ? row_scale(a, m0 + t) : 1.f;
+
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  load_global(0);
+  store_lds(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < nkb) load_global(kb + 1);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      u32x4 A[4], Bhf[4], Blf[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) A[nb] = *(const u32x4*)&As[buf][wn * 64 + nb * 16 + r][kc * 32 + g * 8];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        Bhf[mb] = *(const u32x4*)&Bh[buf][wm * 64 + mb * 16 + r][kc * 32 + g * 8];
+        Blf[mb] = *(const u32x4*)&Bl[buf][wm * 64 + mb * 16 + r][kc * 32 + g * 8];
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          acc[nb][mb] = mfma16(A[nb], Bhf[mb], acc[nb][mb]);
+          acc[nb][mb] = mfma16(A[nb], Blf[mb], acc[nb][mb]);
+        }
+    }
+    if (kb + 1 < nkb) store_lds(buf ^ 1);
+    __syncthreads();
+  }
+
+  // lane (r, g): acc[nb][mb][v] = tile row wn*64 + nb*16 + 4g + v, x row wm*64 + mb*16 + r
+  if (!fused) {
+    float* P = a.part + (size_t)sp * a.M * a.N;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + wm * 64 + mb * 16 + r;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int n = wrow_of(wn * 64 + nb * 16 + 4 * g);  // 4 consecutive logical rows
+        if (n >= 0) *(floatx4*)(P + (size_t)m * a.N + n) = acc[nb][mb];
       }
     }
-  };
-
-  floatx4 acc[AT][MT];
-#pragma unroll
-  for (int at = 0; at < AT; ++at)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[at][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 A0[AT][2], A1[AT][2];
-  auto loadA = [&](u32x4 (&dst)[AT][2], int kb) {
-#pragma unroll
-    for (int at = 0; at < AT; ++at)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) dst[at][j] = *(const u32x4*)(ap[at] + (size_t)kb * TL_BK + j * 8);
-  };
-  auto compute = [&](const u32x4 (&A)[AT][2], int buf) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      u32x4 B[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) B[mt] = *(const u32x4*)&xs[buf][mt * 16 + r][g * 16 + j * 8];
-#pragma unroll
-      for (int at = 0; at < AT; ++at)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[at][mt] = mfma16(A[at][j], B[mt], acc[at][mt]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) B[mt] = *(const u32x4*)&xl[buf][mt * 16 + r][g * 16 + j * 8];
-#pragma unroll
-      for (int at = 0; at < AT; ++at)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[at][mt] = mfma16(A[at][j], B[mt], acc[at][mt]);
-    }
-  };
-
-  load_x(0);
-  store_x(0);
-  loadA(A0, 0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; kb += 2) {
-    if (kb + 1 < nkb) {
-      loadA(A1, kb + 1);
-      load_x(kb + 1);
-    }
-    compute(A0, 0);
-    if (kb + 1 < nkb) store_x(1);
-    __syncthreads();
-    if (kb + 1 >= nkb) break;
-    if (kb + 2 < nkb) {
-      loadA(A0, kb + 2);
-      load_x(kb + 2);
-    }
-    compute(A1, 1);
-    if (kb + 2 < nkb) store_x(0);
-    __syncthreads();
+    return;
   }
-
-  float* P = a.part + (size_t)blockIdx.y * a.M * a.N;
+  if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-  for (int at = 0; at < AT; ++at) {
-    const int n = n_base + at * 16 + g * 4;
-    if (n >= a.N) continue;
+    for (int mb = 0; mb < 4; ++mb) {
+      const int ml = wm * 64 + mb * 16 + r, m = m0 + ml;
+      if (m >= a.M) continue;
+      const float sc = a.sumsq_in ? rs_s[ml] : 1.f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = m_base + mt * 16 + r;
-      if (m < a.M) *(floatx4*)(P + (size_t)m * a.N + n) = acc[at][mt];
+      for (int nb = 0; nb < 2; ++nb) {
+        const int j = nt * 128 + wn * 32 + nb * 16 + 4 * g;
+        if (j >= a.ffn) continue;
+        float4 o;
+        o.x = silu_f(acc[nb][mb][0] * sc) * (acc[nb + 2][mb][0] * sc);
+        o.y = silu_f(acc[nb][mb][1] * sc) * (acc[nb + 2][mb][1] * sc);
+        o.z = silu_f(acc[nb][mb][2] * sc) * (acc[nb + 2][mb][2] * sc);
+        o.w = silu_f(acc[nb][mb][3] * sc) * (acc[nb + 2][mb][3] * sc);
+        *(float4*)(a.yb + (size_t)m * a.ldyb + j) = o;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int ml = wm * 64 + mb * 16 + r, m = m0 + ml;
+      const bool mv = m < a.M;
+      const float sc = (mv && a.sumsq_in) ? rs_s[ml] : 1.f;
+      float ss = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int n = nt * BG_BN + wn * 64 + nb * 16 + 4 * g;
+        if (!mv || n >= a.N) continue;
+        float4 y = make_float4(acc[nb][mb][0] * sc, acc[nb][mb][1] * sc, acc[nb][mb][2] * sc, acc[nb][mb][3] * sc);
+        if constexpr (EPI == EPI_BIAS_SUMSQ) {
+          const bf16_t* bb = (const bf16_t*)a.bias + n;
+          y.x += bf2f(bb[0]); y.y += bf2f(bb[1]); y.z += bf2f(bb[2]); y.w += bf2f(bb[3]);
+        }
+        if constexpr (EPI == EPI_RESID || EPI == EPI_RESID_SUMSQ) {
+          const float4 rr = *(const float4*)(a.resid + (size_t)m * a.ldr + n);
+          y.x += rr.x; y.y += rr.y; y.z += rr.z; y.w += rr.w;
+        }
+        *(float4*)(a.y + (size_t)m * a.ldy + n) = y;
+        if (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
+          if (a.y2) {
+            const bf16_t* gn = (const bf16_t*)a.gain_out + n;
+            *(float4*)(a.y2 + (size_t)m * a.ldy + n) =
+                make_float4(y.x * bf2f(gn[0]), y.y * bf2f(gn[1]), y.z * bf2f(gn[2]), y.w * bf2f(gn[3]));
+          }
+          ss += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+        }
+      }
+      if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
+        ss += __shfl_xor(ss, 16, WAVE);
+        ss += __shfl_xor(ss, 32, WAVE);
+        if (g == 0) ssq_s[wn][ml] = ss;
+      }
+    }
+    if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
+      __syncthreads();
+      if (t < BG_BM && m0 + t < a.M)
+        a.sumsq_out[(size_t)nt * a.M + m0 + t] = ssq_s[0][t] + ssq_s[1][t] + ssq_s[2][t] + ssq_s[3][t];
     }
   }
 }
@@ -576,69 +646,58 @@ hipError_t skinny_launch(const GemmArgs& a, int epi, int* n_part, hipStream_t s)
   return skinny_mq<1, 8>(a, epi, n_part, s);
 }
 
-struct TiledPlan {
-  int mt, mblocks, splits, ntiles;
-};
-
-TiledPlan plan_tiled(int M, int N, int K) {
-  TiledPlan p;
-  // one M block if it fits in 160 rows (weights read once); else blocks of 128
-  if (M <= 160) {
-    p.mt = (M + 15) / 16;
-    p.mt = p.mt <= 4 ? 4 : (p.mt <= 6 ? 6 : (p.mt <= 8 ? 8 : 10));
-    p.mblocks = 1;
-  } else {
-    p.mt = 8;
-    p.mblocks = (M + 127) / 128;
-  }
-  p.ntiles = (N + 127) / 128;
-  const int wgs = p.ntiles * p.mblocks;
-  int splits = 1;
-  while (wgs * splits < 512 && (K % (TL_BK * splits * 2)) == 0 && K / (splits * 2) >= 256) splits *= 2;
-  p.splits = splits;
+// Tiles of the large-M kernel, plus a K split (powers of 2) while the grid
+// has fewer than 256 workgroups (one per CU: the kernel holds 148 KB of LDS).
+BigPlan plan_big(int M, int N, int K, bool swiglu) {
+  BigPlan p;
+  p.tiles_n = swiglu ? (N / 2 + 127) / 128 : (N + BG_BN - 1) / BG_BN;
+  p.tiles_m = (M + BG_BM - 1) / BG_BM;
+  p.splits = 1;
+  while (p.tiles_n * p.tiles_m * p.splits < 256 && K % (BG_BK * p.splits * 2) == 0 && K / (p.splits * 2) >= 512)
+    p.splits *= 2;
   return p;
-}
-
-template <int MT>
-hipError_t tiled_launch(const GemmArgs& a, const TiledPlan& p, hipStream_t s) {
-  dim3 grid(p.ntiles, p.splits, p.mblocks), blk(256);
-  hipLaunchKernelGGL((gemm_tiled<2, MT>), grid, blk, 0, s, a);
-  return hipGetLastError();
 }
 
 }  // namespace
 
 size_t gemm_bf16_partial_bytes(int M, int N, int K) {
   if (M <= 16) return 0;
-  TiledPlan p = plan_tiled(M, N, K);
-  return (size_t)p.splits * M * N * sizeof(float);
+  const BigPlan p = plan_big(M, N, K, false);  // N/2-wide SwiGLU tiles give no more splits than this
+  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s) {
   if (a.K % SK_KSTEP) return hipErrorInvalidValue;  // both kernels step K in whole 128-element blocks
   if ((epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) && a.y2 && !a.gain_out) return hipErrorInvalidValue;
   if (a.M <= 16) return skinny_launch(a, epi, n_part_out, s);
-  // tiled path; for SwiGLU the logical matrix is [gate; up] with N = 2*ffn
-  if (a.part == nullptr) return hipErrorInvalidValue;  // partial buffer is mandatory here
-  if (a.K % TL_BK) return hipErrorInvalidValue;
-  TiledPlan p = plan_tiled(a.M, a.N, a.K);
+  if (a.N % 4) return hipErrorInvalidValue;  // float4 epilogue stores
+  const bool sw = (epi == EPI_SWIGLU);
+  const BigPlan p = plan_big(a.M, a.N, a.K, sw);
   a.splits = p.splits;
-  hipError_t e;
-  switch (p.mt) {
-    case 4: e = tiled_launch<4>(a, p, s); break;
-    case 6: e = tiled_launch<6>(a, p, s); break;
-    case 8: e = tiled_launch<8>(a, p, s); break;
-    default: e = tiled_launch<10>(a, p, s); break;
-  }
-  if (e != hipSuccess) return e;
-  const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
-  dim3 grid((nout + 1023) / 1024, a.M), blk(256);
+  if (p.splits > 1 && a.part == nullptr) return hipErrorInvalidValue;  // partial buffer needed for a K split
+  const dim3 grid(p.tiles_n * p.tiles_m * p.splits), blk(512);
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL(gemm_reduce<EPI_STORE>, grid, blk, 0, s, a); break;
-    case EPI_BIAS_SUMSQ: hipLaunchKernelGGL(gemm_reduce<EPI_BIAS_SUMSQ>, grid, blk, 0, s, a); *n_part_out = grid.x; break;
-    case EPI_RESID: hipLaunchKernelGGL(gemm_reduce<EPI_RESID>, grid, blk, 0, s, a); break;
-    case EPI_RESID_SUMSQ: hipLaunchKernelGGL(gemm_reduce<EPI_RESID_SUMSQ>, grid, blk, 0, s, a); *n_part_out = grid.x; break;
-    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_reduce<EPI_SWIGLU>, grid, blk, 0, s, a); break;
+    case EPI_STORE: hipLaunchKernelGGL(gemm_big<EPI_STORE>, grid, blk, 0, s, a, p); break;
+    case EPI_BIAS_SUMSQ: hipLaunchKernelGGL(gemm_big<EPI_BIAS_SUMSQ>, grid, blk, 0, s, a, p); break;
+    case EPI_RESID: hipLaunchKernelGGL(gemm_big<EPI_RESID>, grid, blk, 0, s, a, p); break;
+    case EPI_RESID_SUMSQ: hipLaunchKernelGGL(gemm_big<EPI_RESID_SUMSQ>, grid, blk, 0, s, a, p); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_big<EPI_SWIGLU>, grid, blk, 0, s, a, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.splits == 1) {
+    if (epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) *n_part_out = p.tiles_n;
+    return hipSuccess;
+  }
+  const int nout = sw ? a.ffn : a.N;
+  dim3 rgrid((nout + 1023) / 1024, a.M), rblk(256);
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL(gemm_reduce<EPI_STORE>, rgrid, rblk, 0, s, a); break;
+    case EPI_BIAS_SUMSQ: hipLaunchKernelGGL(gemm_reduce<EPI_BIAS_SUMSQ>, rgrid, rblk, 0, s, a); *n_part_out = rgrid.x; break;
+    case EPI_RESID: hipLaunchKernelGGL(gemm_reduce<EPI_RESID>, rgrid, rblk, 0, s, a); break;
+    case EPI_RESID_SUMSQ: hipLaunchKernelGGL(gemm_reduce<EPI_RESID_SUMSQ>, rgrid, rblk, 0, s, a); *n_part_out = rgrid.x; break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_reduce<EPI_SWIGLU>, rgrid, rblk, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
