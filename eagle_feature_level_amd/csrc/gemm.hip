@@ -134,7 +134,10 @@ __device__ __forceinline__ int tile_row(const GemmArgs& a, int tile, int at, int
 // Skinny kernel: M <= 16, one workgroup = 16*AT weight rows, NW waves split K.
 // Vector-memory loads complete in issue order, so the activations of a k-step
 // are loaded in the same register stage as its weights: waiting for a stage
-// never waits for a later prefetch.  Three stages, two in flight.
+// never waits for a later prefetch.  NS register stages, NS - 1 in flight: the
+// deeper the ring, the more of a workgroup's weight stream is requested before
+// the first stage returns (with 256 workgroups of 16 rows, a CU owns only a
+// few hundred KB of the weights, so the ramp matters).
 //
 // Activations: a k-step needs 128 fp32 values of each of the M rows, but in
 // the MFMA B layout only the 4*M lanes of real rows hold data, 32 values each,
@@ -152,7 +155,7 @@ struct SkStage {
   u32x4 X[MQ];     // coalesced activation chunk: lane l, quad q -> row (q*64+l)/32, 4 floats
 };
 
-template <int AT, int NW, int MQ, int EPI>
+template <int AT, int NW, int MQ, int NS, int EPI>
 __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
   constexpr int XR = 2 * MQ;  // activation rows this instance can hold
   constexpr int BN = 16 * AT;
@@ -185,7 +188,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
   const bool mv = r < a.M;
 
   const int nks = a.K / SK_KSTEP;
-  SkStage<AT, MQ> S0, S1, S2;
+  SkStage<AT, MQ> S[NS];
   auto issue = [&](SkStage<AT, MQ>& st, int ks) {
 #pragma unroll
     for (int at = 0; at < AT; ++at)
@@ -195,8 +198,9 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
     for (int q = 0; q < MQ; ++q)
       st.X[q] = xv[q] ? *(const u32x4*)(xq[q] + (size_t)ks * SK_KSTEP) : u32x4{0, 0, 0, 0};
   };
-  if (wv < nks) issue(S0, wv);
-  if (wv + NW < nks) issue(S1, wv + NW);
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (wv + st * NW < nks) issue(S[st], wv + st * NW);
 
   // RMSNorm row scales of the input rows (applied in the epilogue), summed
   // while the first stages are in flight; visible after the reduction barrier
@@ -227,15 +231,14 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
     }
   };
 
-  for (int ks = wv; ks < nks; ks += 3 * NW) {
-    if (ks + 2 * NW < nks) issue(S2, ks + 2 * NW);
-    step(S0);
-    if (ks + NW >= nks) break;
-    if (ks + 3 * NW < nks) issue(S0, ks + 3 * NW);
-    step(S1);
-    if (ks + 2 * NW >= nks) break;
-    if (ks + 4 * NW < nks) issue(S1, ks + 4 * NW);
-    step(S2);
+  for (int ks = wv; ks < nks; ks += NS * NW) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int k = ks + st * NW;
+      if (k >= nks) break;
+      if (k + (NS - 1) * NW < nks) issue(S[(st + NS - 1) % NS], k + (NS - 1) * NW);
+      step(S[st]);
+    }
   }
 
   // Cross-wave reduction in a fixed order (over the activation slices: all
@@ -597,26 +600,31 @@ __global__ void __launch_bounds__(64) gemm_f32(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
-template <int AT, int NW, int MQ>
+// Register stages of the skinny ring.  Deeper rings (4-6 stages at 8 waves)
+// measured no faster on the 7B shapes: with every workgroup resident at once,
+// two stages in flight already keep HBM busy.
+constexpr int skinny_ns(int, int, int) { return 3; }
+
+template <int AT, int NW, int MQ, int NS = skinny_ns(AT, NW, MQ)>
 hipError_t skinny_epi(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
   const int BN = 16 * AT;
   dim3 blk(NW * 64);
   const dim3 grid((a.N + BN - 1) / BN);
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, EPI_STORE>), grid, blk, 0, s, a); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, EPI_STORE>), grid, blk, 0, s, a); break;
     case EPI_BIAS_SUMSQ:
-      hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, EPI_BIAS_SUMSQ>), grid, blk, 0, s, a);
+      hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, EPI_BIAS_SUMSQ>), grid, blk, 0, s, a);
       *n_part = grid.x;
       break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, EPI_RESID>), grid, blk, 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, EPI_RESID>), grid, blk, 0, s, a); break;
     case EPI_RESID_SUMSQ:
-      hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, EPI_RESID_SUMSQ>), grid, blk, 0, s, a);
+      hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, EPI_RESID_SUMSQ>), grid, blk, 0, s, a);
       *n_part = grid.x;
       break;
     case EPI_SWIGLU:
       if constexpr (AT >= 2) {  // gate and up tiles pair up inside a workgroup
         const int H = BN / 2;
-        hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, EPI_SWIGLU>), dim3((a.ffn + H - 1) / H), blk, 0, s, a);
+        hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, EPI_SWIGLU>), dim3((a.ffn + H - 1) / H), blk, 0, s, a);
         break;
       } else {
         return hipErrorInvalidValue;
@@ -635,15 +643,24 @@ hipError_t skinny_mq(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
   return skinny_epi<AT, NW, 8>(a, epi, n_part, s);
 }
 
-// One weight tile (16 rows) per workgroup keeps the operand split cheapest per
-// weight byte.  Waves per workgroup: 4 when there are >= 512 row tiles, else 8,
-// so that a launch has ~2000-8000 waves in flight; SwiGLU pairs a gate and an
-// up tile.  (Measured on the 7B shapes with M = 1..16.)
+// Variant choice, measured on the 7B draft-head shapes (N = 4096, 12288,
+// 22016 gate+up, 32000; M = 1..16), weights streamed from HBM:
+//  * fewer than 512 row tiles (N = 4096): one tile x 8 waves, so 256
+//    workgroups of 8 waves cover the chip;
+//  * SwiGLU: a gate and an up tile x 4 waves up to M = 8; x 8 waves above;
+//  * wide N with M > 8: four tiles x 4 waves -- each activation chunk then
+//    feeds four weight tiles, which matters once x is as large as the weights
+//    a wave streams per step;
+//  * wide N, M <= 3, >= 1536 tiles (the LM head): one tile x 8 waves (two
+//    workgroups per CU, ~4 full rounds of workgroups); else one tile x 4 waves.
 hipError_t skinny_launch(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
-  if (epi == EPI_SWIGLU)  // 8 waves of 2 tiles would spill registers at M > 8
-    return a.M > 8 ? skinny_mq<2, 4>(a, epi, n_part, s) : skinny_mq<2, 8>(a, epi, n_part, s);
-  if (a.N / 16 >= 512) return skinny_mq<1, 4>(a, epi, n_part, s);
-  return skinny_mq<1, 8>(a, epi, n_part, s);
+  if (epi == EPI_SWIGLU)
+    return a.M > 8 ? skinny_mq<2, 8>(a, epi, n_part, s) : skinny_mq<2, 4>(a, epi, n_part, s);
+  const int tiles = (a.N + 15) / 16;
+  if (tiles < 512) return skinny_mq<1, 8>(a, epi, n_part, s);
+  if (a.M > 8) return skinny_mq<4, 4>(a, epi, n_part, s);
+  if (a.M <= 3 && tiles >= 1536) return skinny_mq<1, 8>(a, epi, n_part, s);
+  return skinny_mq<1, 4>(a, epi, n_part, s);
 }
 
 // Tiles of the large-M kernel, plus a K split (powers of 2) while the grid
