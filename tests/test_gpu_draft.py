@@ -27,7 +27,7 @@ def _ws(nbytes):
 
 
 @pytest.mark.parametrize("rows,vocab,k", [(1, 32000, 10), (7, 32000, 4), (33, 4096, 16), (200, 32000, 10),
-                                          (3, 512, 1), (961, 32000, 10)])
+                                          (3, 512, 1), (961, 32000, 10), (3, 50000, 16), (4, 32768, 10)])
 def test_softmax_topk_bit_exact(rows, vocab, k):
     g = np.random.default_rng(rows * 7 + k)
     x = (g.standard_normal((rows, vocab)) * 2).astype(np.float32)
@@ -39,6 +39,10 @@ def test_softmax_topk_bit_exact(rows, vocab, k):
     if rows > 1:
         x[1, :] = -0.0
         x[1, 7] = 0.0
+    if rows > 2 and vocab >= 4096 * 8:
+        # the 32 largest values all in the stride-4096 share of one float4 column
+        cols = (8 + 4096 * np.arange(8)[:, None] + np.arange(4)).ravel()
+        x[2, cols] = 10.0 + np.arange(32, dtype=np.float32) % 5
     t = torch.from_numpy(x).cuda()
     lse = torch.empty(rows, device="cuda")
     idx = torch.empty(rows, k, dtype=torch.int32, device="cuda")
