@@ -16,7 +16,8 @@ from ._abi import (EAGLE_BF16, EAGLE_F32, EAGLE_HEAD_ONLY, EAGLE_MAX_SLOTS, EAGL
                    eagle_weights)
 
 __all__ = ["eagle_workspace_bytes", "eagle_draft_step", "eagle_softmax_topk", "eagle_tree_init", "eagle_tree_expand",
-           "eagle_tree_finalize", "eagle_verify", "make_shape", "make_weights", "make_rows", "make_kv", "make_out",
+           "eagle_tree_finalize", "eagle_verify", "eagle_verify_workspace_bytes", "make_shape", "make_weights",
+           "make_rows", "make_kv", "make_out",
            "make_pool", "EagleError", "EAGLE_HEAD_ONLY", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
            "EAGLE_F32", "EAGLE_MAX_SLOTS", "EAGLE_MAX_TOPK", "eagle_profile_enable", "eagle_profile_reset",
            "eagle_profile_disable", "eagle_profile_read"]
@@ -126,12 +127,19 @@ def eagle_tree_finalize(batch, m, n_nodes, pool, prefix_len, tree_parent, tree_t
 
 
 def eagle_verify(batch, n_nodes, vocab, tree_parent, tree_token, target_logits, draft_logits, draft_row, seed, round_,
-                 flags, out_path, out_accept_len, out_next_token, out_flags, stream=None):
+                 flags, out_path, out_accept_len, out_next_token, out_flags, workspace=None, stream=None):
+    """workspace: None, or a device tensor of at least eagle_verify_workspace_bytes(batch, n_nodes) bytes."""
     lib = _abi.load()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib.eagle_verify(batch, n_nodes, vocab, _ptr(tree_parent), _ptr(tree_token), _ptr(target_logits),
                           _ptr(draft_logits), _ptr(draft_row), seed, round_, flags, _ptr(out_path),
-                          _ptr(out_accept_len), _ptr(out_next_token), _ptr(out_flags), _stream(stream))
+                          _ptr(out_accept_len), _ptr(out_next_token), _ptr(out_flags), _ptr(workspace), nbytes,
+                          _stream(stream))
     _abi.check("eagle_verify", rc)
+
+
+def eagle_verify_workspace_bytes(batch, n_nodes):
+    return int(_abi.load().eagle_verify_workspace_bytes(batch, n_nodes))
 
 
 def eagle_profile_enable(max_launches: int):

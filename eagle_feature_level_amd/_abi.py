@@ -64,7 +64,8 @@ _SIGS = {
     "eagle_tree_finalize": (c_i32, [c_i32, c_i32, c_i32, P(eagle_pool), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "eagle_verify": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_u64, c_u64, c_i32, c_vp, c_vp,
-                             c_vp, c_vp, c_vp]),
+                             c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "eagle_verify_workspace_bytes": (ctypes.c_size_t, [c_i32, c_i32]),
     "eagle_profile_enable": (c_i32, [c_i32]),
     "eagle_profile_reset": (c_i32, []),
     "eagle_profile_disable": (c_i32, []),

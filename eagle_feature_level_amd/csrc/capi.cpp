@@ -566,7 +566,7 @@ int eagle_tree_finalize(int32_t batch, int32_t m, int32_t n_nodes, const eagle_p
 int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t* tree_parent, const int32_t* tree_token,
                  const float* target_logits, const float* draft_logits, const int32_t* draft_row, uint64_t seed,
                  uint64_t round, int32_t flags, int32_t* out_path, int32_t* out_accept_len, int32_t* out_next_token,
-                 int32_t* out_flags, eagle_stream_t stream) {
+                 int32_t* out_flags, void* workspace, size_t workspace_bytes, eagle_stream_t stream) {
   if (batch < 0 || n_nodes < 1 || vocab < 1) return EAGLE_EINVAL;
   if (batch == 0) return EAGLE_OK;
   if (!tree_parent || !tree_token || !target_logits || !draft_logits || !draft_row || !out_path ||
@@ -574,6 +574,7 @@ int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t* t
     return EAGLE_EINVAL;
   if (flags & ~(EAGLE_VERIFY_GREEDY | EAGLE_VERIFY_IID)) return EAGLE_EINVAL;
   if (n_nodes > EAGLE_MAX_SLOTS || vocab > 32768) return EAGLE_EUNSUPPORTED;
+  if (workspace && workspace_bytes < verify_workspace_bytes(batch, n_nodes)) return EAGLE_EWORKSPACE;
   int rc = check_device();
   if (rc) return rc;
   VerifyArgs a;
@@ -592,8 +593,13 @@ int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t* t
   a.accept_len = out_accept_len;
   a.next_token = out_next_token;
   a.out_flags = out_flags;
-  hipError_t e = launch_verify(a, (hipStream_t)stream);
+  hipError_t e = launch_verify(a, workspace, (hipStream_t)stream);
   return e == hipSuccess ? EAGLE_OK : hip_fail(e);
+}
+
+size_t eagle_verify_workspace_bytes(int32_t batch, int32_t n_nodes) {
+  if (batch < 0 || n_nodes < 1 || n_nodes > EAGLE_MAX_SLOTS) return 0;
+  return verify_workspace_bytes(batch, n_nodes);
 }
 
 }  // extern "C"

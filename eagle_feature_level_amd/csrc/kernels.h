@@ -108,5 +108,10 @@ struct VerifyArgs {
   uint64_t seed, round;
   int flags;
   int32_t *path, *accept_len, *next_token, *out_flags;
+  // per-node results, [batch*n_nodes] each (workspace)
+  int32_t* node_next;   // accepted child, -1 if none
+  int32_t* node_tok;    // correction / bonus token when node_next < 0
+  int32_t* node_flags;  // status bits raised at the node
 };
-hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
+size_t verify_workspace_bytes(int batch, int n_nodes);
+hipError_t launch_verify(VerifyArgs a, void* ws, hipStream_t s);

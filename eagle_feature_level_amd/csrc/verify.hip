@@ -13,9 +13,16 @@
 // (sequence, node, event, 0), key (seed, round), u = (word0 >> 40) * 2^-24;
 // event i = test of the i-th child, event 64 = correction / bonus draw.
 //
-// One 1024-thread workgroup walks one sequence.  Thread t owns the EPT
-// consecutive tokens [t*EPT, (t+1)*EPT): p and q live in registers, the walk
-// needs block reductions only, and the inverse-CDF draw is one block scan.
+// What happens at a node does not depend on the path that reached it: p and q
+// come from the node's own rows, the uniforms from (sequence, node, event).
+// So with a workspace every node of every tree is processed at once, one
+// 1024-thread workgroup each (which child it accepts, else the correction or
+// bonus token, and the status bits it raises), and a second launch walks the
+// trees through those results, one thread per sequence.  Without a
+// workspace, one workgroup per sequence processes the nodes along its path.
+// Thread t owns the EPT consecutive tokens [t*EPT, (t+1)*EPT): p and q live in
+// registers, a node needs block reductions only, and the inverse-CDF draw is
+// one block scan.
 #include "common.h"
 #include "kernels.h"
 
@@ -128,161 +135,176 @@ __device__ __forceinline__ bool load_row(const float* row, int V, float (&v)[EPT
   return bad;
 }
 
+// Shared state of one node's processing.
 template <int EPT>
-__global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
-  __shared__ float fred[NW];
-  __shared__ int ired[NW];
-  __shared__ int s_parent[64], s_token[64];
-  __shared__ int kids[64];
-  __shared__ int s_nk;
-  __shared__ float s_px, s_dx;
-  // draft logits of the current node, element e of thread t at dl[e * VT + t]
-  // (lanes on consecutive banks); removed tokens are set to -inf
-  __shared__ float dl[EPT * VT];
-  const int b = blockIdx.x, t = threadIdx.x;
-  const int N = a.n_nodes, V = a.vocab;
+struct NodeShared {
+  float fred[NW];
+  int ired[NW];
+  int parent[64], token[64], kids[64];
+  int nk;
+  float px, dx;
+  // draft logits of the node, element e of thread t at dl[e * VT + t] (lanes
+  // on consecutive banks); removed tokens are set to -inf
+  float dl[EPT * VT];
+};
+
+template <int EPT>
+__device__ __forceinline__ void load_tree(const VerifyArgs& a, NodeShared<EPT>& sh, int b) {
+  const int N = a.n_nodes, t = threadIdx.x;
   if (t < N) {
-    s_parent[t] = a.parent[(size_t)b * N + t];
-    s_token[t] = a.token[(size_t)b * N + t];
+    sh.parent[t] = a.parent[(size_t)b * N + t];
+    sh.token[t] = a.token[(size_t)b * N + t];
   }
   __syncthreads();
-  const bool greedy = a.flags & 1, iid = a.flags & 2;
-  int flags = 0, u = 0, nacc = 0, next_tok = 0;
-  float p[EPT];  // current target distribution (normalised)
-#define D(e) dl[(e) * VT + t]
+}
 
-  for (int level = 0; level <= N; ++level) {
-    // target distribution at u
-    if (__syncthreads_or(load_row<EPT>(a.target + ((size_t)b * N + u) * V, V, p))) flags |= 8;
-    float mx = -INFINITY;
+// Node u of sequence b: returns (accepted child, 0) or (-1, correction or
+// bonus token); ORs the status bits it raises into *flags (uniform).
+template <int EPT>
+__device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& sh, int b, int u, int* flags) {
+  const int t = threadIdx.x;
+  const int N = a.n_nodes, V = a.vocab;
+  const bool greedy = a.flags & 1, iid = a.flags & 2;
+  float* fred = sh.fred;
+  int* ired = sh.ired;
+  float p[EPT];  // current target distribution (normalised)
+#define D(e) sh.dl[(e) * VT + t]
+  // target distribution at u
+  if (__syncthreads_or(load_row<EPT>(a.target + ((size_t)b * N + u) * V, V, p))) *flags |= 8;
+  float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) mx = fmaxf(mx, p[e]);
-    mx = bmax(mx, fred);
-    if (greedy) {
-      int cand = 0x7fffffff;
+  for (int e = 0; e < EPT; ++e) mx = fmaxf(mx, p[e]);
+  mx = bmax(mx, fred);
+  if (greedy) {
+    int cand = 0x7fffffff;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if (p[e] == mx && cand == 0x7fffffff) cand = t * EPT + e;
+    const int am = bmin_int(cand, ired);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) p[e] = (t * EPT + e == am) ? 1.f : 0.f;
+  } else {
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      p[e] = (p[e] == -INFINITY) ? 0.f : __expf(p[e] - mx);
+      ls += p[e];
+    }
+    const float inv = 1.f / bsum(ls, fred);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) p[e] *= inv;
+  }
+  // children of u in rank (index) order
+  if (t == 0) {
+    int nk = 0;
+    for (int i = u + 1; i < N; ++i)
+      if (sh.parent[i] == u) sh.kids[nk++] = i;
+    sh.nk = nk;
+  }
+  __syncthreads();
+  const int nk = sh.nk;
+  if (nk == 0) return make_int2(-1, draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired));
+  // draft distribution at u: q(y) = exp(d_y - dmx) / S over the tokens not removed
+  const int drow_idx = a.draft_row[(size_t)b * N + u];
+  if (drow_idx < 0) {  // no draft row for a node with children: invalid input
+    *flags |= 8;
+    return make_int2(-1, draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired));
+  }
+  float dmx = -INFINITY;
+  {
+    float dv[EPT];
+    load_row<EPT>(a.draft + (size_t)drow_idx * V, V, dv);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      dmx = fmaxf(dmx, dv[e]);
+      D(e) = dv[e];
+    }
+  }
+  dmx = bmax(dmx, fred);
+  auto qmass = [&]() {
+    float ds = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) ds += (D(e) == -INFINITY) ? 0.f : __expf(D(e) - dmx);
+    return bsum(ds, fred);
+  };
+  float S = qmass();
+  for (int i = 0; i < nk; ++i) {
+    if (!(S > 0.f)) {
+      *flags |= 4;
+      break;
+    }
+    const int c = sh.kids[i];
+    const int x = sh.token[c];
+    const float r = philox_uniform(a.seed, a.round, b, u, i);
+    const bool x_ok = x >= 0 && x < V;
+    __syncthreads();
+    if (x_ok && t == x / EPT) {
+      float px = 0.f;
 #pragma unroll
       for (int e = 0; e < EPT; ++e)
-        if (p[e] == mx && cand == 0x7fffffff) cand = t * EPT + e;
-      const int am = bmin_int(cand, ired);
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) p[e] = (t * EPT + e == am) ? 1.f : 0.f;
-    } else {
-      float ls = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        p[e] = (p[e] == -INFINITY) ? 0.f : __expf(p[e] - mx);
-        ls += p[e];
-      }
-      const float inv = 1.f / bsum(ls, fred);
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) p[e] *= inv;
-    }
-    // children of u in rank (index) order
-    if (t == 0) {
-      int nk = 0;
-      for (int i = u + 1; i < N; ++i)
-        if (s_parent[i] == u) kids[nk++] = i;
-      s_nk = nk;
+        if (e == x % EPT) px = p[e];
+      sh.px = px;
+      sh.dx = D(x % EPT);
     }
     __syncthreads();
-    const int nk = s_nk;
-    if (nk == 0) {
-      next_tok = draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired);
-      break;
+    const float px = x_ok ? sh.px : 0.f;
+    const float qx = (x_ok && sh.dx != -INFINITY) ? __expf(sh.dx - dmx) / S : 0.f;
+    bool ok;
+    if (qx > 0.f) {
+      ok = r < px / qx;
+    } else {
+      *flags |= 2;
+      ok = px > 0.f;
     }
-    // draft distribution at u: q(y) = exp(d_y - dmx) / S over the tokens not removed
-    const int drow_idx = a.draft_row[(size_t)b * N + u];
-    if (drow_idx < 0) {  // no draft row for a node with children: invalid input
-      flags |= 8;
-      next_tok = draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired);
-      break;
+    if (ok) return make_int2(c, 0);
+    // residual target norm(max(0, p - q))
+    // (mass first, then the update, so a zero mass leaves p untouched)
+    const float invS = 1.f / S;
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const float qy = (D(e) == -INFINITY) ? 0.f : __expf(D(e) - dmx) * invS;
+      rs += fmaxf(0.f, p[e] - qy);
     }
-    float dmx = -INFINITY;
-    {
-      float dv[EPT];
-      load_row<EPT>(a.draft + (size_t)drow_idx * V, V, dv);
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        dmx = fmaxf(dmx, dv[e]);
-        D(e) = dv[e];
-      }
-    }
-    dmx = bmax(dmx, fred);
-    auto qmass = [&]() {
-      float ds = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) ds += (D(e) == -INFINITY) ? 0.f : __expf(D(e) - dmx);
-      return bsum(ds, fred);
-    };
-    float S = qmass();
-    int accepted = -1;
-    for (int i = 0; i < nk; ++i) {
-      if (!(S > 0.f)) {
-        flags |= 4;
-        break;
-      }
-      const int c = kids[i];
-      const int x = s_token[c];
-      const float r = philox_uniform(a.seed, a.round, b, u, i);
-      const bool x_ok = x >= 0 && x < V;
-      __syncthreads();
-      if (x_ok && t == x / EPT) {
-        float px = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e)
-          if (e == x % EPT) px = p[e];
-        s_px = px;
-        s_dx = D(x % EPT);
-      }
-      __syncthreads();
-      const float px = x_ok ? s_px : 0.f;
-      const float qx = (x_ok && s_dx != -INFINITY) ? __expf(s_dx - dmx) / S : 0.f;
-      bool ok;
-      if (qx > 0.f) {
-        ok = r < px / qx;
-      } else {
-        flags |= 2;
-        ok = px > 0.f;
-      }
-      if (ok) {
-        accepted = c;
-        break;
-      }
-      // residual target norm(max(0, p - q))
-      // (mass first, then the update, so a zero mass leaves p untouched)
-      const float invS = 1.f / S;
-      float rs = 0.f;
+    const float Z = bsum(rs, fred);
+    if (Z > 0.f) {
+      const float inv = 1.f / Z;
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
         const float qy = (D(e) == -INFINITY) ? 0.f : __expf(D(e) - dmx) * invS;
-        rs += fmaxf(0.f, p[e] - qy);
+        p[e] = fmaxf(0.f, p[e] - qy) * inv;
       }
-      const float Z = bsum(rs, fred);
-      if (Z > 0.f) {
-        const float inv = 1.f / Z;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-          const float qy = (D(e) == -INFINITY) ? 0.f : __expf(D(e) - dmx) * invS;
-          p[e] = fmaxf(0.f, p[e] - qy) * inv;
-        }
-      } else {
-        flags |= 1;  // zero residual mass (reachable only through rounding): keep p
-      }
-      if (!iid) {
-        if (x_ok && t == x / EPT) D(x % EPT) = -INFINITY;
-        S = qmass();
-      }
+    } else {
+      *flags |= 1;  // zero residual mass (reachable only through rounding): keep p
     }
-    if (accepted < 0) {
-      next_tok = draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired);
-      break;
+    if (!iid) {
+      if (x_ok && t == x / EPT) D(x % EPT) = -INFINITY;
+      S = qmass();
     }
-    if (t == 0) a.path[(size_t)b * N + nacc] = accepted;
-    ++nacc;
-    u = accepted;
   }
 #undef D
-  if (t == 0) {
+  // every child rejected: correction from the residual
+  return make_int2(-1, draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired));
+}
+
+// One workgroup per sequence, along its path.
+template <int EPT>
+__global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
+  __shared__ NodeShared<EPT> sh;
+  const int b = blockIdx.x, N = a.n_nodes;
+  load_tree<EPT>(a, sh, b);
+  int flags = 0, u = 0, nacc = 0, next_tok = 0;
+  for (int level = 0; level <= N; ++level) {
+    const int2 r = node_step<EPT>(a, sh, b, u, &flags);
+    if (r.x < 0) {
+      next_tok = r.y;
+      break;
+    }
+    if (threadIdx.x == 0) a.path[(size_t)b * N + nacc] = r.x;
+    ++nacc;
+    u = r.x;
+  }
+  if (threadIdx.x == 0) {
     for (int j = nacc; j < N; ++j) a.path[(size_t)b * N + j] = -1;
     a.accept_len[b] = nacc + 1;
     a.next_token[b] = next_tok;
@@ -290,16 +312,71 @@ __global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
   }
 }
 
+// One workgroup per node of every tree: its result into the workspace.
+template <int EPT>
+__global__ void __launch_bounds__(VT) verify_node_kernel(VerifyArgs a) {
+  __shared__ NodeShared<EPT> sh;
+  const int N = a.n_nodes;
+  const int b = blockIdx.x / N, u = blockIdx.x % N;
+  load_tree<EPT>(a, sh, b);
+  int flags = 0;
+  const int2 r = node_step<EPT>(a, sh, b, u, &flags);
+  if (threadIdx.x == 0) {
+    a.node_next[blockIdx.x] = r.x;
+    a.node_tok[blockIdx.x] = r.y;
+    a.node_flags[blockIdx.x] = flags;
+  }
+}
+
+// One thread per sequence: the walk through the per-node results.
+__global__ void __launch_bounds__(64) verify_walk_kernel(VerifyArgs a) {
+  const int b = blockIdx.x * 64 + threadIdx.x;
+  if (b >= a.batch) return;
+  const int N = a.n_nodes;
+  int flags = 0, u = 0, nacc = 0, next_tok = 0;
+  for (int level = 0; level <= N; ++level) {
+    const size_t bu = (size_t)b * N + u;
+    flags |= a.node_flags[bu];
+    const int c = a.node_next[bu];
+    if (c < 0) {
+      next_tok = a.node_tok[bu];
+      break;
+    }
+    a.path[(size_t)b * N + nacc] = c;
+    ++nacc;
+    u = c;
+  }
+  for (int j = nacc; j < N; ++j) a.path[(size_t)b * N + j] = -1;
+  a.accept_len[b] = nacc + 1;
+  a.next_token[b] = next_tok;
+  a.out_flags[b] = flags;
+}
+
 }  // namespace
 
-hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
-  if (a.vocab <= VT)
-    hipLaunchKernelGGL(verify_kernel<1>, dim3(a.batch), dim3(VT), 0, s, a);
-  else if (a.vocab <= 4 * VT)
-    hipLaunchKernelGGL(verify_kernel<4>, dim3(a.batch), dim3(VT), 0, s, a);
-  else if (a.vocab <= 32 * VT)
-    hipLaunchKernelGGL(verify_kernel<32>, dim3(a.batch), dim3(VT), 0, s, a);
-  else
-    return hipErrorInvalidValue;
+size_t verify_workspace_bytes(int batch, int n_nodes) { return (size_t)batch * n_nodes * 12 + 1024; }
+
+hipError_t launch_verify(VerifyArgs a, void* ws, hipStream_t s) {
+  if (a.vocab > 32 * VT) return hipErrorInvalidValue;
+  const int EPT = a.vocab <= VT ? 1 : a.vocab <= 4 * VT ? 4 : 32;
+  if (!ws) {
+    if (EPT == 1) hipLaunchKernelGGL(verify_kernel<1>, dim3(a.batch), dim3(VT), 0, s, a);
+    else if (EPT == 4) hipLaunchKernelGGL(verify_kernel<4>, dim3(a.batch), dim3(VT), 0, s, a);
+    else hipLaunchKernelGGL(verify_kernel<32>, dim3(a.batch), dim3(VT), 0, s, a);
+    return hipGetLastError();
+  }
+  const size_t n = (size_t)a.batch * a.n_nodes;
+  const size_t step = (n * 4 + 255) / 256 * 256;
+  char* w = (char*)ws;
+  a.node_next = (int32_t*)w;
+  a.node_tok = (int32_t*)(w + step);
+  a.node_flags = (int32_t*)(w + 2 * step);
+  const dim3 g((unsigned)n);
+  if (EPT == 1) hipLaunchKernelGGL(verify_node_kernel<1>, g, dim3(VT), 0, s, a);
+  else if (EPT == 4) hipLaunchKernelGGL(verify_node_kernel<4>, g, dim3(VT), 0, s, a);
+  else hipLaunchKernelGGL(verify_node_kernel<32>, g, dim3(VT), 0, s, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_walk_kernel, dim3((a.batch + 63) / 64), dim3(64), 0, s, a);
   return hipGetLastError();
 }

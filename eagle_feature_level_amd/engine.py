@@ -17,8 +17,8 @@ import dataclasses
 import torch
 
 from . import (EAGLE_HEAD_ONLY, eagle_draft_step, eagle_tree_expand, eagle_tree_finalize, eagle_tree_init,
-               eagle_verify, eagle_workspace_bytes, make_kv, make_out, make_pool, make_rows, make_shape,
-               make_weights)
+               eagle_verify, eagle_verify_workspace_bytes, eagle_workspace_bytes, make_kv, make_out, make_pool,
+               make_rows, make_shape, make_weights)
 
 
 @dataclasses.dataclass
@@ -123,7 +123,8 @@ class EagleRound:
         self.tw_kv = make_kv(prefix["k"], prefix["v"], prefix["off"], prefix["len"], prefix["max_len"],
                              self.tw_tree_k, self.tw_tree_v)
         max_rows = max([B] + [B * n for n in ns] + [nw])
-        ws = eagle_workspace_bytes(self.shape, max_rows, B, prefix["max_len"])
+        ws = max(eagle_workspace_bytes(self.shape, max_rows, B, prefix["max_len"]),
+                 eagle_verify_workspace_bytes(B, self.n_nodes))
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
         # verify outputs
         self.v_path = torch.zeros(B * N, **i32)
@@ -190,4 +191,5 @@ class EagleRound:
     def verify(self, target_logits: torch.Tensor, seed: int, round_: int, flags: int = 0):
         t = self.tree
         eagle_verify(self.B, self.n_nodes, self.shape_d["vocab"], t["parent"], t["token"], target_logits,
-                     self.logits, t["qrow"], seed, round_, flags, self.v_path, self.v_len, self.v_next, self.v_flags)
+                     self.logits, t["qrow"], seed, round_, flags, self.v_path, self.v_len, self.v_next, self.v_flags,
+                     workspace=self.workspace)

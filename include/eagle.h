@@ -247,11 +247,23 @@ enum { EAGLE_F_ZRES = 1, EAGLE_F_QZERO = 2, EAGLE_F_QEMPTY = 4, EAGLE_F_NAN = 8 
  * from that leaf's p the same way.
  * Outputs: out_path[b*n_nodes + j] = j-th accepted node (-1 padded),
  * out_accept_len[b] = accepted nodes + 1, out_next_token[b], out_flags[b].
+ * workspace: device memory of at least eagle_verify_workspace_bytes(batch,
+ * n_nodes) bytes, owned by the caller and overwritten, or NULL.  What happens
+ * at a node depends only on the node (its rows, its children, its uniforms),
+ * so with a workspace every node of every tree is processed at once, one
+ * workgroup each, and a second launch walks the trees through the per-node
+ * results; without it, one workgroup per sequence processes the nodes on its
+ * path.  Both run the same per-node arithmetic, so the outputs are identical.
+ * A non-NULL workspace below the size returns EAGLE_EWORKSPACE.
  * vocab <= 32768, n_nodes <= 64. */
 int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t *tree_parent, const int32_t *tree_token,
                  const float *target_logits, const float *draft_logits, const int32_t *draft_row, uint64_t seed,
                  uint64_t round, int32_t flags, int32_t *out_path, int32_t *out_accept_len, int32_t *out_next_token,
-                 int32_t *out_flags, eagle_stream_t stream);
+                 int32_t *out_flags, void *workspace, size_t workspace_bytes, eagle_stream_t stream);
+
+/* Bytes of workspace eagle_verify uses for batch x n_nodes trees (12 per node
+ * plus alignment); 0 for an invalid size. */
+size_t eagle_verify_workspace_bytes(int32_t batch, int32_t n_nodes);
 
 /* Measurement hook.  While enabled, each kernel launch of eagle_draft_step is
  * bracketed by a pair of HIP events recorded on the call's stream, tagged

@@ -52,9 +52,13 @@ def test_argument_errors_need_no_device():
                               ctypes.byref(out), None, 0, None)
     assert rc == _abi.EAGLE_EINVAL
     # verify: bad sizes and flags
-    assert lib.eagle_verify(-1, 5, 10, *([None] * 5), 0, 0, 0, *([None] * 5)) == _abi.EAGLE_EINVAL
-    assert lib.eagle_verify(1, 0, 10, *([None] * 5), 0, 0, 0, *([None] * 5)) == _abi.EAGLE_EINVAL
-    assert lib.eagle_verify(0, 5, 10, *([None] * 5), 0, 0, 0, *([None] * 5)) == _abi.EAGLE_OK  # empty batch
+    assert lib.eagle_verify(-1, 5, 10, *([None] * 5), 0, 0, 0, *([None] * 5), 0, None) == _abi.EAGLE_EINVAL
+    assert lib.eagle_verify(1, 0, 10, *([None] * 5), 0, 0, 0, *([None] * 5), 0, None) == _abi.EAGLE_EINVAL
+    assert lib.eagle_verify(0, 5, 10, *([None] * 5), 0, 0, 0, *([None] * 5), 0, None) == _abi.EAGLE_OK  # empty batch
+    # a workspace below eagle_verify_workspace_bytes is refused before anything runs
+    need = lib.eagle_verify_workspace_bytes(2, 26)
+    assert need >= 2 * 26 * 12 and lib.eagle_verify_workspace_bytes(1, 0) == 0
+    assert lib.eagle_verify(2, 26, 10, *([1] * 5), 0, 0, 0, *([1] * 4), 1, need - 1, None) == _abi.EAGLE_EWORKSPACE
     # top-k larger than supported / than the vocabulary
     assert lib.eagle_softmax_topk(1, 8, 1, 9, 1, 1, 1, 1, 1 << 20, None) == _abi.EAGLE_EINVAL
     assert lib.eagle_softmax_topk(1, 64, 1, 17, 1, 1, 1, 1, 1 << 20, None) == _abi.EAGLE_EUNSUPPORTED

@@ -29,7 +29,7 @@ AMBIG = 1e-5  # |u - p/q| below this: the decision is a near-tie between fp32 an
 AMBIG_DRAW = 3e-6  # inverse-CDF target within this fraction of the mass from a boundary
 
 
-def _run(parent_list, tokens, target, draft, B, N, V, seed, rnd, flags=0, draft_row=None):
+def _run(parent_list, tokens, target, draft, B, N, V, seed, rnd, flags=0, draft_row=None, ws=True):
     par = np.tile(np.asarray(parent_list, np.int32), B)
     out = dict(path=torch.zeros(B * N, dtype=torch.int32, device="cuda"),
                len=torch.zeros(B, dtype=torch.int32, device="cuda"),
@@ -37,9 +37,11 @@ def _run(parent_list, tokens, target, draft, B, N, V, seed, rnd, flags=0, draft_
                flags=torch.zeros(B, dtype=torch.int32, device="cuda"))
     if draft_row is None:
         draft_row = np.arange(B * N, dtype=np.int32)
+    # with a workspace: every node processed at once, then the walk; without: one workgroup per sequence
+    work = torch.empty(E.eagle_verify_workspace_bytes(B, N), dtype=torch.uint8, device="cuda") if ws else None
     E.eagle_verify(B, N, V, dev.ints(par), dev.ints(tokens.reshape(-1)), torch.from_numpy(target).cuda(),
                    torch.from_numpy(draft).cuda(), dev.ints(draft_row), seed, rnd, flags, out["path"], out["len"],
-                   out["next"], out["flags"])
+                   out["next"], out["flags"], workspace=work)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
@@ -81,12 +83,13 @@ def _compare(parent_list, tokens, target, draft, B, N, V, seed, rnd, got, greedy
 
 @pytest.mark.parametrize("V,B", [(32000, 8), (3000, 16), (512, 24), (8, 40)])
 @pytest.mark.parametrize("flags", [0, E.EAGLE_VERIFY_GREEDY, E.EAGLE_VERIFY_IID])
-def test_verify_bit_exact_static26(V, B, flags):
+@pytest.mark.parametrize("ws", [True, False])
+def test_verify_bit_exact_static26(V, B, flags, ws):
     g = np.random.default_rng(V + B + flags)
     tmpl = TEMPLATES["static26"]
     N = len(tmpl)
     draft, target, tokens = _tree_case(g, tmpl, B, V, noise=0.5 if V > 100 else 1.0)
-    got = _run(tmpl, tokens, target, draft, B, N, V, seed=1234, rnd=7, flags=flags)
+    got = _run(tmpl, tokens, target, draft, B, N, V, seed=1234, rnd=7, flags=flags, ws=ws)
     _compare(tmpl, tokens, target, draft, B, N, V, 1234, 7, got, greedy=bool(flags & 1), iid=bool(flags & 2))
 
 
@@ -102,6 +105,41 @@ def test_verify_bit_exact_dynamic_shape_with_rejections():
     got = _run(parent, tokens, target, draft, B, 61, V, seed=0, rnd=3)
     _compare(parent, tokens, target, draft, B, 61, V, 0, 3, got)
     assert got["len"].min() >= 1
+
+
+@pytest.mark.parametrize("ws", [True, False])
+def test_verify_nan_target_row_is_flagged(ws):
+    g = np.random.default_rng(11)
+    tmpl = TEMPLATES["static26"]
+    N, V, B = len(tmpl), 512, 2
+    draft, target, tokens = _tree_case(g, tmpl, B, V)
+    target[0, 5] = np.nan  # root row of sequence 0
+    got = _run(tmpl, tokens, target, draft, B, N, V, seed=1, rnd=0, ws=ws)
+    assert got["flags"][0] & 8 and not got["flags"][1] & 8
+
+
+def test_verify_with_and_without_workspace_identical():
+    g = np.random.default_rng(12)
+    tmpl = TEMPLATES["static26"]
+    N, V, B = len(tmpl), 32000, 8
+    draft, target, tokens = _tree_case(g, tmpl, B, V, noise=1.5)
+    for flags in (0, E.EAGLE_VERIFY_GREEDY, E.EAGLE_VERIFY_IID):
+        a = _run(tmpl, tokens, target, draft, B, N, V, seed=3, rnd=2, flags=flags, ws=True)
+        b = _run(tmpl, tokens, target, draft, B, N, V, seed=3, rnd=2, flags=flags, ws=False)
+        for key in a:
+            assert np.array_equal(a[key], b[key]), (flags, key)
+
+
+def test_verify_rejection_heavy_without_workspace():
+    g = np.random.default_rng(5)
+    parent = [-1] + [0] * 10
+    while len(parent) < 61:
+        parent.append(int(g.integers(1, len(parent))))
+    parent = [-1] + sorted(parent[1:])
+    V, B = 32000, 6
+    draft, target, tokens = _tree_case(g, parent, B, V, noise=2.0)
+    got = _run(parent, tokens, target, draft, B, 61, V, seed=0, rnd=3, ws=False)
+    _compare(parent, tokens, target, draft, B, 61, V, 0, 3, got)
 
 
 def test_greedy_worked_example():
