@@ -142,10 +142,10 @@ struct NodeShared {
   int ired[NW];
   int parent[64], token[64], kids[64];
   int nk;
-  float px, dx;
-  // draft logits of the node, element e of thread t at dl[e * VT + t] (lanes
-  // on consecutive banks); removed tokens are set to -inf
-  float dl[EPT * VT];
+  float px, qx;
+  // exp(draft logit - max) of the node, element e of thread t at ql[e * VT +
+  // t] (lanes on consecutive banks); removed tokens are set to 0
+  float ql[EPT * VT];
 };
 
 template <int EPT>
@@ -168,7 +168,7 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
   float* fred = sh.fred;
   int* ired = sh.ired;
   float p[EPT];  // current target distribution (normalised)
-#define D(e) sh.dl[(e) * VT + t]
+#define Q(e) sh.ql[(e) * VT + t]
   // target distribution at u
   if (__syncthreads_or(load_row<EPT>(a.target + ((size_t)b * N + u) * V, V, p))) *flags |= 8;
   float mx = -INFINITY;
@@ -204,27 +204,32 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
   __syncthreads();
   const int nk = sh.nk;
   if (nk == 0) return make_int2(-1, draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired));
-  // draft distribution at u: q(y) = exp(d_y - dmx) / S over the tokens not removed
+  // draft distribution at u: q(y) = exp(d_y - dmx) / S over the tokens not removed,
+  // the exponentials taken once
   const int drow_idx = a.draft_row[(size_t)b * N + u];
   if (drow_idx < 0) {  // no draft row for a node with children: invalid input
     *flags |= 8;
     return make_int2(-1, draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired));
   }
-  float dmx = -INFINITY;
   {
-    float dv[EPT];
-    load_row<EPT>(a.draft + (size_t)drow_idx * V, V, dv);
+    float dmx = -INFINITY;
+    {
+      float dv[EPT];
+      load_row<EPT>(a.draft + (size_t)drow_idx * V, V, dv);
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      dmx = fmaxf(dmx, dv[e]);
-      D(e) = dv[e];
+      for (int e = 0; e < EPT; ++e) {
+        dmx = fmaxf(dmx, dv[e]);
+        Q(e) = dv[e];  // raw logits first: keeps the row out of registers across the reduction
+      }
     }
+    dmx = bmax(dmx, fred);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) Q(e) = (Q(e) == -INFINITY) ? 0.f : __expf(Q(e) - dmx);
   }
-  dmx = bmax(dmx, fred);
   auto qmass = [&]() {
     float ds = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) ds += (D(e) == -INFINITY) ? 0.f : __expf(D(e) - dmx);
+    for (int e = 0; e < EPT; ++e) ds += Q(e);
     return bsum(ds, fred);
   };
   float S = qmass();
@@ -244,11 +249,11 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
       for (int e = 0; e < EPT; ++e)
         if (e == x % EPT) px = p[e];
       sh.px = px;
-      sh.dx = D(x % EPT);
+      sh.qx = Q(x % EPT);
     }
     __syncthreads();
     const float px = x_ok ? sh.px : 0.f;
-    const float qx = (x_ok && sh.dx != -INFINITY) ? __expf(sh.dx - dmx) / S : 0.f;
+    const float qx = x_ok ? sh.qx / S : 0.f;
     bool ok;
     if (qx > 0.f) {
       ok = r < px / qx;
@@ -262,27 +267,21 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
     const float invS = 1.f / S;
     float rs = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const float qy = (D(e) == -INFINITY) ? 0.f : __expf(D(e) - dmx) * invS;
-      rs += fmaxf(0.f, p[e] - qy);
-    }
+    for (int e = 0; e < EPT; ++e) rs += fmaxf(0.f, p[e] - Q(e) * invS);
     const float Z = bsum(rs, fred);
     if (Z > 0.f) {
       const float inv = 1.f / Z;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const float qy = (D(e) == -INFINITY) ? 0.f : __expf(D(e) - dmx) * invS;
-        p[e] = fmaxf(0.f, p[e] - qy) * inv;
-      }
+      for (int e = 0; e < EPT; ++e) p[e] = fmaxf(0.f, p[e] - Q(e) * invS) * inv;
     } else {
       *flags |= 1;  // zero residual mass (reachable only through rounding): keep p
     }
     if (!iid) {
-      if (x_ok && t == x / EPT) D(x % EPT) = -INFINITY;
+      if (x_ok && t == x / EPT) Q(x % EPT) = 0.f;
       S = qmass();
     }
   }
-#undef D
+#undef Q
   // every child rejected: correction from the residual
   return make_int2(-1, draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired));
 }
