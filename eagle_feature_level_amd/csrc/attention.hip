@@ -63,12 +63,19 @@ constexpr int ROPE_HPB = 4;
 template <typename T>
 __global__ void __launch_bounds__(256) rope_kv_kernel(RopeArgs a) {
   __shared__ float cs[64], sn[64];
+  __shared__ int s_b;
   const int r = blockIdx.x;
   const int hd = a.hd, half = hd / 2;
   const int nheads = a.hq + 2 * a.hkv;
   const int h0 = blockIdx.y * ROPE_HPB;
   const float* src = a.qkv + (size_t)r * nheads * hd;
-  const int b = a.seq_of_row ? a.seq_of_row[r] : 0;
+  // the row's sequence: the one b with row_start[b] <= r < row_start[b+1]
+  if (threadIdx.x == 0) s_b = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.batch; i += blockDim.x)
+    if (a.row_start[i] <= r && r < a.row_start[i + 1]) s_b = i;
+  __syncthreads();
+  const int b = s_b;
   const int slot = a.slot[r];
   T* tk = (T*)a.tree_k + (((size_t)b * 64 + slot) * a.hkv) * hd;
   T* tv = (T*)a.tree_v + (((size_t)b * 64 + slot) * a.hkv) * hd;

@@ -88,7 +88,6 @@ hipError_t timed(hipStream_t st, int role, double bytes, double flops, F&& launc
 }
 
 struct DraftWs {
-  int32_t* seq_of_row;
   float* xin;  // [f_parent ; e(token)], 2d per row
   float* x;
   float* xg;  // x * gain of the next RMSNorm (first x * g1, then h * g2)
@@ -128,7 +127,6 @@ DraftWs carve(const eagle_shape* s, int M, int B, int max_prefix, char* base) {
     off += align256(bytes);
     return (void*)p;
   };
-  w.seq_of_row = (int32_t*)take((size_t)M * 4);
   w.xin = (float*)take((size_t)M * 2 * s->d * 4);
   w.x = (float*)take((size_t)M * s->d * 4);
   w.xg = (float*)take((size_t)M * s->d * 4);
@@ -244,13 +242,12 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
   const int d = s.d, hq = s.n_heads * s.head_dim, hkv = s.n_kv_heads * s.head_dim, F = s.ffn;
 
   if (!head_only) {
-    // a1: the rows' inputs [f_parent ; e(token)] and sequence indices
-    {
+    // a1: the rows' inputs [f_parent ; e(token)]: gathered by the FC GEMM itself
+    // up to 16 rows (bf16), else concatenated here
+    const bool gather = bf16 && M <= 16;
+    if (!gather) {
       RowSetupArgs r;
-      r.row_start = rows->row_start;
-      r.batch = rows->batch;
       r.n_rows = M;
-      r.seq_of_row = ws.seq_of_row;
       r.parent = rows->parent;
       r.token = rows->token;
       r.feat = feat_in;
@@ -267,8 +264,16 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     {
       GemmArgs a = gemm_base(M, d, 2 * d);
       a.w0 = w->fc_w;
-      a.x = ws.xin;
-      a.ldx = 2 * d;
+      if (gather) {
+        a.gfeat = feat_in;
+        a.gparent = rows->parent;
+        a.gtoken = rows->token;
+        a.gembed = w->embed;
+        a.gd = d;
+      } else {
+        a.x = ws.xin;
+        a.ldx = 2 * d;
+      }
       a.bias = w->fc_b;
       a.y = ws.x;
       a.ldy = d;
@@ -302,7 +307,8 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       r.qkv = ws.qkv;
       r.pos = rows->pos;
       r.slot = rows->slot;
-      r.seq_of_row = ws.seq_of_row;
+      r.row_start = rows->row_start;
+      r.batch = rows->batch;
       r.q_out = (float*)ws.qrot;
       r.tree_k = kv->tree_k;
       r.tree_v = kv->tree_v;

@@ -25,6 +25,12 @@ struct GemmArgs {
   const float* x;
   int ldx;
   const int32_t* xrows;
+  // or, for M <= 16 with K = 2 gd: row m = [gfeat[gparent[m]] (fp32) ; gembed[gtoken[m]] (bf16)]
+  const float* gfeat;
+  const int32_t* gparent;
+  const int32_t* gtoken;
+  const void* gembed;
+  int gd;
   // RMSNorm of the input rows, when sumsq_in is set: acc[m, :] *= rsqrt(sum_p sumsq_in[p][m] / K + eps)
   // (x then already carries the gain)
   const float* sumsq_in;  // [n_part_in][M]

@@ -173,16 +173,27 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
     const int n = tile_row<AT, EPI>(a, tile, at, r, &ok);
     ap[at] = wrow<bf16_t>(a, n) + g * 32;
   }
-  // coalesced chunk: quad q of lane l covers row xm[q], columns xc..xc+3 of the k-step
+  // coalesced chunk: quad q of lane l covers row xm[q], columns xc..xc+3 of the k-step.
+  // Gathered rows: columns below gd from the parent's feature row (fp32), the
+  // rest from the token's embedding row (bf16, widened exactly); gd is a
+  // multiple of the k-step, so a k-step reads one of the two.
   const int xc = (lane & 31) * 4;
+  const bool gather = a.gfeat != nullptr;
   const float* xq[MQ];
+  const bf16_t* xe[MQ];
   bool xv[MQ];
 #pragma unroll
   for (int q = 0; q < MQ; ++q) {
     const int m = 2 * q + (lane >> 5);
     xv[q] = m < a.M;
-    const int row = xv[q] ? (a.xrows ? a.xrows[m] : m) : 0;
-    xq[q] = a.x + (size_t)row * a.ldx + xc;
+    if (gather) {
+      xq[q] = a.gfeat + (size_t)(xv[q] ? a.gparent[m] : 0) * a.gd + xc;
+      xe[q] = (const bf16_t*)a.gembed + (size_t)(xv[q] ? a.gtoken[m] : 0) * a.gd + xc;
+    } else {
+      const int row = xv[q] ? (a.xrows ? a.xrows[m] : m) : 0;
+      xq[q] = a.x + (size_t)row * a.ldx + xc;
+      xe[q] = nullptr;
+    }
   }
   float* xw = &smem[wv * XR * SK_XROW];
   const bool mv = r < a.M;
@@ -194,9 +205,17 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
     for (int at = 0; at < AT; ++at)
 #pragma unroll
       for (int j = 0; j < 4; ++j) st.A[at][j] = *(const u32x4*)(ap[at] + (size_t)ks * SK_KSTEP + j * 8);
+    const int k0 = ks * SK_KSTEP;
+    if (!gather || k0 < a.gd) {  // uniform: ks is the wave's
 #pragma unroll
-    for (int q = 0; q < MQ; ++q)
-      st.X[q] = xv[q] ? *(const u32x4*)(xq[q] + (size_t)ks * SK_KSTEP) : u32x4{0, 0, 0, 0};
+      for (int q = 0; q < MQ; ++q) st.X[q] = xv[q] ? *(const u32x4*)(xq[q] + k0) : u32x4{0, 0, 0, 0};
+    } else {
+#pragma unroll
+      for (int q = 0; q < MQ; ++q) {
+        const uint2 e = xv[q] ? *(const uint2*)(xe[q] + (k0 - a.gd)) : make_uint2(0u, 0u);
+        st.X[q] = u32x4{e.x << 16, e.x & 0xffff0000u, e.y << 16, e.y & 0xffff0000u};
+      }
+    }
   };
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
@@ -685,6 +704,7 @@ size_t gemm_bf16_partial_bytes(int M, int N, int K) {
 
 hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s) {
   if (a.K % SK_KSTEP) return hipErrorInvalidValue;  // both kernels step K in whole 128-element blocks
+  if (a.gfeat && (a.M > 16 || a.gd % SK_KSTEP || a.K != 2 * a.gd)) return hipErrorInvalidValue;
   if ((epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) && a.y2 && !a.gain_out) return hipErrorInvalidValue;
   if (a.M <= 16) return skinny_launch(a, epi, n_part_out, s);
   if (a.N % 4) return hipErrorInvalidValue;  // float4 epilogue stores

@@ -7,7 +7,8 @@ struct RopeArgs {
   const float* qkv;  // [n_rows, (hq + 2 hkv) hd] fp32
   const int32_t* pos;
   const int32_t* slot;
-  const int32_t* seq_of_row;
+  const int32_t* row_start;  // [batch + 1]: rows of sequence b are [row_start[b], row_start[b+1])
+  int batch;
   float* q_out;  // [n_rows, hq hd] rotated q
   void* tree_k;
   void* tree_v;
@@ -30,11 +31,9 @@ struct AttnArgs {
   int n_rows, batch, hq, hkv, split_len, n_splits;
 };
 
-// Row set-up: seq_of_row[m]; when xin is set, also xin[m] = [feat[parent[m]] ; embed[token[m]]] (fp32, 2d).
+// Row set-up: xin[m] = [feat[parent[m]] ; embed[token[m]]] (fp32, 2d).
 struct RowSetupArgs {
-  const int32_t* row_start;
-  int batch, n_rows;
-  int32_t* seq_of_row;
+  int n_rows;
   const int32_t* parent;
   const int32_t* token;
   const float* feat;  // [*, d] fp32

@@ -1,5 +1,6 @@
-// Per-call row set-up of a draft step: each row's sequence index and the
-// draft layer's input [f_parent ; e(token)] as one fp32 row of 2d values.
+// Row set-up of a draft step over more than 16 rows: the draft layer's input
+// [f_parent ; e(token)] as one fp32 row of 2d values (up to 16 rows the FC
+// GEMM gathers the two halves itself).
 //
 // The draft head concatenates the parent's feature vector with the embedding
 // of the token sampled after it, then reduces the 2d values to d with a fully
@@ -12,20 +13,10 @@
 
 namespace {
 
-// One workgroup per row.  Thread 0 finds the row's sequence (rows of a
-// sequence are contiguous, row_start ascending).
+// One workgroup per row.
 template <typename T>
 __global__ void __launch_bounds__(256) row_setup_kernel(RowSetupArgs a) {
   const int m = blockIdx.x;
-  if (threadIdx.x == 0) {
-    int lo = 0, hi = a.batch - 1;
-    while (lo < hi) {  // last b with row_start[b] <= m
-      const int mid = (lo + hi + 1) / 2;
-      if (a.row_start[mid] <= m) lo = mid; else hi = mid - 1;
-    }
-    a.seq_of_row[m] = lo;
-  }
-  if (a.xin == nullptr) return;
   const int d = a.d;
   float* out = a.xin + (size_t)m * 2 * d;
   const float* fr = a.feat + (size_t)a.parent[m] * d;
