@@ -131,7 +131,8 @@ def cpu_baseline(cfg, host):
             rows["slot"].append(t)
             rows["mask"].append(int(tr["mask"][t]))
     tk, tv = OD.new_tree_kv(s, B)
-    tw = OD.draft_step(s, host["w"], rows, res["feat_buf"], host["ks"], host["vs"], host["lens"], tk, tv)["logits"]
+    tw = OD.draft_step(s, host["w"], rows, res["feat_buf"], host["ks"], host["vs"], host["lens"], tk, tv,
+                       act_bf16=False)["logits"]
     N = len(res["trees"][0]["parent"])
     noise = make_target_noise(cfg, B * N).reshape(B, N, -1)
     targets = [np.concatenate([res["logits"][b:b + 1], tw[b * (N - 1):(b + 1) * (N - 1)] + noise[b, 1:]])

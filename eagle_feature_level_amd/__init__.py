@@ -11,14 +11,14 @@ from __future__ import annotations
 import ctypes
 
 from . import _abi
-from ._abi import (EAGLE_BF16, EAGLE_F32, EAGLE_HEAD_ONLY, EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK, EAGLE_VERIFY_GREEDY,
+from ._abi import (EAGLE_ACT_BF16, EAGLE_BF16, EAGLE_F32, EAGLE_HEAD_ONLY, EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK, EAGLE_VERIFY_GREEDY,
                    EAGLE_VERIFY_IID, EagleError, eagle_draft_out, eagle_kv, eagle_pool, eagle_rows, eagle_shape,
                    eagle_weights)
 
 __all__ = ["eagle_workspace_bytes", "eagle_draft_step", "eagle_softmax_topk", "eagle_tree_init", "eagle_tree_expand",
            "eagle_tree_finalize", "eagle_verify", "eagle_verify_workspace_bytes", "make_shape", "make_weights",
            "make_rows", "make_kv", "make_out",
-           "make_pool", "EagleError", "EAGLE_HEAD_ONLY", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
+           "make_pool", "EagleError", "EAGLE_HEAD_ONLY", "EAGLE_ACT_BF16", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
            "EAGLE_F32", "EAGLE_MAX_SLOTS", "EAGLE_MAX_TOPK", "eagle_profile_enable", "eagle_profile_reset",
            "eagle_profile_disable", "eagle_profile_read"]
 

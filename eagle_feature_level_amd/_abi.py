@@ -16,7 +16,7 @@ c_i32, c_u64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_uint64, ctypes.c_fl
 
 EAGLE_OK, EAGLE_EINVAL, EAGLE_EUNSUPPORTED, EAGLE_EWORKSPACE, EAGLE_EHIP = 0, -1, -2, -3, -4
 EAGLE_F32, EAGLE_BF16 = 0, 1
-EAGLE_HEAD_ONLY = 1
+EAGLE_HEAD_ONLY, EAGLE_ACT_BF16 = 1, 2
 EAGLE_VERIFY_GREEDY, EAGLE_VERIFY_IID = 1, 2
 EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK = 64, 16
 ROLES = ("fc", "qkv", "rope", "attn", "o", "gate_up", "down", "lm_head", "topk", "rows")

@@ -196,8 +196,10 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
                      const float* feat_in, const eagle_kv* kv, const eagle_draft_out* out, void* workspace,
                      size_t workspace_bytes, eagle_stream_t stream) {
   if (!shape_ok(shape) || !w || !rows || !out) return EAGLE_EINVAL;
-  if (flags & ~EAGLE_HEAD_ONLY) return EAGLE_EINVAL;
+  if (flags & ~(EAGLE_HEAD_ONLY | EAGLE_ACT_BF16)) return EAGLE_EINVAL;
   const bool head_only = flags & EAGLE_HEAD_ONLY;
+  const int act16 = (flags & EAGLE_ACT_BF16) ? 1 : 0;
+  if (act16 && shape && shape->dtype != EAGLE_BF16) return EAGLE_EINVAL;  // a bf16 rounding of an fp32 workload
   const int M = rows->n_rows;
   if (M < 0 || rows->batch <= 0) return EAGLE_EINVAL;
   if (M == 0) return EAGLE_OK;
@@ -230,7 +232,8 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
   // algorithmic bytes of a GEMM launch: weights once, fp32 activations in and out
   auto gemm = [&](GemmArgs a, int epi, int* np, int role) -> hipError_t {
     int dummy = 0;
-    a.part = ws.gemm_part;  // split-K partials of the tiled kernel
+    a.part = ws.gemm_part;  // split-K partials of the tiled kernel (+ the bf16 operand)
+    a.act_bf16 = act16;
     const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
     const double bytes = wbytes * a.N * a.K + 4.0 * a.M * (a.K + nout) + (a.y2 ? 4.0 * a.M * a.N : 0.0);
     const double flops = 2.0 * a.M * a.N * a.K;
@@ -243,8 +246,8 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
 
   if (!head_only) {
     // a1: the rows' inputs [f_parent ; e(token)]: gathered by the FC GEMM itself
-    // up to 16 rows (bf16), else concatenated here
-    const bool gather = bf16 && M <= 16;
+    // (its loader, or its operand prep pass) for bf16 weights, else concatenated here
+    const bool gather = bf16;
     if (!gather) {
       RowSetupArgs r;
       r.n_rows = M;

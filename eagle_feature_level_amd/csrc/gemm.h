@@ -51,6 +51,10 @@ struct GemmArgs {
   // split-K partials for the tiled kernel
   float* part;
   int splits;
+  // activation precision: 0 = each fp32 activation enters the matrix units as
+  // a (hi, lo) pair of bf16 values (two MFMAs per product); 1 = it is rounded
+  // once to bf16 (round to nearest even) after the RMSNorm row scale, one MFMA
+  int act_bf16;
 };
 
 // Launch helpers (host).  Return hipSuccess or the launch error.

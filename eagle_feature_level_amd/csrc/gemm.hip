@@ -9,8 +9,10 @@
 //    through LDS because every W element is used by exactly one wave.
 //  * x (fp32) is the MFMA "B" operand (M padded to 16).  The skinny kernel
 //    (M <= 16) loads each k-step's rows of x coalesced and re-reads them in the
-//    B layout from the wave's own LDS slice; the large-M kernel stages weight
-//    and x tiles through LDS so the waves of a workgroup share both.
+//    B layout from the wave's own LDS slice.  Above 16 rows a prep pass writes
+//    the operand once in bf16 (hi and lo halves, or one rounded half), and the
+//    wide kernel (weights to VGPRs, activation tile shared through LDS) or the
+//    large-M kernel (both operands through LDS) consume it.
 //  * Activations enter the matrix units as a pair of bf16 values, hi = x cut
 //    to bf16 and lo = bf16(x - hi), two MFMAs into one fp32 accumulator: the
 //    product then carries ~16 significant bits of x instead of 8, which keeps a
@@ -106,8 +108,18 @@ __device__ __forceinline__ B8 split8(float4 v0, float4 v1) {
   return r;
 }
 
-__device__ __forceinline__ float4 as_f4(u32x4 v) {
-  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+// fp32 -> bf16 round to nearest even, two values per instruction
+// (v_cvt_pk_bf16_f32; value a in the low half).
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ u32x4 round8(float4 v0, float4 v1, float sc) {
+  return u32x4{cvt2(v0.x * sc, v0.y * sc), cvt2(v0.z * sc, v0.w * sc), cvt2(v1.x * sc, v1.y * sc),
+               cvt2(v1.z * sc, v1.w * sc)};
 }
 
 __device__ __forceinline__ floatx4 mfma16(u32x4 a, u32x4 b, floatx4 c) {
@@ -155,7 +167,7 @@ struct SkStage {
   u32x4 X[MQ];     // coalesced activation chunk: lane l, quad q -> row (q*64+l)/32, 4 floats
 };
 
-template <int AT, int NW, int MQ, int NS, int EPI>
+template <int AT, int NW, int MQ, int NS, bool A16, int EPI>
 __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
   constexpr int XR = 2 * MQ;  // activation rows this instance can hold
   constexpr int BN = 16 * AT;
@@ -225,6 +237,15 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
   // while the first stages are in flight; visible after the reduction barrier
   __shared__ float scale[16];
   if (a.sumsq_in) row_scales_lds<NW * 64>(a, 16, scale);
+  // bf16 activations are rounded after the RMSNorm row scale, so the scales
+  // are needed before the first product
+  float xs = 1.f;
+  if constexpr (A16) {
+    if (a.sumsq_in) {
+      __syncthreads();
+      xs = scale[r];
+    }
+  }
 
   floatx4 acc[AT];
 #pragma unroll
@@ -241,11 +262,17 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
         v0 = make_float4(0.f, 0.f, 0.f, 0.f);
         v1 = v0;
       }
-      const B8 B = split8(v0, v1);
+      if constexpr (A16) {
+        const u32x4 B = round8(v0, v1, xs);
 #pragma unroll
-      for (int at = 0; at < AT; ++at) {
-        acc[at] = mfma16(st.A[at][j], B.hi, acc[at]);
-        acc[at] = mfma16(st.A[at][j], B.lo, acc[at]);
+        for (int at = 0; at < AT; ++at) acc[at] = mfma16(st.A[at][j], B, acc[at]);
+      } else {
+        const B8 B = split8(v0, v1);
+#pragma unroll
+        for (int at = 0; at < AT; ++at) {
+          acc[at] = mfma16(st.A[at][j], B.hi, acc[at]);
+          acc[at] = mfma16(st.A[at][j], B.lo, acc[at]);
+        }
       }
     }
   };
@@ -282,7 +309,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
           gs += red[w][m][jl];
           us += red[w][m][jl + H];
         }
-        if (a.sumsq_in) {
+        if (!A16 && a.sumsq_in) {
           gs *= scale[m];
           us *= scale[m];
         }
@@ -301,7 +328,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
       if (live) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) y += red[w][m][nl];
-        if (a.sumsq_in) y *= scale[m];
+        if (!A16 && a.sumsq_in) y *= scale[m];
         if constexpr (EPI == EPI_BIAS_SUMSQ) y += bf2f(((const bf16_t*)a.bias)[n]);
         if constexpr (EPI == EPI_RESID || EPI == EPI_RESID_SUMSQ) y += a.resid[(size_t)m * a.ldr + n];
         a.y[(size_t)m * a.ldy + n] = y;
@@ -318,20 +345,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Large-M kernel (M > 16): the matrix units are the bound once M reaches a few
-// hundred rows.  A workgroup of 8 waves computes 256 weight rows x 128 rows of
-// x (64 x 64 per wave, 4 x 4 blocks of v_mfma_f32_16x16x32_bf16, hi and lo).
-// Per 64-wide K step the weight tile and the hi/lo split of the x tile are
-// staged in LDS (two buffers); the next step's global loads sit in registers
-// while the current step is multiplied.  Row blocks of x vary fastest over the
-// grid, and consecutive tiles are kept on one XCD, so the workgroups sharing
-// a weight tile run together and share an L2.  With a K split the raw
-// partial sums go to a.part and gemm_reduce applies the epilogue; otherwise
-// the epilogue runs here on the accumulators.
-// SwiGLU: the 256 rows of a tile are, per wave quarter, 32 gate rows and the
-// 32 up rows of the same ffn columns, so gate and up meet in one lane.
-// ---------------------------------------------------------------------------
+// Tile geometry of the large-M kernel (gemm_big16 below): 256 weight rows x
+// 128 activation rows per workgroup, 64-wide K blocks staged in LDS.
 constexpr int BG_BN = 256, BG_BM = 128, BG_BK = 64;
 constexpr int BG_LD = BG_BK + 8;  // LDS row (bf16): 144 B, rows 4 banks apart
 
@@ -339,12 +354,235 @@ struct BigPlan {
   int tiles_n, tiles_m, splits;
 };
 
-template <int EPI>
-__global__ void __launch_bounds__(512) gemm_big(GemmArgs a, BigPlan p) {
+// ---------------------------------------------------------------------------
+// Wide kernel: bf16 activations (act_bf16) and M > 16.  Both operands are
+// bf16 in memory: a prep pass (act_prep) writes the activation operand once,
+// bf16(x * RMSNorm row scale), or bf16 of the gathered [f ; e] rows.
+//  * 4 waves; wave w owns 16*AT weight rows (the MFMA A operand), streamed from
+//    HBM straight into VGPRs through an NS-stage register ring exactly as in
+//    the skinny kernel (lane (r, g) takes 32 contiguous k of row r per k-step).
+//  * The activation tile [16*MB rows][128 k] is the B operand, shared by the
+//    four waves through LDS (two buffers, one barrier per k-step); each
+//    thread prefetches its part of the next-but-one tile into registers.
+//  * M is split into tiles of at most 128 rows; consecutive workgroups take
+//    the M tiles of one weight tile and are kept on one XCD (shared L2), so
+//    the weights leave HBM about once.  K is split over the grid while the
+//    grid would leave CUs idle; gemm_reduce then sums the partials.
+// ---------------------------------------------------------------------------
+constexpr int WD_XLD = SK_KSTEP + 8;  // LDS row of the activation tile (bf16): 272 B, rows 4 banks apart
+
+struct WidePlan {
+  int tiles_n, tiles_m, splits, ks_per_split;
+};
+
+template <int NW, int AT, int MB, int NS, bool SPLIT, int EPI>
+__global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* __restrict__ xb, WidePlan p) {
+  constexpr int NT = NW * 64, BM = 16 * MB;
+  constexpr int NH = SPLIT ? 2 : 1;  // operand halves: hi (and lo, at xb + M*K)
+  constexpr int XCH = (BM * 16 + NT - 1) / NT;  // 16-byte activation chunks per thread per k-step and half
+  __shared__ __attribute__((aligned(16))) bf16_t Xs[2][NH][BM][WD_XLD];
+  __shared__ float ssq_s[NW][BM];
+  const int nwg = gridDim.x, bid = blockIdx.x;
+  const int lid = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;  // consecutive tiles on one XCD
+  const int mt = lid % p.tiles_m, rest = lid / p.tiles_m;
+  const int nt = rest % p.tiles_n, sp = rest / p.tiles_n;
+  const int m0 = mt * BM;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int nks_all = a.K / SK_KSTEP;
+  const int ks0 = sp * p.ks_per_split;
+  const int nks = max(0, min(nks_all - ks0, p.ks_per_split));
+
+  const int wtile = nt * NW + wv;  // this wave's tile of 16*AT weight rows
+  const bf16_t* ap[AT];
+#pragma unroll
+  for (int at = 0; at < AT; ++at) {
+    bool ok;
+    const int n = tile_row<AT, EPI>(a, wtile, at, r, &ok);
+    ap[at] = wrow<bf16_t>(a, n) + g * 32;
+  }
+  // activation chunks: chunk c = t + NT u covers tile row c / 16, columns 8 (c % 16) .. + 7
+  const bf16_t* xp[XCH];
+  bool xv[XCH], xl[XCH];
+#pragma unroll
+  for (int u = 0; u < XCH; ++u) {
+    const int c = t + NT * u, m = m0 + (c >> 4);
+    xl[u] = c < BM * 16;  // chunk inside the tile
+    xv[u] = xl[u] && m < a.M;
+    xp[u] = xb + (size_t)(xv[u] ? m : 0) * a.K + (c & 15) * 8;
+  }
+  const size_t lo_off = (size_t)a.M * a.K;
+  u32x4 xr[NH][XCH];
+  auto load_x = [&](int ks) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int u = 0; u < XCH; ++u)
+        xr[h][u] = xv[u] ? *(const u32x4*)(xp[u] + h * lo_off + (size_t)ks * SK_KSTEP) : u32x4{0, 0, 0, 0};
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int u = 0; u < XCH; ++u) {
+        const int c = t + NT * u;
+        if (xl[u]) *(u32x4*)&Xs[buf][h][c >> 4][(c & 15) * 8] = xr[h][u];
+      }
+  };
+  struct Stage {
+    u32x4 A[AT][4];
+  };
+  Stage S[NS];
+  auto issue = [&](Stage& st, int ks) {
+#pragma unroll
+    for (int at = 0; at < AT; ++at)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st.A[at][j] = *(const u32x4*)(ap[at] + (size_t)ks * SK_KSTEP + j * 8);
+  };
+
+  floatx4 acc[AT][MB];
+#pragma unroll
+  for (int at = 0; at < AT; ++at)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[at][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nks) issue(S[st], ks0 + st);
+  if (nks > 0) {
+    load_x(ks0);
+    store_x(0);
+    if (nks > 1) load_x(ks0 + 1);
+  }
+  __syncthreads();
+
+  for (int s0 = 0; s0 < nks; s0 += NS) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int s = s0 + st;
+      if (s >= nks) break;
+      if (s + NS - 1 < nks) issue(S[(st + NS - 1) % NS], ks0 + s + NS - 1);
+      const int buf = s & 1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          u32x4 B[MB];
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) B[mb] = *(const u32x4*)&Xs[buf][h][mb * 16 + r][g * 32 + j * 8];
+#pragma unroll
+          for (int at = 0; at < AT; ++at)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[at][mb] = mfma16(S[st].A[at][j], B[mb], acc[at][mb]);
+        }
+      }
+      if (s + 1 < nks) {
+        store_x(buf ^ 1);
+        if (s + 2 < nks) load_x(ks0 + s + 2);
+      }
+      __syncthreads();
+    }
+  }
+
+  // lane (r, g): acc[at][mb][v] = output row m0 + 16 mb + r, logical weight row 16 at + 4 g + v of the wave's tile
+  if (p.splits > 1) {
+    float* P = a.part + (size_t)sp * a.M * a.N;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + mb * 16 + r;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int at = 0; at < AT; ++at) {
+        bool ok;
+        const int n = tile_row<AT, EPI>(a, wtile, at, 4 * g, &ok);  // 4 consecutive logical rows
+        if (ok) *(floatx4*)(P + (size_t)m * a.N + n) = acc[at][mb];
+      }
+    }
+    return;
+  }
+  if constexpr (EPI == EPI_SWIGLU) {
+    constexpr int H = AT / 2;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + mb * 16 + r;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int at = 0; at < H; ++at) {
+        const int j = wtile * 16 * H + at * 16 + 4 * g;
+        if (j >= a.ffn) continue;
+        float4 o;
+        o.x = silu_f(acc[at][mb][0]) * acc[at + H][mb][0];
+        o.y = silu_f(acc[at][mb][1]) * acc[at + H][mb][1];
+        o.z = silu_f(acc[at][mb][2]) * acc[at + H][mb][2];
+        o.w = silu_f(acc[at][mb][3]) * acc[at + H][mb][3];
+        *(float4*)(a.yb + (size_t)m * a.ldyb + j) = o;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int ml = mb * 16 + r, m = m0 + ml;
+      const bool mv = m < a.M;
+      float ss = 0.f;
+#pragma unroll
+      for (int at = 0; at < AT; ++at) {
+        const int n = wtile * 16 * AT + at * 16 + 4 * g;
+        if (!mv || n >= a.N) continue;
+        float4 y = make_float4(acc[at][mb][0], acc[at][mb][1], acc[at][mb][2], acc[at][mb][3]);
+        if constexpr (EPI == EPI_BIAS_SUMSQ) {
+          const bf16_t* bb = (const bf16_t*)a.bias + n;
+          y.x += bf2f(bb[0]); y.y += bf2f(bb[1]); y.z += bf2f(bb[2]); y.w += bf2f(bb[3]);
+        }
+        if constexpr (EPI == EPI_RESID || EPI == EPI_RESID_SUMSQ) {
+          const float4 rr = *(const float4*)(a.resid + (size_t)m * a.ldr + n);
+          y.x += rr.x; y.y += rr.y; y.z += rr.z; y.w += rr.w;
+        }
+        *(float4*)(a.y + (size_t)m * a.ldy + n) = y;
+        if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
+          if (a.y2) {
+            const bf16_t* gn = (const bf16_t*)a.gain_out + n;
+            *(float4*)(a.y2 + (size_t)m * a.ldy + n) =
+                make_float4(y.x * bf2f(gn[0]), y.y * bf2f(gn[1]), y.z * bf2f(gn[2]), y.w * bf2f(gn[3]));
+          }
+          ss += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+        }
+      }
+      if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
+        ss += __shfl_xor(ss, 16, WAVE);
+        ss += __shfl_xor(ss, 32, WAVE);
+        if (g == 0) ssq_s[wv][ml] = ss;
+      }
+    }
+    if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
+      __syncthreads();
+      if (t < BM && m0 + t < a.M) {
+        float q = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) q += ssq_s[w][t];
+        a.sumsq_out[(size_t)nt * a.M + m0 + t] = q;
+      }
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Large-M kernel (M above a few hundred rows, where the matrix units are the
+// bound): 256 weight rows x 128 activation rows per workgroup, 8 waves of
+// 64 x 64, both operands staged through LDS in two buffers, fed from the
+// prepared bf16 operand (one half, or the hi and lo halves: two MFMAs per
+// product), with PD k-blocks of global loads in flight in registers ahead of
+// the LDS buffer being multiplied.  Row blocks of the activations vary
+// fastest over the grid and consecutive tiles stay on one XCD, so the
+// workgroups sharing a weight tile run together and share an L2.  SwiGLU: the
+// 256 rows of a tile are, per wave quarter, 32 gate rows and the 32 up rows
+// of the same ffn columns, so gate and up meet in one lane.
+// ---------------------------------------------------------------------------
+template <int EPI, int PD, bool SPLIT>
+__global__ void __launch_bounds__(512) gemm_big16(GemmArgs a, const bf16_t* __restrict__ xb, BigPlan p) {
+  constexpr int NH = SPLIT ? 2 : 1;  // operand halves: hi (and lo, at xb + M*K)
   __shared__ __attribute__((aligned(16))) bf16_t As[2][BG_BN][BG_LD];
-  __shared__ __attribute__((aligned(16))) bf16_t Bh[2][BG_BM][BG_LD];
-  __shared__ __attribute__((aligned(16))) bf16_t Bl[2][BG_BM][BG_LD];
-  __shared__ float rs_s[BG_BM];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][NH][BG_BM][BG_LD];
   __shared__ float ssq_s[4][BG_BM];
   const int nwg = gridDim.x, bid = blockIdx.x;
   const int lid = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;  // consecutive tiles on one XCD
@@ -356,7 +594,6 @@ __global__ void __launch_bounds__(512) gemm_big(GemmArgs a, BigPlan p) {
   const int r = lane & 15, g = lane >> 4;
   const int kper = a.K / p.splits, kbeg = sp * kper, nkb = kper / BG_BK;
 
-  // logical weight row of tile row i (-1 past the end)
   auto wrow_of = [&](int i) -> int {
     if constexpr (EPI == EPI_SWIGLU) {
       const int q = i >> 6, w = i & 63;
@@ -368,40 +605,42 @@ __global__ void __launch_bounds__(512) gemm_big(GemmArgs a, BigPlan p) {
       return n < a.N ? n : -1;
     }
   };
-  // staging: weights rows t/8 + 64u, 8 columns at 8*(t%8); x rows t/16 + 32u, 4 columns at 4*(t%16)
-  const int ac = (t & 7) * 8, xc = (t & 15) * 4;
+  // staging: weight rows t/8 + 64u (u < 4), activation rows t/8 + 64u (u < 2); 8 columns at 8*(t%8)
+  const int cc = (t & 7) * 8;
   const bf16_t* ap[4];
-  const float* xp[4];
+  const bf16_t* xp[2];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int n = wrow_of((t >> 3) + 64 * u);
-    ap[u] = (n >= 0) ? wrow<bf16_t>(a, n) + kbeg + ac : nullptr;
-    const int m = m0 + (t >> 4) + 32 * u;
-    xp[u] = (m < a.M) ? a.x + (size_t)(a.xrows ? a.xrows[m] : m) * a.ldx + kbeg + xc : nullptr;
+    ap[u] = (n >= 0) ? wrow<bf16_t>(a, n) + kbeg + cc : nullptr;
   }
-  u32x4 areg[4];
-  float4 xreg[4];
-  auto load_global = [&](int kb) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int m = m0 + (t >> 3) + 64 * u;
+    xp[u] = (m < a.M) ? xb + (size_t)m * a.K + kbeg + cc : nullptr;
+  }
+  const size_t lo_off = (size_t)a.M * a.K;
+  struct Pf {
+    u32x4 A[4], X[NH][2];
+  };
+  Pf pf[PD];
+  auto load = [&](Pf& f, int kb) {
     const int k0 = kb * BG_BK;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      areg[u] = ap[u] ? *(const u32x4*)(ap[u] + k0) : u32x4{0, 0, 0, 0};
-      xreg[u] = xp[u] ? *(const float4*)(xp[u] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  auto store_lds = [&](int buf) {
+    for (int u = 0; u < 4; ++u) f.A[u] = ap[u] ? *(const u32x4*)(ap[u] + k0) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      *(u32x4*)&As[buf][(t >> 3) + 64 * u][ac] = areg[u];
-      uint32_t l0, l1;
-      const uint32_t h0 = split2(xreg[u].x, xreg[u].y, &l0), h1 = split2(xreg[u].z, xreg[u].w, &l1);
-      *(uint2*)&Bh[buf][(t >> 4) + 32 * u][xc] = make_uint2(h0, h1);
-      *(uint2*)&Bl[buf][(t >> 4) + 32 * u][xc] = make_uint2(l0, l1);
-    }
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) f.X[h][u] = xp[u] ? *(const u32x4*)(xp[u] + h * lo_off + k0) : u32x4{0, 0, 0, 0};
   };
-
-  const bool fused = (p.splits == 1);
-  if (fused && a.sumsq_in && t < BG_BM) rs_s[t] = (m0 + t < a.M) ? row_scale(a, m0 + t) : 1.f;
+  auto store = [&](const Pf& f, int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *(u32x4*)&As[buf][(t >> 3) + 64 * u][cc] = f.A[u];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) *(u32x4*)&Bs[buf][h][(t >> 3) + 64 * u][cc] = f.X[h][u];
+  };
 
   floatx4 acc[4][4];
 #pragma unroll
@@ -409,36 +648,48 @@ __global__ void __launch_bounds__(512) gemm_big(GemmArgs a, BigPlan p) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  load_global(0);
-  store_lds(0);
+  // slot j % PD holds k-block j for j in (kb, kb + PD]
+#pragma unroll
+  for (int i = 0; i < PD; ++i)
+    if (i < nkb) load(pf[i], i);
+  if (nkb > 0) {
+    store(pf[0], 0);
+    if (PD < nkb) load(pf[0], PD);
+  }
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) load_global(kb + 1);
+  for (int kb0 = 0; kb0 < nkb; kb0 += PD) {
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      u32x4 A[4], Bhf[4], Blf[4];
+    for (int i = 0; i < PD; ++i) {
+      const int kb = kb0 + i;
+      if (kb >= nkb) break;
+      const int buf = kb & 1;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) A[nb] = *(const u32x4*)&As[buf][wn * 64 + nb * 16 + r][kc * 32 + g * 8];
+      for (int kc = 0; kc < 2; ++kc) {
+        u32x4 A[4];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        Bhf[mb] = *(const u32x4*)&Bh[buf][wm * 64 + mb * 16 + r][kc * 32 + g * 8];
-        Blf[mb] = *(const u32x4*)&Bl[buf][wm * 64 + mb * 16 + r][kc * 32 + g * 8];
-      }
+        for (int nb = 0; nb < 4; ++nb) A[nb] = *(const u32x4*)&As[buf][wn * 64 + nb * 16 + r][kc * 32 + g * 8];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+        for (int h = 0; h < NH; ++h) {
+          u32x4 B[4];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          acc[nb][mb] = mfma16(A[nb], Bhf[mb], acc[nb][mb]);
-          acc[nb][mb] = mfma16(A[nb], Blf[mb], acc[nb][mb]);
+          for (int mb = 0; mb < 4; ++mb)
+            B[mb] = *(const u32x4*)&Bs[buf][h][wm * 64 + mb * 16 + r][kc * 32 + g * 8];
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma16(A[nb], B[mb], acc[nb][mb]);
         }
+      }
+      if (kb + 1 < nkb) {
+        store(pf[(i + 1) % PD], buf ^ 1);
+        if (kb + 1 + PD < nkb) load(pf[(i + 1) % PD], kb + 1 + PD);
+      }
+      __syncthreads();
     }
-    if (kb + 1 < nkb) store_lds(buf ^ 1);
-    __syncthreads();
   }
 
-  // lane (r, g): acc[nb][mb][v] = tile row wn*64 + nb*16 + 4g + v, x row wm*64 + mb*16 + r
-  if (!fused) {
+  // lane (r, g): acc[nb][mb][v] = tile row wn*64 + nb*16 + 4g + v, activation row wm*64 + mb*16 + r
+  if (p.splits > 1) {
     float* P = a.part + (size_t)sp * a.M * a.N;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -446,7 +697,7 @@ __global__ void __launch_bounds__(512) gemm_big(GemmArgs a, BigPlan p) {
       if (m >= a.M) continue;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const int n = wrow_of(wn * 64 + nb * 16 + 4 * g);  // 4 consecutive logical rows
+        const int n = wrow_of(wn * 64 + nb * 16 + 4 * g);
         if (n >= 0) *(floatx4*)(P + (size_t)m * a.N + n) = acc[nb][mb];
       }
     }
@@ -455,18 +706,17 @@ __global__ void __launch_bounds__(512) gemm_big(GemmArgs a, BigPlan p) {
   if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const int ml = wm * 64 + mb * 16 + r, m = m0 + ml;
+      const int m = m0 + wm * 64 + mb * 16 + r;
       if (m >= a.M) continue;
-      const float sc = a.sumsq_in ? rs_s[ml] : 1.f;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int j = nt * 128 + wn * 32 + nb * 16 + 4 * g;
         if (j >= a.ffn) continue;
         float4 o;
-        o.x = silu_f(acc[nb][mb][0] * sc) * (acc[nb + 2][mb][0] * sc);
-        o.y = silu_f(acc[nb][mb][1] * sc) * (acc[nb + 2][mb][1] * sc);
-        o.z = silu_f(acc[nb][mb][2] * sc) * (acc[nb + 2][mb][2] * sc);
-        o.w = silu_f(acc[nb][mb][3] * sc) * (acc[nb + 2][mb][3] * sc);
+        o.x = silu_f(acc[nb][mb][0]) * acc[nb + 2][mb][0];
+        o.y = silu_f(acc[nb][mb][1]) * acc[nb + 2][mb][1];
+        o.z = silu_f(acc[nb][mb][2]) * acc[nb + 2][mb][2];
+        o.w = silu_f(acc[nb][mb][3]) * acc[nb + 2][mb][3];
         *(float4*)(a.yb + (size_t)m * a.ldyb + j) = o;
       }
     }
@@ -475,13 +725,12 @@ __global__ void __launch_bounds__(512) gemm_big(GemmArgs a, BigPlan p) {
     for (int mb = 0; mb < 4; ++mb) {
       const int ml = wm * 64 + mb * 16 + r, m = m0 + ml;
       const bool mv = m < a.M;
-      const float sc = (mv && a.sumsq_in) ? rs_s[ml] : 1.f;
       float ss = 0.f;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int n = nt * BG_BN + wn * 64 + nb * 16 + 4 * g;
         if (!mv || n >= a.N) continue;
-        float4 y = make_float4(acc[nb][mb][0] * sc, acc[nb][mb][1] * sc, acc[nb][mb][2] * sc, acc[nb][mb][3] * sc);
+        float4 y = make_float4(acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]);
         if constexpr (EPI == EPI_BIAS_SUMSQ) {
           const bf16_t* bb = (const bf16_t*)a.bias + n;
           y.x += bf2f(bb[0]); y.y += bf2f(bb[1]); y.z += bf2f(bb[2]); y.w += bf2f(bb[3]);
@@ -491,7 +740,7 @@ __global__ void __launch_bounds__(512) gemm_big(GemmArgs a, BigPlan p) {
           y.x += rr.x; y.y += rr.y; y.z += rr.z; y.w += rr.w;
         }
         *(float4*)(a.y + (size_t)m * a.ldy + n) = y;
-        if (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
+        if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
           if (a.y2) {
             const bf16_t* gn = (const bf16_t*)a.gain_out + n;
             *(float4*)(a.y2 + (size_t)m * a.ldy + n) =
@@ -514,6 +763,53 @@ __global__ void __launch_bounds__(512) gemm_big(GemmArgs a, BigPlan p) {
   }
 }
 
+// The bf16 activation operand of the wide and large-M kernels, from
+// v = x[row(m)][k] * rs(m) (rs the RMSNorm row scale when sumsq_in is set,
+// else 1) or from the gathered row [f_parent ; e(token)]:
+//   SPLIT: xb[m][k] = hi(v) and xb[M*K + m*K + k] = lo(v), the split2 pair;
+//   else:  xb[m][k] = bf16(v), round to nearest even.
+// grid (ceil(K / 2048), M), 8 values per thread.
+template <bool SPLIT>
+__global__ void __launch_bounds__(256) act_prep(GemmArgs a, bf16_t* __restrict__ xb) {
+  __shared__ float red[4];
+  const int m = blockIdx.y;
+  const int k = (blockIdx.x * 256 + threadIdx.x) * 8;
+  float rs = 1.f;
+  if (a.sumsq_in) {
+    float sq = 0.f;
+    for (int q = threadIdx.x; q < a.n_part_in; q += 256) sq += a.sumsq_in[(size_t)q * a.M + m];
+    rs = rms_scale(block_sum<256>(sq, red), a);
+  }
+  if (k >= a.K) return;
+  float4 v0, v1;
+  if (a.gfeat) {
+    if (k < a.gd) {
+      const float* f = a.gfeat + (size_t)a.gparent[m] * a.gd + k;
+      v0 = *(const float4*)f;
+      v1 = *(const float4*)(f + 4);
+    } else {
+      const u32x4 e = *(const u32x4*)((const bf16_t*)a.gembed + (size_t)a.gtoken[m] * a.gd + (k - a.gd));
+      v0 = make_float4(__uint_as_float(e[0] << 16), __uint_as_float(e[0] & 0xffff0000u), __uint_as_float(e[1] << 16),
+                       __uint_as_float(e[1] & 0xffff0000u));
+      v1 = make_float4(__uint_as_float(e[2] << 16), __uint_as_float(e[2] & 0xffff0000u), __uint_as_float(e[3] << 16),
+                       __uint_as_float(e[3] & 0xffff0000u));
+    }
+  } else {
+    const float* x = a.x + (size_t)(a.xrows ? a.xrows[m] : m) * a.ldx + k;
+    v0 = *(const float4*)x;
+    v1 = *(const float4*)(x + 4);
+  }
+  if constexpr (SPLIT) {
+    v0.x *= rs; v0.y *= rs; v0.z *= rs; v0.w *= rs;
+    v1.x *= rs; v1.y *= rs; v1.z *= rs; v1.w *= rs;
+    const B8 h = split8(v0, v1);
+    *(u32x4*)(xb + (size_t)m * a.K + k) = h.hi;
+    *(u32x4*)(xb + (size_t)a.M * a.K + (size_t)m * a.K + k) = h.lo;
+  } else {
+    *(u32x4*)(xb + (size_t)m * a.K + k) = round8(v0, v1, rs);
+  }
+}
+
 // Sum split-K partials and apply the epilogue.  grid (ceil(Nout/1024), M).
 template <int EPI>
 __global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a) {
@@ -523,7 +819,7 @@ __global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a) {
   const int nout = (EPI == EPI_SWIGLU) ? a.ffn : a.N;
   const size_t stride = (size_t)a.M * a.N;
   float rs = 1.f;
-  if (a.sumsq_in) {
+  if (a.sumsq_in && !a.act_bf16) {  // bf16 activations were scaled before rounding
     float s = 0.f;
     for (int p = threadIdx.x; p < a.n_part_in; p += 256) s += a.sumsq_in[(size_t)p * a.M + m];
     rs = rms_scale(block_sum<256>(s, red), a);
@@ -624,26 +920,26 @@ __global__ void __launch_bounds__(64) gemm_f32(GemmArgs a) {
 // two stages in flight already keep HBM busy.
 constexpr int skinny_ns(int, int, int) { return 3; }
 
-template <int AT, int NW, int MQ, int NS = skinny_ns(AT, NW, MQ)>
+template <int AT, int NW, int MQ, bool A16, int NS = skinny_ns(AT, NW, MQ)>
 hipError_t skinny_epi(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
   const int BN = 16 * AT;
   dim3 blk(NW * 64);
   const dim3 grid((a.N + BN - 1) / BN);
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, EPI_STORE>), grid, blk, 0, s, a); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, A16, EPI_STORE>), grid, blk, 0, s, a); break;
     case EPI_BIAS_SUMSQ:
-      hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, EPI_BIAS_SUMSQ>), grid, blk, 0, s, a);
+      hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, A16, EPI_BIAS_SUMSQ>), grid, blk, 0, s, a);
       *n_part = grid.x;
       break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, EPI_RESID>), grid, blk, 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, A16, EPI_RESID>), grid, blk, 0, s, a); break;
     case EPI_RESID_SUMSQ:
-      hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, EPI_RESID_SUMSQ>), grid, blk, 0, s, a);
+      hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, A16, EPI_RESID_SUMSQ>), grid, blk, 0, s, a);
       *n_part = grid.x;
       break;
     case EPI_SWIGLU:
       if constexpr (AT >= 2) {  // gate and up tiles pair up inside a workgroup
         const int H = BN / 2;
-        hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, EPI_SWIGLU>), dim3((a.ffn + H - 1) / H), blk, 0, s, a);
+        hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, A16, EPI_SWIGLU>), dim3((a.ffn + H - 1) / H), blk, 0, s, a);
         break;
       } else {
         return hipErrorInvalidValue;
@@ -654,12 +950,12 @@ hipError_t skinny_epi(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int AT, int NW>
+template <int AT, int NW, bool A16>
 hipError_t skinny_mq(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
-  if (a.M <= 2) return skinny_epi<AT, NW, 1>(a, epi, n_part, s);
-  if (a.M <= 4) return skinny_epi<AT, NW, 2>(a, epi, n_part, s);
-  if (a.M <= 8) return skinny_epi<AT, NW, 4>(a, epi, n_part, s);
-  return skinny_epi<AT, NW, 8>(a, epi, n_part, s);
+  if (a.M <= 2) return skinny_epi<AT, NW, 1, A16>(a, epi, n_part, s);
+  if (a.M <= 4) return skinny_epi<AT, NW, 2, A16>(a, epi, n_part, s);
+  if (a.M <= 8) return skinny_epi<AT, NW, 4, A16>(a, epi, n_part, s);
+  return skinny_epi<AT, NW, 8, A16>(a, epi, n_part, s);
 }
 
 // Variant choice, measured on the 7B draft-head shapes (N = 4096, 12288,
@@ -672,15 +968,17 @@ hipError_t skinny_mq(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
 //    a wave streams per step;
 //  * wide N, M <= 3, >= 1536 tiles (the LM head): one tile x 8 waves (two
 //    workgroups per CU, ~4 full rounds of workgroups); else one tile x 4 waves.
+template <bool A16>
 hipError_t skinny_launch(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
   if (epi == EPI_SWIGLU)
-    return a.M > 8 ? skinny_mq<2, 8>(a, epi, n_part, s) : skinny_mq<2, 4>(a, epi, n_part, s);
+    return a.M > 8 ? skinny_mq<2, 8, A16>(a, epi, n_part, s) : skinny_mq<2, 4, A16>(a, epi, n_part, s);
   const int tiles = (a.N + 15) / 16;
-  if (tiles < 512) return skinny_mq<1, 8>(a, epi, n_part, s);
-  if (a.M > 8) return skinny_mq<4, 4>(a, epi, n_part, s);
-  if (a.M <= 3 && tiles >= 1536) return skinny_mq<1, 8>(a, epi, n_part, s);
-  return skinny_mq<1, 4>(a, epi, n_part, s);
+  if (tiles < 512) return skinny_mq<1, 8, A16>(a, epi, n_part, s);
+  if (a.M > 8) return skinny_mq<4, 4, A16>(a, epi, n_part, s);
+  if (a.M <= 3 && tiles >= 1536) return skinny_mq<1, 8, A16>(a, epi, n_part, s);
+  return skinny_mq<1, 4, A16>(a, epi, n_part, s);
 }
+
 
 // Tiles of the large-M kernel, plus a K split (powers of 2) while the grid
 // has fewer than 256 workgroups (one per CU: the kernel holds 148 KB of LDS).
@@ -694,40 +992,85 @@ BigPlan plan_big(int M, int N, int K, bool swiglu) {
   return p;
 }
 
-}  // namespace
+// Wide-kernel shape: NW waves of 16*AT weight rows each, ring depth NS.
+template <int NW, int AT, int NS>
+struct WideCfg {
+  static constexpr int nw = NW, at = AT, ns = NS, bn = 16 * AT * NW;
+};
+// Measured on the 13B / 70B per-depth shapes (M = 80, 160): 8 waves of 32
+// weight rows with a two-stage ring (two waves per SIMD) beat 4 waves of 64
+// rows with three stages by 5-10%.
+using WideDefault = WideCfg<8, 2, 2>;
 
-size_t gemm_bf16_partial_bytes(int M, int N, int K) {
-  if (M <= 16) return 0;
-  const BigPlan p = plan_big(M, N, K, false);  // N/2-wide SwiGLU tiles give no more splits than this
-  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+// Wide-kernel plan: M tiles of at most 16*mb_max rows (16*MB rows each, MB
+// as small as covers M), BN-row weight tiles (BN/2 ffn columns for SwiGLU),
+// and a K split while the grid has fewer workgroups than ~CUs.
+WidePlan plan_wide(int M, int N, int K, bool swiglu, int BN, int mb_max, int* mb) {
+  WidePlan p;
+  const int blocks16 = (M + 15) / 16;
+  p.tiles_m = (blocks16 + mb_max - 1) / mb_max;
+  *mb = (blocks16 + p.tiles_m - 1) / p.tiles_m;
+  p.tiles_n = swiglu ? (N / 2 + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
+  const int nks = K / SK_KSTEP;
+  const int base = p.tiles_n * p.tiles_m;
+  int splits = 1;
+  while (base * splits * 2 <= 320 && nks / (splits * 2) >= 4) splits *= 2;
+  p.ks_per_split = (nks + splits - 1) / splits;
+  p.splits = (nks + p.ks_per_split - 1) / p.ks_per_split;
+  return p;
 }
 
-hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s) {
-  if (a.K % SK_KSTEP) return hipErrorInvalidValue;  // both kernels step K in whole 128-element blocks
-  if (a.gfeat && (a.M > 16 || a.gd % SK_KSTEP || a.K != 2 * a.gd)) return hipErrorInvalidValue;
-  if ((epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) && a.y2 && !a.gain_out) return hipErrorInvalidValue;
-  if (a.M <= 16) return skinny_launch(a, epi, n_part_out, s);
-  if (a.N % 4) return hipErrorInvalidValue;  // float4 epilogue stores
-  const bool sw = (epi == EPI_SWIGLU);
-  const BigPlan p = plan_big(a.M, a.N, a.K, sw);
-  a.splits = p.splits;
-  if (p.splits > 1 && a.part == nullptr) return hipErrorInvalidValue;  // partial buffer needed for a K split
-  const dim3 grid(p.tiles_n * p.tiles_m * p.splits), blk(512);
+size_t align_up256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+template <class C, int MB, bool SPLIT>
+hipError_t wide_epi(const GemmArgs& a, int epi, const bf16_t* xb, const WidePlan& p, hipStream_t s) {
+  constexpr int NS = (C::ns == 3 && MB > 6 && C::at == 4) ? 2 : C::ns;
+  const dim3 grid(p.tiles_n * p.tiles_m * p.splits), blk(C::nw * 64);
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL(gemm_big<EPI_STORE>, grid, blk, 0, s, a, p); break;
-    case EPI_BIAS_SUMSQ: hipLaunchKernelGGL(gemm_big<EPI_BIAS_SUMSQ>, grid, blk, 0, s, a, p); break;
-    case EPI_RESID: hipLaunchKernelGGL(gemm_big<EPI_RESID>, grid, blk, 0, s, a, p); break;
-    case EPI_RESID_SUMSQ: hipLaunchKernelGGL(gemm_big<EPI_RESID_SUMSQ>, grid, blk, 0, s, a, p); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_big<EPI_SWIGLU>, grid, blk, 0, s, a, p); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_wide<C::nw, C::at, MB, NS, SPLIT, EPI_STORE>), grid, blk, 0, s, a, xb, p); break;
+    case EPI_BIAS_SUMSQ:
+      hipLaunchKernelGGL((gemm_wide<C::nw, C::at, MB, NS, SPLIT, EPI_BIAS_SUMSQ>), grid, blk, 0, s, a, xb, p);
+      break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_wide<C::nw, C::at, MB, NS, SPLIT, EPI_RESID>), grid, blk, 0, s, a, xb, p); break;
+    case EPI_RESID_SUMSQ:
+      hipLaunchKernelGGL((gemm_wide<C::nw, C::at, MB, NS, SPLIT, EPI_RESID_SUMSQ>), grid, blk, 0, s, a, xb, p);
+      break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_wide<C::nw, C::at, MB, NS, SPLIT, EPI_SWIGLU>), grid, blk, 0, s, a, xb, p); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (p.splits == 1) {
-    if (epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) *n_part_out = p.tiles_n;
-    return hipSuccess;
+  return hipGetLastError();
+}
+
+template <class C, bool SPLIT>
+hipError_t wide_mb(const GemmArgs& a, int epi, const bf16_t* xb, const WidePlan& p, int mb, hipStream_t s) {
+  switch (mb) {
+    case 2: return wide_epi<C, 2, SPLIT>(a, epi, xb, p, s);
+    case 3: return wide_epi<C, 3, SPLIT>(a, epi, xb, p, s);
+    case 4: return wide_epi<C, 4, SPLIT>(a, epi, xb, p, s);
+    case 5: return wide_epi<C, 5, SPLIT>(a, epi, xb, p, s);
+    case 6: return wide_epi<C, 6, SPLIT>(a, epi, xb, p, s);
+    case 7: return wide_epi<C, 7, SPLIT>(a, epi, xb, p, s);
+    case 8: return wide_epi<C, 8, SPLIT>(a, epi, xb, p, s);
+    default: return hipErrorInvalidValue;  // M > 16 gives at least two 16-row blocks
   }
-  const int nout = sw ? a.ffn : a.N;
+}
+
+template <int PD, bool SPLIT>
+hipError_t big16_epi(const GemmArgs& a, int epi, const bf16_t* xb, const BigPlan& p, hipStream_t s) {
+  const dim3 grid(p.tiles_n * p.tiles_m * p.splits), blk(512);
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL((gemm_big16<EPI_STORE, PD, SPLIT>), grid, blk, 0, s, a, xb, p); break;
+    case EPI_BIAS_SUMSQ: hipLaunchKernelGGL((gemm_big16<EPI_BIAS_SUMSQ, PD, SPLIT>), grid, blk, 0, s, a, xb, p); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_big16<EPI_RESID, PD, SPLIT>), grid, blk, 0, s, a, xb, p); break;
+    case EPI_RESID_SUMSQ: hipLaunchKernelGGL((gemm_big16<EPI_RESID_SUMSQ, PD, SPLIT>), grid, blk, 0, s, a, xb, p); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_big16<EPI_SWIGLU, PD, SPLIT>), grid, blk, 0, s, a, xb, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t reduce_launch(const GemmArgs& a, int epi, int* n_part_out, hipStream_t s) {
+  const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
   dim3 rgrid((nout + 1023) / 1024, a.M), rblk(256);
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL(gemm_reduce<EPI_STORE>, rgrid, rblk, 0, s, a); break;
@@ -738,6 +1081,73 @@ hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s)
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Row count from which the bf16 path uses the LDS-tiled large-M kernel
+// (at M = 480 and 960 it runs 5-15% faster than the wide kernel; deeper
+// register prefetch measured no faster).
+constexpr int BIG16_MIN_M = 257;
+
+// Launch for M > 16 on a prepared operand: the prep pass (RMSNorm row scale
+// applied, then split into hi/lo halves or rounded once to bf16), then the
+// wide kernel (weight-stream bound shapes) or the large-M kernel, then the
+// K-split reduce.  The prepared operand and the partials live in a.part.
+template <bool SPLIT>
+hipError_t prepared_launch(GemmArgs a, int epi, int* n_part_out, hipStream_t s) {
+  const bool sw = (epi == EPI_SWIGLU);
+  if (a.part == nullptr) return hipErrorInvalidValue;  // scratch: bf16 operand (+ partials)
+  bf16_t* xb = (bf16_t*)a.part;
+  a.part = (float*)((char*)a.part + align_up256((size_t)a.M * a.K * 2 * (SPLIT ? 2 : 1)));
+  hipLaunchKernelGGL(act_prep<SPLIT>, dim3((a.K + 2047) / 2048, a.M), dim3(256), 0, s, a, xb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  a.sumsq_in = nullptr;  // the row scale is in the prepared operand
+  int splits, tiles_n;
+  if (a.M >= BIG16_MIN_M) {
+    const BigPlan p = plan_big(a.M, a.N, a.K, sw);
+    a.splits = splits = p.splits;
+    tiles_n = p.tiles_n;
+    e = big16_epi<1, SPLIT>(a, epi, xb, p, s);
+  } else {
+    using C = WideDefault;
+    int mb;
+    const WidePlan p = plan_wide(a.M, a.N, a.K, sw, C::bn, 8, &mb);
+    a.splits = splits = p.splits;
+    tiles_n = p.tiles_n;
+    e = wide_mb<C, SPLIT>(a, epi, xb, p, mb, s);
+  }
+  if (e != hipSuccess) return e;
+  if (splits == 1) {
+    if (epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) *n_part_out = tiles_n;
+    return hipSuccess;
+  }
+  return reduce_launch(a, epi, n_part_out, s);
+}
+
+}  // namespace
+
+size_t gemm_bf16_partial_bytes(int M, int N, int K) {
+  if (M <= 16) return 0;
+  // the prepared operand (hi and lo halves), then the partials of the K split
+  int splits;
+  if (M >= BIG16_MIN_M) {
+    splits = plan_big(M, N, K, false).splits;  // N/2-wide SwiGLU tiles give no more splits than this
+  } else {
+    int mb;
+    const WidePlan w = plan_wide(M, N, K, false, WideDefault::bn, 8, &mb);
+    const WidePlan ws = plan_wide(M, N, K, true, WideDefault::bn, 8, &mb);
+    splits = w.splits > ws.splits ? w.splits : ws.splits;
+  }
+  return align_up256((size_t)M * K * 4) + (splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0);
+}
+
+hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s) {
+  if (a.K % SK_KSTEP) return hipErrorInvalidValue;  // every kernel steps K in whole 128-element blocks
+  if (a.gfeat && (a.gd % SK_KSTEP || a.K != 2 * a.gd)) return hipErrorInvalidValue;
+  if ((epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) && a.y2 && !a.gain_out) return hipErrorInvalidValue;
+  if (a.M <= 16) return a.act_bf16 ? skinny_launch<true>(a, epi, n_part_out, s) : skinny_launch<false>(a, epi, n_part_out, s);
+  if (a.N % 4 || (epi == EPI_SWIGLU && a.ffn % 4)) return hipErrorInvalidValue;  // float4 epilogue stores
+  return a.act_bf16 ? prepared_launch<false>(a, epi, n_part_out, s) : prepared_launch<true>(a, epi, n_part_out, s);
 }
 
 hipError_t launch_gemm_f32(GemmArgs a, int epi, int* n_part_out, hipStream_t s) {

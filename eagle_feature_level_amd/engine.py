@@ -16,7 +16,7 @@ import dataclasses
 
 import torch
 
-from . import (EAGLE_HEAD_ONLY, eagle_draft_step, eagle_tree_expand, eagle_tree_finalize, eagle_tree_init,
+from . import (EAGLE_ACT_BF16, EAGLE_HEAD_ONLY, eagle_draft_step, eagle_tree_expand, eagle_tree_finalize, eagle_tree_init,
                eagle_verify, eagle_verify_workspace_bytes, eagle_workspace_bytes, make_kv, make_out, make_pool,
                make_rows, make_shape, make_weights)
 
@@ -36,9 +36,16 @@ class Step:
 
 class EagleRound:
     def __init__(self, shape: dict, weights: dict, batch: int, kind: str, k: int, depth: int, m: int = 0,
-                 template=None, prefix=None, device="cuda"):
+                 template=None, prefix=None, device="cuda", act_bf16=False):
         """shape: d, n_heads, n_kv_heads, head_dim, ffn, vocab, rms_eps, rope_theta, dtype.
-        weights: name -> device tensor.  prefix: dict(k, v, off, len, max_len) device tensors."""
+        weights: name -> device tensor.  prefix: dict(k, v, off, len, max_len) device tensors.
+        act_bf16: False (default: split-bf16 operands, within 2e-2 of the fp64
+        oracle at every workload), True (EAGLE_ACT_BF16 on every draft step of a
+        bf16 workload), or "auto" (EAGLE_ACT_BF16 on steps over more than
+        ACT_BF16_MIN_ROWS rows, where one MFMA per product instead of two matters).
+        Rounding the activations to bf16 measured 0.03-0.18 max-abs off the fp64
+        logits at the 7B-70B shapes, so it is opt-in."""
+        self.act_bf16 = act_bf16
         self.shape_d = shape
         self.shape = make_shape(**shape)
         self.weights_t = weights
@@ -133,12 +140,22 @@ class EagleRound:
         self.v_flags = torch.zeros(B, **i32)
 
     # ------------------------------------------------------------------ calls
+    ACT_BF16_MIN_ROWS = 16
+
+    def act_flag(self, n_rows: int) -> int:
+        """EAGLE_ACT_BF16 or 0 for a draft step over n_rows rows."""
+        if self.shape_d["dtype"] != "bf16":
+            return 0
+        on = self.act_bf16 if self.act_bf16 != "auto" else n_rows > self.ACT_BF16_MIN_ROWS
+        return EAGLE_ACT_BF16 if on else 0
+
     def root_head(self, root_feat: torch.Tensor):
         B = self.B
         self.feat[:B].copy_(root_feat)
         rows = make_rows(B, B, 1, self.root_start, None, self.root_rows)
         out = make_out(None, self.logits, self.lse, self.topk, self.topk_idx, self.topk_logq)
-        eagle_draft_step(self.shape, self.weights, EAGLE_HEAD_ONLY, rows, self.feat, None, out, self.workspace)
+        eagle_draft_step(self.shape, self.weights, EAGLE_HEAD_ONLY | self.act_flag(B), rows, self.feat, None, out,
+                         self.workspace)
 
     def draft_phase(self, root_feat: torch.Tensor, root_token: torch.Tensor):
         """Root head, then expand + draft step per depth, then rerank/flatten."""
@@ -164,7 +181,7 @@ class EagleRound:
             rows = make_rows(n, B, st.n_next, st.row_start, st.token, st.parent, st.pos, st.slot, st.mask)
             out = make_out(self.feat[st.feat_row0:], self.logits[st.feat_row0:], self.lse[st.feat_row0:], self.topk,
                            self.topk_idx[st.feat_row0:], self.topk_logq[st.feat_row0:])
-            eagle_draft_step(self.shape, self.weights, 0, rows, self.feat, self.kv, out, self.workspace)
+            eagle_draft_step(self.shape, self.weights, self.act_flag(n), rows, self.feat, self.kv, out, self.workspace)
             prev_row0, n_prev = st.feat_row0, st.n_next
         t = self.tree
         eagle_tree_finalize(B, self.m, self.n_nodes, self.pool, self.prefix["len"], t["parent"], t["token"],
@@ -186,7 +203,8 @@ class EagleRound:
         rows = make_rows(nw, self.B, self.n_nodes - 1, self.tw["row_start"], self.tw["token"], self.tw["parent"],
                          self.tw["pos"], self.tw["slot"], self.tw["mask"])
         out = make_out(self.tw_feat, self.tw_logits, self.tw_lse, 1, self.tw_idx, self.tw_logq)
-        eagle_draft_step(self.shape, self.weights, 0, rows, self.feat, self.tw_kv, out, self.workspace)
+        eagle_draft_step(self.shape, self.weights, self.act_flag(nw), rows, self.feat, self.tw_kv, out,
+                         self.workspace)
 
     def verify(self, target_logits: torch.Tensor, seed: int, round_: int, flags: int = 0):
         t = self.tree

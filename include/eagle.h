@@ -118,8 +118,19 @@ typedef struct {
   float *topk_logq;  /* [n_rows, topk] logit - lse of those tokens               */
 } eagle_draft_out;
 
-/* Flags of eagle_draft_step. */
-enum { EAGLE_HEAD_ONLY = 1 };
+/* Flags of eagle_draft_step.
+ * EAGLE_HEAD_ONLY: the root distribution only (see below).
+ * EAGLE_ACT_BF16 (bf16 workloads only, else EAGLE_EINVAL): the activation
+ *   operand of each of the six weight GEMMs (FC, QKV, O, gate/up, down, LM
+ *   head) is rounded once to bf16, round to nearest even, and enters the
+ *   matrix units as one bf16 value: one MFMA per product instead of two.  The
+ *   rounded values are [f ; e], RMSNorm(x) * norm1, the attention output,
+ *   RMSNorm(h) * norm2 (rounded after the row scale), the SwiGLU activation
+ *   and f^ (for the LM head).  Everything else is unchanged (fp32 activations,
+ *   fp32 accumulation, attention on split operands).  For steps over many rows
+ *   (the matrix units are the bound above a few hundred rows) this halves the
+ *   matrix work; it is the usual bf16 inference contract. */
+enum { EAGLE_HEAD_ONLY = 1, EAGLE_ACT_BF16 = 2 };
 
 /* Bytes of workspace needed by eagle_draft_step / eagle_softmax_topk for up
  * to max_rows rows, max_batch sequences and prefixes up to max_prefix_len.
@@ -147,7 +158,9 @@ size_t eagle_workspace_bytes(const eagle_shape *shape, int32_t max_rows, int32_t
  * bf16; activations (features, residuals, q, attention output, SwiGLU
  * activation) are fp32 and enter the matrix units as a pair of bf16 values
  * (hi, lo = x - hi) with fp32 accumulation, so the only activation rounding to
- * bf16 is the store of k and v into the tree slots.  feat_in is fp32 [*, d].
+ * bf16 is the store of k and v into the tree slots; with EAGLE_ACT_BF16 the
+ * GEMM activation operands are rounded to bf16 as described above.  feat_in is
+ * fp32 [*, d].
  * Rows that attend to each other's slots may share one call: every row's
  * k, v is written before any row's attention runs. */
 int eagle_draft_step(const eagle_shape *shape, const eagle_weights *w, int32_t flags, const eagle_rows *rows,

@@ -24,6 +24,13 @@ Precision reading for bf16 workloads: weights, embedding, LM head and the KV
 cache are bf16 values; activations are carried at full precision.  So with
 ``mirror=True`` the only rounding is of the rotated k and of v when they are
 stored into the bf16 tree slots (the cache format); everything else is fp64.
+
+``act_bf16=True`` is the other bf16 contract a draft step can be run under
+(bf16 matrix-unit operands on both sides): the activation operand of each of
+the six weight products -- [f ; e], RMSNorm(x)*g1, the attention output,
+RMSNorm(h)*g2, the SwiGLU activation and f^ entering the LM head -- is rounded
+to the nearest bf16 value before the product; the products, norms, softmax and
+residual stream stay fp64.
 """
 from __future__ import annotations
 
@@ -45,10 +52,10 @@ def new_tree_kv(shape, batch: int):
     return k, k.copy()
 
 
-def head_logits(shape, w, feats: np.ndarray, mirror: bool = True) -> np.ndarray:
+def head_logits(shape, w, feats: np.ndarray, mirror: bool = True, act_bf16: bool = False) -> np.ndarray:
     """Root distribution logits from true features: LM_Head(f) (no final norm,
     no bias: f is exactly the LM head's input)."""
-    return matmul_t(feats, w.lm_head)
+    return matmul_t(_r(feats, act_bf16 and shape.dtype == "bf16"), w.lm_head)
 
 
 def tree_attention_row(q_heads, seq_prefix_k, seq_prefix_v, L, tree_k_seq, tree_v_seq, mask, n_heads,
@@ -72,7 +79,8 @@ def tree_attention_row(q_heads, seq_prefix_k, seq_prefix_v, L, tree_k_seq, tree_
 
 
 def draft_step(shape, w, rows: dict, feat_buf: np.ndarray, prefix_k, prefix_v, prefix_len,
-               tree_k: np.ndarray, tree_v: np.ndarray, mirror: bool = True, want_logits: bool = True):
+               tree_k: np.ndarray, tree_v: np.ndarray, mirror: bool = True, want_logits: bool = True,
+               act_bf16: bool = False):
     """One draft step over a set of tree rows.
 
     rows: dict of equal-length arrays
@@ -89,6 +97,7 @@ def draft_step(shape, w, rows: dict, feat_buf: np.ndarray, prefix_k, prefix_v, p
     Returns dict with f^ ('feat'), 'logits' and intermediates.
     """
     on = mirror and shape.dtype == "bf16"
+    ra = act_bf16 and shape.dtype == "bf16"  # bf16 operand of each weight product
     d, hq, hkv, hd = shape.d, shape.n_heads, shape.n_kv_heads, shape.head_dim
     seq = np.asarray(rows["seq"])
     M = len(seq)
@@ -100,10 +109,10 @@ def draft_step(shape, w, rows: dict, feat_buf: np.ndarray, prefix_k, prefix_v, p
 
     # a1, a2: [f_parent ; e(t)] -> FC 2d->d with bias
     a = np.concatenate([np.asarray(feat_buf, np.float64)[par], np.asarray(w.embed, np.float64)[tok]], axis=1)
-    x = matmul_t(a, w.fc_w) + np.asarray(w.fc_b, np.float64)
+    x = matmul_t(_r(a, ra), w.fc_w) + np.asarray(w.fc_b, np.float64)
 
     # a3: RMSNorm -> q, k, v
-    n1 = rmsnorm(x, w.norm1, shape.rms_eps)
+    n1 = _r(rmsnorm(x, w.norm1, shape.rms_eps), ra)
     q = matmul_t(n1, w.wq).reshape(M, hq, hd)
     k = matmul_t(n1, w.wk).reshape(M, hkv, hd)
     v = matmul_t(n1, w.wv).reshape(M, hkv, hd)
@@ -131,15 +140,15 @@ def draft_step(shape, w, rows: dict, feat_buf: np.ndarray, prefix_k, prefix_v, p
     attn = attn.reshape(M, hq * hd)
 
     # a6: O projection + residual
-    h_res = x + matmul_t(attn, w.wo)
+    h_res = x + matmul_t(_r(attn, ra), w.wo)
 
     # a7: RMSNorm -> SwiGLU MLP + residual
-    n2 = rmsnorm(h_res, w.norm2, shape.rms_eps)
+    n2 = _r(rmsnorm(h_res, w.norm2, shape.rms_eps), ra)
     act = silu(matmul_t(n2, w.w_gate)) * matmul_t(n2, w.w_up)
-    feat = h_res + matmul_t(act, w.w_down)
+    feat = h_res + matmul_t(_r(act, ra), w.w_down)
 
     out = {"x": x, "q": q, "k": k, "v": v, "attn": attn, "h": h_res, "feat": feat}
     # a8: frozen shared LM head
     if want_logits:
-        out["logits"] = matmul_t(feat, w.lm_head)
+        out["logits"] = matmul_t(_r(feat, ra), w.lm_head)
     return out

@@ -13,6 +13,11 @@ the four-step inference pipeline):
   5. recursive rejection sampling over the tree.
 Feature rows and logit rows share one index space: rows [0, B) hold the true
 root features / root logits, each later step appends its rows.
+
+act_bf16 chooses the bf16 contract of each step's weight products (see
+draft.draft_step): False (full-precision operands, the default), True, or
+"auto" = bf16 operands for steps over more than ACT_BF16_MIN_ROWS rows of a
+bf16 workload.
 """
 from __future__ import annotations
 
@@ -24,8 +29,15 @@ from .topk import softmax_topk
 from .verify import verify_sequence
 
 
+ACT_BF16_MIN_ROWS = 16
+
+
+def act_for(act_bf16, n_rows: int) -> bool:
+    return bool(act_bf16) if act_bf16 != "auto" else n_rows > ACT_BF16_MIN_ROWS
+
+
 def draft_phase(shape, w, root_feat, root_token, prefix_k, prefix_v, prefix_len, kind: str, k: int, depth: int,
-                m: int = 0, template=None, mirror: bool = True, tree_wide: bool = True):
+                m: int = 0, template=None, mirror: bool = True, tree_wide: bool = True, act_bf16=False):
     B = root_feat.shape[0]
     nchild = None
     if kind != "dynamic":
@@ -33,7 +45,7 @@ def draft_phase(shape, w, root_feat, root_token, prefix_k, prefix_v, prefix_len,
         for p in template[1:]:
             nchild[p] += 1
     feats = [np.asarray(root_feat, np.float64)]
-    root_logits = D.head_logits(shape, w, root_feat, mirror)
+    root_logits = D.head_logits(shape, w, root_feat, mirror, act_for(act_bf16, B))
     logits = [root_logits]
     _, idx, logq = softmax_topk(root_logits.astype(np.float32), k)
     pools = [T.Pool(root_token[b], b) for b in range(B)]
@@ -60,7 +72,8 @@ def draft_phase(shape, w, root_feat, root_token, prefix_k, prefix_v, prefix_len,
                 rows["slot"].append(slot)
                 rows["mask"].append(mask)
         fb = np.concatenate(feats, axis=0)
-        out = D.draft_step(shape, w, rows, fb, prefix_k, prefix_v, prefix_len, tree_k, tree_v, mirror)
+        out = D.draft_step(shape, w, rows, fb, prefix_k, prefix_v, prefix_len, tree_k, tree_v, mirror,
+                           act_bf16=act_for(act_bf16, len(rows["seq"])))
         feats.append(out["feat"])
         logits.append(out["logits"])
         n_rows += len(rows["seq"])
@@ -88,7 +101,8 @@ def draft_phase(shape, w, root_feat, root_token, prefix_k, prefix_v, prefix_len,
                 rows["slot"].append(t)
                 rows["mask"].append(int(tr["mask"][t]))
         tk, tv = D.new_tree_kv(shape, B)
-        out = D.draft_step(shape, w, rows, res["feat_buf"], prefix_k, prefix_v, prefix_len, tk, tv, mirror)
+        out = D.draft_step(shape, w, rows, res["feat_buf"], prefix_k, prefix_v, prefix_len, tk, tv, mirror,
+                           act_bf16=act_for(act_bf16, len(rows["seq"])))
         res["tree_wide_rows"] = rows
         res["tree_wide"] = out
     return res

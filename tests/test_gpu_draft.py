@@ -89,8 +89,8 @@ def _rows(cfg, counts, lens, seed, n_feat):
     return rows, start
 
 
-def _run_draft(shape, counts, lens, seed, head_only=False, topk=4):
-    cfg, w, ks, vs = _setup(shape, len(counts), lens, seed)
+def _run_draft(shape, counts, lens, seed, head_only=False, topk=4, act=False, std=0.05):
+    cfg, w, ks, vs = _setup(shape, len(counts), lens, seed, std=std)
     B = len(counts)
     n_feat = 9
     feat = normal_array(200 + seed, 0, (n_feat, shape.d))
@@ -125,15 +125,16 @@ def _run_draft(shape, counts, lens, seed, head_only=False, topk=4):
     out = E.make_out(o_feat, o_log, o_lse, topk, o_idx, o_lq)
     ws = _ws(E.eagle_workspace_bytes(es, M, B, pf["max_len"]))
     ws.fill_(0xFF)  # poisoned workspace: every value read must have been written in this call
-    E.eagle_draft_step(es, ew, E.EAGLE_HEAD_ONLY if head_only else 0, er, f_in, kv, out, ws)
+    flags = (E.EAGLE_HEAD_ONLY if head_only else 0) | (E.EAGLE_ACT_BF16 if act else 0)
+    E.eagle_draft_step(es, ew, flags, er, f_in, kv, out, ws)
     torch.cuda.synchronize()
     # oracle
     tk, tv = tk0.astype(np.float64).copy(), tv0.astype(np.float64).copy()
     if head_only:
         from oracle.draft import head_logits
-        ref = {"logits": head_logits(shape, w, feat[rows["parent"]])}
+        ref = {"logits": head_logits(shape, w, feat[rows["parent"]], act_bf16=act)}
     else:
-        ref = OD.draft_step(shape, w, rows, feat, ks, vs, lens, tk, tv, mirror=True)
+        ref = OD.draft_step(shape, w, rows, feat, ks, vs, lens, tk, tv, mirror=True, act_bf16=act)
     gpu = dict(logits=o_log.cpu().numpy(), feat=o_feat.cpu().numpy(), idx=o_idx.cpu().numpy(),
                lse=o_lse.cpu().numpy(), tree_k=tree_k.float().cpu().numpy(), tree_v=tree_v.float().cpu().numpy())
     return ref, gpu, rows, tk, tv
@@ -167,6 +168,31 @@ def test_draft_step_bf16_gqa(counts, lens):
     _check_topk_valid(ref["logits"], gpu["idx"], tol)
 
 
+# bf16 GEMM operands (EAGLE_ACT_BF16) against the oracle under the same contract,
+# through the three kernels: up to 16 rows (register-streamed weights), 17..256
+# (wide kernel), 257+ (LDS-tiled kernel); the d = 1024 cases split K over the
+# grid (partial sums + reduce, including the sum-of-squares epilogues).
+@pytest.mark.parametrize("d,counts,lens", [(256, [1], [37]), (256, [9, 0, 8], [130, 5, 64]),
+                                           (256, [20, 20, 1], [130, 0, 77]),
+                                           (256, [56, 56, 56, 56, 40], [200, 64, 1, 0, 33]),
+                                           (1024, [6, 7], [3, 100]), (1024, [30, 10], [64, 9]),
+                                           (1024, [56, 56, 56, 56, 56], [40, 0, 3, 77, 128])])
+def test_draft_step_bf16_act(d, counts, lens):
+    shape = Shape(d, d // 128 * 2, d // 128, 128, 3 * d // 2 if d == 256 else 2816, 1000 if d == 256 else 4096)
+    # weights ~N(0, 0.02) as in the draft-head workloads
+    ref, gpu, rows, tk, tv = _run_draft(shape, counts, lens, seed=5 + sum(counts) + d, act=True, std=0.02)
+    tol = TOL["bf16"]
+    print(f"feature max-abs {np.max(np.abs(gpu['feat'] - ref['feat'])):.2e}, "
+          f"logit max-abs {np.max(np.abs(gpu['logits'] - ref['logits'])):.2e}")
+    assert np.max(np.abs(gpu["feat"] - ref["feat"])) < tol
+    assert np.max(np.abs(gpu["logits"] - ref["logits"])) < tol
+    for r in range(len(rows["seq"])):
+        b, s = rows["seq"][r], rows["slot"][r]
+        for got, want in ((gpu["tree_k"][b, s], tk[b, s]), (gpu["tree_v"][b, s], tv[b, s])):
+            assert np.all(np.abs(got - want) <= 2.0**-7 * np.abs(want) + 1e-3)
+    _check_topk_valid(ref["logits"], gpu["idx"], tol)
+
+
 @pytest.mark.parametrize("counts,lens", [([1], [32]), ([4, 1], [32, 3]), ([3, 3, 3], [0, 17, 40])])
 def test_draft_step_f32_tiny(counts, lens):
     shape = CONFIGS[1].shape
@@ -177,10 +203,10 @@ def test_draft_step_f32_tiny(counts, lens):
     _check_topk_valid(ref["logits"], gpu["idx"], tol)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_head_only_is_root_distribution(dtype):
+@pytest.mark.parametrize("dtype,act", [("bf16", False), ("bf16", True), ("f32", False)])
+def test_head_only_is_root_distribution(dtype, act):
     shape = Shape(256, 4, 2, 128, 384, 1000) if dtype == "bf16" else CONFIGS[1].shape
-    ref, gpu, rows, _, _ = _run_draft(shape, [2, 1], [10, 20], seed=3, head_only=True)
+    ref, gpu, rows, _, _ = _run_draft(shape, [2, 1], [10, 20], seed=3, head_only=True, act=act)
     tol = TOL[dtype]
     assert np.max(np.abs(gpu["logits"] - ref["logits"])) < tol
     _check_topk_valid(ref["logits"], gpu["idx"], tol)

@@ -35,6 +35,7 @@ pytestmark = pytest.mark.gpu
 TOL_BF16 = 2e-2
 AMBIG = 1e-5
 AMBIG_DRAW = 3e-6
+ACT = False  # the engine's default operand contract (split bf16 pairs)
 
 
 def _np(t):
@@ -74,9 +75,13 @@ def _sample(rows, idx):
 
 
 def _check_floats(cfg, w, rows, sample, feat_buf, ks, vs, lens, tk, tv, got_feat, got_logits):
-    ref = OD.draft_step(cfg.shape, w, _sample(rows, sample), feat_buf, ks, vs, lens, tk.copy(), tv.copy(), mirror=True)
+    # the oracle runs each sampled row under the bf16 contract the engine chose for the whole step
+    act = OP.act_for(ACT, len(rows["seq"]))
+    ref = OD.draft_step(cfg.shape, w, _sample(rows, sample), feat_buf, ks, vs, lens, tk.copy(), tv.copy(), mirror=True,
+                        act_bf16=act)
     ef = float(np.max(np.abs(got_feat[sample] - ref["feat"])))
     el = float(np.max(np.abs(got_logits[sample] - ref["logits"])))
+    print(f"rows {len(rows['seq'])} bf16 operands {act}: feature max-abs {ef:.2e}, logit max-abs {el:.2e}")
     assert ef < TOL_BF16 and el < TOL_BF16, (ef, el)
     return ef, el
 
@@ -91,7 +96,7 @@ def _staged_parity(cid, n_sample=3):
 
     # root head on two sequences
     for b in sorted(set([0, B - 1])):
-        ref = OD.head_logits(s, w, feat[b:b + 1])
+        ref = OD.head_logits(s, w, feat[b:b + 1], act_bf16=OP.act_for(ACT, B))
         assert np.max(np.abs(logits[b] - ref[0])) < TOL_BF16
 
     # top-k of every draft row, on the GPU's logits

@@ -73,10 +73,12 @@ def test_visibility_table_from_masks():
         assert sorted(names[j] for j in vs[i]) == sorted(fx["visible"][nm])
 
 
-def _scalar_row(shape, w, fparent, tok, pos, prefix_k, prefix_v, L, anc_k, anc_v):
-    """One decoder row written with scalar loops only (no vector algebra)."""
+def _scalar_row(shape, w, fparent, tok, pos, prefix_k, prefix_v, L, anc_k, anc_v, rb=None):
+    """One decoder row written with scalar loops only (no vector algebra).
+    rb, if given, rounds the activation operand of each weight product."""
     d, H, Hkv, hd, F, V = shape.d, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.ffn, shape.vocab
-    a = [float(fparent[i]) for i in range(d)] + [float(w.embed[tok][i]) for i in range(d)]
+    rb = rb or (lambda v: v)
+    a = rb([float(fparent[i]) for i in range(d)] + [float(w.embed[tok][i]) for i in range(d)])
     x = []
     for o in range(d):
         s = float(w.fc_b[o])
@@ -102,7 +104,7 @@ def _scalar_row(shape, w, fparent, tok, pos, prefix_k, prefix_v, L, anc_k, anc_v
             out[i + half] = vec[i + half] * c + vec[i] * s
         return out
 
-    n1 = rms(x, w.norm1)
+    n1 = rb(rms(x, w.norm1))
     q = lin(w.wq, n1, H * hd)
     k = lin(w.wk, n1, Hkv * hd)
     v = lin(w.wv, n1, Hkv * hd)
@@ -119,15 +121,16 @@ def _scalar_row(shape, w, fparent, tok, pos, prefix_k, prefix_v, L, anc_k, anc_v
         e = [math.exp(s - mx) for s in sc]
         z = sum(e)
         attn += [sum(e[j] / z * vals[j][i] for j in range(len(keys))) for i in range(hd)]
-    o = lin(w.wo, attn, d)
+    o = lin(w.wo, rb(attn), d)
     h_res = [x[i] + o[i] for i in range(d)]
-    n2 = rms(h_res, w.norm2)
+    n2 = rb(rms(h_res, w.norm2))
     gt = lin(w.w_gate, n2, F)
     up = lin(w.w_up, n2, F)
     act = [gt[i] / (1.0 + math.exp(-gt[i])) * up[i] for i in range(F)]
-    dn = lin(w.w_down, act, d)
+    dn = lin(w.w_down, rb(act), d)
     feat = [h_res[i] + dn[i] for i in range(d)]
-    logits = [sum(float(w.lm_head[t][i]) * feat[i] for i in range(d)) for t in range(V)]
+    fr = rb(feat)
+    logits = [sum(float(w.lm_head[t][i]) * fr[i] for i in range(d)) for t in range(V)]
     return np.array(feat), np.array(logits), np.array(kh), np.array(vh)
 
 
@@ -156,6 +159,35 @@ def test_draft_row_matches_scalar_loops():
     assert np.allclose(out["feat"][0], feat, rtol=0, atol=1e-10)
     assert np.allclose(out["logits"][0], logits, rtol=0, atol=1e-10)
     assert np.allclose(tk[0, 5], kh, rtol=0, atol=1e-12) and np.allclose(tv[0, 5], vh, rtol=0, atol=1e-12)
+
+
+def test_draft_row_bf16_operands_match_scalar_loops():
+    """act_bf16: the six weight-product operands rounded to bf16, checked
+    against the scalar-loop row with torch's own bf16 conversion doing the
+    rounding."""
+    import torch
+
+    small = Shape(64, 4, 2, 16, 172, 512, dtype="bf16")
+    shape, w, lens, pk, pv = _tiny_setup(small)
+    fparent = normal_array(1, 0, (3, shape.d))
+    tk, tv = D.new_tree_kv(shape, 1)
+    anc_k = normal_array(1, 1, (shape.n_kv_heads, shape.head_dim))
+    anc_v = normal_array(1, 2, (shape.n_kv_heads, shape.head_dim))
+    tk[0, 3], tv[0, 3] = anc_k, anc_v
+    rows = dict(seq=[0], token=[77], parent=[2], pos=[7], slot=[5], mask=[(1 << 3) | (1 << 5)])
+    out = D.draft_step(shape, w, rows, fparent, pk, pv, lens, tk, tv, mirror=False, act_bf16=True)
+
+    def rb(v):
+        return [float(t) for t in torch.tensor(v, dtype=torch.float64).to(torch.bfloat16).double()]
+
+    feat, logits, kh, vh = _scalar_row(shape, w, fparent[2], 77, 7, pk[0], pv[0], 6, [anc_k], [anc_v], rb=rb)
+    assert np.allclose(out["feat"][0], feat, rtol=0, atol=1e-10)
+    assert np.allclose(out["logits"][0], logits, rtol=0, atol=1e-10)
+    # and the rounding is felt: the split-operand contract gives other values
+    tk2, tv2 = D.new_tree_kv(shape, 1)
+    tk2[0, 3], tv2[0, 3] = anc_k, anc_v
+    ref = D.draft_step(shape, w, rows, fparent, pk, pv, lens, tk2, tv2, mirror=False)
+    assert np.max(np.abs(ref["logits"][0] - logits)) > 1e-4
 
 
 def test_gqa_equals_mha_with_replicated_kv():
