@@ -14,7 +14,8 @@ tree (depth 5, branching 4/3/2/1).  Weights ~N(0, 0.02), features and prefix
 KV ~N(0, 1), target logits = draft logits + N(0, 0.5) (root: exact copy).
 
 Prints one JSON line.  value = drafted tree nodes per second through draft +
-verify (whole job, one GPU).  `roofline` covers the dominant kernel, with its
+verify (whole job, one GPU), from K replays of the round captured as one HIP
+graph (--no-graph: K eager rounds; both are reported).  `roofline` covers the dominant kernel, with its
 per-launch duration measured by HIP events around each launch on the stream
 it runs on; `cpu_baseline` times the fp64 CPU oracle on a bounded sample.
 """
@@ -175,6 +176,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = 7B static-26, the bench line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -220,6 +222,26 @@ def main():
     ms_step = ms_total / args.steps
     ms_draft = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps
     ms_verify = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps
+    ms_eager = ms_step
+
+    # the same round captured as one HIP graph (every kernel of the round, the
+    # launches pre-recorded): exactly K replays, timed the same way
+    ms_graph = None
+    if not args.no_graph:
+        eng.capture_round(feat, tok, tgt, 0, 0)
+        for _ in range(args.warmup):
+            eng.replay_round()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_g = time.perf_counter()
+        g0.record()
+        for _ in range(args.steps):
+            eng.replay_round()
+        g1.record()
+        torch.cuda.synchronize()
+        t_g = time.perf_counter() - t_g
+        ms_graph = g0.elapsed_time(g1) / args.steps
+        ms_step, t_wall = ms_graph, t_g  # the step of record: graph replay
 
     # per-kernel durations: HIP events around every draft-step launch, same K steps again
     E.eagle_profile_enable(args.steps * 200)
@@ -272,6 +294,8 @@ def main():
                    "parallelism": "single GPU"},
         "draft_nodes_per_s": round(drafted / (ms_draft * 1e-3), 1),
         "verify_nodes_per_s": round(B * N / (ms_verify * 1e-3), 1),
+        "ms_per_step_eager": round(ms_eager, 4),
+        "ms_per_step_graph": round(ms_graph, 4) if ms_graph is not None else None,
         "ms_draft_phase": round(ms_draft, 4),
         "ms_verify": round(ms_verify, 4),
         "wall_s_timed": round(t_wall, 4),

@@ -954,6 +954,7 @@ template <int AT, int NW, bool A16>
 hipError_t skinny_mq(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
   if (a.M <= 2) return skinny_epi<AT, NW, 1, A16>(a, epi, n_part, s);
   if (a.M <= 4) return skinny_epi<AT, NW, 2, A16>(a, epi, n_part, s);
+  if (a.M <= 6) return skinny_epi<AT, NW, 3, A16>(a, epi, n_part, s);
   if (a.M <= 8) return skinny_epi<AT, NW, 4, A16>(a, epi, n_part, s);
   return skinny_epi<AT, NW, 8, A16>(a, epi, n_part, s);
 }

@@ -211,3 +211,28 @@ class EagleRound:
         eagle_verify(self.B, self.n_nodes, self.shape_d["vocab"], t["parent"], t["token"], target_logits,
                      self.logits, t["qrow"], seed, round_, flags, self.v_path, self.v_len, self.v_next, self.v_flags,
                      workspace=self.workspace)
+
+    # ------------------------------------------------------------ HIP graph
+    def capture_round(self, root_feat: torch.Tensor, root_token: torch.Tensor, target_logits: torch.Tensor,
+                      seed: int, round_: int, flags: int = 0):
+        """Record one whole round (draft phase + verify) as a HIP graph over
+        this engine's buffers; replay_round() re-runs every kernel of it.  The
+        inputs are read from the given tensors at replay time (write new root
+        features, tokens or target logits into them in place); seed, round and
+        flags are fixed at capture.  Nothing in a round allocates or clears
+        memory with a memset, so the whole round is capturable."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # one eager round on the capture stream's side first
+            self.draft_phase(root_feat, root_token)
+            self.verify(target_logits, seed, round_, flags)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.draft_phase(root_feat, root_token)
+            self.verify(target_logits, seed, round_, flags)
+        self._graph = g
+        return g
+
+    def replay_round(self):
+        self._graph.replay()

@@ -153,3 +153,42 @@ def test_7b_static26_round_is_valid(seven_b):
             assert par[b] == a
         assert 0 <= int(eng.v_next[0]) < cfg.shape.vocab
         lens_seen.append(L)
+
+
+def test_graph_replay_equals_eager_round():
+    """A round captured as a HIP graph and replayed three times, with eager
+    rounds and synchronisations in between, reproduces the eager round's tree,
+    logits and verification every time."""
+    cfg = CONFIGS[2]
+    s = cfg.shape
+    w = make_weights(cfg)
+    lens = make_prefix_lens(cfg)
+    ks, vs = make_prefix_kv(cfg, lens)
+    feat = torch.from_numpy(make_root_features(cfg)).cuda()
+    tok = dev.ints(make_root_tokens(cfg))
+    eng = EagleRound(dev.shape_dict(s), dev.weights(w, s.dtype), cfg.batch, "static", cfg.topk, cfg.depth, 0,
+                     TEMPLATES[cfg.tree], dev.prefix(ks, vs, lens, s.dtype))
+    eng.draft_phase(feat, tok)
+    eng.tree_wide()
+    tgt = torch.cat([eng.logits[0:1], eng.tw_logits + 0.5]).contiguous()
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return dict(logits=eng.logits.clone(), parent=eng.tree["parent"].clone(), token=eng.tree["token"].clone(),
+                    path=eng.v_path.clone(), len=eng.v_len.clone(), next=eng.v_next.clone(), flags=eng.v_flags.clone())
+
+    eng.draft_phase(feat, tok)
+    eng.verify(tgt, 0, 3)
+    want = snapshot()
+    eng.capture_round(feat, tok, tgt, 0, 3)
+    for rep in range(3):
+        eng.logits.fill_(float("nan"))
+        eng.v_path.fill_(-7)
+        eng.replay_round()
+        got = snapshot()
+        for k in want:
+            assert torch.equal(got[k], want[k]), (rep, k)
+        # eager work between replays
+        eng.draft_phase(feat, tok)
+        eng.verify(tgt, 0, 3)
+        torch.cuda.synchronize()
