@@ -75,12 +75,20 @@ Prof g_prof;
 
 // Brackets one launch; returns the launch's error.
 template <typename F>
-hipError_t timed(hipStream_t st, int role, double bytes, double flops, F&& launch) {
+hipError_t timed(hipStream_t st, int role, double bytes, double flops, F&& launch, bool kernel_events = false) {
   const bool rec = g_prof.on && g_prof.used < g_prof.rec.size();
-  if (rec) hipEventRecord(g_prof.ev[2 * g_prof.used], st);
+  // a single-kernel GEMM records its own execution start/stop; other launches
+  // are bracketed by events on the stream (dispatch gap included)
+  if (rec && kernel_events)
+    gemm_set_kernel_events(g_prof.ev[2 * g_prof.used], g_prof.ev[2 * g_prof.used + 1]);
+  else if (rec)
+    hipEventRecord(g_prof.ev[2 * g_prof.used], st);
   hipError_t e = launch();
   if (rec) {
-    hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st);
+    if (kernel_events)
+      gemm_set_kernel_events(nullptr, nullptr);
+    else
+      hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st);
     g_prof.rec[g_prof.used] = ProfRec{role, bytes, flops};
     ++g_prof.used;
   }
@@ -237,9 +245,13 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
     const double bytes = wbytes * a.N * a.K + 4.0 * a.M * (a.K + nout) + (a.y2 ? 4.0 * a.M * a.N : 0.0);
     const double flops = 2.0 * a.M * a.N * a.K;
-    return timed(st, role, bytes, flops, [&] {
-      return bf16 ? launch_gemm_bf16(a, epi, np ? np : &dummy, st) : launch_gemm_f32(a, epi, np ? np : &dummy, st);
-    });
+    return timed(
+        st, role, bytes, flops,
+        [&] {
+          return bf16 ? launch_gemm_bf16(a, epi, np ? np : &dummy, st)
+                      : launch_gemm_f32(a, epi, np ? np : &dummy, st);
+        },
+        bf16 && a.M <= 16);
   };
   hipError_t e;
   const int d = s.d, hq = s.n_heads * s.head_dim, hkv = s.n_kv_heads * s.head_dim, F = s.ffn;

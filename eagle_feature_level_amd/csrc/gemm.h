@@ -62,5 +62,9 @@ struct GemmArgs {
 // the tiled kernel's split-K partials.  Sum-of-squares epilogues store their
 // number of partial tiles in *n_part_out.
 hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s);
+// Measurement hook: the next bf16 launch with M <= 16 (a single kernel) is
+// issued with hipExtLaunchKernelGGL and records its own start and stop into
+// these events (kernel execution only, no dispatch gap); then they are cleared.
+void gemm_set_kernel_events(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_gemm_f32(GemmArgs a, int epi, int* n_part_out, hipStream_t s);
 size_t gemm_bf16_partial_bytes(int M, int N, int K);

@@ -34,10 +34,25 @@
 //    deterministic and need no global atomics.
 // MFMA v_mfma_f32_16x16x32_bf16 lane layout (lane l, r = l%16, g = l/16):
 // A[r][g*8+i], B[g*8+i][r], D[g*4+v][r].
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "gemm.h"
 
 namespace {
+
+// Kernel start/stop events for the next skinny launch (gemm_set_kernel_events).
+hipEvent_t g_kev_start = nullptr, g_kev_stop = nullptr;
+
+template <typename K>
+void launch_skinny_kernel(K kernel, dim3 grid, dim3 blk, hipStream_t s, const GemmArgs& a) {
+  if (g_kev_start) {
+    hipExtLaunchKernelGGL(kernel, grid, blk, 0, s, g_kev_start, g_kev_stop, 0, a);
+    g_kev_start = g_kev_stop = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, blk, 0, s, a);
+  }
+}
 
 constexpr int SK_KSTEP = 128;  // K covered by one wave iteration (4 lane groups x 32)
 
@@ -926,20 +941,20 @@ hipError_t skinny_epi(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
   dim3 blk(NW * 64);
   const dim3 grid((a.N + BN - 1) / BN);
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, A16, EPI_STORE>), grid, blk, 0, s, a); break;
+    case EPI_STORE: launch_skinny_kernel(gemm_skinny<AT, NW, MQ, NS, A16, EPI_STORE>, grid, blk, s, a); break;
     case EPI_BIAS_SUMSQ:
-      hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, A16, EPI_BIAS_SUMSQ>), grid, blk, 0, s, a);
+      launch_skinny_kernel(gemm_skinny<AT, NW, MQ, NS, A16, EPI_BIAS_SUMSQ>, grid, blk, s, a);
       *n_part = grid.x;
       break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, A16, EPI_RESID>), grid, blk, 0, s, a); break;
+    case EPI_RESID: launch_skinny_kernel(gemm_skinny<AT, NW, MQ, NS, A16, EPI_RESID>, grid, blk, s, a); break;
     case EPI_RESID_SUMSQ:
-      hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, A16, EPI_RESID_SUMSQ>), grid, blk, 0, s, a);
+      launch_skinny_kernel(gemm_skinny<AT, NW, MQ, NS, A16, EPI_RESID_SUMSQ>, grid, blk, s, a);
       *n_part = grid.x;
       break;
     case EPI_SWIGLU:
       if constexpr (AT >= 2) {  // gate and up tiles pair up inside a workgroup
         const int H = BN / 2;
-        hipLaunchKernelGGL((gemm_skinny<AT, NW, MQ, NS, A16, EPI_SWIGLU>), dim3((a.ffn + H - 1) / H), blk, 0, s, a);
+        launch_skinny_kernel(gemm_skinny<AT, NW, MQ, NS, A16, EPI_SWIGLU>, dim3((a.ffn + H - 1) / H), blk, s, a);
         break;
       } else {
         return hipErrorInvalidValue;
@@ -1126,6 +1141,11 @@ hipError_t prepared_launch(GemmArgs a, int epi, int* n_part_out, hipStream_t s) 
 }
 
 }  // namespace
+
+void gemm_set_kernel_events(hipEvent_t start, hipEvent_t stop) {
+  g_kev_start = start;
+  g_kev_stop = stop;
+}
 
 size_t gemm_bf16_partial_bytes(int M, int N, int K) {
   if (M <= 16) return 0;

@@ -279,7 +279,10 @@ int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t *t
 size_t eagle_verify_workspace_bytes(int32_t batch, int32_t n_nodes);
 
 /* Measurement hook.  While enabled, each kernel launch of eagle_draft_step is
- * bracketed by a pair of HIP events recorded on the call's stream, tagged
+ * timed by a pair of HIP events: a bf16 GEMM over at most 16 rows (one kernel)
+ * records its own execution start and stop (hipExtLaunchKernel events, no
+ * dispatch gap); every other launch is bracketed by events recorded on the
+ * call's stream.  Each pair is tagged
  * with its role and with the algorithmic bytes it must move (weights once,
  * activations in and out) and flops.  The events are created by
  * eagle_profile_enable (not during a call); recording stops silently once
