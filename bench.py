@@ -169,6 +169,56 @@ def traffic_for(kernel_role: str, config_name: str):
                  r["write_kib_per_dispatch"] * 1024 * c["write_factor"])
 
 
+def tree_wide_bench(args, cfg, eng, feat, tok):
+    """K tree-wide draft steps (B x (N-1) rows in one eagle_draft_step) after one
+    draft phase built the tree; per-role time, TFLOP/s and fraction of the
+    bf16 MFMA peak from the library's measurement hook."""
+    import torch
+    import eagle_feature_level_amd as E
+    eng.draft_phase(feat, tok)
+    for _ in range(args.warmup):
+        eng.tree_wide()
+    torch.cuda.synchronize()
+    rows = cfg.batch * (eng.n_nodes - 1)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        eng.tree_wide()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    E.eagle_profile_enable(args.steps * 200)
+    for _ in range(args.steps):
+        eng.tree_wide()
+    torch.cuda.synchronize()
+    kernels = {}
+    for role in E._abi.ROLES:
+        r = E.eagle_profile_read(role)
+        if r["launches"]:
+            kernels[role] = dict(avg_us=round(1e3 * r["ms"] / r["launches"], 2),
+                                 tflops=round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 1) if r["ms"] > 0 else None,
+                                 ms_per_step=round(r["ms"] / args.steps, 4))
+    E.eagle_profile_disable()
+    gemm = ["fc", "qkv", "o", "gate_up", "down", "lm_head"]
+    g_ms = sum(kernels[r]["ms_per_step"] for r in gemm if r in kernels)
+    g_fl = sum(kernels[r]["tflops"] * kernels[r]["ms_per_step"] for r in gemm if r in kernels)  # TF/s x ms
+    dom = max(gemm, key=lambda r: kernels[r]["ms_per_step"])
+    ach = kernels[dom]["tflops"]
+    s = cfg.shape
+    out = {"metric": "tree-wide draft rows/sec (one draft step over every drafted node)",
+           "value": round(rows / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": s.dtype,
+           "data": "synthetic", "config": {"workload": cfg.name, "rows": rows, "d": s.d, "ffn": s.ffn,
+                                           "heads": f"{s.n_heads}q/{s.n_kv_heads}kv x {s.head_dim}",
+                                           "operands": "split bf16 (hi, lo): two MFMAs per product"},
+           "gemm_tflops": round(g_fl / g_ms, 1) if g_ms else None,
+           "roofline": {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(ach / BF16_PEAK_TFLOPS, 4), "mfma_pipe_frac": round(2 * ach / BF16_PEAK_TFLOPS, 4),
+                        "kernel": dom, "avg_launch_us": kernels[dom]["avg_us"]},
+           "kernels": kernels}
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +227,9 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = 7B static-26, the bench line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--tree-wide", action="store_true",
+                    help="time only the tree-wide draft step (every drafted node of the flattened tree in one call: "
+                         "the matrix-unit bound shape at batch 8 / 16) and print its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -201,6 +254,9 @@ def main():
     cfg, eng, feat, tok, host = build_engine(args.config)
     B, N = cfg.batch, eng.n_nodes
     drafted = B * (N - 1)
+    if args.tree_wide:
+        tree_wide_bench(args, cfg, eng, feat, tok)
+        return
     # target logits resident in HBM before timing
     eng.draft_phase(feat, tok)
     tgt = synth_target(cfg, eng)
