@@ -11,14 +11,15 @@ from __future__ import annotations
 import ctypes
 
 from . import _abi
-from ._abi import (EAGLE_ACT_BF16, EAGLE_BF16, EAGLE_F32, EAGLE_HEAD_ONLY, EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK, EAGLE_VERIFY_GREEDY,
+from ._abi import (EAGLE_ACT_BF16, EAGLE_SAMPLE_CHILDREN, EAGLE_BF16, EAGLE_F32, EAGLE_HEAD_ONLY, EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK, EAGLE_VERIFY_GREEDY,
                    EAGLE_VERIFY_IID, EagleError, eagle_draft_out, eagle_kv, eagle_pool, eagle_rows, eagle_shape,
                    eagle_weights)
 
 __all__ = ["eagle_workspace_bytes", "eagle_draft_step", "eagle_softmax_topk", "eagle_tree_init", "eagle_tree_expand",
            "eagle_tree_finalize", "eagle_verify", "eagle_verify_workspace_bytes", "make_shape", "make_weights",
            "make_rows", "make_kv", "make_out",
-           "make_pool", "EagleError", "EAGLE_HEAD_ONLY", "EAGLE_ACT_BF16", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
+           "make_pool", "EagleError", "EAGLE_HEAD_ONLY", "EAGLE_ACT_BF16", "EAGLE_SAMPLE_CHILDREN",
+           "eagle_sample_topk", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
            "EAGLE_F32", "EAGLE_MAX_SLOTS", "EAGLE_MAX_TOPK", "eagle_profile_enable", "eagle_profile_reset",
            "eagle_profile_disable", "eagle_profile_read"]
 
@@ -68,9 +69,9 @@ def make_kv(prefix_k, prefix_v, prefix_off, prefix_len, max_prefix_len, tree_k, 
                           _ptr(tree_k), _ptr(tree_v)), prefix_k, prefix_v, prefix_off, prefix_len, tree_k, tree_v)
 
 
-def make_out(feat, logits, lse, topk, topk_idx, topk_logq):
-    return _keep(eagle_draft_out(_ptr(feat), _ptr(logits), _ptr(lse), topk, _ptr(topk_idx), _ptr(topk_logq)), feat,
-                 logits, lse, topk_idx, topk_logq)
+def make_out(feat, logits, lse, topk, topk_idx, topk_logq, seed=0, round_=0, row_base=0):
+    return _keep(eagle_draft_out(_ptr(feat), _ptr(logits), _ptr(lse), topk, _ptr(topk_idx), _ptr(topk_logq), seed,
+                                 round_, row_base), feat, logits, lse, topk_idx, topk_logq)
 
 
 def make_pool(cap, parent, token, depth, logv, feat_row, slot, mask, count, frontier):
@@ -96,6 +97,15 @@ def eagle_softmax_topk(n_rows, vocab, logits, topk, lse, topk_idx, topk_logq, wo
     rc = lib.eagle_softmax_topk(n_rows, vocab, _ptr(logits), topk, _ptr(lse), _ptr(topk_idx), _ptr(topk_logq),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _abi.check("eagle_softmax_topk", rc)
+
+
+def eagle_sample_topk(n_rows, vocab, logits, topk, seed, round_, row_base, lse, topk_idx, topk_logq, workspace,
+                      stream=None):
+    lib = _abi.load()
+    rc = lib.eagle_sample_topk(n_rows, vocab, _ptr(logits), topk, seed, round_, row_base, _ptr(lse), _ptr(topk_idx),
+                               _ptr(topk_logq), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+    _abi.check("eagle_sample_topk", rc)
 
 
 def eagle_tree_init(batch, pool, root_token, root_feat_row0, stream=None):

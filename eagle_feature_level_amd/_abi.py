@@ -16,7 +16,7 @@ c_i32, c_u64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_uint64, ctypes.c_fl
 
 EAGLE_OK, EAGLE_EINVAL, EAGLE_EUNSUPPORTED, EAGLE_EWORKSPACE, EAGLE_EHIP = 0, -1, -2, -3, -4
 EAGLE_F32, EAGLE_BF16 = 0, 1
-EAGLE_HEAD_ONLY, EAGLE_ACT_BF16 = 1, 2
+EAGLE_HEAD_ONLY, EAGLE_ACT_BF16, EAGLE_SAMPLE_CHILDREN = 1, 2, 4
 EAGLE_VERIFY_GREEDY, EAGLE_VERIFY_IID = 1, 2
 EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK = 64, 16
 ROLES = ("fc", "qkv", "rope", "attn", "o", "gate_up", "down", "lm_head", "topk", "rows")
@@ -44,7 +44,7 @@ class eagle_kv(ctypes.Structure):
 
 class eagle_draft_out(ctypes.Structure):
     _fields_ = [("feat", c_vp), ("logits", c_vp), ("lse", c_vp), ("topk", c_i32), ("topk_idx", c_vp),
-                ("topk_logq", c_vp)]
+                ("topk_logq", c_vp), ("seed", c_u64), ("round", c_u64), ("row_base", c_i32)]
 
 
 class eagle_pool(ctypes.Structure):
@@ -58,6 +58,8 @@ _SIGS = {
     "eagle_draft_step": (c_i32, [P(eagle_shape), P(eagle_weights), c_i32, P(eagle_rows), c_vp, P(eagle_kv),
                                  P(eagle_draft_out), c_vp, c_size, c_vp]),
     "eagle_softmax_topk": (c_i32, [c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "eagle_sample_topk": (c_i32, [c_i32, c_i32, c_vp, c_i32, c_u64, c_u64, c_i32, c_vp, c_vp, c_vp, c_vp, c_size,
+                                  c_vp]),
     "eagle_tree_init": (c_i32, [c_i32, P(eagle_pool), c_vp, c_i32, c_vp]),
     "eagle_tree_expand": (c_i32, [c_i32, c_i32, c_i32, c_vp, P(eagle_pool), c_i32, c_i32, c_vp, c_vp, c_i32, c_i32,
                                   c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),

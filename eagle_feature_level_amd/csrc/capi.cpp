@@ -200,11 +200,29 @@ int eagle_softmax_topk(int32_t n_rows, int32_t vocab, const float* logits, int32
   return e == hipSuccess ? EAGLE_OK : hip_fail(e);
 }
 
+int eagle_sample_topk(int32_t n_rows, int32_t vocab, const float* logits, int32_t topk, uint64_t seed, uint64_t round,
+                      int32_t row_base, float* lse, int32_t* topk_idx, float* topk_logq, void* workspace,
+                      size_t workspace_bytes, eagle_stream_t stream) {
+  if (n_rows < 0 || vocab <= 0 || topk < 1 || topk > vocab) return EAGLE_EINVAL;
+  if (n_rows == 0) return EAGLE_OK;
+  if (!logits || !lse || !topk_idx || !topk_logq || !workspace) return EAGLE_EINVAL;
+  if (topk > EAGLE_MAX_TOPK || vocab % 4 || vocab > TOPK_SAMPLE_MAX_VOCAB) return EAGLE_EUNSUPPORTED;
+  if (workspace_bytes < topk_workspace_bytes(n_rows, vocab)) return EAGLE_EWORKSPACE;
+  int rc = check_device();
+  if (rc) return rc;
+  const TopkSample smp{seed, round, row_base};
+  hipError_t e = launch_softmax_topk(n_rows, vocab, logits, topk, lse, topk_idx, topk_logq, workspace,
+                                     (hipStream_t)stream, &smp);
+  return e == hipSuccess ? EAGLE_OK : hip_fail(e);
+}
+
 int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t flags, const eagle_rows* rows,
                      const float* feat_in, const eagle_kv* kv, const eagle_draft_out* out, void* workspace,
                      size_t workspace_bytes, eagle_stream_t stream) {
   if (!shape_ok(shape) || !w || !rows || !out) return EAGLE_EINVAL;
-  if (flags & ~(EAGLE_HEAD_ONLY | EAGLE_ACT_BF16)) return EAGLE_EINVAL;
+  if (flags & ~(EAGLE_HEAD_ONLY | EAGLE_ACT_BF16 | EAGLE_SAMPLE_CHILDREN)) return EAGLE_EINVAL;
+  const bool sample = flags & EAGLE_SAMPLE_CHILDREN;
+  if (sample && shape && shape->vocab > TOPK_SAMPLE_MAX_VOCAB) return EAGLE_EUNSUPPORTED;
   const bool head_only = flags & EAGLE_HEAD_ONLY;
   const int act16 = (flags & EAGLE_ACT_BF16) ? 1 : 0;
   if (act16 && shape && shape->dtype != EAGLE_BF16) return EAGLE_EINVAL;  // a bf16 rounding of an fp32 workload
@@ -427,10 +445,11 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     e = gemm(a, EPI_STORE, nullptr, EAGLE_ROLE_LM_HEAD);
     if (e != hipSuccess) return hip_fail(e);
   }
-  // a9: softmax normaliser + top-k
+  // a9: softmax normaliser + top-k (or k sampled children)
+  const TopkSample smp{out->seed, out->round, out->row_base};
   e = timed(st, EAGLE_ROLE_TOPK, 4.0 * M * s.vocab, 0.0, [&] {
     return launch_softmax_topk(M, s.vocab, out->logits, out->topk, out->lse, out->topk_idx, out->topk_logq, ws.topk,
-                               st);
+                               st, sample ? &smp : nullptr);
   });
   if (e != hipSuccess) return hip_fail(e);
   return EAGLE_OK;

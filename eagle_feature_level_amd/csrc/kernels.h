@@ -53,10 +53,19 @@ struct AttnPlan {
 AttnPlan attn_plan(bool bf16, int max_prefix, int batch, int hkv, int max_queries);
 hipError_t launch_attention(const AttnArgs& a, bool bf16, int hd, int max_queries, hipStream_t s);
 
-// softmax + top-k
+// softmax + top-k.  With `smp`, the ranking key of token v in row r is
+// logit + g, g = -log(-log(u)) from Philox counter (smp->row_base + r, v / 4,
+// 0, 1) under key (seed, round), word v % 4, u = ((w >> 41) + 0.5) 2^-23: the k
+// tokens then are k draws without replacement from the row's softmax, in draw
+// order (Gumbel-top-k); lse and logq stay those of the plain logits.
+struct TopkSample {
+  uint64_t seed, round;
+  int row_base;
+};
+constexpr int TOPK_SAMPLE_MAX_VOCAB = 64 * 32 * 256;  // the chunked pass only
 size_t topk_workspace_bytes(int n_rows, int vocab);
 hipError_t launch_softmax_topk(int n_rows, int vocab, const float* logits, int k, float* lse, int32_t* idx,
-                               float* logq, void* ws, hipStream_t s);
+                               float* logq, void* ws, hipStream_t s, const TopkSample* smp = nullptr);
 
 // tree builder
 struct PoolArgs {

@@ -238,6 +238,24 @@ struct LaneList {
   }
 };
 
+// Gumbel perturbation of the ranking keys (sampled proposals): g(v) =
+// -log(-log(u)), u from word v % 4 of Philox counter (row id, v / 4, 0, 1),
+// u = ((w >> 41) + 0.5) 2^-23, exactly representable and inside (0, 1).  Adding
+// independent Gumbel noise to the logits and keeping the k largest gives k
+// draws without replacement from softmax(logits), in draw order (the
+// Gumbel-top-k construction).
+__device__ __forceinline__ float4 gumbel4(const TopkSample& sm, int row, int v0) {
+  uint64_t w[4];
+  philox4x64_10(sm.seed, sm.round, (uint64_t)(uint32_t)(sm.row_base + row), (uint64_t)(v0 >> 2), 0, 1, w);
+  float g[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float u = ((float)(w[c] >> 41) + 0.5f) * 1.1920928955078125e-07f;  // 2^-23
+    g[c] = -logf(-logf(u));
+  }
+  return make_float4(g[0], g[1], g[2], g[3]);
+}
+
 // Entry j*256 + lane*4 + c of a chunk (c < 4): consecutive lanes hold
 // consecutive float4s.  Only entries ranking below `below` are offered.
 template <int NE>
@@ -259,9 +277,11 @@ __device__ __forceinline__ void fill_list(LaneList& L, const float4 (&v)[NE], in
 }
 
 // grid (chunks, rows), one wave; chunk c covers [c * NE * 256, +NE * 256).
-template <int NE>
+// SAMPLE: the chunk's k best by Gumbel-perturbed logits (lse from the plain ones).
+template <int NE, bool SAMPLE>
 __global__ void __launch_bounds__(64) topk_chunk_part(const float* __restrict__ logits, int vocab, int k,
-                                                     float2* __restrict__ ms_out, uint64_t* __restrict__ keys_out) {
+                                                     float2* __restrict__ ms_out, uint64_t* __restrict__ keys_out,
+                                                     TopkSample sm) {
   const int row = blockIdx.y, c = blockIdx.x, nch = gridDim.x, lane = threadIdx.x;
   const float* x = logits + (size_t)row * vocab;
   const int base = c * NE * 256, end = min(vocab, base + NE * 256);
@@ -287,6 +307,17 @@ __global__ void __launch_bounds__(64) topk_chunk_part(const float* __restrict__ 
     const float m2 = __shfl_xor(m, o, WAVE), s2 = __shfl_xor(s, o, WAVE);
     ms_merge(m, s, m2, s2);
   }
+  if constexpr (SAMPLE) {  // ranking keys: the perturbed logits (-inf padding stays -inf)
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      const int i0 = base + j * 256 + lane * 4;
+      const float4 g = gumbel4(sm, row, i0);
+      v[j].x += g.x;
+      v[j].y += g.y;
+      v[j].z += g.z;
+      v[j].w += g.w;
+    }
+  }
   LaneList L;
   fill_list<NE>(L, v, base, end, ~0ull);
   uint64_t mine = 0ull;  // lane r: the chunk's r-th best
@@ -304,10 +335,12 @@ __global__ void __launch_bounds__(64) topk_chunk_part(const float* __restrict__ 
   if (lane == 0) ms_out[o] = make_float2(m, s);
 }
 
-// One wave per row: lane c holds chunk c's sorted list.
+// One wave per row: lane c holds chunk c's sorted list.  With sampled keys
+// (logits != nullptr) logq is taken from the plain logit of each chosen token.
 __global__ void __launch_bounds__(64) topk_chunk_merge(const float2* __restrict__ ms_in,
                                                       const uint64_t* __restrict__ keys_in, int nch, int k, float* lse,
-                                                      int32_t* idx, float* logq) {
+                                                      int32_t* idx, float* logq, const float* __restrict__ logits,
+                                                      int vocab) {
   const int row = blockIdx.x, lane = threadIdx.x;
   const size_t o = (size_t)row * nch + lane;
   uint64_t cand[TK_KMAX];
@@ -338,8 +371,10 @@ __global__ void __launch_bounds__(64) topk_chunk_merge(const float2* __restrict_
   const float l = __shfl(m, 0, WAVE) + __logf(__shfl(s, 0, WAVE));
   if (lane == 0) lse[row] = l;
   if (lane < k) {
-    idx[(size_t)row * k + lane] = (int32_t)key_index(fin);
-    logq[(size_t)row * k + lane] = key_value(fin) - l;
+    const uint32_t t = key_index(fin);
+    idx[(size_t)row * k + lane] = (int32_t)t;
+    const bool raw = logits != nullptr && t < (uint32_t)vocab;  // an empty key (0) names no token
+    logq[(size_t)row * k + lane] = (raw ? logits[(size_t)row * vocab + t] : key_value(fin)) - l;
   }
 }
 
@@ -375,24 +410,35 @@ size_t topk_workspace_bytes(int n_rows, int vocab) {
   return generic > chunked ? generic : chunked;
 }
 
+template <bool SAMPLE>
+void launch_chunk_part(int ne, dim3 g, dim3 b, hipStream_t s, const float* logits, int vocab, int k, float2* cms,
+                       uint64_t* ckeys, const TopkSample& sm) {
+  switch (ne) {
+    case 1: hipLaunchKernelGGL((topk_chunk_part<1, SAMPLE>), g, b, 0, s, logits, vocab, k, cms, ckeys, sm); break;
+    case 2: hipLaunchKernelGGL((topk_chunk_part<2, SAMPLE>), g, b, 0, s, logits, vocab, k, cms, ckeys, sm); break;
+    case 4: hipLaunchKernelGGL((topk_chunk_part<4, SAMPLE>), g, b, 0, s, logits, vocab, k, cms, ckeys, sm); break;
+    case 8: hipLaunchKernelGGL((topk_chunk_part<8, SAMPLE>), g, b, 0, s, logits, vocab, k, cms, ckeys, sm); break;
+    case 16: hipLaunchKernelGGL((topk_chunk_part<16, SAMPLE>), g, b, 0, s, logits, vocab, k, cms, ckeys, sm); break;
+    default: hipLaunchKernelGGL((topk_chunk_part<32, SAMPLE>), g, b, 0, s, logits, vocab, k, cms, ckeys, sm); break;
+  }
+}
+
 hipError_t launch_softmax_topk(int n_rows, int vocab, const float* logits, int k, float* lse, int32_t* idx,
-                               float* logq, void* ws, hipStream_t s) {
+                               float* logq, void* ws, hipStream_t s, const TopkSample* smp) {
   if (n_rows == 0) return hipSuccess;
   const int ne = topk_ne(n_rows, vocab);
+  if (smp && ne == 0) return hipErrorInvalidValue;  // sampled keys: chunked pass only
   if (ne > 0) {
     const int nch = (vocab + ne * 256 - 1) / (ne * 256);
     float2* cms = (float2*)ws;
     uint64_t* ckeys = (uint64_t*)((char*)ws + (((size_t)n_rows * TK_CHUNKS * sizeof(float2) + 255) / 256) * 256);
     const dim3 g(nch, n_rows), b(64);
-    switch (ne) {
-      case 1: hipLaunchKernelGGL(topk_chunk_part<1>, g, b, 0, s, logits, vocab, k, cms, ckeys); break;
-      case 2: hipLaunchKernelGGL(topk_chunk_part<2>, g, b, 0, s, logits, vocab, k, cms, ckeys); break;
-      case 4: hipLaunchKernelGGL(topk_chunk_part<4>, g, b, 0, s, logits, vocab, k, cms, ckeys); break;
-      case 8: hipLaunchKernelGGL(topk_chunk_part<8>, g, b, 0, s, logits, vocab, k, cms, ckeys); break;
-      case 16: hipLaunchKernelGGL(topk_chunk_part<16>, g, b, 0, s, logits, vocab, k, cms, ckeys); break;
-      default: hipLaunchKernelGGL(topk_chunk_part<32>, g, b, 0, s, logits, vocab, k, cms, ckeys); break;
-    }
-    hipLaunchKernelGGL(topk_chunk_merge, dim3(n_rows), b, 0, s, cms, ckeys, nch, k, lse, idx, logq);
+    if (smp)
+      launch_chunk_part<true>(ne, g, b, s, logits, vocab, k, cms, ckeys, *smp);
+    else
+      launch_chunk_part<false>(ne, g, b, s, logits, vocab, k, cms, ckeys, TopkSample{0, 0, 0});
+    hipLaunchKernelGGL(topk_chunk_merge, dim3(n_rows), b, 0, s, cms, ckeys, nch, k, lse, idx, logq,
+                       smp ? logits : (const float*)nullptr, vocab);
     return hipGetLastError();
   }
   const int chunk = topk_chunk(n_rows, vocab);

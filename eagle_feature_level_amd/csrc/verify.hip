@@ -32,25 +32,9 @@ constexpr int VT = 1024;
 constexpr int NW = VT / WAVE;
 
 __device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t round, uint64_t c0, uint64_t c1, uint64_t c2) {
-  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-  uint64_t x0 = c0, x1 = c1, x2 = c2, x3 = 0;
-  uint64_t k0 = seed, k1 = round;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r) {
-      k0 += W0;
-      k1 += W1;
-    }
-    const uint64_t hi0 = __umul64hi(M0, x0), lo0 = M0 * x0;
-    const uint64_t hi1 = __umul64hi(M1, x2), lo1 = M1 * x2;
-    const uint64_t y0 = hi1 ^ x1 ^ k0, y2 = hi0 ^ x3 ^ k1;
-    x0 = y0;
-    x1 = lo1;
-    x2 = y2;
-    x3 = lo0;
-  }
-  return (float)(x0 >> 40) * 5.9604644775390625e-08f;  // 2^-24
+  uint64_t w[4];
+  philox4x64_10(seed, round, c0, c1, c2, 0, w);
+  return (float)(w[0] >> 40) * 5.9604644775390625e-08f;  // 2^-24
 }
 
 __device__ __forceinline__ float bsum(float v, float* red) { return block_sum<VT>(v, red); }

@@ -16,7 +16,7 @@ import dataclasses
 
 import torch
 
-from . import (EAGLE_ACT_BF16, EAGLE_HEAD_ONLY, eagle_draft_step, eagle_tree_expand, eagle_tree_finalize, eagle_tree_init,
+from . import (EAGLE_ACT_BF16, EAGLE_HEAD_ONLY, EAGLE_SAMPLE_CHILDREN, eagle_draft_step, eagle_tree_expand, eagle_tree_finalize, eagle_tree_init,
                eagle_verify, eagle_verify_workspace_bytes, eagle_workspace_bytes, make_kv, make_out, make_pool,
                make_rows, make_shape, make_weights)
 
@@ -149,18 +149,25 @@ class EagleRound:
         on = self.act_bf16 if self.act_bf16 != "auto" else n_rows > self.ACT_BF16_MIN_ROWS
         return EAGLE_ACT_BF16 if on else 0
 
-    def root_head(self, root_feat: torch.Tensor):
+    def _sample_flag(self, sample):
+        return EAGLE_SAMPLE_CHILDREN if sample is not None else 0
+
+    def root_head(self, root_feat: torch.Tensor, sample=None):
         B = self.B
         self.feat[:B].copy_(root_feat)
         rows = make_rows(B, B, 1, self.root_start, None, self.root_rows)
-        out = make_out(None, self.logits, self.lse, self.topk, self.topk_idx, self.topk_logq)
-        eagle_draft_step(self.shape, self.weights, EAGLE_HEAD_ONLY | self.act_flag(B), rows, self.feat, None, out,
-                         self.workspace)
+        seed, rnd = sample if sample is not None else (0, 0)
+        out = make_out(None, self.logits, self.lse, self.topk, self.topk_idx, self.topk_logq, seed, rnd, 0)
+        eagle_draft_step(self.shape, self.weights, EAGLE_HEAD_ONLY | self.act_flag(B) | self._sample_flag(sample),
+                         rows, self.feat, None, out, self.workspace)
 
-    def draft_phase(self, root_feat: torch.Tensor, root_token: torch.Tensor):
-        """Root head, then expand + draft step per depth, then rerank/flatten."""
+    def draft_phase(self, root_feat: torch.Tensor, root_token: torch.Tensor, sample=None):
+        """Root head, then expand + draft step per depth, then rerank/flatten.
+        sample = (seed, round): every expanded node's children are drawn
+        without replacement from its draft distribution (EAGLE_SAMPLE_CHILDREN,
+        row ids = the round's feature rows) instead of taken as its top-k."""
         B, k = self.B, self.k
-        self.root_head(root_feat)
+        self.root_head(root_feat, sample)
         eagle_tree_init(B, self.pool, root_token, 0)
         prev_row0, n_prev = 0, 1
         for s in range(self.depth):
@@ -179,9 +186,11 @@ class EagleRound:
                 break
             n = B * st.n_next
             rows = make_rows(n, B, st.n_next, st.row_start, st.token, st.parent, st.pos, st.slot, st.mask)
+            seed, rnd = sample if sample is not None else (0, 0)
             out = make_out(self.feat[st.feat_row0:], self.logits[st.feat_row0:], self.lse[st.feat_row0:], self.topk,
-                           self.topk_idx[st.feat_row0:], self.topk_logq[st.feat_row0:])
-            eagle_draft_step(self.shape, self.weights, self.act_flag(n), rows, self.feat, self.kv, out, self.workspace)
+                           self.topk_idx[st.feat_row0:], self.topk_logq[st.feat_row0:], seed, rnd, st.feat_row0)
+            eagle_draft_step(self.shape, self.weights, self.act_flag(n) | self._sample_flag(sample), rows, self.feat,
+                             self.kv, out, self.workspace)
             prev_row0, n_prev = st.feat_row0, st.n_next
         t = self.tree
         eagle_tree_finalize(B, self.m, self.n_nodes, self.pool, self.prefix["len"], t["parent"], t["token"],

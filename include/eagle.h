@@ -116,6 +116,11 @@ typedef struct {
   int32_t topk;      /* 1..16                                                   */
   int32_t *topk_idx; /* [n_rows, topk] ranked tokens, ties -> lower index        */
   float *topk_logq;  /* [n_rows, topk] logit - lse of those tokens               */
+  /* EAGLE_SAMPLE_CHILDREN only: Philox key (seed, round) and the id of the
+   * call's first row (row r draws with counter row_base + r; give every row
+   * of a round a distinct id). */
+  uint64_t seed, round;
+  int32_t row_base;
 } eagle_draft_out;
 
 /* Flags of eagle_draft_step.
@@ -130,7 +135,14 @@ typedef struct {
  *   fp32 accumulation, attention on split operands).  For steps over many rows
  *   (the matrix units are the bound above a few hundred rows) this halves the
  *   matrix work; it is the usual bf16 inference contract. */
-enum { EAGLE_HEAD_ONLY = 1, EAGLE_ACT_BF16 = 2 };
+/* EAGLE_SAMPLE_CHILDREN: topk_idx holds `topk` tokens drawn without
+ *   replacement from each row's softmax, in draw order (Gumbel-top-k, as in
+ *   eagle_sample_topk below) instead of the `topk` most probable ones; lse and
+ *   topk_logq are unchanged in meaning.  Children proposed this way are the
+ *   without-replacement draw that eagle_verify's default rule is exact for
+ *   ("eagle feature-level speculative decoding", sampled verification: the
+ *   siblings' sampling scheme must match the verifier's). */
+enum { EAGLE_HEAD_ONLY = 1, EAGLE_ACT_BF16 = 2, EAGLE_SAMPLE_CHILDREN = 4 };
 
 /* Bytes of workspace needed by eagle_draft_step / eagle_softmax_topk for up
  * to max_rows rows, max_batch sequences and prefixes up to max_prefix_len.
@@ -174,6 +186,18 @@ int eagle_draft_step(const eagle_shape *shape, const eagle_weights *w, int32_t f
 int eagle_softmax_topk(int32_t n_rows, int32_t vocab, const float *logits, int32_t topk, float *lse,
                        int32_t *topk_idx, float *topk_logq, void *workspace, size_t workspace_bytes,
                        eagle_stream_t stream);
+
+/* Sampled proposals: like eagle_softmax_topk, but the ranking key of token v
+ * in row r is logit + g with g = -log(-log(u)), u from word v % 4 of
+ * Philox4x64-10 (Salmon et al., SC'11) counter (row_base + r, v / 4, 0, 1) under
+ * key (seed, round), u = ((w >> 41) + 0.5) * 2^-23 (fp32 throughout).  The
+ * `topk` tokens are then `topk` draws without replacement from softmax(row),
+ * in draw order (Gumbel-top-k); lse and topk_logq (= logit - lse) are those of
+ * the plain logits.  vocab <= 524288 (else EAGLE_EUNSUPPORTED).  Uses the
+ * workspace sized by eagle_workspace_bytes. */
+int eagle_sample_topk(int32_t n_rows, int32_t vocab, const float *logits, int32_t topk, uint64_t seed, uint64_t round,
+                      int32_t row_base, float *lse, int32_t *topk_idx, float *topk_logq, void *workspace,
+                      size_t workspace_bytes, eagle_stream_t stream);
 
 /* Candidate pool of the tree builder: per sequence b, entries
  * [b*cap, (b+1)*cap) of each array; node 0 is the root. */

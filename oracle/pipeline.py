@@ -25,7 +25,7 @@ import numpy as np
 
 from . import draft as D
 from . import tree as T
-from .topk import softmax_topk
+from .topk import gumbel_topk, softmax_topk
 from .verify import verify_sequence
 
 
@@ -37,7 +37,19 @@ def act_for(act_bf16, n_rows: int) -> bool:
 
 
 def draft_phase(shape, w, root_feat, root_token, prefix_k, prefix_v, prefix_len, kind: str, k: int, depth: int,
-                m: int = 0, template=None, mirror: bool = True, tree_wide: bool = True, act_bf16=False):
+                m: int = 0, template=None, mirror: bool = True, tree_wide: bool = True, act_bf16=False,
+                sample=None):
+    """sample = (seed, round): children drawn without replacement from each
+    expanded node's q (Gumbel-top-k over the row's fp32 logits, row id = the
+    row's index in the round) instead of its top-k."""
+
+    def select(lg, row0):
+        if sample is None:
+            _, i_, q_ = softmax_topk(lg.astype(np.float32), k)
+        else:
+            _, i_, q_, _ = gumbel_topk(lg.astype(np.float32), k, sample[0], sample[1], np.arange(lg.shape[0]) + row0)
+        return i_, q_
+
     B = root_feat.shape[0]
     nchild = None
     if kind != "dynamic":
@@ -47,7 +59,7 @@ def draft_phase(shape, w, root_feat, root_token, prefix_k, prefix_v, prefix_len,
     feats = [np.asarray(root_feat, np.float64)]
     root_logits = D.head_logits(shape, w, root_feat, mirror, act_for(act_bf16, B))
     logits = [root_logits]
-    _, idx, logq = softmax_topk(root_logits.astype(np.float32), k)
+    idx, logq = select(root_logits, 0)
     pools = [T.Pool(root_token[b], b) for b in range(B)]
     frontier = [[0] for _ in range(B)]
     sel_idx = [[idx[b]] for b in range(B)]
@@ -78,7 +90,7 @@ def draft_phase(shape, w, root_feat, root_token, prefix_k, prefix_v, prefix_len,
         logits.append(out["logits"])
         n_rows += len(rows["seq"])
         steps.append(rows)
-        _, idx, logq = softmax_topk(out["logits"].astype(np.float32), k)
+        idx, logq = select(out["logits"], base)
         o = 0
         for b in range(B):
             nf = len(frontier[b])

@@ -218,3 +218,37 @@ def test_draft_step_is_deterministic():
     _, g2, _, _, _ = _run_draft(shape, [20, 13], [90, 3], seed=11)
     for key in ("feat", "logits", "idx", "lse"):
         assert np.array_equal(g1[key], g2[key]), key
+
+
+@pytest.mark.parametrize("rows,vocab,k,row_base", [(3, 32000, 10, 0), (40, 32000, 4, 1000), (7, 512, 1, 5),
+                                                   (961, 32000, 10, 77), (2, 4096, 16, 3)])
+def test_sample_topk_matches_oracle(rows, vocab, k, row_base):
+    """Sampled proposals (Gumbel-top-k) against the oracle on the same fp32
+    logits: identical draws and log-probabilities; a row whose k-th and
+    (k+1)-th perturbed keys lie within 1e-5 of each other counts as a near-tie
+    (the two sides' fp32 log may differ in the last bit) and is skipped."""
+    from oracle.topk import gumbel_topk
+    g = np.random.default_rng(rows + vocab + k)
+    x = (g.standard_normal((rows, vocab)) * 2).astype(np.float32)
+    x[0, :50] = 3.25  # a plateau of equal logits
+    t = torch.from_numpy(x).cuda()
+    lse = torch.empty(rows, device="cuda")
+    idx = torch.empty(rows, k, dtype=torch.int32, device="cuda")
+    lq = torch.empty(rows, k, device="cuda")
+    shape = E.make_shape(256, 2, 2, 128, 256, vocab)
+    ws = _ws(E.eagle_workspace_bytes(shape, rows, 1, 0))
+    seed, rnd = 12345, 6
+    E.eagle_sample_topk(rows, vocab, t, k, seed, rnd, row_base, lse, idx, lq, ws)
+    torch.cuda.synchronize()
+    o_lse, o_idx, o_lq, margin = gumbel_topk(x, k, seed, rnd, np.arange(rows) + row_base)
+    gi = idx.cpu().numpy()
+    near = margin < 1e-5
+    assert near.sum() <= max(1, rows // 100)
+    assert np.array_equal(gi[~near], o_idx[~near])
+    assert np.allclose(lse.cpu().numpy(), o_lse, rtol=1e-6, atol=1e-5)
+    assert np.allclose(lq.cpu().numpy()[~near], o_lq[~near], rtol=0, atol=2e-5)
+    # draws without replacement; not the deterministic top-k
+    assert all(len(set(r)) == k for r in gi)
+    if k > 1:
+        _, det, _ = o_topk(x, k)
+        assert not np.array_equal(gi, det)

@@ -38,15 +38,16 @@ def _engine(cfg, w=None):
     return eng, w, lens, ks, vs, tmpl
 
 
-def test_tiny_round_matches_oracle_pipeline():
+@pytest.mark.parametrize("sample", [None, (3, 1)])
+def test_tiny_round_matches_oracle_pipeline(sample):
     cfg = CONFIGS[1]
     eng, w, lens, ks, vs, tmpl = _engine(cfg)
     feat = make_root_features(cfg)
     tok = make_root_tokens(cfg)
-    eng.draft_phase(torch.from_numpy(feat).cuda(), dev.ints(tok))
+    eng.draft_phase(torch.from_numpy(feat).cuda(), dev.ints(tok), sample=sample)
     eng.tree_wide()
     torch.cuda.synchronize()
-    ref = OP.draft_phase(cfg.shape, w, feat, tok, ks, vs, lens, "static", cfg.topk, cfg.depth, 0, tmpl)
+    ref = OP.draft_phase(cfg.shape, w, feat, tok, ks, vs, lens, "static", cfg.topk, cfg.depth, 0, tmpl, sample=sample)
     # near-ties in the oracle's top-1 choices would legitimately change the tree
     gaps = []
     for r in range(ref["logits"].shape[0]):
@@ -192,3 +193,35 @@ def test_graph_replay_equals_eager_round():
         eng.draft_phase(feat, tok)
         eng.verify(tgt, 0, 3)
         torch.cuda.synchronize()
+
+
+def test_sampled_round_7b_static26_staged():
+    """A 7B static-26 round with sampled children (EAGLE_SAMPLE_CHILDREN): the
+    oracle's Gumbel-top-k on the GPU's own fp32 logits draws the same tokens
+    for every row (near-ties closer than 1e-5 excepted), and every node's
+    children in the flattened tree are the first draws of its row, in draw
+    order."""
+    from oracle.topk import gumbel_topk
+    cfg = CONFIGS[2]
+    eng, w, lens, ks, vs, tmpl = _engine(cfg)
+    feat = torch.from_numpy(make_root_features(cfg)).cuda()
+    tok = dev.ints(make_root_tokens(cfg))
+    eng.draft_phase(feat, tok, sample=(9, 4))
+    torch.cuda.synchronize()
+    logits = eng.logits.cpu().numpy()
+    gidx = eng.topk_idx.cpu().numpy()
+    _, oidx, _, margin = gumbel_topk(logits, eng.topk, 9, 4, np.arange(logits.shape[0]))
+    near = margin < 1e-5
+    assert near.sum() <= 1
+    assert np.array_equal(gidx[~near], oidx[~near])
+    parent = eng.tree["parent"].cpu().numpy()
+    token = eng.tree["token"].cpu().numpy()
+    qrow = eng.tree["qrow"].cpu().numpy()
+    differs = False
+    for u in range(len(parent)):
+        kids = [i for i in range(len(parent)) if parent[i] == u]
+        if kids:
+            assert [int(token[i]) for i in kids] == [int(t) for t in gidx[qrow[u], :len(kids)]], u
+            _, det, _ = o_topk(logits[qrow[u]:qrow[u] + 1], len(kids))
+            differs |= list(det[0]) != [int(token[i]) for i in kids]
+    assert differs  # sampled, not the deterministic top-k

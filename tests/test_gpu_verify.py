@@ -180,7 +180,10 @@ def _chi_case(V, B, proposal, seed):
     N = len(parent)
     tokens = np.zeros((B, N), np.int32)
     qc = softmax(child_d)
-    for b in range(B):
+    if proposal == "kernel":  # the library's sampled proposals (eagle_sample_topk), one row per sequence
+        tokens[:, 1:4] = _sample_children(np.log(q0), B, 3, seed, 0)
+        tokens[:, 4:6] = _sample_children(child_d, B, 2, seed, B)
+    for b in range(B if proposal != "kernel" else 0):
         if proposal == "wor":
             tokens[b, 1:4] = g.choice(V, size=3, replace=False, p=q0)
             tokens[b, 4:6] = g.choice(V, size=2, replace=False, p=qc)
@@ -198,6 +201,27 @@ def _chi_case(V, B, proposal, seed):
 def test_chi_square_first_token_matches_target():
     assert _chi_case(8, 40000, "wor", 21) > 1e-3
     assert _chi_case(12, 40000, "wor", 22) > 1e-3
+
+
+def _sample_children(logits_row, B, k, seed, row_base):
+    V = len(logits_row)
+    rows = torch.from_numpy(np.tile(np.asarray(logits_row, np.float32), (B, 1))).cuda()
+    lse = torch.empty(B, device="cuda")
+    idx = torch.empty(B, k, dtype=torch.int32, device="cuda")
+    lq = torch.empty(B, k, device="cuda")
+    shape = E.make_shape(256, 2, 2, 128, 256, V)
+    ws = torch.empty(E.eagle_workspace_bytes(shape, B, 1, 0), dtype=torch.uint8, device="cuda")
+    E.eagle_sample_topk(B, V, rows, k, seed, 5, row_base, lse, idx, lq, ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+def test_chi_square_with_sampled_children_from_the_kernel():
+    """End to end on the GPU: children proposed by eagle_sample_topk
+    (Gumbel-top-k, without replacement from q) and verified by eagle_verify's
+    default rule give first tokens distributed as the target p, with q != p."""
+    assert _chi_case(8, 40000, "kernel", 23) > 1e-3
+    assert _chi_case(12, 40000, "kernel", 24) > 1e-3
 
 
 def test_chi_square_has_power_on_topk_proposals():

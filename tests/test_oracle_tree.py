@@ -152,3 +152,46 @@ def test_static_expand_reproduces_template():
     for i in range(1, 26):
         r = sum(1 for j in range(1, i) if s26[j] == s26[i])
         assert pool.token[i] == 100 * s26[i] + r
+
+
+def test_gumbel_topk_draws_without_replacement_from_softmax():
+    """Gumbel-top-k against the law it must follow: the first proposal ~ p, and
+    the ordered pair (first, second) ~ p_i p_j / (1 - p_i), the probability of
+    drawing i then j without replacement.  Pearson chi-square over 20000
+    seeded rows, alpha = 1e-3."""
+    from scipy.stats import chi2
+
+    from oracle.topk import gumbel_topk
+
+    logits = np.array([1.2, -0.3, 0.5, 2.0, -1.0], dtype=np.float32)
+    p = np.exp(logits.astype(np.float64) - logits.max())
+    p /= p.sum()
+    n = 20000
+    rows = np.tile(logits, (n, 1))
+    _, idx, _, _ = gumbel_topk(rows, 2, 7, 3, np.arange(n))
+    first = np.bincount(idx[:, 0], minlength=5)
+    stat = np.sum((first - n * p) ** 2 / (n * p))
+    assert stat < chi2.ppf(1 - 1e-3, 4), stat
+    V = 5
+    pair = np.zeros((V, V))
+    for a, b in idx:
+        pair[a, b] += 1
+    exp = np.array([[p[i] * p[j] / (1 - p[i]) if i != j else 0.0 for j in range(V)] for i in range(V)]) * n
+    m = exp > 0
+    stat2 = np.sum((pair[m] - exp[m]) ** 2 / exp[m])
+    assert stat2 < chi2.ppf(1 - 1e-3, m.sum() - 1), stat2
+    # no repeats within a row, and the proposals differ from the deterministic top-2
+    assert np.all(idx[:, 0] != idx[:, 1])
+    assert np.mean(idx[:, 0] == 3) < 0.6
+
+
+def test_gumbel_uniforms_are_inside_the_open_interval():
+    from oracle.philox import philox4x64_10
+    from oracle.topk import gumbel_keys
+
+    # word v % 4 of counter (row, v // 4, 0, 1): recompute token 6 with the scalar generator
+    w = philox4x64_10((11, 6 // 4, 0, 1), (5, 9))[6 % 4]
+    u = ((w >> 41) + 0.5) * 2.0 ** -23
+    assert 0.0 < u < 1.0
+    key = gumbel_keys(np.zeros(8, np.float32), 5, 9, 11)
+    assert abs(float(key[6]) - (-np.log(-np.log(u)))) < 1e-5
