@@ -360,11 +360,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
   }
 }
 
-// Tile geometry of the large-M kernel (gemm_big16 below): 256 weight rows x
-// 128 activation rows per workgroup, 64-wide K blocks staged in LDS.
-constexpr int BG_BN = 256, BG_BM = 128, BG_BK = 64;
-constexpr int BG_LD = BG_BK + 8;  // LDS row (bf16): 144 B, rows 4 banks apart
-
+// Grid of the large-M kernel: weight tiles x activation tiles x K splits.
 struct BigPlan {
   int tiles_n, tiles_m, splits;
 };
@@ -583,167 +579,178 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
 
 // ---------------------------------------------------------------------------
 // Large-M kernel (M above a few hundred rows, where the matrix units are the
-// bound): 256 weight rows x 128 activation rows per workgroup, 8 waves of
-// 64 x 64, both operands staged through LDS in two buffers, fed from the
-// prepared bf16 operand (one half, or the hi and lo halves: two MFMAs per
-// product), with PD k-blocks of global loads in flight in registers ahead of
-// the LDS buffer being multiplied.  Row blocks of the activations vary
-// fastest over the grid and consecutive tiles stay on one XCD, so the
-// workgroups sharing a weight tile run together and share an L2.  SwiGLU: the
-// 256 rows of a tile are, per wave quarter, 32 gate rows and the 32 up rows
-// of the same ffn columns, so gate and up meet in one lane.
+// bound): WN x WM waves, each owning TN x TM blocks of 16 x 16 outputs
+// (weight rows x activation rows), K staged in blocks of BK through LDS (two
+// buffers, the next block's global loads in flight in registers), both
+// operands from the prepared bf16 operand (hi and lo halves: two MFMAs per
+// product).  The MFMAs per LDS fragment a wave reads grow with its tile,
+// TN*TM / (TN + NH*TM); the LDS footprint, two buffers of (BN + NH*BM) x
+// (BK + 8) bf16, bounds the workgroup tile.  Consecutive tiles stay on one XCD
+// so the workgroups sharing a weight tile share an L2.  SwiGLU: per wave, TN/2
+// blocks of gate rows, then the up rows of the same ffn columns, so gate and
+// up meet in one lane.
 // ---------------------------------------------------------------------------
-template <int EPI, int PD, bool SPLIT>
-__global__ void __launch_bounds__(512) gemm_big16(GemmArgs a, const bf16_t* __restrict__ xb, BigPlan p) {
-  constexpr int NH = SPLIT ? 2 : 1;  // operand halves: hi (and lo, at xb + M*K)
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BG_BN][BG_LD];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][NH][BG_BM][BG_LD];
-  __shared__ float ssq_s[4][BG_BM];
+template <int WN_, int WM_, int TN_, int TM_, int BK_>
+struct TileCfg {
+  static constexpr int WN = WN_, WM = WM_, TN = TN_, TM = TM_, BK = BK_;
+  static constexpr int BN = WN * TN * 16, BM = WM * TM * 16, LD = BK + 8, KC = BK / 32;
+  static_assert(WN * WM == 8, "512 threads");
+  static_assert(BK % 32 == 0, "whole MFMA k-steps");
+};
+
+template <int EPI, bool SPLIT, class T>
+__global__ void __launch_bounds__(512) gemm_tile(GemmArgs a, const bf16_t* __restrict__ xb, BigPlan p) {
+  constexpr int NH = SPLIT ? 2 : 1;
+  constexpr int BN = T::BN, BM = T::BM, BK = T::BK, LD = T::LD, TN = T::TN, TM = T::TM;
+  constexpr int CPR = BK / 8;                    // 16-byte chunks per tile row and k-block
+  constexpr int ACH = (BN * CPR + 511) / 512;    // weight chunks per thread
+  constexpr int XCH = (BM * CPR + 511) / 512;    // activation chunks per thread and half
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BN][LD];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][NH][BM][LD];
+  __shared__ float ssq_s[T::WN][BM];
   const int nwg = gridDim.x, bid = blockIdx.x;
   const int lid = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;  // consecutive tiles on one XCD
   const int mt = lid % p.tiles_m, rest = lid / p.tiles_m;
   const int nt = rest % p.tiles_n, sp = rest / p.tiles_n;
-  const int m0 = mt * BG_BM;
+  const int m0 = mt * BM;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int wn = wv & 3, wm = wv >> 2;
+  const int wn = wv % T::WN, wm = wv / T::WN;
   const int r = lane & 15, g = lane >> 4;
-  const int kper = a.K / p.splits, kbeg = sp * kper, nkb = kper / BG_BK;
+  const int kper = a.K / p.splits, kbeg = sp * kper, nkb = kper / BK;
 
+  // logical weight row of tile row i (-1 past the end); SwiGLU: per wave, TN/2
+  // blocks of gate rows, then the up rows of the same ffn columns
   auto wrow_of = [&](int i) -> int {
     if constexpr (EPI == EPI_SWIGLU) {
-      const int q = i >> 6, w = i & 63;
-      const int j = nt * 128 + q * 32 + (w & 31);
+      constexpr int WR = TN * 16, HR = TN * 8;
+      const int q = i / WR, w = i % WR;
+      const int j = nt * (BN / 2) + q * HR + (w % HR);
       if (j >= a.ffn) return -1;
-      return (w < 32) ? j : a.ffn + j;
+      return (w < HR) ? j : a.ffn + j;
     } else {
-      const int n = nt * BG_BN + i;
+      const int n = nt * BN + i;
       return n < a.N ? n : -1;
     }
   };
-  // staging: weight rows t/8 + 64u (u < 4), activation rows t/8 + 64u (u < 2); 8 columns at 8*(t%8)
-  const int cc = (t & 7) * 8;
-  const bf16_t* ap[4];
-  const bf16_t* xp[2];
+  const bf16_t* ap[ACH];
+  const bf16_t* xp[XCH];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int n = wrow_of((t >> 3) + 64 * u);
-    ap[u] = (n >= 0) ? wrow<bf16_t>(a, n) + kbeg + cc : nullptr;
+  for (int u = 0; u < ACH; ++u) {
+    const int c = t + 512 * u;
+    const int n = (c < BN * CPR) ? wrow_of(c / CPR) : -1;
+    ap[u] = (n >= 0) ? wrow<bf16_t>(a, n) + kbeg + (c % CPR) * 8 : nullptr;
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int m = m0 + (t >> 3) + 64 * u;
-    xp[u] = (m < a.M) ? xb + (size_t)m * a.K + kbeg + cc : nullptr;
+  for (int u = 0; u < XCH; ++u) {
+    const int c = t + 512 * u;
+    const int m = m0 + c / CPR;
+    xp[u] = (c < BM * CPR && m < a.M) ? xb + (size_t)m * a.K + kbeg + (c % CPR) * 8 : nullptr;
   }
   const size_t lo_off = (size_t)a.M * a.K;
-  struct Pf {
-    u32x4 A[4], X[NH][2];
-  };
-  Pf pf[PD];
-  auto load = [&](Pf& f, int kb) {
-    const int k0 = kb * BG_BK;
+  u32x4 ra[ACH], rx[NH][XCH];
+  auto load = [&](int kb) {
+    const int k0 = kb * BK;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) f.A[u] = ap[u] ? *(const u32x4*)(ap[u] + k0) : u32x4{0, 0, 0, 0};
+    for (int u = 0; u < ACH; ++u) ra[u] = ap[u] ? *(const u32x4*)(ap[u] + k0) : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) f.X[h][u] = xp[u] ? *(const u32x4*)(xp[u] + h * lo_off + k0) : u32x4{0, 0, 0, 0};
+      for (int u = 0; u < XCH; ++u) rx[h][u] = xp[u] ? *(const u32x4*)(xp[u] + h * lo_off + k0) : u32x4{0, 0, 0, 0};
   };
-  auto store = [&](const Pf& f, int buf) {
+  auto store = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) *(u32x4*)&As[buf][(t >> 3) + 64 * u][cc] = f.A[u];
+    for (int u = 0; u < ACH; ++u) {
+      const int c = t + 512 * u;
+      if (c < BN * CPR) *(u32x4*)&As[buf][c / CPR][(c % CPR) * 8] = ra[u];
+    }
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) *(u32x4*)&Bs[buf][h][(t >> 3) + 64 * u][cc] = f.X[h][u];
+      for (int u = 0; u < XCH; ++u) {
+        const int c = t + 512 * u;
+        if (c < BM * CPR) *(u32x4*)&Bs[buf][h][c / CPR][(c % CPR) * 8] = rx[h][u];
+      }
   };
 
-  floatx4 acc[4][4];
+  floatx4 acc[TN][TM];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb = 0; nb < TN; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < TM; ++mb) acc[nb][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // slot j % PD holds k-block j for j in (kb, kb + PD]
-#pragma unroll
-  for (int i = 0; i < PD; ++i)
-    if (i < nkb) load(pf[i], i);
   if (nkb > 0) {
-    store(pf[0], 0);
-    if (PD < nkb) load(pf[0], PD);
+    load(0);
+    store(0);
+    if (nkb > 1) load(1);
   }
   __syncthreads();
-  for (int kb0 = 0; kb0 < nkb; kb0 += PD) {
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
 #pragma unroll
-    for (int i = 0; i < PD; ++i) {
-      const int kb = kb0 + i;
-      if (kb >= nkb) break;
-      const int buf = kb & 1;
+    for (int kc = 0; kc < T::KC; ++kc) {
+      u32x4 A[TN];
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        u32x4 A[4];
+      for (int nb = 0; nb < TN; ++nb) A[nb] = *(const u32x4*)&As[buf][(wn * TN + nb) * 16 + r][kc * 32 + g * 8];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) A[nb] = *(const u32x4*)&As[buf][wn * 64 + nb * 16 + r][kc * 32 + g * 8];
+      for (int h = 0; h < NH; ++h) {
+        u32x4 B[TM];
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          u32x4 B[4];
+        for (int mb = 0; mb < TM; ++mb) B[mb] = *(const u32x4*)&Bs[buf][h][(wm * TM + mb) * 16 + r][kc * 32 + g * 8];
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-            B[mb] = *(const u32x4*)&Bs[buf][h][wm * 64 + mb * 16 + r][kc * 32 + g * 8];
+        for (int nb = 0; nb < TN; ++nb)
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma16(A[nb], B[mb], acc[nb][mb]);
-        }
+          for (int mb = 0; mb < TM; ++mb) acc[nb][mb] = mfma16(A[nb], B[mb], acc[nb][mb]);
       }
-      if (kb + 1 < nkb) {
-        store(pf[(i + 1) % PD], buf ^ 1);
-        if (kb + 1 + PD < nkb) load(pf[(i + 1) % PD], kb + 1 + PD);
-      }
-      __syncthreads();
     }
+    if (kb + 1 < nkb) {
+      store(buf ^ 1);
+      if (kb + 2 < nkb) load(kb + 2);
+    }
+    __syncthreads();
   }
 
-  // lane (r, g): acc[nb][mb][v] = tile row wn*64 + nb*16 + 4g + v, activation row wm*64 + mb*16 + r
+  // lane (r, g): acc[nb][mb][v] = tile row (wn*TN + nb)*16 + 4g + v, activation row (wm*TM + mb)*16 + r
   if (p.splits > 1) {
     float* P = a.part + (size_t)sp * a.M * a.N;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 64 + mb * 16 + r;
+    for (int mb = 0; mb < TM; ++mb) {
+      const int m = m0 + (wm * TM + mb) * 16 + r;
       if (m >= a.M) continue;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int n = wrow_of(wn * 64 + nb * 16 + 4 * g);
+      for (int nb = 0; nb < TN; ++nb) {
+        const int n = wrow_of((wn * TN + nb) * 16 + 4 * g);
         if (n >= 0) *(floatx4*)(P + (size_t)m * a.N + n) = acc[nb][mb];
       }
     }
     return;
   }
   if constexpr (EPI == EPI_SWIGLU) {
+    constexpr int H = TN / 2;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 64 + mb * 16 + r;
+    for (int mb = 0; mb < TM; ++mb) {
+      const int m = m0 + (wm * TM + mb) * 16 + r;
       if (m >= a.M) continue;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int j = nt * 128 + wn * 32 + nb * 16 + 4 * g;
+      for (int nb = 0; nb < H; ++nb) {
+        const int j = nt * (BN / 2) + wn * (TN * 8) + nb * 16 + 4 * g;
         if (j >= a.ffn) continue;
         float4 o;
-        o.x = silu_f(acc[nb][mb][0]) * acc[nb + 2][mb][0];
-        o.y = silu_f(acc[nb][mb][1]) * acc[nb + 2][mb][1];
-        o.z = silu_f(acc[nb][mb][2]) * acc[nb + 2][mb][2];
-        o.w = silu_f(acc[nb][mb][3]) * acc[nb + 2][mb][3];
+        o.x = silu_f(acc[nb][mb][0]) * acc[nb + H][mb][0];
+        o.y = silu_f(acc[nb][mb][1]) * acc[nb + H][mb][1];
+        o.z = silu_f(acc[nb][mb][2]) * acc[nb + H][mb][2];
+        o.w = silu_f(acc[nb][mb][3]) * acc[nb + H][mb][3];
         *(float4*)(a.yb + (size_t)m * a.ldyb + j) = o;
       }
     }
   } else {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int ml = wm * 64 + mb * 16 + r, m = m0 + ml;
+    for (int mb = 0; mb < TM; ++mb) {
+      const int ml = (wm * TM + mb) * 16 + r, m = m0 + ml;
       const bool mv = m < a.M;
       float ss = 0.f;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int n = nt * BG_BN + wn * 64 + nb * 16 + 4 * g;
+      for (int nb = 0; nb < TN; ++nb) {
+        const int n = nt * BN + (wn * TN + nb) * 16 + 4 * g;
         if (!mv || n >= a.N) continue;
         float4 y = make_float4(acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]);
         if constexpr (EPI == EPI_BIAS_SUMSQ) {
@@ -772,8 +779,12 @@ __global__ void __launch_bounds__(512) gemm_big16(GemmArgs a, const bf16_t* __re
     }
     if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
       __syncthreads();
-      if (t < BG_BM && m0 + t < a.M)
-        a.sumsq_out[(size_t)nt * a.M + m0 + t] = ssq_s[0][t] + ssq_s[1][t] + ssq_s[2][t] + ssq_s[3][t];
+      if (t < BM && m0 + t < a.M) {
+        float q = 0.f;
+#pragma unroll
+        for (int w = 0; w < T::WN; ++w) q += ssq_s[w][t];
+        a.sumsq_out[(size_t)nt * a.M + m0 + t] = q;
+      }
     }
   }
 }
@@ -996,17 +1007,6 @@ hipError_t skinny_launch(const GemmArgs& a, int epi, int* n_part, hipStream_t s)
 }
 
 
-// Tiles of the large-M kernel, plus a K split (powers of 2) while the grid
-// has fewer than 256 workgroups (one per CU: the kernel holds 148 KB of LDS).
-BigPlan plan_big(int M, int N, int K, bool swiglu) {
-  BigPlan p;
-  p.tiles_n = swiglu ? (N / 2 + 127) / 128 : (N + BG_BN - 1) / BG_BN;
-  p.tiles_m = (M + BG_BM - 1) / BG_BM;
-  p.splits = 1;
-  while (p.tiles_n * p.tiles_m * p.splits < 256 && K % (BG_BK * p.splits * 2) == 0 && K / (p.splits * 2) >= 512)
-    p.splits *= 2;
-  return p;
-}
 
 // Wide-kernel shape: NW waves of 16*AT weight rows each, ring depth NS.
 template <int NW, int AT, int NS>
@@ -1071,15 +1071,28 @@ hipError_t wide_mb(const GemmArgs& a, int epi, const bf16_t* xb, const WidePlan&
   }
 }
 
-template <int PD, bool SPLIT>
-hipError_t big16_epi(const GemmArgs& a, int epi, const bf16_t* xb, const BigPlan& p, hipStream_t s) {
+// Tiles of gemm_tile plus a K split (powers of 2) while the grid has fewer
+// workgroups than CUs.
+template <class T>
+BigPlan plan_tile(int M, int N, int K, bool swiglu) {
+  BigPlan p;
+  p.tiles_n = swiglu ? (N / 2 + T::BN / 2 - 1) / (T::BN / 2) : (N + T::BN - 1) / T::BN;
+  p.tiles_m = (M + T::BM - 1) / T::BM;
+  p.splits = 1;
+  while (p.tiles_n * p.tiles_m * p.splits < 256 && K % (T::BK * p.splits * 2) == 0 && K / (p.splits * 2) >= 512)
+    p.splits *= 2;
+  return p;
+}
+
+template <class T, bool SPLIT>
+hipError_t tile_epi(const GemmArgs& a, int epi, const bf16_t* xb, const BigPlan& p, hipStream_t s) {
   const dim3 grid(p.tiles_n * p.tiles_m * p.splits), blk(512);
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_big16<EPI_STORE, PD, SPLIT>), grid, blk, 0, s, a, xb, p); break;
-    case EPI_BIAS_SUMSQ: hipLaunchKernelGGL((gemm_big16<EPI_BIAS_SUMSQ, PD, SPLIT>), grid, blk, 0, s, a, xb, p); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_big16<EPI_RESID, PD, SPLIT>), grid, blk, 0, s, a, xb, p); break;
-    case EPI_RESID_SUMSQ: hipLaunchKernelGGL((gemm_big16<EPI_RESID_SUMSQ, PD, SPLIT>), grid, blk, 0, s, a, xb, p); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_big16<EPI_SWIGLU, PD, SPLIT>), grid, blk, 0, s, a, xb, p); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_tile<EPI_STORE, SPLIT, T>), grid, blk, 0, s, a, xb, p); break;
+    case EPI_BIAS_SUMSQ: hipLaunchKernelGGL((gemm_tile<EPI_BIAS_SUMSQ, SPLIT, T>), grid, blk, 0, s, a, xb, p); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_tile<EPI_RESID, SPLIT, T>), grid, blk, 0, s, a, xb, p); break;
+    case EPI_RESID_SUMSQ: hipLaunchKernelGGL((gemm_tile<EPI_RESID_SUMSQ, SPLIT, T>), grid, blk, 0, s, a, xb, p); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_tile<EPI_SWIGLU, SPLIT, T>), grid, blk, 0, s, a, xb, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1099,10 +1112,13 @@ hipError_t reduce_launch(const GemmArgs& a, int epi, int* n_part_out, hipStream_
   return hipGetLastError();
 }
 
-// Row count from which the bf16 path uses the LDS-tiled large-M kernel
-// (at M = 480 and 960 it runs 5-15% faster than the wide kernel; deeper
-// register prefetch measured no faster).
+// Row count from which the bf16 path uses the LDS-tiled large-M kernel (at
+// M = 480 and 960 it runs 5-15% faster than the wide kernel).  Its tile,
+// measured on the 13B / 70B tree-wide shapes: 256 x 256 per workgroup, 8 waves
+// of 128 weight rows x 64 activation rows, 32-wide K blocks -- 6-19% faster
+// than 256 x 128 with 64 x 64 per wave (fewer LDS fragment reads per MFMA).
 constexpr int BIG16_MIN_M = 257;
+using LargeTile = TileCfg<2, 4, 8, 4, 32>;
 
 // Launch for M > 16 on a prepared operand: the prep pass (RMSNorm row scale
 // applied, then split into hi/lo halves or rounded once to bf16), then the
@@ -1120,10 +1136,10 @@ hipError_t prepared_launch(GemmArgs a, int epi, int* n_part_out, hipStream_t s) 
   a.sumsq_in = nullptr;  // the row scale is in the prepared operand
   int splits, tiles_n;
   if (a.M >= BIG16_MIN_M) {
-    const BigPlan p = plan_big(a.M, a.N, a.K, sw);
+    const BigPlan p = plan_tile<LargeTile>(a.M, a.N, a.K, sw);
     a.splits = splits = p.splits;
     tiles_n = p.tiles_n;
-    e = big16_epi<1, SPLIT>(a, epi, xb, p, s);
+    e = tile_epi<LargeTile, SPLIT>(a, epi, xb, p, s);
   } else {
     using C = WideDefault;
     int mb;
@@ -1152,7 +1168,7 @@ size_t gemm_bf16_partial_bytes(int M, int N, int K) {
   // the prepared operand (hi and lo halves), then the partials of the K split
   int splits;
   if (M >= BIG16_MIN_M) {
-    splits = plan_big(M, N, K, false).splits;  // N/2-wide SwiGLU tiles give no more splits than this
+    splits = plan_tile<LargeTile>(M, N, K, false).splits;  // N/2-wide SwiGLU tiles give no more splits
   } else {
     int mb;
     const WidePlan w = plan_wide(M, N, K, false, WideDefault::bn, 8, &mb);
