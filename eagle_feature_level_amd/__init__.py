@@ -19,7 +19,7 @@ __all__ = ["eagle_workspace_bytes", "eagle_draft_step", "eagle_softmax_topk", "e
            "eagle_tree_finalize", "eagle_verify", "eagle_verify_workspace_bytes", "make_shape", "make_weights",
            "make_rows", "make_kv", "make_out",
            "make_pool", "EagleError", "EAGLE_HEAD_ONLY", "EAGLE_ACT_BF16", "EAGLE_SAMPLE_CHILDREN",
-           "eagle_sample_topk", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
+           "eagle_sample_topk", "eagle_fuse_features", "eagle_fuse_workspace_bytes", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
            "EAGLE_F32", "EAGLE_MAX_SLOTS", "EAGLE_MAX_TOPK", "eagle_profile_enable", "eagle_profile_reset",
            "eagle_profile_disable", "eagle_profile_read"]
 
@@ -97,6 +97,18 @@ def eagle_softmax_topk(n_rows, vocab, logits, topk, lse, topk_idx, topk_logq, wo
     rc = lib.eagle_softmax_topk(n_rows, vocab, _ptr(logits), topk, _ptr(lse), _ptr(topk_idx), _ptr(topk_logq),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _abi.check("eagle_softmax_topk", rc)
+
+
+def eagle_fuse_workspace_bytes(shape, max_rows):
+    return _abi.load().eagle_fuse_workspace_bytes(ctypes.byref(shape), max_rows)
+
+
+def eagle_fuse_features(shape, w_fuse, b_fuse, n_rows, low, mid, high, g, workspace, stream=None):
+    lib = _abi.load()
+    rc = lib.eagle_fuse_features(ctypes.byref(shape), _ptr(w_fuse), _ptr(b_fuse), n_rows, _ptr(low), _ptr(mid),
+                                 _ptr(high), _ptr(g), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream))
+    _abi.check("eagle_fuse_features", rc)
 
 
 def eagle_sample_topk(n_rows, vocab, logits, topk, seed, round_, row_base, lse, topk_idx, topk_logq, workspace,

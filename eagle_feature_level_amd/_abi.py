@@ -58,6 +58,8 @@ _SIGS = {
     "eagle_draft_step": (c_i32, [P(eagle_shape), P(eagle_weights), c_i32, P(eagle_rows), c_vp, P(eagle_kv),
                                  P(eagle_draft_out), c_vp, c_size, c_vp]),
     "eagle_softmax_topk": (c_i32, [c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "eagle_fuse_workspace_bytes": (c_size, [P(eagle_shape), c_i32]),
+    "eagle_fuse_features": (c_i32, [P(eagle_shape), c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "eagle_sample_topk": (c_i32, [c_i32, c_i32, c_vp, c_i32, c_u64, c_u64, c_i32, c_vp, c_vp, c_vp, c_vp, c_size,
                                   c_vp]),
     "eagle_tree_init": (c_i32, [c_i32, P(eagle_pool), c_vp, c_i32, c_vp]),

@@ -200,6 +200,68 @@ int eagle_softmax_topk(int32_t n_rows, int32_t vocab, const float* logits, int32
   return e == hipSuccess ? EAGLE_OK : hip_fail(e);
 }
 
+// Fusion workspace: the [l ; m ; h] rows (fp32), per-tile sums of squares of
+// the bias epilogue (unused), the GEMM's prepared operand and partials.
+struct FuseWs {
+  float* cat;
+  float* sumsq;
+  float* part;
+  size_t total;
+};
+FuseWs carve_fuse(const eagle_shape* s, int M, char* base) {
+  FuseWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return (void*)p;
+  };
+  w.cat = (float*)take((size_t)M * 3 * s->d * 4);
+  w.sumsq = (float*)take((size_t)(s->d / 16 + 2) * M * 4);
+  w.part = (float*)take(s->dtype == EAGLE_BF16 ? gemm_bf16_partial_bytes(M, s->d, 3 * s->d) : 0);
+  w.total = off;
+  return w;
+}
+
+size_t eagle_fuse_workspace_bytes(const eagle_shape* shape, int32_t max_rows) {
+  if (!shape_ok(shape) || max_rows <= 0) return 0;
+  return carve_fuse(shape, max_rows, nullptr).total;
+}
+
+int eagle_fuse_features(const eagle_shape* shape, const void* w_fuse, const void* b_fuse, int32_t n_rows,
+                        const float* low, const float* mid, const float* high, float* g, void* workspace,
+                        size_t workspace_bytes, eagle_stream_t stream) {
+  if (!shape_ok(shape) || n_rows < 0) return EAGLE_EINVAL;
+  if (n_rows == 0) return EAGLE_OK;
+  if (!w_fuse || !low || !mid || !high || !g || !workspace) return EAGLE_EINVAL;
+  int rc = shape_supported(shape);
+  if (rc) return rc;
+  const FuseWs ws = carve_fuse(shape, n_rows, (char*)workspace);
+  if (workspace_bytes < ws.total) return EAGLE_EWORKSPACE;
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int d = shape->d;
+  hipError_t e = launch_concat3(low, mid, high, n_rows, d, ws.cat, st);
+  if (e != hipSuccess) return hip_fail(e);
+  GemmArgs a = gemm_base(n_rows, d, 3 * d);
+  a.w0 = w_fuse;
+  a.x = ws.cat;
+  a.ldx = 3 * d;
+  a.y = g;
+  a.ldy = d;
+  a.part = ws.part;
+  int np = 0;
+  int epi = EPI_STORE;
+  if (b_fuse) {
+    a.bias = b_fuse;
+    a.sumsq_out = ws.sumsq;
+    epi = EPI_BIAS_SUMSQ;
+  }
+  e = shape->dtype == EAGLE_BF16 ? launch_gemm_bf16(a, epi, &np, st) : launch_gemm_f32(a, epi, &np, st);
+  return e == hipSuccess ? EAGLE_OK : hip_fail(e);
+}
+
 int eagle_sample_topk(int32_t n_rows, int32_t vocab, const float* logits, int32_t topk, uint64_t seed, uint64_t round,
                       int32_t row_base, float* lse, int32_t* topk_idx, float* topk_logq, void* workspace,
                       size_t workspace_bytes, eagle_stream_t stream) {

@@ -42,6 +42,9 @@ struct RowSetupArgs {
   float* xin;  // [n_rows, 2d]
 };
 hipError_t launch_row_setup(const RowSetupArgs& a, bool bf16, hipStream_t s);
+// out[m] = [low[m] ; mid[m] ; high[m]], fp32 rows of d values each
+hipError_t launch_concat3(const float* low, const float* mid, const float* high, int n_rows, int d, float* out,
+                          hipStream_t s);
 hipError_t launch_rope_kv(const RopeArgs& a, bool bf16, hipStream_t s);
 // Key splits of one attention call: split s covers prefix keys [s*split_len,
 // (s+1)*split_len).  bf16: the tree slots go with the last split; fp32: they

@@ -1,6 +1,7 @@
-// Row set-up of a draft step over more than 16 rows: the draft layer's input
-// [f_parent ; e(token)] as one fp32 row of 2d values (up to 16 rows the FC
-// GEMM gathers the two halves itself).
+// Row set-up of an fp32 draft step: the draft layer's input [f_parent ;
+// e(token)] as one fp32 row of 2d values (bf16 draft steps gather the two
+// halves in the FC GEMM's loader or operand prep pass instead).  Also the
+// [l ; m ; h] rows of the three-feature fusion.
 //
 // The draft head concatenates the parent's feature vector with the embedding
 // of the token sampled after it, then reduces the 2d values to d with a fully
@@ -46,7 +47,25 @@ __global__ void __launch_bounds__(256) row_setup_kernel(RowSetupArgs a) {
   }
 }
 
+// [low ; mid ; high] rows of 3d fp32 values, one workgroup per row.
+__global__ void __launch_bounds__(256) concat3_kernel(const float* __restrict__ low, const float* __restrict__ mid,
+                                                      const float* __restrict__ high, int d, float* __restrict__ out) {
+  const int m = blockIdx.x;
+  const float* src[3] = {low + (size_t)m * d, mid + (size_t)m * d, high + (size_t)m * d};
+  float* o = out + (size_t)m * 3 * d;
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+    for (int i = threadIdx.x; i < d; i += blockDim.x) o[s * d + i] = src[s][i];
+}
+
 }  // namespace
+
+hipError_t launch_concat3(const float* low, const float* mid, const float* high, int n_rows, int d, float* out,
+                          hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(concat3_kernel, dim3(n_rows), dim3(256), 0, s, low, mid, high, d, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_row_setup(const RowSetupArgs& a, bool bf16, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;

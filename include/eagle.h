@@ -199,6 +199,19 @@ int eagle_sample_topk(int32_t n_rows, int32_t vocab, const float *logits, int32_
                       int32_t row_base, float *lse, int32_t *topk_idx, float *topk_logq, void *workspace,
                       size_t workspace_bytes, eagle_stream_t stream);
 
+/* EAGLE-3 three-feature fusion: g = [l ; m ; h] w_fuse^T (+ b_fuse), the
+ * target's low-, mid- and high-layer features of one position concatenated
+ * (3d) and compressed back to d by an FC layer ("EAGLE 完全拆解", EAGLE-3
+ * part: g = FC([l; m; h]), then [g ; e(t)] enters the draft layer as the
+ * feature does in EAGLE-1/2).  w_fuse [d, 3d] and b_fuse [d] (NULL: no bias)
+ * in shape.dtype; low, mid, high, g fp32 [n_rows, d] device arrays.  The GEMM
+ * runs like the draft step's (split-bf16 operands for bf16 weights).
+ * Workspace: eagle_fuse_workspace_bytes(shape, max_rows). */
+size_t eagle_fuse_workspace_bytes(const eagle_shape *shape, int32_t max_rows);
+int eagle_fuse_features(const eagle_shape *shape, const void *w_fuse, const void *b_fuse, int32_t n_rows,
+                        const float *low, const float *mid, const float *high, float *g, void *workspace,
+                        size_t workspace_bytes, eagle_stream_t stream);
+
 /* Candidate pool of the tree builder: per sequence b, entries
  * [b*cap, (b+1)*cap) of each array; node 0 is the root. */
 typedef struct {

@@ -152,3 +152,16 @@ def draft_step(shape, w, rows: dict, feat_buf: np.ndarray, prefix_k, prefix_v, p
     if want_logits:
         out["logits"] = matmul_t(_r(feat, ra), w.lm_head)
     return out
+
+
+def fuse_features(shape, w_fuse, b_fuse, low, mid, high) -> np.ndarray:
+    """EAGLE-3 input fusion ("EAGLE 完全拆解", EAGLE-3 part): the target's low-,
+    mid- and high-layer features of a position, each d wide, concatenated to 3d
+    and compressed back to d by an FC layer, g = FC([l; m; h]) = [l; m; h] W^T
+    (+ b).  g then stands where the feature f stands in [f ; e(t)]."""
+    cat = np.concatenate([np.asarray(low, np.float64), np.asarray(mid, np.float64), np.asarray(high, np.float64)],
+                         axis=1)
+    g = matmul_t(cat, w_fuse)
+    if b_fuse is not None:
+        g = g + np.asarray(b_fuse, np.float64)
+    return g

@@ -252,3 +252,29 @@ def test_sample_topk_matches_oracle(rows, vocab, k, row_base):
     if k > 1:
         _, det, _ = o_topk(x, k)
         assert not np.array_equal(gi, det)
+
+
+@pytest.mark.parametrize("dtype,rows,bias", [("bf16", 1, True), ("bf16", 5, False), ("bf16", 40, True),
+                                             ("bf16", 300, True), ("f32", 3, True)])
+def test_fuse_features_matches_oracle(dtype, rows, bias):
+    """EAGLE-3 three-feature fusion on the GPU against the oracle: d = 4096
+    (the 7B draft head; 12288-wide fused input) through the skinny, wide and
+    large-M GEMMs, and the tiny fp32 head."""
+    shape = Shape(4096, 32, 32, 128, 11008, 32000) if dtype == "bf16" else CONFIGS[1].shape
+    d = shape.d
+    g = np.random.default_rng(rows + d)
+    w = (g.standard_normal((d, 3 * d)) * 0.02).astype(np.float32)
+    b = (g.standard_normal(d) * 0.02).astype(np.float32) if bias else None
+    if dtype == "bf16":
+        w = bf16_values(w)
+        b = bf16_values(b) if bias else None
+    low, mid, high = ((g.standard_normal((rows, d)) + 0.1 * s).astype(np.float32) for s in range(3))
+    es = E.make_shape(**dev.shape_dict(shape))
+    t = lambda a: dev.tensor(a.reshape(-1), shape.dtype)
+    out = torch.full((rows, d), float("nan"), device="cuda")
+    ws = _ws(E.eagle_fuse_workspace_bytes(es, rows))
+    E.eagle_fuse_features(es, t(w), t(b) if bias else None, rows, torch.from_numpy(low).cuda(),
+                          torch.from_numpy(mid).cuda(), torch.from_numpy(high).cuda(), out, ws)
+    torch.cuda.synchronize()
+    ref = OD.fuse_features(shape, w, b, low, mid, high)
+    assert np.max(np.abs(out.cpu().numpy() - ref)) < TOL[dtype]

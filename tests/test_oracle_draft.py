@@ -240,3 +240,27 @@ def test_bf16_mirror_rounds_only_the_kv_cache():
     assert np.array_equal(a["x"], b["x"]) and np.array_equal(a["q"], b["q"])
     # the readings differ only through the cache rounding, by a little
     assert 0 < np.max(np.abs(a["feat"] - b["feat"])) < 0.05
+
+
+def test_fuse_features_selecting_the_top_layer_is_eagle_one():
+    """With W = [0 | 0 | I] and no bias, the fused feature is the high-layer
+    feature itself: EAGLE-3's fusion reduces to EAGLE-1's single feature."""
+    d = 8
+    g = np.random.default_rng(4)
+    low, mid, high = (g.standard_normal((3, d)) for _ in range(3))
+    w = np.concatenate([np.zeros((d, d)), np.zeros((d, d)), np.eye(d)], axis=1)
+    assert np.array_equal(D.fuse_features(None, w, None, low, mid, high), high)
+
+
+def test_fuse_features_matches_scalar_loops():
+    d = 6
+    g = np.random.default_rng(5)
+    low, mid, high = (g.standard_normal((2, d)) for _ in range(3))
+    w = g.standard_normal((d, 3 * d))
+    b = g.standard_normal(d)
+    got = D.fuse_features(None, w, b, low, mid, high)
+    for r in range(2):
+        cat = list(low[r]) + list(mid[r]) + list(high[r])
+        for o in range(d):
+            want = float(b[o]) + sum(float(w[o][i]) * cat[i] for i in range(3 * d))
+            assert abs(got[r, o] - want) < 1e-12
