@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 
 from . import _abi
-from ._abi import (EAGLE_ACT_BF16, EAGLE_SAMPLE_CHILDREN, EAGLE_BF16, EAGLE_F32, EAGLE_HEAD_ONLY, EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK, EAGLE_VERIFY_GREEDY,
+from ._abi import (EAGLE_COMMIT_BAD_PATH, EAGLE_COMMIT_OVERFLOW, EAGLE_ACT_BF16, EAGLE_SAMPLE_CHILDREN, EAGLE_BF16, EAGLE_F32, EAGLE_HEAD_ONLY, EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK, EAGLE_VERIFY_GREEDY,
                    EAGLE_VERIFY_IID, EagleError, eagle_draft_out, eagle_kv, eagle_pool, eagle_rows, eagle_shape,
                    eagle_weights)
 
@@ -19,7 +19,8 @@ __all__ = ["eagle_workspace_bytes", "eagle_draft_step", "eagle_softmax_topk", "e
            "eagle_tree_finalize", "eagle_verify", "eagle_verify_workspace_bytes", "make_shape", "make_weights",
            "make_rows", "make_kv", "make_out",
            "make_pool", "EagleError", "EAGLE_HEAD_ONLY", "EAGLE_ACT_BF16", "EAGLE_SAMPLE_CHILDREN",
-           "eagle_sample_topk", "eagle_fuse_features", "eagle_fuse_workspace_bytes", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
+           "eagle_sample_topk", "eagle_fuse_features", "eagle_fuse_workspace_bytes", "eagle_commit",
+           "EAGLE_COMMIT_OVERFLOW", "EAGLE_COMMIT_BAD_PATH", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
            "EAGLE_F32", "EAGLE_MAX_SLOTS", "EAGLE_MAX_TOPK", "eagle_profile_enable", "eagle_profile_reset",
            "eagle_profile_disable", "eagle_profile_read"]
 
@@ -64,9 +65,10 @@ def make_rows(n_rows, batch, max_rows_per_seq, row_start, token, parent, pos=Non
                             _ptr(slot), _ptr(mask)), row_start, token, parent, pos, slot, mask)
 
 
-def make_kv(prefix_k, prefix_v, prefix_off, prefix_len, max_prefix_len, tree_k, tree_v):
+def make_kv(prefix_k, prefix_v, prefix_off, prefix_len, max_prefix_len, tree_k, tree_v, prefix_cap=None):
     return _keep(eagle_kv(_ptr(prefix_k), _ptr(prefix_v), _ptr(prefix_off), _ptr(prefix_len), max_prefix_len,
-                          _ptr(tree_k), _ptr(tree_v)), prefix_k, prefix_v, prefix_off, prefix_len, tree_k, tree_v)
+                          _ptr(tree_k), _ptr(tree_v), _ptr(prefix_cap)), prefix_k, prefix_v, prefix_off, prefix_len,
+                 tree_k, tree_v, prefix_cap)
 
 
 def make_out(feat, logits, lse, topk, topk_idx, topk_logq, seed=0, round_=0, row_base=0):
@@ -97,6 +99,15 @@ def eagle_softmax_topk(n_rows, vocab, logits, topk, lse, topk_idx, topk_logq, wo
     rc = lib.eagle_softmax_topk(n_rows, vocab, _ptr(logits), topk, _ptr(lse), _ptr(topk_idx), _ptr(topk_logq),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _abi.check("eagle_softmax_topk", rc)
+
+
+def eagle_commit(shape, batch, n_nodes, path, accept_len, node_slot, tree_k, tree_v, prefix_k, prefix_v, prefix_off,
+                 prefix_len, prefix_cap, out_flags, stream=None):
+    lib = _abi.load()
+    rc = lib.eagle_commit(ctypes.byref(shape), batch, n_nodes, _ptr(path), _ptr(accept_len), _ptr(node_slot),
+                          _ptr(tree_k), _ptr(tree_v), _ptr(prefix_k), _ptr(prefix_v), _ptr(prefix_off),
+                          _ptr(prefix_len), _ptr(prefix_cap), _ptr(out_flags), _stream(stream))
+    _abi.check("eagle_commit", rc)
 
 
 def eagle_fuse_workspace_bytes(shape, max_rows):

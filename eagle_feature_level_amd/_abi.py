@@ -19,6 +19,7 @@ EAGLE_F32, EAGLE_BF16 = 0, 1
 EAGLE_HEAD_ONLY, EAGLE_ACT_BF16, EAGLE_SAMPLE_CHILDREN = 1, 2, 4
 EAGLE_VERIFY_GREEDY, EAGLE_VERIFY_IID = 1, 2
 EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK = 64, 16
+EAGLE_COMMIT_OVERFLOW, EAGLE_COMMIT_BAD_PATH = 1, 2
 ROLES = ("fc", "qkv", "rope", "attn", "o", "gate_up", "down", "lm_head", "topk", "rows")
 
 
@@ -39,7 +40,7 @@ class eagle_rows(ctypes.Structure):
 
 class eagle_kv(ctypes.Structure):
     _fields_ = [("prefix_k", c_vp), ("prefix_v", c_vp), ("prefix_off", c_vp), ("prefix_len", c_vp),
-                ("max_prefix_len", c_i32), ("tree_k", c_vp), ("tree_v", c_vp)]
+                ("max_prefix_len", c_i32), ("tree_k", c_vp), ("tree_v", c_vp), ("prefix_cap", c_vp)]
 
 
 class eagle_draft_out(ctypes.Structure):
@@ -60,6 +61,8 @@ _SIGS = {
     "eagle_softmax_topk": (c_i32, [c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "eagle_fuse_workspace_bytes": (c_size, [P(eagle_shape), c_i32]),
     "eagle_fuse_features": (c_i32, [P(eagle_shape), c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "eagle_commit": (c_i32, [P(eagle_shape), c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                             c_vp, c_vp, c_vp]),
     "eagle_sample_topk": (c_i32, [c_i32, c_i32, c_vp, c_i32, c_u64, c_u64, c_i32, c_vp, c_vp, c_vp, c_vp, c_size,
                                   c_vp]),
     "eagle_tree_init": (c_i32, [c_i32, P(eagle_pool), c_vp, c_i32, c_vp]),

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libeagle.so")
 
-SOURCES = ["gemm.hip", "rows.hip", "attention.hip", "topk.hip", "tree.hip", "verify.hip", "capi.cpp"]
+SOURCES = ["gemm.hip", "rows.hip", "attention.hip", "topk.hip", "tree.hip", "verify.hip", "commit.hip", "capi.cpp"]
 
 # Packed-fp32 instructions stay off: ordinary fp32 code is compiled to scalar
 # VALU ops only.

@@ -139,8 +139,9 @@ __global__ void __launch_bounds__(256) attn_partial_kernel(AttnArgs a) {
   const bool do_tree = (s == a.n_splits - 1);
   const int kbeg = do_tree ? 0 : s * a.split_len;
   const int kend = do_tree ? 0 : min(L, kbeg + a.split_len);
-  const T* pk = (const T*)a.prefix_k + a.prefix_off[b] + (size_t)g * L * HD;
-  const T* pv = (const T*)a.prefix_v + a.prefix_off[b] + (size_t)g * L * HD;
+  const int C = a.prefix_cap ? a.prefix_cap[b] : L;  // per-head stride
+  const T* pk = (const T*)a.prefix_k + a.prefix_off[b] + (size_t)g * C * HD;
+  const T* pv = (const T*)a.prefix_v + a.prefix_off[b] + (size_t)g * C * HD;
   const T* tk = (const T*)a.tree_k + ((size_t)b * 64 * a.hkv + g) * HD;  // slot stride hkv*HD
   const T* tv = (const T*)a.tree_v + ((size_t)b * 64 * a.hkv + g) * HD;
   const float scale = rsqrtf((float)HD);
@@ -395,8 +396,9 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a) {
   const bool with_tree = (s == a.n_splits - 1);
   const int n_prefix_tiles = (kend > kbeg) ? (kend - kbeg + KT - 1) / KT : 0;
   const int n_tiles = n_prefix_tiles + (with_tree ? 1 : 0);
-  const bf16_t* pk = (const bf16_t*)a.prefix_k + a.prefix_off[b] + (size_t)g * L * 128;
-  const bf16_t* pv = (const bf16_t*)a.prefix_v + a.prefix_off[b] + (size_t)g * L * 128;
+  const int C = a.prefix_cap ? a.prefix_cap[b] : L;  // per-head stride
+  const bf16_t* pk = (const bf16_t*)a.prefix_k + a.prefix_off[b] + (size_t)g * C * 128;
+  const bf16_t* pv = (const bf16_t*)a.prefix_v + a.prefix_off[b] + (size_t)g * C * 128;
   const bf16_t* tk = (const bf16_t*)a.tree_k + ((size_t)b * 64 * a.hkv + g) * 128;  // slot stride hkv*128
   const bf16_t* tv = (const bf16_t*)a.tree_v + ((size_t)b * 64 * a.hkv + g) * 128;
 

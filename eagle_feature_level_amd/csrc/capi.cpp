@@ -262,6 +262,40 @@ int eagle_fuse_features(const eagle_shape* shape, const void* w_fuse, const void
   return e == hipSuccess ? EAGLE_OK : hip_fail(e);
 }
 
+static_assert(kCommitOverflow == EAGLE_COMMIT_OVERFLOW && kCommitBadPath == EAGLE_COMMIT_BAD_PATH, "commit flags");
+
+int eagle_commit(const eagle_shape* shape, int32_t batch, int32_t n_nodes, const int32_t* path,
+                 const int32_t* accept_len, const int32_t* node_slot, const void* tree_k, const void* tree_v,
+                 void* prefix_k, void* prefix_v, const int64_t* prefix_off, int32_t* prefix_len,
+                 const int32_t* prefix_cap, int32_t* out_flags, eagle_stream_t stream) {
+  if (!shape_ok(shape) || batch < 0 || n_nodes < 1) return EAGLE_EINVAL;
+  if (batch == 0) return EAGLE_OK;
+  if (!path || !accept_len || !tree_k || !tree_v || !prefix_k || !prefix_v || !prefix_off || !prefix_len ||
+      !out_flags)
+    return EAGLE_EINVAL;
+  if (n_nodes > EAGLE_MAX_SLOTS) return EAGLE_EUNSUPPORTED;
+  int rc = check_device();
+  if (rc) return rc;
+  CommitArgs a;
+  a.batch = batch;
+  a.n_nodes = n_nodes;
+  a.hkv = shape->n_kv_heads;
+  a.hd = shape->head_dim;
+  a.path = path;
+  a.accept_len = accept_len;
+  a.node_slot = node_slot;
+  a.tree_k = tree_k;
+  a.tree_v = tree_v;
+  a.prefix_k = prefix_k;
+  a.prefix_v = prefix_v;
+  a.prefix_off = prefix_off;
+  a.prefix_len = prefix_len;
+  a.prefix_cap = prefix_cap;
+  a.out_flags = out_flags;
+  hipError_t e = launch_commit(a, shape->dtype == EAGLE_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? EAGLE_OK : hip_fail(e);
+}
+
 int eagle_sample_topk(int32_t n_rows, int32_t vocab, const float* logits, int32_t topk, uint64_t seed, uint64_t round,
                       int32_t row_base, float* lse, int32_t* topk_idx, float* topk_logq, void* workspace,
                       size_t workspace_bytes, eagle_stream_t stream) {
@@ -426,6 +460,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       at.prefix_v = kv->prefix_v;
       at.prefix_off = kv->prefix_off;
       at.prefix_len = kv->prefix_len;
+      at.prefix_cap = kv->prefix_cap;
       at.tree_k = kv->tree_k;
       at.tree_v = kv->tree_v;
       at.part = ws.attn_part;

@@ -24,6 +24,7 @@ struct AttnArgs {
   const void* prefix_v;
   const int64_t* prefix_off;
   const int32_t* prefix_len;
+  const int32_t* prefix_cap;  // per-head stride in positions, or nullptr: L_b
   const void* tree_k;
   const void* tree_v;
   float* part;  // [n_splits, n_rows, hq, hd + 2]
@@ -126,3 +127,21 @@ struct VerifyArgs {
 };
 size_t verify_workspace_bytes(int batch, int n_nodes);
 hipError_t launch_verify(VerifyArgs a, void* ws, hipStream_t s);
+
+// accepted-path commit of the draft KV cache
+constexpr int kCommitOverflow = 1, kCommitBadPath = 2;  // = EAGLE_COMMIT_OVERFLOW / _BAD_PATH
+struct CommitArgs {
+  int batch, n_nodes, hkv, hd;
+  const int32_t* path;        // [batch, n_nodes]: accepted drafted nodes, -1 padded
+  const int32_t* accept_len;  // [batch]: accepted nodes + 1
+  const int32_t* node_slot;   // [batch, n_nodes] tree slot of each node, or nullptr: slot = node
+  const void* tree_k;
+  const void* tree_v;
+  void* prefix_k;
+  void* prefix_v;
+  const int64_t* prefix_off;
+  int32_t* prefix_len;
+  const int32_t* prefix_cap;  // or nullptr: capacity = length (no room)
+  int32_t* out_flags;
+};
+hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t s);

@@ -16,7 +16,7 @@ import dataclasses
 
 import torch
 
-from . import (EAGLE_ACT_BF16, EAGLE_HEAD_ONLY, EAGLE_SAMPLE_CHILDREN, eagle_draft_step, eagle_tree_expand, eagle_tree_finalize, eagle_tree_init,
+from . import (EAGLE_ACT_BF16, EAGLE_HEAD_ONLY, EAGLE_SAMPLE_CHILDREN, eagle_commit, eagle_draft_step, eagle_tree_expand, eagle_tree_finalize, eagle_tree_init,
                eagle_verify, eagle_verify_workspace_bytes, eagle_workspace_bytes, make_kv, make_out, make_pool,
                make_rows, make_shape, make_weights)
 
@@ -38,7 +38,8 @@ class EagleRound:
     def __init__(self, shape: dict, weights: dict, batch: int, kind: str, k: int, depth: int, m: int = 0,
                  template=None, prefix=None, device="cuda", act_bf16=False):
         """shape: d, n_heads, n_kv_heads, head_dim, ffn, vocab, rms_eps, rope_theta, dtype.
-        weights: name -> device tensor.  prefix: dict(k, v, off, len, max_len) device tensors.
+        weights: name -> device tensor.  prefix: dict(k, v, off, len, max_len[, cap]) device tensors (cap:
+        per-sequence capacity of each kv head's positions, needed by commit(); max_len must cover it).
         act_bf16: False (default: split-bf16 operands, within 2e-2 of the fp64
         oracle at every workload), True (EAGLE_ACT_BF16 on every draft step of a
         bf16 workload), or "auto" (EAGLE_ACT_BF16 on steps over more than
@@ -126,9 +127,10 @@ class EagleRound:
         self.tw_tree_v = torch.zeros_like(self.tree_v)
         self.prefix = prefix
         self.kv = make_kv(prefix["k"], prefix["v"], prefix["off"], prefix["len"], prefix["max_len"], self.tree_k,
-                          self.tree_v)
+                          self.tree_v, prefix.get("cap"))
         self.tw_kv = make_kv(prefix["k"], prefix["v"], prefix["off"], prefix["len"], prefix["max_len"],
-                             self.tw_tree_k, self.tw_tree_v)
+                             self.tw_tree_k, self.tw_tree_v, prefix.get("cap"))
+        self.c_flags = torch.zeros(B, dtype=torch.int32, device=device)
         max_rows = max([B] + [B * n for n in ns] + [nw])
         ws = max(eagle_workspace_bytes(self.shape, max_rows, B, prefix["max_len"]),
                  eagle_verify_workspace_bytes(B, self.n_nodes))
@@ -220,6 +222,15 @@ class EagleRound:
         eagle_verify(self.B, self.n_nodes, self.shape_d["vocab"], t["parent"], t["token"], target_logits,
                      self.logits, t["qrow"], seed, round_, flags, self.v_path, self.v_len, self.v_next, self.v_flags,
                      workspace=self.workspace)
+
+    def commit(self):
+        """Append each sequence's verified path (this round's verify) to its
+        prefix KV cache: the accepted drafted nodes' k, v from the tree-wide
+        step's slots (slot = tree node), then the prefix lengths grow in place
+        (eagle_commit).  Needs prefix capacity; per-sequence status in c_flags."""
+        p = self.prefix
+        eagle_commit(self.shape, self.B, self.n_nodes, self.v_path, self.v_len, None, self.tw_tree_k, self.tw_tree_v,
+                     p["k"], p["v"], p["off"], p["len"], p.get("cap"), self.c_flags)
 
     # ------------------------------------------------------------ HIP graph
     def capture_round(self, root_feat: torch.Tensor, root_token: torch.Tensor, target_logits: torch.Tensor,

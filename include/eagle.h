@@ -97,15 +97,18 @@ typedef struct {
   const uint64_t *mask;     /* tree slots visible to the row: ancestors + self */
 } eagle_rows;
 
-/* Draft-layer KV.  Prefix K (already rotated) and V are packed per sequence
- * as [Hkv][L_b][hd] starting at element prefix_off[b].  Tree slots hold the
- * k, v of drafted nodes: [batch][64][Hkv][hd].  Element type = shape.dtype. */
+/* Draft-layer KV.  Prefix K (already rotated) and V are stored per sequence
+ * as [Hkv][C_b][hd] starting at element prefix_off[b], positions 0..L_b-1 of
+ * each kv head used; C_b = prefix_cap[b] (room for eagle_commit to append), or
+ * C_b = L_b when prefix_cap is NULL (packed).  Tree slots hold the k, v of
+ * drafted nodes: [batch][64][Hkv][hd].  Element type = shape.dtype. */
 typedef struct {
   const void *prefix_k, *prefix_v;
-  const int64_t *prefix_off; /* [batch] element offsets         */
-  const int32_t *prefix_len; /* [batch] L_b >= 0                */
-  int32_t max_prefix_len;    /* host: max over b of L_b          */
-  void *tree_k, *tree_v;     /* written: the rows' slots         */
+  const int64_t *prefix_off; /* [batch] element offsets                        */
+  const int32_t *prefix_len; /* [batch] L_b >= 0                               */
+  int32_t max_prefix_len;    /* host: max over b of L_b (an upper bound is fine) */
+  void *tree_k, *tree_v;     /* written: the rows' slots                        */
+  const int32_t *prefix_cap; /* [batch] C_b >= L_b, or NULL (C_b = L_b)         */
 } eagle_kv;
 
 /* Outputs of a draft step. */
@@ -310,6 +313,26 @@ int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t *t
                  const float *target_logits, const float *draft_logits, const int32_t *draft_row, uint64_t seed,
                  uint64_t round, int32_t flags, int32_t *out_path, int32_t *out_accept_len, int32_t *out_next_token,
                  int32_t *out_flags, void *workspace, size_t workspace_bytes, eagle_stream_t stream);
+
+/* Accepted-path commit of the draft layer's KV cache ("eagle feature-level
+ * speculative decoding", KV commit as a transaction: only the accepted path
+ * enters the cache, rejected branches are dropped).  For each sequence b with
+ * A = accept_len[b] - 1 accepted drafted nodes (out_path / out_accept_len of
+ * eagle_verify): node path[b*n_nodes + j], j < A, has its k, v in tree slot
+ * node_slot[b*n_nodes + node] (node_slot NULL: slot = node, the tree-wide
+ * step's layout) of tree_k/tree_v [batch][64][Hkv][hd]; it is copied to
+ * prefix position prefix_len[b] + j of every kv head (layout of eagle_kv with
+ * capacity prefix_cap[b]; NULL = no room), then prefix_len[b] += A.
+ * out_flags[b] (written): 0, EAGLE_COMMIT_OVERFLOW (L_b + A > capacity: nothing
+ * copied, length unchanged) or EAGLE_COMMIT_BAD_PATH (a node or slot index out
+ * of range: nothing done).  Element type = shape->dtype.  Device arrays,
+ * caller-owned; asynchronous on `stream`.  A later draft step must be given a
+ * max_prefix_len that covers the grown lengths (e.g. the capacities). */
+enum { EAGLE_COMMIT_OVERFLOW = 1, EAGLE_COMMIT_BAD_PATH = 2 };
+int eagle_commit(const eagle_shape *shape, int32_t batch, int32_t n_nodes, const int32_t *path,
+                 const int32_t *accept_len, const int32_t *node_slot, const void *tree_k, const void *tree_v,
+                 void *prefix_k, void *prefix_v, const int64_t *prefix_off, int32_t *prefix_len,
+                 const int32_t *prefix_cap, int32_t *out_flags, eagle_stream_t stream);
 
 /* Bytes of workspace eagle_verify uses for batch x n_nodes trees (12 per node
  * plus alignment); 0 for an invalid size. */

@@ -225,3 +225,72 @@ def test_sampled_round_7b_static26_staged():
             _, det, _ = o_topk(logits[qrow[u]:qrow[u] + 1], len(kids))
             differs |= list(det[0]) != [int(token[i]) for i in kids]
     assert differs  # sampled, not the deterministic top-k
+
+
+def test_commit_then_next_round_7b():
+    """Two rounds on the 7B static-26 workload with the accepted path
+    committed in between: the prefix cache after eagle_commit equals the
+    oracle's commit of the GPU's own tree K/V and verified path bit for bit
+    (room past the new length untouched), and the next round's first draft
+    step, attending to the grown prefix at the new positions, matches the
+    oracle within 2e-2."""
+    from oracle.commit import commit as o_commit
+    cfg = CONFIGS[2]
+    s = cfg.shape
+    w = make_weights(cfg)
+    lens = make_prefix_lens(cfg)
+    ks, vs = make_prefix_kv(cfg, lens)
+    extra = 16
+    pf = dev.prefix(ks, vs, lens, s.dtype, extra=extra)
+    eng = EagleRound(dev.shape_dict(s), dev.weights(w, s.dtype), cfg.batch, "static", cfg.topk, cfg.depth, 0,
+                     TEMPLATES[cfg.tree], pf)
+    feat = make_root_features(cfg)
+    tok = make_root_tokens(cfg)
+    eng.draft_phase(torch.from_numpy(feat).cuda(), dev.ints(tok))
+    eng.tree_wide()
+    N, B = eng.n_nodes, cfg.batch
+    tgt = torch.cat([eng.logits[0:1], eng.tw_logits + 0.25]).contiguous()  # a shifted target: some accepted
+    eng.verify(tgt, 0, 2)
+    torch.cuda.synchronize()
+    path = eng.v_path.cpu().numpy().reshape(B, N)
+    alen = eng.v_len.cpu().numpy()
+    ttk = eng.tw_tree_k.float().cpu().numpy().astype(np.float64)
+    ttv = eng.tw_tree_v.float().cpu().numpy().astype(np.float64)
+    eng.commit()
+    torch.cuda.synchronize()
+    want_k, want_v, want_len, want_flags = o_commit([k.astype(np.float64) for k in ks],
+                                                    [v.astype(np.float64) for v in vs], lens, lens + extra, ttk, ttv,
+                                                    [list(p) for p in path], alen)
+    assert list(eng.c_flags.cpu().numpy()) == want_flags == [0] * B
+    assert list(pf["len"].cpu().numpy()) == want_len
+    H, hd = s.n_kv_heads, s.head_dim
+    gk = pf["k"].float().cpu().numpy()
+    gv = pf["v"].float().cpu().numpy()
+    off = pf["off"].cpu().numpy()
+    for b in range(B):
+        C = int(lens[b]) + extra
+        blk_k = gk[off[b]:off[b] + H * C * hd].reshape(H, C, hd)
+        blk_v = gv[off[b]:off[b] + H * C * hd].reshape(H, C, hd)
+        Ln = want_len[b]
+        assert np.array_equal(blk_k[:, :Ln], want_k[b]) and np.array_equal(blk_v[:, :Ln], want_v[b])
+        assert not blk_k[:, Ln:].any() and not blk_v[:, Ln:].any()  # room past the new length untouched
+    assert want_len[0] > lens[0]  # something was accepted and appended
+    # next round: root token = the round's next token, root feature = the last accepted node's predicted
+    # feature (the stand-in for the target's true feature at that position)
+    last = int(path[0, alen[0] - 2])
+    feat2 = eng.tw_feat[last - 1:last].clone()
+    tok2 = eng.v_next.clone()
+    eng.draft_phase(feat2, tok2)
+    torch.cuda.synchronize()
+    st = eng.steps[0]
+    n = B * st.n_next
+    rows = dict(seq=[0] * n, token=st.token.cpu().numpy().astype(np.int64),
+                parent=st.parent.cpu().numpy().astype(np.int64), pos=st.pos.cpu().numpy().astype(np.int64),
+                slot=st.slot.cpu().numpy().astype(np.int64), mask=st.mask.cpu().numpy().view(np.uint64))
+    assert all(int(p_) == want_len[0] for p_ in rows["pos"])  # depth-1 rows sit right after the grown prefix
+    tk, tv = OD.new_tree_kv(s, B)
+    ref = OD.draft_step(s, w, rows, eng.feat.cpu().numpy().astype(np.float64), want_k, want_v, want_len, tk, tv,
+                        mirror=True)
+    got_f = eng.feat[st.feat_row0:st.feat_row0 + n].cpu().numpy()
+    got_l = eng.logits[st.feat_row0:st.feat_row0 + n].cpu().numpy()
+    assert np.max(np.abs(got_f - ref["feat"])) < 2e-2 and np.max(np.abs(got_l - ref["logits"])) < 2e-2

@@ -195,3 +195,31 @@ def test_gumbel_uniforms_are_inside_the_open_interval():
     assert 0.0 < u < 1.0
     key = gumbel_keys(np.zeros(8, np.float32), 5, 9, 11)
     assert abs(float(key[6]) - (-np.log(-np.log(u)))) < 1e-5
+
+
+def test_commit_special_cases():
+    """Accepted-path commit: a fully accepted chain appends its slots in order,
+    nothing accepted changes nothing, capacity and malformed paths are flagged
+    and leave the prefix as it was."""
+    from oracle.commit import BAD_PATH, OVERFLOW, commit
+
+    g = np.random.default_rng(2)
+    H, hd, L = 2, 4, 3
+    pk = [g.standard_normal((H, L, hd)), g.standard_normal((H, L, hd))]
+    pv = [g.standard_normal((H, L, hd)), g.standard_normal((H, L, hd))]
+    tk, tv = g.standard_normal((2, 64, H, hd)), g.standard_normal((2, 64, H, hd))
+    paths = [[1, 2, 3, -1, -1], [-1, -1, -1, -1, -1]]
+    k2, v2, lens, flags = commit(pk, pv, [L, L], [L + 4, L + 4], tk, tv, paths, [4, 1])
+    assert lens == [L + 3, L] and flags == [0, 0]
+    assert np.array_equal(k2[0][:, :L], pk[0]) and np.array_equal(k2[1], pk[1])
+    for j in range(3):
+        assert np.array_equal(k2[0][:, L + j], tk[0, 1 + j]) and np.array_equal(v2[0][:, L + j], tv[0, 1 + j])
+    # explicit slots: node n lives in slot 10 + n
+    slots = [[10 + n for n in range(5)]] * 2
+    k3, _, _, _ = commit(pk, pv, [L, L], [L + 4, L + 4], tk, tv, [[2, 4, -1, -1, -1]] * 2, [3, 3], slots)
+    assert np.array_equal(k3[1][:, L], tk[1, 12]) and np.array_equal(k3[1][:, L + 1], tk[1, 14])
+    # no room; then a node index out of range
+    _, _, lens, flags = commit(pk, pv, [L, L], None, tk, tv, [[1, 2, 3, -1, -1], [1, -1, -1, -1, -1]], [4, 2])
+    assert flags == [OVERFLOW, OVERFLOW] and lens == [L, L]
+    _, _, lens, flags = commit(pk, pv, [L, L], [9, 9], tk, tv, [[1, 7, -1, -1, -1]] * 2, [3, 3])
+    assert flags == [BAD_PATH, BAD_PATH] and lens == [L, L]

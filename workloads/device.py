@@ -24,17 +24,30 @@ def shape_dict(s: Shape) -> dict:
                 rms_eps=s.rms_eps, rope_theta=s.rope_theta, dtype=s.dtype)
 
 
-def prefix(ks, vs, lens, dtype: str, device="cuda") -> dict:
-    """Pack per-sequence [Hkv, L, hd] K and V contiguously; offsets in elements."""
-    offs, o = [], 0
-    for k in ks:
+def prefix(ks, vs, lens, dtype: str, device="cuda", extra: int = 0) -> dict:
+    """Per-sequence [Hkv, L, hd] K and V in one buffer, offsets in elements.
+    extra = 0: packed [Hkv][L][hd].  extra > 0: each kv head gets room for
+    `extra` more positions, [Hkv][L + extra][hd] (zero-filled), and the dict
+    carries the capacities ("cap") and max_len = the largest capacity."""
+    offs, o, parts_k, parts_v = [], 0, [], []
+    for k, v in zip(ks, vs):
+        H, L, hd = k.shape
         offs.append(o)
-        o += k.size
-    flat_k = np.concatenate([k.reshape(-1) for k in ks]) if o else np.zeros(8, np.float32)
-    flat_v = np.concatenate([v.reshape(-1) for v in vs]) if o else np.zeros(8, np.float32)
-    return dict(k=tensor(flat_k, dtype, device), v=tensor(flat_v, dtype, device),
-                off=torch.tensor(offs, dtype=torch.int64, device=device),
-                len=torch.tensor(np.asarray(lens, dtype=np.int32), device=device), max_len=int(max(lens)) if len(lens) else 0)
+        pk = np.zeros((H, L + extra, hd), np.float32)
+        pv = np.zeros((H, L + extra, hd), np.float32)
+        pk[:, :L], pv[:, :L] = k, v
+        parts_k.append(pk.reshape(-1))
+        parts_v.append(pv.reshape(-1))
+        o += pk.size
+    flat_k = np.concatenate(parts_k) if o else np.zeros(8, np.float32)
+    flat_v = np.concatenate(parts_v) if o else np.zeros(8, np.float32)
+    lens = np.asarray(lens, dtype=np.int32)
+    out = dict(k=tensor(flat_k, dtype, device), v=tensor(flat_v, dtype, device),
+               off=torch.tensor(offs, dtype=torch.int64, device=device),
+               len=torch.tensor(lens, device=device), max_len=int(lens.max() + extra) if len(lens) else 0)
+    if extra:
+        out["cap"] = torch.tensor(lens + extra, dtype=torch.int32, device=device)
+    return out
 
 
 def ints(a, device="cuda", dtype=torch.int32) -> torch.Tensor:
