@@ -625,13 +625,18 @@ static AttnPlan plan_scalar(int max_prefix, int batch, int hkv) {
   return AttnPlan{split_len, (max_prefix + split_len - 1) / split_len + 1};
 }
 
-// bf16 matrix-core kernel: splits of whole tiles aiming at ~1024 workgroups
-// counting the query blocks; the tree slots ride with the last split.
+// bf16 matrix-core kernel: splits of whole tiles; the tree slots ride with
+// the last split.  Aim: ~256 workgroups when fewer than 256 (sequence, kv head,
+// query block) units exist, else ~1024.  Measured on the 7B shapes (32 units):
+// 256 workgroups of 2-4 tiles beat 1024 of one tile by 10-43 % (each workgroup
+// pays its set-up, and the split partials must be combined); at 256-1024 units
+// (13B / 70B batched) the ~1024 target was within a few % of the best plan.
 static AttnPlan plan_mfma(int max_prefix, int batch, int hkv, int max_queries) {
   const long qblocks = (max_queries + AQ - 1) / AQ;
   const long per = (long)batch * hkv * (qblocks > 0 ? qblocks : 1);
   const int tiles = (max_prefix + KT - 1) / KT;
-  int splits = (int)((1024 + per - 1) / per);
+  const long target = per < 256 ? 256 : 1024;
+  int splits = (int)((target + per - 1) / per);
   if (splits > tiles) splits = tiles;
   if (splits < 1) splits = 1;
   const int tiles_per = (tiles + splits - 1) / splits;

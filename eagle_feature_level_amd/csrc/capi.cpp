@@ -118,8 +118,16 @@ DraftWs carve(const eagle_shape* s, int M, int B, int max_prefix, char* base) {
   const int hq = s->n_heads * s->head_dim, hkv = s->n_kv_heads * s->head_dim;
   const int nqkv = hq + 2 * hkv;
   const int npart = s->d / 16 + 2;  // >= partial tiles of any GEMM producing a d-wide output
-  // most splits an attention call can use: one query block per (sequence, kv head)
-  const int nsplit = attn_plan(s->dtype == EAGLE_BF16, max_prefix, B, s->n_kv_heads, 1).n_splits;
+  // most splits an attention call over at most M rows can use: the plan
+  // depends on the query blocks per (sequence, kv head), so take the largest
+  // over every block count a call could have (64 queries per block)
+  int nsplit = 1;
+  const int max_q = M * (s->n_heads / s->n_kv_heads);
+  for (int q = 1;; q += 64) {
+    const int n = attn_plan(s->dtype == EAGLE_BF16, max_prefix, B, s->n_kv_heads, q).n_splits;
+    if (n > nsplit) nsplit = n;
+    if (q >= max_q) break;
+  }
   size_t gp = 0;
   if (s->dtype == EAGLE_BF16) {
     const int Ns[6] = {s->d, nqkv, s->d, 2 * s->ffn, s->d, s->vocab};
