@@ -169,6 +169,43 @@ def traffic_for(kernel_role: str, config_name: str):
                  r["write_kib_per_dispatch"] * 1024 * c["write_factor"])
 
 
+def round_bench(cid: int, steps: int, warmup: int) -> dict:
+    """One full round (draft phase + verify) of workload `cid`, replayed as a
+    HIP graph `steps` times after `warmup` replays; draft / verify split from
+    as many eager rounds with events between the phases."""
+    import torch
+    cfg, eng, feat, tok, _ = build_engine(cid)
+    B, N = cfg.batch, eng.n_nodes
+    eng.draft_phase(feat, tok)
+    tgt = synth_target(cfg, eng)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    run_steps(eng, feat, tok, tgt, warmup)
+    run_steps(eng, feat, tok, tgt, steps, marks)
+    torch.cuda.synchronize()
+    ms_draft = sum(m[0].elapsed_time(m[1]) for m in marks) / steps
+    ms_verify = sum(m[1].elapsed_time(m[2]) for m in marks) / steps
+    eng.capture_round(feat, tok, tgt, 0, 0)
+    for _ in range(warmup):
+        eng.replay_round()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        eng.replay_round()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    s = cfg.shape
+    out = {"workload": cfg.name, "batch": B, "drafted_nodes_per_seq": N - 1, "d": s.d, "vocab": s.vocab,
+           "value": round(B * (N - 1) / (ms * 1e-3), 1), "unit": "draft-tree nodes/s", "ms_per_round": round(ms, 4),
+           "ms_draft_phase_eager": round(ms_draft, 4), "ms_verify_eager": round(ms_verify, 4),
+           "draft_nodes_per_s": round(B * (N - 1) / (ms_draft * 1e-3), 1),
+           "verify_nodes_per_s": round(B * N / (ms_verify * 1e-3), 1)}
+    del eng, tgt
+    torch.cuda.empty_cache()
+    return out
+
+
 def tree_wide_bench(args, cfg, eng, feat, tok):
     """K tree-wide draft steps (B x (N-1) rows in one eagle_draft_step) after one
     draft phase built the tree; per-role time, TFLOP/s and fraction of the
@@ -227,6 +264,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = 7B static-26, the bench line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the full-round measurements of the other workloads (7B EAGLE-2, 13B, 70B)")
     ap.add_argument("--tree-wide", action="store_true",
                     help="time only the tree-wide draft step (every drafted node of the flattened tree in one call: "
                          "the matrix-unit bound shape at batch 8 / 16) and print its own JSON line")
@@ -325,6 +364,14 @@ def main():
     g_ms = sum(kernels[r]["ms_per_step"] for r in gemm_roles if r in kernels)
     g_bytes = sum(kernels[r]["bytes_per_launch"] * kernels[r]["launches_per_step"] for r in gemm_roles if r in kernels)
 
+    others = []
+    if not args.headline_only and args.config == 2:
+        del eng, tgt
+        torch.cuda.empty_cache()
+        for cid in (3, 4, 5):
+            log(f"[bench] full round of workload {cid} ...")
+            others.append(round_bench(cid, 10, 2))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on one round ...")
@@ -360,6 +407,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "roofline": roofline,
+        "other_workloads": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
