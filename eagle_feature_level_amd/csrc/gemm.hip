@@ -383,7 +383,7 @@ struct BigPlan {
 constexpr int WD_XLD = SK_KSTEP + 8;  // LDS row of the activation tile (bf16): 272 B, rows 4 banks apart
 
 struct WidePlan {
-  int tiles_n, tiles_m, splits, ks_per_split;
+  int tiles_n, tiles_m, splits;  // K split sp covers k-steps [sp*nks/splits, (sp+1)*nks/splits)
 };
 
 template <int NW, int AT, int MB, int NS, bool SPLIT, int EPI>
@@ -401,8 +401,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int nks_all = a.K / SK_KSTEP;
-  const int ks0 = sp * p.ks_per_split;
-  const int nks = max(0, min(nks_all - ks0, p.ks_per_split));
+  const int ks0 = sp * nks_all / p.splits;
+  const int nks = (sp + 1) * nks_all / p.splits - ks0;
 
   const int wtile = nt * NW + wv;  // this wave's tile of 16*AT weight rows
   const bf16_t* ap[AT];
@@ -993,8 +993,10 @@ hipError_t skinny_mq(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
 //  * wide N with M > 8: four tiles x 4 waves -- each activation chunk then
 //    feeds four weight tiles, which matters once x is as large as the weights
 //    a wave streams per step;
-//  * wide N, M <= 3, >= 1536 tiles (the LM head): one tile x 8 waves (two
-//    workgroups per CU, ~4 full rounds of workgroups); else one tile x 4 waves.
+//  * the LM head (>= 1536 tiles, no input norm), M <= 4: one tile x 8 waves
+//    (two workgroups per CU), with a four-stage ring at M <= 2; else, and
+//    for qkv (whose workgroups first sum the input norm's partials), one tile
+//    x 4 waves -- x 8 waves measured 15-20% slower for qkv inside the round.
 template <bool A16>
 hipError_t skinny_launch(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
   if (epi == EPI_SWIGLU)
@@ -1002,7 +1004,8 @@ hipError_t skinny_launch(const GemmArgs& a, int epi, int* n_part, hipStream_t s)
   const int tiles = (a.N + 15) / 16;
   if (tiles < 512) return skinny_mq<1, 8, A16>(a, epi, n_part, s);
   if (a.M > 8) return skinny_mq<4, 4, A16>(a, epi, n_part, s);
-  if (a.M <= 3 && tiles >= 1536) return skinny_mq<1, 8, A16>(a, epi, n_part, s);
+  if (tiles >= 1536 && a.M <= 2) return skinny_epi<1, 8, 1, A16, 4>(a, epi, n_part, s);
+  if (tiles >= 1536 && a.M <= 4) return skinny_epi<1, 8, 2, A16>(a, epi, n_part, s);
   return skinny_mq<1, 4, A16>(a, epi, n_part, s);
 }
 
@@ -1020,8 +1023,14 @@ using WideDefault = WideCfg<8, 2, 2>;
 
 // Wide-kernel plan: M tiles of at most 16*mb_max rows (16*MB rows each, MB
 // as small as covers M), BN-row weight tiles (BN/2 ffn columns for SwiGLU),
-// and a K split while the grid has fewer workgroups than ~CUs.
-WidePlan plan_wide(int M, int N, int K, bool swiglu, int BN, int mb_max, int* mb) {
+// and a K split of any count that keeps the grid within one workgroup per CU
+// (target; the workgroup's LDS allows no second one) and each split at four
+// or more k-steps.  Measured at M = 80 (13B shapes): split counts of 12
+// instead of the next power of two (8 or 16, the latter a second, mostly
+// empty wave of workgroups) make the K = 10240 and 13824 products 25-30%
+// faster.
+WidePlan plan_wide(int M, int N, int K, bool swiglu, int BN, int mb_max, int* mb, int target = 256,
+                   bool pow2 = false) {
   WidePlan p;
   const int blocks16 = (M + 15) / 16;
   p.tiles_m = (blocks16 + mb_max - 1) / mb_max;
@@ -1030,9 +1039,12 @@ WidePlan plan_wide(int M, int N, int K, bool swiglu, int BN, int mb_max, int* mb
   const int nks = K / SK_KSTEP;
   const int base = p.tiles_n * p.tiles_m;
   int splits = 1;
-  while (base * splits * 2 <= 320 && nks / (splits * 2) >= 4) splits *= 2;
-  p.ks_per_split = (nks + splits - 1) / splits;
-  p.splits = (nks + p.ks_per_split - 1) / p.ks_per_split;
+  if (pow2) {
+    while (base * splits * 2 <= target && nks / (splits * 2) >= 4) splits *= 2;
+  } else {
+    while (base * (splits + 1) <= target && nks / (splits + 1) >= 4) ++splits;
+  }
+  p.splits = splits;
   return p;
 }
 

@@ -124,41 +124,97 @@ template <int EPT>
 struct NodeShared {
   float fred[NW];
   int ired[NW];
-  int parent[64], token[64], kids[64];
-  int nk;
-  float px, qx;
+  // one-barrier reductions: partials alternate between two buffers, and a
+  // buffer is written again only after every thread has passed the barrier
+  // of the reduction that followed its last use
+  float rv[2][2][NW];
+  int rany[2][NW];
+  float2 pq[2];  // (p(x), raw q(x)) of the child under test, same buffer as its reduction
+  int kids[64], ktok[64];
   // exp(draft logit - max) of the node, element e of thread t at ql[e * VT +
   // t] (lanes on consecutive banks); removed tokens are set to 0
   float ql[EPT * VT];
 };
 
-template <int EPT>
-__device__ __forceinline__ void load_tree(const VerifyArgs& a, NodeShared<EPT>& sh, int b) {
-  const int N = a.n_nodes, t = threadIdx.x;
-  if (t < N) {
-    sh.parent[t] = a.parent[(size_t)b * N + t];
-    sh.token[t] = a.token[(size_t)b * N + t];
+// Sum (SUM) or max of two values per thread over the block, with one barrier;
+// also ORs `flag` over the block into *any when any is set.
+template <bool SUM, int EPT>
+__device__ __forceinline__ float2 red2(float x, float y, NodeShared<EPT>& sh, int& buf, bool flag = false,
+                                       bool* any = nullptr) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  x = SUM ? wave_sum(x) : wave_max(x);
+  y = SUM ? wave_sum(y) : wave_max(y);
+  const bool wf = __ballot(flag) != 0ull;
+  if (l == 0) {
+    sh.rv[buf][0][w] = x;
+    sh.rv[buf][1][w] = y;
+    sh.rany[buf][w] = wf;
   }
   __syncthreads();
+  float sx = SUM ? 0.f : -INFINITY, sy = sx;
+  int f = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    sx = SUM ? sx + sh.rv[buf][0][i] : fmaxf(sx, sh.rv[buf][0][i]);
+    sy = SUM ? sy + sh.rv[buf][1][i] : fmaxf(sy, sh.rv[buf][1][i]);
+    f |= sh.rany[buf][i];
+  }
+  if (any) *any = f != 0;
+  buf ^= 1;
+  return make_float2(sx, sy);
 }
 
 // Node u of sequence b: returns (accepted child, 0) or (-1, correction or
-// bonus token); ORs the status bits it raises into *flags (uniform).
+// bonus token); ORs the status bits it raises into *flags (uniform).  buf is
+// the reduction buffer parity, carried across calls.
 template <int EPT>
-__device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& sh, int b, int u, int* flags) {
+__device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& sh, int b, int u, int* flags,
+                                          int& buf) {
   const int t = threadIdx.x;
   const int N = a.n_nodes, V = a.vocab;
+  const size_t nb = (size_t)b * N;
   const bool greedy = a.flags & 1, iid = a.flags & 2;
   float* fred = sh.fred;
   int* ired = sh.ired;
-  float p[EPT];  // current target distribution (normalised)
 #define Q(e) sh.ql[(e) * VT + t]
-  // target distribution at u
-  if (__syncthreads_or(load_row<EPT>(a.target + ((size_t)b * N + u) * V, V, p))) *flags |= 8;
+  // children of u in index order (n_nodes <= 64): every wave takes the same
+  // ballot over the parent array, so the count needs no barrier; wave 0
+  // publishes the list (visible after the first reduction's barrier)
+  const int lane = t & (WAVE - 1);
+  const int drow_idx = a.draft_row[nb + u];
+  const int par = lane < N ? a.parent[nb + lane] : -2;
+  float p[EPT];  // current target distribution (normalised)
+  const bool bad = load_row<EPT>(a.target + (nb + u) * V, V, p);
+  const bool kid = lane > u && lane < N && par == u;
+  const uint64_t km = __ballot(kid);
+  const int nk = __popcll(km);
+  if (t < WAVE && kid) {
+    const int rk = __popcll(km & ((1ull << lane) - 1ull));
+    sh.kids[rk] = lane;
+    sh.ktok[rk] = a.token[nb + lane];
+  }
+  // the draft row, only for a node with children: raw logits into q's columns
+  // (only thread t touches its column)
+  const bool have_q = nk > 0 && drow_idx >= 0;
+  float dmx = -INFINITY;
+  if (have_q) {
+    float dv[EPT];
+    load_row<EPT>(a.draft + (size_t)drow_idx * V, V, dv);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      dmx = fmaxf(dmx, dv[e]);
+      Q(e) = dv[e];
+    }
+  }
   float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) mx = fmaxf(mx, p[e]);
-  mx = bmax(mx, fred);
+  bool any_nan;
+  const float2 mm = red2<false>(mx, dmx, sh, buf, bad, &any_nan);  // also publishes the children
+  if (any_nan) *flags |= 8;
+  mx = mm.x;
+  dmx = mm.y;
+  float ls = 0.f, ds = 0.f;
   if (greedy) {
     int cand = 0x7fffffff;
 #pragma unroll
@@ -168,76 +224,62 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
 #pragma unroll
     for (int e = 0; e < EPT; ++e) p[e] = (t * EPT + e == am) ? 1.f : 0.f;
   } else {
-    float ls = 0.f;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       p[e] = (p[e] == -INFINITY) ? 0.f : __expf(p[e] - mx);
       ls += p[e];
     }
-    const float inv = 1.f / bsum(ls, fred);
+  }
+  if (have_q) {
+    // q(y) = exp(d_y - dmx) / S over the tokens not removed, the exponentials taken once
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) p[e] *= inv;
+    for (int e = 0; e < EPT; ++e) {
+      Q(e) = (Q(e) == -INFINITY) ? 0.f : __expf(Q(e) - dmx);
+      ds += Q(e);
+    }
   }
-  // children of u in rank (index) order
-  if (t == 0) {
-    int nk = 0;
-    for (int i = u + 1; i < N; ++i)
-      if (sh.parent[i] == u) sh.kids[nk++] = i;
-    sh.nk = nk;
+  float S = 0.f;
+  if (!greedy || have_q) {
+    const float2 sums = red2<true>(ls, ds, sh, buf);
+    if (!greedy) {
+      const float inv = 1.f / sums.x;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) p[e] *= inv;
+    }
+    S = sums.y;
   }
-  __syncthreads();
-  const int nk = sh.nk;
   if (nk == 0) return make_int2(-1, draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired));
-  // draft distribution at u: q(y) = exp(d_y - dmx) / S over the tokens not removed,
-  // the exponentials taken once
-  const int drow_idx = a.draft_row[(size_t)b * N + u];
   if (drow_idx < 0) {  // no draft row for a node with children: invalid input
     *flags |= 8;
     return make_int2(-1, draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired));
   }
-  {
-    float dmx = -INFINITY;
-    {
-      float dv[EPT];
-      load_row<EPT>(a.draft + (size_t)drow_idx * V, V, dv);
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        dmx = fmaxf(dmx, dv[e]);
-        Q(e) = dv[e];  // raw logits first: keeps the row out of registers across the reduction
-      }
-    }
-    dmx = bmax(dmx, fred);
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) Q(e) = (Q(e) == -INFINITY) ? 0.f : __expf(Q(e) - dmx);
-  }
-  auto qmass = [&]() {
-    float ds = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) ds += Q(e);
-    return bsum(ds, fred);
-  };
-  float S = qmass();
   for (int i = 0; i < nk; ++i) {
     if (!(S > 0.f)) {
       *flags |= 4;
       break;
     }
     const int c = sh.kids[i];
-    const int x = sh.token[c];
+    const int x = sh.ktok[i];
     const float r = philox_uniform(a.seed, a.round, b, u, i);
     const bool x_ok = x >= 0 && x < V;
-    __syncthreads();
-    if (x_ok && t == x / EPT) {
+    const bool owner = x_ok && t == x / EPT;
+    // residual mass norm(max(0, p - q)) taken before the test (needed only on a
+    // rejection; a zero mass leaves p untouched), one reduction with p(x), q(x)
+    const float invS = 1.f / S;
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) rs += fmaxf(0.f, p[e] - Q(e) * invS);
+    const int pb = buf;
+    if (owner) {
       float px = 0.f;
 #pragma unroll
       for (int e = 0; e < EPT; ++e)
         if (e == x % EPT) px = p[e];
-      sh.px = px;
-      sh.qx = Q(x % EPT);
+      sh.pq[pb] = make_float2(px, Q(x % EPT));
     }
-    __syncthreads();
-    const float px = x_ok ? sh.px : 0.f;
-    const float qx = x_ok ? sh.qx / S : 0.f;
+    const float Z = red2<true>(rs, 0.f, sh, buf).x;
+    const float px = x_ok ? sh.pq[pb].x : 0.f;
+    const float qx = x_ok ? sh.pq[pb].y / S : 0.f;
     bool ok;
     if (qx > 0.f) {
       ok = r < px / qx;
@@ -246,13 +288,6 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
       ok = px > 0.f;
     }
     if (ok) return make_int2(c, 0);
-    // residual target norm(max(0, p - q))
-    // (mass first, then the update, so a zero mass leaves p untouched)
-    const float invS = 1.f / S;
-    float rs = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) rs += fmaxf(0.f, p[e] - Q(e) * invS);
-    const float Z = bsum(rs, fred);
     if (Z > 0.f) {
       const float inv = 1.f / Z;
 #pragma unroll
@@ -260,9 +295,12 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
     } else {
       *flags |= 1;  // zero residual mass (reachable only through rounding): keep p
     }
-    if (!iid) {
-      if (x_ok && t == x / EPT) Q(x % EPT) = 0.f;
-      S = qmass();
+    if (!iid) {  // remove the rejected token from q and renormalise
+      if (owner) Q(x % EPT) = 0.f;
+      float qs = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) qs += Q(e);
+      S = red2<true>(qs, 0.f, sh, buf).x;
     }
   }
 #undef Q
@@ -275,10 +313,9 @@ template <int EPT>
 __global__ void __launch_bounds__(VT) verify_kernel(VerifyArgs a) {
   __shared__ NodeShared<EPT> sh;
   const int b = blockIdx.x, N = a.n_nodes;
-  load_tree<EPT>(a, sh, b);
-  int flags = 0, u = 0, nacc = 0, next_tok = 0;
+  int flags = 0, u = 0, nacc = 0, next_tok = 0, buf = 0;
   for (int level = 0; level <= N; ++level) {
-    const int2 r = node_step<EPT>(a, sh, b, u, &flags);
+    const int2 r = node_step<EPT>(a, sh, b, u, &flags, buf);
     if (r.x < 0) {
       next_tok = r.y;
       break;
@@ -301,9 +338,8 @@ __global__ void __launch_bounds__(VT) verify_node_kernel(VerifyArgs a) {
   __shared__ NodeShared<EPT> sh;
   const int N = a.n_nodes;
   const int b = blockIdx.x / N, u = blockIdx.x % N;
-  load_tree<EPT>(a, sh, b);
-  int flags = 0;
-  const int2 r = node_step<EPT>(a, sh, b, u, &flags);
+  int flags = 0, buf = 0;
+  const int2 r = node_step<EPT>(a, sh, b, u, &flags, buf);
   if (threadIdx.x == 0) {
     a.node_next[blockIdx.x] = r.x;
     a.node_tok[blockIdx.x] = r.y;
