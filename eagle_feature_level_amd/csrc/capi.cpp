@@ -365,7 +365,9 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     a.part = ws.gemm_part;  // split-K partials of the tiled kernel (+ the bf16 operand)
     a.act_bf16 = act16;
     const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
-    const double bytes = wbytes * a.N * a.K + 4.0 * a.M * (a.K + nout) + (a.y2 ? 4.0 * a.M * a.N : 0.0);
+    const double out_bytes = (epi == EPI_ROPE) ? 4.0 * a.M * a.rp_hq * a.rp_hd + 2.0 * wbytes * a.M * a.rp_hkv * a.rp_hd
+                                               : 4.0 * a.M * nout;
+    const double bytes = wbytes * a.N * a.K + 4.0 * a.M * a.K + out_bytes + (a.y2 ? 4.0 * a.M * a.N : 0.0);
     const double flops = 2.0 * a.M * a.N * a.K;
     return timed(
         st, role, bytes, flops,
@@ -377,6 +379,10 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
   };
   hipError_t e;
   const int d = s.d, hq = s.n_heads * s.head_dim, hkv = s.n_kv_heads * s.head_dim, F = s.ffn;
+  // the skinny QKV GEMM rotates q, k and writes the tree slots in its epilogue up to
+  // M = 8 (one 16-row weight tile per workgroup); above, the four-tile QKV variant
+  // plus the RoPE launch is faster (measured on the 7B shapes)
+  const bool rope_fused = bf16 && M <= 8 && s.head_dim % 16 == 0;
 
   if (!head_only) {
     // a1: the rows' inputs [f_parent ; e(token)]: gathered by the FC GEMM itself
@@ -433,13 +439,29 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.sumsq_in = ws.sumsq1;
       a.n_part_in = np1;
       a.eps = s.rms_eps;
-      a.y = ws.qkv;
-      a.ldy = hq + 2 * hkv;
-      e = gemm(a, EPI_STORE, nullptr, EAGLE_ROLE_QKV);
+      if (rope_fused) {  // a4 in the epilogue: rotated q out, k and v into the rows' tree slots
+        a.y = (float*)ws.qrot;
+        a.ldy = hq;
+        a.rp_pos = rows->pos;
+        a.rp_slot = rows->slot;
+        a.rp_row_start = rows->row_start;
+        a.rp_batch = rows->batch;
+        a.rp_tree_k = kv->tree_k;
+        a.rp_tree_v = kv->tree_v;
+        a.rp_hd = s.head_dim;
+        a.rp_hq = s.n_heads;
+        a.rp_hkv = s.n_kv_heads;
+        a.rp_theta = s.rope_theta;
+        e = gemm(a, EPI_ROPE, nullptr, EAGLE_ROLE_QKV);
+      } else {
+        a.y = ws.qkv;
+        a.ldy = hq + 2 * hkv;
+        e = gemm(a, EPI_STORE, nullptr, EAGLE_ROLE_QKV);
+      }
       if (e != hipSuccess) return hip_fail(e);
     }
     // a4: RoPE at each row's position; k, v into the rows' tree slots
-    {
+    if (!rope_fused) {
       RopeArgs r;
       r.qkv = ws.qkv;
       r.pos = rows->pos;

@@ -11,7 +11,9 @@ enum GemmEpi {
   EPI_BIAS_SUMSQ = 1,   // y = acc + bias[n]; sum of squares partials; y2 = y * gain_out[n] if y2
   EPI_RESID = 2,        // y = acc + resid[m, n]
   EPI_RESID_SUMSQ = 3,  // y = acc + resid[m, n]; sum of squares partials; y2 = y * gain_out[n] if y2
-  EPI_SWIGLU = 4        // yb[m, j] = silu(gate) * up, gate row j, up row ffn + j
+  EPI_SWIGLU = 4,       // yb[m, j] = silu(gate) * up, gate row j, up row ffn + j
+  EPI_ROPE = 5          // [q; k; v] rows of whole heads: rotary embedding of q and k at the
+                        // row's position, q to y, k and v (bf16) into the row's tree slot
 };
 
 struct GemmArgs {
@@ -55,6 +57,18 @@ struct GemmArgs {
   // a (hi, lo) pair of bf16 values (two MFMAs per product); 1 = it is rounded
   // once to bf16 (round to nearest even) after the RMSNorm row scale, one MFMA
   int act_bf16;
+  // EPI_ROPE (M <= 16, bf16 weights): heads of rp_hd columns, rp_hq query heads
+  // then rp_hkv key heads then rp_hkv value heads; row m of sequence b (the b
+  // with rp_row_start[b] <= m < rp_row_start[b + 1]) at position rp_pos[m]
+  // writes k, v to tree slot rp_slot[m]: rp_tree_k/v[b][slot][head][rp_hd]
+  const int32_t* rp_pos;
+  const int32_t* rp_slot;
+  const int32_t* rp_row_start;
+  int rp_batch;
+  void* rp_tree_k;
+  void* rp_tree_v;
+  int rp_hd, rp_hq, rp_hkv;
+  float rp_theta;
 };
 
 // Launch helpers (host).  Return hipSuccess or the launch error.

@@ -150,6 +150,14 @@ __device__ __forceinline__ int tile_row(const GemmArgs& a, int tile, int at, int
     const int j = tile * 16 * H + (at % H) * 16 + r;
     *ok = j < a.ffn;
     return (at < H ? 0 : a.ffn) + (*ok ? j : 0);
+  } else if constexpr (EPI == EPI_ROPE) {
+    // a 16-row tile holds 8 rotary pairs (e, e + hd/2) of one head: rows 0-7
+    // are columns 8j..8j+7 of the head, rows 8-15 the same plus hd/2
+    static_assert(AT == 1, "one 16-row tile per workgroup");
+    const int tph = a.rp_hd >> 4, hb = tile / tph, j = tile % tph;
+    const int n = hb * a.rp_hd + (r < 8 ? 8 * j + r : (a.rp_hd >> 1) + 8 * j + r - 8);
+    *ok = n < a.N;
+    return *ok ? n : 0;
   } else {
     const int n = tile * 16 * AT + at * 16 + r;
     *ok = n < a.N;
@@ -312,7 +320,52 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
     for (int v = 0; v < 4; ++v) red[wv][r][at * 16 + g * 4 + v] = acc[at][v];
   __syncthreads();
 
-  if constexpr (EPI == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_ROPE) {
+    // rows m, pairs pi: x0 = column 8j + pi of head hb, x1 = its partner hd/2
+    // further.  Angles pos * theta^(-2e/hd) in fp64 (a position in the
+    // thousands keeps its phase exact to fp32), the rotation in fp32.
+    const int hd = a.rp_hd, half = hd >> 1, tph = hd >> 4;
+    const int hb = tile / tph, j = tile % tph;
+    for (int e = threadIdx.x; e < 16 * 8; e += NW * 64) {
+      const int m = e >> 3, pi = e & 7;
+      if (m >= a.M || hb * hd >= a.N) continue;
+      float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        x0 += red[w][m][pi];
+        x1 += red[w][m][pi + 8];
+      }
+      if (!A16 && a.sumsq_in) {
+        x0 *= scale[m];
+        x1 *= scale[m];
+      }
+      const int ee = 8 * j + pi;
+      float y0 = x0, y1 = x1;
+      if (hb < a.rp_hq + a.rp_hkv) {
+        const double inv = exp2(-2.0 * (double)ee / (double)hd * log2((double)a.rp_theta));
+        double sd, cd;
+        sincos((double)a.rp_pos[m] * inv, &sd, &cd);
+        const float c = (float)cd, sv = (float)sd;
+        y0 = x0 * c - x1 * sv;
+        y1 = x1 * c + x0 * sv;
+      }
+      if (hb < a.rp_hq) {
+        float* qo = a.y + (size_t)m * a.ldy + (size_t)hb * hd;
+        qo[ee] = y0;
+        qo[ee + half] = y1;
+      } else {
+        int b = 0;
+        for (int i = 0; i < a.rp_batch; ++i)
+          if (a.rp_row_start[i] <= m && m < a.rp_row_start[i + 1]) b = i;
+        const bool isk = hb < a.rp_hq + a.rp_hkv;
+        const int g = isk ? hb - a.rp_hq : hb - a.rp_hq - a.rp_hkv;
+        bf16_t* dst = (bf16_t*)(isk ? a.rp_tree_k : a.rp_tree_v) +
+                      (((size_t)b * 64 + a.rp_slot[m]) * a.rp_hkv + g) * hd;
+        dst[ee] = f2bf(y0);
+        dst[ee + half] = f2bf(y1);
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
     constexpr int H = BN / 2;
     for (int e = threadIdx.x; e < 16 * H; e += NW * 64) {
       const int m = e / H, jl = e % H;
@@ -962,6 +1015,14 @@ hipError_t skinny_epi(const GemmArgs& a, int epi, int* n_part, hipStream_t s) {
       launch_skinny_kernel(gemm_skinny<AT, NW, MQ, NS, A16, EPI_RESID_SUMSQ>, grid, blk, s, a);
       *n_part = grid.x;
       break;
+    case EPI_ROPE:
+      if constexpr (AT == 1) {
+        if (a.rp_hd % 16 || a.N % a.rp_hd) return hipErrorInvalidValue;  // whole heads of 16-column pairs
+        launch_skinny_kernel(gemm_skinny<AT, NW, MQ, NS, A16, EPI_ROPE>, grid, blk, s, a);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
     case EPI_SWIGLU:
       if constexpr (AT >= 2) {  // gate and up tiles pair up inside a workgroup
         const int H = BN / 2;
@@ -1003,6 +1064,7 @@ hipError_t skinny_launch(const GemmArgs& a, int epi, int* n_part, hipStream_t s)
     return a.M > 8 ? skinny_mq<2, 8, A16>(a, epi, n_part, s) : skinny_mq<2, 4, A16>(a, epi, n_part, s);
   const int tiles = (a.N + 15) / 16;
   if (tiles < 512) return skinny_mq<1, 8, A16>(a, epi, n_part, s);
+  if (epi == EPI_ROPE) return skinny_mq<1, 4, A16>(a, epi, n_part, s);  // one 16-row tile per workgroup
   if (a.M > 8) return skinny_mq<4, 4, A16>(a, epi, n_part, s);
   if (tiles >= 1536 && a.M <= 2) return skinny_epi<1, 8, 1, A16, 4>(a, epi, n_part, s);
   if (tiles >= 1536 && a.M <= 4) return skinny_epi<1, 8, 2, A16>(a, epi, n_part, s);
@@ -1195,6 +1257,7 @@ hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s)
   if (a.gfeat && (a.gd % SK_KSTEP || a.K != 2 * a.gd)) return hipErrorInvalidValue;
   if ((epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) && a.y2 && !a.gain_out) return hipErrorInvalidValue;
   if (a.M <= 16) return a.act_bf16 ? skinny_launch<true>(a, epi, n_part_out, s) : skinny_launch<false>(a, epi, n_part_out, s);
+  if (epi == EPI_ROPE) return hipErrorInvalidValue;  // the fused rotary epilogue is the skinny kernel's
   if (a.N % 4 || (epi == EPI_SWIGLU && a.ffn % 4)) return hipErrorInvalidValue;  // float4 epilogue stores
   return a.act_bf16 ? prepared_launch<false>(a, epi, n_part_out, s) : prepared_launch<true>(a, epi, n_part_out, s);
 }
