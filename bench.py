@@ -63,7 +63,10 @@ def build_engine(cid: int):
     eng = EagleRound(dev.shape_dict(s), wt, cfg.batch, kind, cfg.topk, cfg.depth, cfg.rerank_m,
                      TEMPLATES.get(cfg.tree), pf)
     host = dict(w=w, lens=lens, ks=ks, vs=vs, feat=feat, tok=tok)
-    return cfg, eng, torch.from_numpy(feat).cuda(), dev.ints(tok), host
+    # root features staged into the engine's own rows (input resident before the round)
+    root = eng.root_features()
+    root.copy_(torch.from_numpy(feat).cuda())
+    return cfg, eng, root, dev.ints(tok), host
 
 
 def synth_target(cfg, eng):

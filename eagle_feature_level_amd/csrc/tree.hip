@@ -31,27 +31,43 @@ __global__ void tree_init_kernel(PoolArgs p, const int32_t* root_token, int root
 
 constexpr int EX_MAX_CHILD = 256;  // 16 x 16
 
+// Every global read the kernel needs is issued in its first phase (the
+// frontier, then the frontier nodes' own fields and the sequence's counters),
+// and in the second (the children's top-k entries); the rest works from LDS.
 __global__ void __launch_bounds__(256) tree_expand_kernel(ExpandArgs a) {
   __shared__ int off[65];
-  __shared__ int fr[64];
+  __shared__ int fr[64], fcnt[64], fdep[64], ffrow[64];
+  __shared__ float flogv[64];
+  __shared__ uint64_t fmask[64];
   __shared__ float clogv[EX_MAX_CHILD];
-  __shared__ int cqual[EX_MAX_CHILD];
+  __shared__ int cqual[EX_MAX_CHILD], cf[EX_MAX_CHILD], ctok[EX_MAX_CHILD];
   __shared__ int nf[64];
-  __shared__ int s_total, s_cnt;
+  __shared__ int s_total, s_cnt, s_plen;
   const int b = blockIdx.x, t = threadIdx.x;
   const PoolArgs& p = a.pool;
   const size_t base = (size_t)b * p.cap;
-  if (t < a.n_prev) fr[t] = p.frontier[(size_t)b * 64 + t];
+  if (t < a.n_prev) {
+    const int u = p.frontier[(size_t)b * 64 + t];
+    fr[t] = u;
+    fcnt[t] = a.nchild ? a.nchild[u] : a.k;
+    flogv[t] = p.logv[base + u];
+    fdep[t] = p.depth[base + u];
+    fmask[t] = p.mask[base + u];
+    ffrow[t] = p.feat_row[base + u];
+  }
+  if (t == 255) {
+    s_cnt = p.count[b];
+    s_plen = a.prefix_len[b];
+  }
   __syncthreads();
   if (t == 0) {
     int acc = 0;
     for (int f = 0; f < a.n_prev; ++f) {
       off[f] = acc;
-      acc += a.nchild ? a.nchild[fr[f]] : a.k;
+      acc += fcnt[f];
     }
     off[a.n_prev] = acc;
     s_total = acc;
-    s_cnt = p.count[b];
   }
   __syncthreads();
   const int total = s_total, cnt = s_cnt;
@@ -66,15 +82,18 @@ __global__ void __launch_bounds__(256) tree_expand_kernel(ExpandArgs a) {
     const int u = fr[f];
     const int row = b * a.n_prev + f;
     const int id = cnt + t;
-    const float lv = __fadd_rn(p.logv[base + u], a.topk_logq[(size_t)row * a.topk + r]);
+    const int tok = a.topk_idx[(size_t)row * a.topk + r];
+    const float lv = __fadd_rn(flogv[f], a.topk_logq[(size_t)row * a.topk + r]);
     p.parent[base + id] = u;
-    p.token[base + id] = a.topk_idx[(size_t)row * a.topk + r];
-    p.depth[base + id] = p.depth[base + u] + 1;
+    p.token[base + id] = tok;
+    p.depth[base + id] = fdep[f] + 1;
     p.logv[base + id] = lv;
     p.feat_row[base + id] = -1;
     p.slot[base + id] = -1;
     p.mask[base + id] = 0ull;
     clogv[t] = lv;
+    cf[t] = f;
+    ctok[t] = tok;
     cqual[t] = a.nchild ? (a.nchild[id] > 0) : 1;
   }
   __syncthreads();
@@ -82,31 +101,31 @@ __global__ void __launch_bounds__(256) tree_expand_kernel(ExpandArgs a) {
     int rank = 0;
     if (a.nchild) {
       for (int j = 0; j < t; ++j) rank += cqual[j];
-      if (cqual[t] && rank < a.n_next) nf[rank] = cnt + t;
+      if (cqual[t] && rank < a.n_next) nf[rank] = t;
     } else {
       const float v = clogv[t];
       for (int j = 0; j < total; ++j) {
         const float w = clogv[j];
         rank += (w > v) || (w == v && j < t);
       }
-      if (rank < a.n_next) nf[rank] = cnt + t;
+      if (rank < a.n_next) nf[rank] = t;
     }
   }
   __syncthreads();
   if (t < a.n_next) {
-    const int node = nf[t];
-    const int u = p.parent[base + node];
+    const int c = nf[t];  // the candidate (child index) of rank t
+    const int node = cnt + c, f = cf[c];
     const int slot = a.nchild ? node : a.step * a.k + t;
-    const uint64_t mask = p.mask[base + u] | (1ull << slot);
+    const uint64_t mask = fmask[f] | (1ull << slot);
     const int frow = a.feat_row0 + b * a.n_next + t;
     p.feat_row[base + node] = frow;
     p.slot[base + node] = slot;
     p.mask[base + node] = mask;
     p.frontier[(size_t)b * 64 + t] = node;
     const int r = b * a.n_next + t;
-    a.next_token[r] = p.token[base + node];
-    a.next_parent[r] = p.feat_row[base + u];
-    a.next_pos[r] = a.prefix_len[b] + p.depth[base + node] - 1;
+    a.next_token[r] = ctok[c];
+    a.next_parent[r] = ffrow[f];
+    a.next_pos[r] = s_plen + fdep[f];  // prefix length + depth(node) - 1
     a.next_slot[r] = slot;
     a.next_mask[r] = mask;
   }

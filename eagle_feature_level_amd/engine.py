@@ -154,9 +154,15 @@ class EagleRound:
     def _sample_flag(self, sample):
         return EAGLE_SAMPLE_CHILDREN if sample is not None else 0
 
+    def root_features(self) -> torch.Tensor:
+        """The engine's own root-feature rows [B, d] (fp32): a caller that writes
+        the target's last features here before a round saves the round's copy."""
+        return self.feat[:self.B]
+
     def root_head(self, root_feat: torch.Tensor, sample=None):
         B = self.B
-        self.feat[:B].copy_(root_feat)
+        if root_feat.data_ptr() != self.feat.data_ptr():  # already in place: no copy
+            self.feat[:B].copy_(root_feat)
         rows = make_rows(B, B, 1, self.root_start, None, self.root_rows)
         seed, rnd = sample if sample is not None else (0, 0)
         out = make_out(None, self.logits, self.lse, self.topk, self.topk_idx, self.topk_logq, seed, rnd, 0)
