@@ -143,6 +143,8 @@ __global__ void __launch_bounds__(512) tree_finalize_kernel(FinalizeArgs a) {
   __shared__ int dp[FIN_MAX_POOL];
   __shared__ int where[FIN_MAX_POOL];
   __shared__ int kept[FIN_MAX_POOL];
+  __shared__ int ppar[FIN_MAX_POOL], ptok[FIN_MAX_POOL], pfrow[FIN_MAX_POOL];
+  __shared__ int s_plen;
   __shared__ int tpool[64];
   __shared__ int tpar[64];
   __shared__ uint64_t tmask[64];
@@ -151,11 +153,16 @@ __global__ void __launch_bounds__(512) tree_finalize_kernel(FinalizeArgs a) {
   const size_t base = (size_t)b * p.cap;
   int cnt = p.count[b];
   if (cnt < 1 || cnt > FIN_MAX_POOL) cnt = 1;  // invalid pool: root only
+  // every pool field the kernel reads, in one parallel pass (the later phases use LDS)
   for (int i = t; i < cnt; i += 512) {
     lv[i] = p.logv[base + i];
     dp[i] = p.depth[base + i];
+    ppar[i] = p.parent[base + i];
+    ptok[i] = p.token[base + i];
+    pfrow[i] = p.feat_row[base + i];
     where[i] = -1;
   }
+  if (t == 511) s_plen = a.prefix_len[b];
   __syncthreads();
   // selection: rank among candidates 1..cnt-1 by (logv desc, depth asc, id asc)
   const int ncand = cnt - 1;
@@ -195,13 +202,13 @@ __global__ void __launch_bounds__(512) tree_finalize_kernel(FinalizeArgs a) {
     const size_t o = (size_t)b * n + t;
     if (t < nreal) {
       const int i = tpool[t];
-      const int pp = (t == 0) ? -1 : where[p.parent[base + i]];
+      const int pp = (t == 0) ? -1 : where[ppar[i]];
       tpar[t] = pp;
       a.tree_parent[o] = pp;
-      a.tree_token[o] = p.token[base + i];
+      a.tree_token[o] = ptok[i];
       a.tree_depth[o] = dp[i];
       a.tree_pool[o] = i;
-      a.tree_qrow[o] = p.feat_row[base + i];
+      a.tree_qrow[o] = pfrow[i];
     } else {
       tpar[t] = -2;
       a.tree_parent[o] = -2;
@@ -223,13 +230,13 @@ __global__ void __launch_bounds__(512) tree_finalize_kernel(FinalizeArgs a) {
       const int r = b * (n - 1) + (t - 1);
       if (t < nreal) {
         const int i = tpool[t];
-        a.row_token[r] = p.token[base + i];
-        a.row_parent[r] = p.feat_row[base + p.parent[base + i]];
-        a.row_pos[r] = a.prefix_len[b] + dp[i] - 1;
+        a.row_token[r] = ptok[i];
+        a.row_parent[r] = pfrow[ppar[i]];
+        a.row_pos[r] = s_plen + dp[i] - 1;
       } else {
         a.row_token[r] = 0;
-        a.row_parent[r] = p.feat_row[base];
-        a.row_pos[r] = a.prefix_len[b];
+        a.row_parent[r] = pfrow[0];
+        a.row_pos[r] = s_plen;
       }
       a.row_slot[r] = t;
       a.row_mask[r] = tmask[t];
