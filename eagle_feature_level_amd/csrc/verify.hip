@@ -288,20 +288,25 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
       ok = px > 0.f;
     }
     if (ok) return make_int2(c, 0);
+    // residual update; without iid the rejected token leaves q (its column
+    // zeroed) and the remaining mass is summed in the same pass over q
+    const int xe = (!iid && owner) ? x % EPT : -1;
+    float qs = 0.f;
     if (Z > 0.f) {
       const float inv = 1.f / Z;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) p[e] = fmaxf(0.f, p[e] - Q(e) * invS) * inv;
+      for (int e = 0; e < EPT; ++e) {
+        const float qe = Q(e);
+        p[e] = fmaxf(0.f, p[e] - qe * invS) * inv;
+        qs += (e == xe) ? 0.f : qe;
+      }
     } else {
       *flags |= 1;  // zero residual mass (reachable only through rounding): keep p
-    }
-    if (!iid) {  // remove the rejected token from q and renormalise
-      if (owner) Q(x % EPT) = 0.f;
-      float qs = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) qs += Q(e);
-      S = red2<true>(qs, 0.f, sh, buf).x;
+      for (int e = 0; e < EPT; ++e) qs += (e == xe) ? 0.f : Q(e);
     }
+    if (xe >= 0) Q(xe) = 0.f;
+    if (!iid) S = red2<true>(qs, 0.f, sh, buf).x;  // renormalise q
   }
 #undef Q
   // every child rejected: correction from the residual
@@ -347,28 +352,36 @@ __global__ void __launch_bounds__(VT) verify_node_kernel(VerifyArgs a) {
   }
 }
 
-// One thread per sequence: the walk through the per-node results.
+// One wave per sequence: lane u holds node u's result (n_nodes <= 64), and
+// the walk through them moves by lane shuffles, with no dependent global reads.
 __global__ void __launch_bounds__(64) verify_walk_kernel(VerifyArgs a) {
-  const int b = blockIdx.x * 64 + threadIdx.x;
-  if (b >= a.batch) return;
+  const int b = blockIdx.x, l = threadIdx.x;
   const int N = a.n_nodes;
-  int flags = 0, u = 0, nacc = 0, next_tok = 0;
+  const size_t base = (size_t)b * N;
+  int nx = -1, tk = 0, fl = 0;
+  if (l < N) {
+    nx = a.node_next[base + l];
+    tk = a.node_tok[base + l];
+    fl = a.node_flags[base + l];
+  }
+  int flags = 0, u = 0, nacc = 0, next_tok = 0, mine = -1;
   for (int level = 0; level <= N; ++level) {
-    const size_t bu = (size_t)b * N + u;
-    flags |= a.node_flags[bu];
-    const int c = a.node_next[bu];
+    flags |= __shfl(fl, u, WAVE);
+    const int c = __shfl(nx, u, WAVE);
     if (c < 0) {
-      next_tok = a.node_tok[bu];
+      next_tok = __shfl(tk, u, WAVE);
       break;
     }
-    a.path[(size_t)b * N + nacc] = c;
+    if (l == nacc) mine = c;
     ++nacc;
     u = c;
   }
-  for (int j = nacc; j < N; ++j) a.path[(size_t)b * N + j] = -1;
-  a.accept_len[b] = nacc + 1;
-  a.next_token[b] = next_tok;
-  a.out_flags[b] = flags;
+  if (l < N) a.path[base + l] = l < nacc ? mine : -1;
+  if (l == 0) {
+    a.accept_len[b] = nacc + 1;
+    a.next_token[b] = next_tok;
+    a.out_flags[b] = flags;
+  }
 }
 
 }  // namespace
@@ -396,6 +409,6 @@ hipError_t launch_verify(VerifyArgs a, void* ws, hipStream_t s) {
   else hipLaunchKernelGGL(verify_node_kernel<32>, g, dim3(VT), 0, s, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_walk_kernel, dim3((a.batch + 63) / 64), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(verify_walk_kernel, dim3(a.batch), dim3(64), 0, s, a);
   return hipGetLastError();
 }
