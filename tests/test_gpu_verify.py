@@ -248,3 +248,45 @@ def test_expected_tokens_worked_example_on_gpu():
         got = _run(parent, tokens, target, draft, B, N, V, seed=4, rnd=case["expected_tokens"].__hash__() % 1000)
         mean, sd = got["len"].mean(), got["len"].std()
         assert abs(mean - case["expected_tokens"]) < 4 * sd / np.sqrt(B) + 1e-3, (case, mean)
+
+
+def _crafted_flag_case():
+    """Root with three children, V = 64, four sequences built to take the rare
+    branches: (0) q one-hot on the first child's token, which p excludes: that
+    child is rejected, its removal leaves q no mass, the remaining children are
+    skipped with the zero-draft-mass bit (4) and the correction comes from p;
+    (1) the first child's token has q = 0 but p > 0: accepted under the q = 0
+    bit (2); (2) q = 0 and p = 0 at the first child's token: rejected under the
+    same bit, the walk goes on to the siblings; (3) an ordinary random row."""
+    g = np.random.default_rng(17)
+    parent = [-1, 0, 0, 0]
+    B, N, V = 4, 4, 64
+    draft = (g.standard_normal((B, N, V)) * 1.5).astype(np.float32)
+    target = (draft + g.standard_normal((B, N, V)) * 0.7).astype(np.float32)
+    tokens = np.zeros((B, N), np.int32)
+    for b in range(B):
+        tokens[b, 1:] = g.choice(V, size=3, replace=False)
+    a0, a1 = tokens[0, 1], tokens[0, 2]
+    draft[0, 0, :] = -np.inf
+    draft[0, 0, a0] = 0.0  # q one-hot at child 0's token
+    target[0, 0, a0] = -np.inf  # p(a0) = 0
+    target[0, 0, a1] = 3.0
+    draft[1, 0, tokens[1, 1]] = -np.inf  # q(x) = 0, p(x) > 0
+    draft[2, 0, tokens[2, 1]] = -np.inf  # q(x) = 0 and p(x) = 0
+    target[2, 0, tokens[2, 1]] = -np.inf
+    return parent, tokens, target.reshape(B * N, V), draft.reshape(B * N, V), B, N, V
+
+
+@pytest.mark.parametrize("ws", [True, False])
+def test_verify_rare_branches_match_oracle(ws):
+    parent, tokens, target, draft, B, N, V = _crafted_flag_case()
+    got = _run(parent, tokens, target, draft, B, N, V, seed=21, rnd=4, ws=ws)
+    refs = [verify_sequence(parent, tokens[b], target[b * N:(b + 1) * N], draft[b * N:(b + 1) * N], 21, 4, b, False,
+                            False) for b in range(B)]
+    assert refs[0]["flags"] & 4 and refs[1]["flags"] & 2 and refs[2]["flags"] & 2  # the cases are what they claim
+    assert refs[1]["accept_len"] >= 2 and refs[1]["path"][0] == 1
+    for b in range(B):
+        assert got["len"][b] == refs[b]["accept_len"], b
+        assert list(got["path"][b * N:b * N + len(refs[b]["path"])]) == refs[b]["path"], b
+        assert got["next"][b] == refs[b]["next_token"], b
+        assert got["flags"][b] == refs[b]["flags"], b
