@@ -354,7 +354,10 @@ size_t eagle_verify_workspace_bytes(int32_t batch, int32_t n_nodes);
 enum {
   EAGLE_ROLE_FC = 0, EAGLE_ROLE_QKV, EAGLE_ROLE_ROPE, EAGLE_ROLE_ATTN, EAGLE_ROLE_O, EAGLE_ROLE_GATE_UP,
   EAGLE_ROLE_DOWN, EAGLE_ROLE_LM_HEAD, EAGLE_ROLE_TOPK, EAGLE_ROLE_ROWS, EAGLE_ROLE_COUNT
-};  /* EAGLE_ROLE_ROWS: per-row set-up (sequence index, [f ; e] concatenation) */
+};  /* EAGLE_ROLE_ROWS: per-row set-up (sequence index, [f ; e] concatenation).
+     * With bf16 weights and at most 8 rows, RoPE and the tree-slot write run in
+     * the QKV launch's epilogue: that call records no EAGLE_ROLE_ROPE launch, and
+     * its QKV bytes count rotated q out (fp32) and k, v out (cache type). */
 int eagle_profile_enable(int32_t max_launches);
 int eagle_profile_reset(void);
 int eagle_profile_disable(void);
