@@ -20,9 +20,11 @@
 // bonus token, and the status bits it raises), and a second launch walks the
 // trees through those results, one thread per sequence.  Without a
 // workspace, one workgroup per sequence processes the nodes along its path.
-// Thread t owns the EPT consecutive tokens [t*EPT, (t+1)*EPT): p and q live in
-// registers, a node needs block reductions only, and the inverse-CDF draw is
-// one block scan.
+// Thread t holds EPT tokens, in runs of up to 4 consecutive ones laid out so
+// that each load instruction of a wave reads one contiguous span of the row
+// (coalesced); p lives in registers, q in the thread's own LDS column, a node
+// needs block reductions only, and the inverse-CDF draw is one token-order
+// scan.
 #include "common.h"
 #include "kernels.h"
 
@@ -52,46 +54,75 @@ __device__ __forceinline__ int bmin_int(int v, int* red) {
   return r;
 }
 
-// Exclusive block scan of one float per thread (fixed order).
-__device__ __forceinline__ float bscan_excl(float v, float* red, float* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float t = __shfl_up(inc, o, WAVE);
-    if (lane >= o) inc += t;
-  }
-  __syncthreads();
-  if (lane == 63) red[w] = inc;
-  __syncthreads();
-  float before = 0.f, all = 0.f;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    if (i < w) before += red[i];
-    all += red[i];
-  }
-  *total = all;
-  return before + inc - v;
+// Token layout: thread t (wave w, lane l) holds its EPT tokens in chunks of
+// CW = min(EPT, 4) consecutive ones; chunk j sits at w*EPT*64 + j*64*CW + l*CW,
+// so a wave's load of chunk j is 64*CW consecutive floats.  Element e = j*CW + c.
+template <int EPT>
+struct Lay {
+  static constexpr int CW = EPT < 4 ? EPT : 4, J = EPT / CW, SPAN = EPT * WAVE;
+};
+template <int EPT>
+__device__ __forceinline__ int tok_of(int t, int e) {
+  using L = Lay<EPT>;
+  return (t / WAVE) * L::SPAN + (e / L::CW) * (WAVE * L::CW) + (t % WAVE) * L::CW + e % L::CW;
+}
+// the thread and element holding token y
+template <int EPT>
+__device__ __forceinline__ void owner_of(int y, int* t, int* e) {
+  using L = Lay<EPT>;
+  const int w = y / L::SPAN, r = y % L::SPAN;
+  const int j = r / (WAVE * L::CW), r2 = r % (WAVE * L::CW);
+  *t = w * WAVE + r2 / L::CW;
+  *e = j * L::CW + r2 % L::CW;
 }
 
-// Inverse CDF in token order: smallest y with cum(y) > u * sum(w).
+// Inverse CDF in token order: smallest y with cum(y) > u * sum(w).  The
+// running sum before a token is (waves before) + (chunks before, in this wave)
+// + (lanes before, in this chunk) + (this run's earlier tokens).
 template <int EPT>
 __device__ int draw_token(const float (&w)[EPT], int vocab, float u, float* fred, int* ired) {
-  float own = 0.f;
+  using L = Lay<EPT>;
+  const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+  float lex[L::J], coff[L::J];
+  float off = 0.f;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) own += w[e];
-  float total;
-  const float excl = bscan_excl(own, fred, &total);
+  for (int j = 0; j < L::J; ++j) {
+    float sj = 0.f;
+#pragma unroll
+    for (int c = 0; c < L::CW; ++c) sj += w[j * L::CW + c];
+    float inc = sj;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+      const float tv = __shfl_up(inc, o, WAVE);
+      if (lane >= o) inc += tv;
+    }
+    lex[j] = inc - sj;
+    coff[j] = off;
+    off += __shfl(inc, WAVE - 1, WAVE);
+  }
+  __syncthreads();
+  if (lane == 0) fred[wv] = off;
+  __syncthreads();
+  float before = 0.f, total = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    if (i < wv) before += fred[i];
+    total += fred[i];
+  }
   const float T = u * total;
   int cand = 0x7fffffff, last = -1;
-  float c = excl;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int y = threadIdx.x * EPT + e;
-    if (y < vocab) {
-      c += w[e];
-      if (w[e] > 0.f) last = y;
-      if (c > T && cand == 0x7fffffff && w[e] > 0.f) cand = y;
+  for (int j = 0; j < L::J; ++j) {
+    float c = before + coff[j] + lex[j];
+#pragma unroll
+    for (int cc = 0; cc < L::CW; ++cc) {
+      const int e = j * L::CW + cc;
+      const int y = tok_of<EPT>(threadIdx.x, e);
+      if (y < vocab) {
+        c += w[e];
+        if (w[e] > 0.f) last = y;
+        if (c > T && cand == 0x7fffffff && w[e] > 0.f) cand = y;
+      }
     }
   }
   const int y = bmin_int(cand, ired);
@@ -99,20 +130,31 @@ __device__ int draw_token(const float (&w)[EPT], int vocab, float u, float* fred
   return -bmin_int(-last, ired);  // rounding left no boundary above T: last positive token
 }
 
-// Thread t's EPT consecutive entries of a row; -inf beyond the vocabulary.
+// Thread t's EPT entries of a row in the layout above; -inf beyond the vocabulary.
+// With V a multiple of 4 and an aligned row, every chunk is one 16-byte load
+// per lane (from an address clamped into the row; lanes past the end discard
+// it); otherwise element loads.  The choice is uniform over the launch.
 template <int EPT>
 __device__ __forceinline__ bool load_row(const float* row, int V, float (&v)[EPT]) {
-  const int y0 = threadIdx.x * EPT;
+  using L = Lay<EPT>;
   bool bad = false;
-  if (EPT % 4 == 0 && y0 + EPT <= V) {
+  if (L::CW == 4 && V % 4 == 0 && ((uintptr_t)row & 15) == 0) {
 #pragma unroll
-    for (int e = 0; e < EPT; e += 4) {
-      const float4 f = *(const float4*)(row + y0 + e);
-      v[e] = f.x; v[e + 1] = f.y; v[e + 2] = f.z; v[e + 3] = f.w;
+    for (int j = 0; j < L::J; ++j) {
+      const int y0 = tok_of<EPT>(threadIdx.x, j * L::CW);
+      const float4 f = *(const float4*)(row + min(y0, V - 4));
+      const bool in = y0 < V;
+      v[j * L::CW] = in ? f.x : -INFINITY;
+      v[j * L::CW + 1] = in ? f.y : -INFINITY;
+      v[j * L::CW + 2] = in ? f.z : -INFINITY;
+      v[j * L::CW + 3] = in ? f.w : -INFINITY;
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) v[e] = (y0 + e < V) ? row[y0 + e] : -INFINITY;
+    for (int e = 0; e < EPT; ++e) {
+      const int y = tok_of<EPT>(threadIdx.x, e);
+      v[e] = y < V ? row[y] : -INFINITY;
+    }
   }
 #pragma unroll
   for (int e = 0; e < EPT; ++e) bad |= (v[e] != v[e]);
@@ -219,10 +261,10 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
     int cand = 0x7fffffff;
 #pragma unroll
     for (int e = 0; e < EPT; ++e)
-      if (p[e] == mx && cand == 0x7fffffff) cand = t * EPT + e;
+      if (p[e] == mx) cand = min(cand, tok_of<EPT>(t, e));
     const int am = bmin_int(cand, ired);
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) p[e] = (t * EPT + e == am) ? 1.f : 0.f;
+    for (int e = 0; e < EPT; ++e) p[e] = (tok_of<EPT>(t, e) == am) ? 1.f : 0.f;
   } else {
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
@@ -262,7 +304,9 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
     const int x = sh.ktok[i];
     const float r = philox_uniform(a.seed, a.round, b, u, i);
     const bool x_ok = x >= 0 && x < V;
-    const bool owner = x_ok && t == x / EPT;
+    int ot = -1, oe = 0;
+    if (x_ok) owner_of<EPT>(x, &ot, &oe);
+    const bool owner = t == ot;
     // residual mass norm(max(0, p - q)) taken before the test (needed only on a
     // rejection; a zero mass leaves p untouched), one reduction with p(x), q(x)
     const float invS = 1.f / S;
@@ -274,8 +318,8 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
       float px = 0.f;
 #pragma unroll
       for (int e = 0; e < EPT; ++e)
-        if (e == x % EPT) px = p[e];
-      sh.pq[pb] = make_float2(px, Q(x % EPT));
+        if (e == oe) px = p[e];
+      sh.pq[pb] = make_float2(px, Q(oe));
     }
     const float Z = red2<true>(rs, 0.f, sh, buf).x;
     const float px = x_ok ? sh.pq[pb].x : 0.f;
@@ -290,7 +334,7 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
     if (ok) return make_int2(c, 0);
     // residual update; without iid the rejected token leaves q (its column
     // zeroed) and the remaining mass is summed in the same pass over q
-    const int xe = (!iid && owner) ? x % EPT : -1;
+    const int xe = (!iid && owner) ? oe : -1;
     float qs = 0.f;
     if (Z > 0.f) {
       const float inv = 1.f / Z;
