@@ -305,12 +305,24 @@ __global__ void __launch_bounds__(256) attn_partial_kernel(AttnArgs a) {
 
 // Merge split partials: out[row, h*hd + d] (fp32) = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
 // One workgroup per (row, head); the split weights are computed once in LDS.
+// Up to CMB_PRE splits, a thread loads its output element's partial from every
+// split at the start, beside the statistics (one round of independent loads
+// instead of the statistics and then the values); the sum runs in split order
+// either way.
+constexpr int CMB_PRE = 16;
+
 __global__ void __launch_bounds__(128) attn_combine_kernel(AttnArgs a, int hd) {
   __shared__ float wsplit[1024];
   __shared__ float s_inv;
   const int row = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const size_t stride = (size_t)a.n_rows * a.hq * (hd + 2);
   const float* base = a.part + ((size_t)row * a.hq + h) * (hd + 2);
+  const bool pre = a.n_splits <= CMB_PRE && hd <= 128;  // uniform
+  float v[CMB_PRE];
+  if (pre) {
+#pragma unroll
+    for (int s = 0; s < CMB_PRE; ++s) v[s] = (s < a.n_splits && t < hd) ? base[s * stride + 2 + t] : 0.f;
+  }
   if (t < WAVE) {
     float M = -INFINITY;
     for (int s = t; s < a.n_splits; s += WAVE) M = fmaxf(M, base[s * stride]);
@@ -326,6 +338,16 @@ __global__ void __launch_bounds__(128) attn_combine_kernel(AttnArgs a, int hd) {
     if (t == 0) s_inv = 1.f / L;
   }
   __syncthreads();
+  if (pre) {
+    if (t < hd) {
+      float acc = 0.f;
+#pragma unroll
+      for (int s = 0; s < CMB_PRE; ++s)
+        if (s < a.n_splits) acc += wsplit[s] * v[s];
+      a.out[((size_t)row * a.hq + h) * hd + t] = acc * s_inv;
+    }
+    return;
+  }
   for (int dd = t; dd < hd; dd += 128) {
     float acc = 0.f;
     for (int s = 0; s < a.n_splits; ++s) acc += wsplit[s] * base[s * stride + 2 + dd];
