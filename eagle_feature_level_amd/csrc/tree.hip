@@ -100,13 +100,15 @@ __global__ void __launch_bounds__(256) tree_expand_kernel(ExpandArgs a) {
   if (t < total) {
     int rank = 0;
     if (a.nchild) {
+#pragma unroll 8
       for (int j = 0; j < t; ++j) rank += cqual[j];
       if (cqual[t] && rank < a.n_next) nf[rank] = t;
     } else {
       const float v = clogv[t];
+#pragma unroll 8
       for (int j = 0; j < total; ++j) {
         const float w = clogv[j];
-        rank += (w > v) || (w == v && j < t);
+        rank += (int)(w > v) | ((int)(w == v) & (int)(j < t));
       }
       if (rank < a.n_next) nf[rank] = t;
     }
@@ -173,9 +175,11 @@ __global__ void __launch_bounds__(512) tree_finalize_kernel(FinalizeArgs a) {
       const float v = lv[i];
       const int d = dp[i];
       int rank = 0;
-      for (int j = 1; j < cnt; ++j) {
+#pragma unroll 8
+      for (int j = 1; j < cnt; ++j) {  // branch-free: both fields read, the test in bit operations
         const float w = lv[j];
-        rank += (w > v) || (w == v && (dp[j] < d || (dp[j] == d && j < i)));
+        const int dj = dp[j];
+        rank += (int)(w > v) | ((int)(w == v) & ((int)(dj < d) | ((int)(dj == d) & (int)(j < i))));
       }
       keep = rank < a.m;
     }
@@ -187,7 +191,11 @@ __global__ void __launch_bounds__(512) tree_finalize_kernel(FinalizeArgs a) {
     if (!kept[i]) continue;
     const int d = dp[i];
     int pos = 1;
-    for (int j = 1; j < cnt; ++j) pos += kept[j] && (dp[j] < d || (dp[j] == d && j < i));
+#pragma unroll 8
+    for (int j = 1; j < cnt; ++j) {
+      const int dj = dp[j];
+      pos += kept[j] & ((int)(dj < d) | ((int)(dj == d) & (int)(j < i)));
+    }
     where[i] = pos;
     if (pos < 64) tpool[pos] = i;
   }
@@ -219,9 +227,16 @@ __global__ void __launch_bounds__(512) tree_finalize_kernel(FinalizeArgs a) {
     }
   }
   __syncthreads();
-  if (t == 0) {
-    tmask[0] = 0ull;
-    for (int u = 1; u < n; ++u) tmask[u] = (u < nreal && tpar[u] >= 0) ? (tmask[tpar[u]] | (1ull << u)) : (1ull << u);
+  // mask of node u: its own bit and its ancestors' up to (not including) the
+  // root, each thread walking its own chain (parents precede children)
+  if (t < n) {
+    uint64_t m = 0ull;
+    if (t >= 1) {
+      m = 1ull << t;
+      if (t < nreal)
+        for (int v = tpar[t], hop = 0; v > 0 && hop < 64; v = tpar[v], ++hop) m |= 1ull << v;
+    }
+    tmask[t] = m;
   }
   __syncthreads();
   if (t < n) {
