@@ -5,6 +5,11 @@ as a transaction: after verification only the accepted path's entries join
 the cache; rejected branches are dropped.  The j-th accepted drafted node
 (depth j + 1) sits at rotary position L_b + j, so its k, v become prefix
 position L_b + j and the prefix grows by the number of accepted drafts.
+
+``commit_slots`` is the same transaction for the catch-up rows of the next
+round (the drafter's own rows over the committed tokens, recomputed from the
+target's true features): their k, v sit in tree slots 0..n-1 in position order
+and become prefix positions L_b..L_b+n-1.
 """
 from __future__ import annotations
 
@@ -39,5 +44,30 @@ def commit(prefix_k, prefix_v, lens, caps, tree_k, tree_v, paths, accept_len, no
         out_k.append(np.concatenate([np.asarray(prefix_k[b])[:, :L], add_k], axis=1))
         out_v.append(np.concatenate([np.asarray(prefix_v[b])[:, :L], add_v], axis=1))
         out_len.append(L + A)
+        flags.append(0)
+    return out_k, out_v, out_len, flags
+
+
+def commit_slots(prefix_k, prefix_v, lens, caps, tree_k, tree_v, counts):
+    """Append tree slots 0..counts[b]-1 of sequence b to its prefix at
+    positions L_b.. (caps: per-sequence capacity, None = no room).  A count
+    outside 0..64 is a malformed request.  Returns the new prefixes, lengths
+    and flags (OVERFLOW / BAD_PATH leave the sequence unchanged)."""
+    out_k, out_v, out_len, flags = [], [], [], []
+    for b in range(len(prefix_k)):
+        L = int(lens[b])
+        C = L if caps is None else int(caps[b])
+        n = int(counts[b])
+        if n < 0 or n > 64 or L + n > C:
+            out_k.append(np.asarray(prefix_k[b]).copy())
+            out_v.append(np.asarray(prefix_v[b]).copy())
+            out_len.append(L)
+            flags.append(BAD_PATH if (n < 0 or n > 64) else OVERFLOW)
+            continue
+        add_k = np.stack([tree_k[b, s] for s in range(n)], axis=1) if n else np.zeros_like(prefix_k[b][:, :0])
+        add_v = np.stack([tree_v[b, s] for s in range(n)], axis=1) if n else np.zeros_like(prefix_v[b][:, :0])
+        out_k.append(np.concatenate([np.asarray(prefix_k[b])[:, :L], add_k], axis=1))
+        out_v.append(np.concatenate([np.asarray(prefix_v[b])[:, :L], add_v], axis=1))
+        out_len.append(L + n)
         flags.append(0)
     return out_k, out_v, out_len, flags

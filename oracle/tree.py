@@ -34,9 +34,13 @@ import numpy as np
 
 
 class Pool:
-    """Candidate pool of one sequence (node 0 = root)."""
+    """Candidate pool of one sequence (node 0 = root).  `invalid` is set when an
+    expansion cannot be carried out (a NaN value, or a template asking a node
+    for more children than its row ranks); the pool then stops growing and its
+    flattened tree is the root alone."""
 
     def __init__(self, root_token: int, root_feat_row: int):
+        self.invalid = False
         self.parent = [-1]
         self.token = [int(root_token)]
         self.depth = [0]
@@ -64,13 +68,21 @@ def expand(pool: Pool, frontier, topk_idx, topk_logq, k: int, nchild=None):
 
     topk_idx / topk_logq: per frontier position, the node's ranked tokens.
     nchild: static template child counts by node id (None = EAGLE-2).
-    Returns the next frontier (pool ids).
+    Returns the next frontier (pool ids).  A NaN log-value among the new
+    children (a NaN logit row makes every log q of that row NaN), or a
+    template count beyond the ranked tokens a row provides, marks the pool
+    invalid instead: nothing is added and the frontier is empty.
     """
+    if pool.invalid:
+        return []
+    want = [(f, r) for f, u in enumerate(frontier) for r in range(k if nchild is None else int(nchild[u]))]
+    if any(r >= len(topk_idx[f]) for f, r in want) or any(
+            np.isnan(np.float32(np.float32(pool.logv[frontier[f]]) + np.float32(topk_logq[f][r]))) for f, r in want):
+        pool.invalid = True
+        return []
     children = []
-    for f, u in enumerate(frontier):
-        c = k if nchild is None else int(nchild[u])
-        for r in range(c):
-            children.append(pool.add(u, topk_idx[f][r], topk_logq[f][r]))
+    for f, r in want:
+        children.append(pool.add(frontier[f], topk_idx[f][r], topk_logq[f][r]))
     if nchild is None:
         ranked = sorted(children, key=lambda i: (-float(pool.logv[i]), i))
         return ranked[:k]
@@ -97,9 +109,10 @@ def assign_rows(pool: Pool, frontier, step: int, k: int, static: bool, feat_row_
 def finalize(pool: Pool, m: int = 0):
     """Rerank (top-m by value, ties to shallower then earlier) and flatten.
 
-    m = 0 keeps every pool node (static templates).  Returns dict of arrays over
-    tree indices: pool_id, parent, token, depth, mask (uint64)."""
-    cand = list(range(1, len(pool)))
+    m = 0 keeps every pool node (static templates).  An invalid pool gives the
+    root alone.  Returns dict of arrays over tree indices: pool_id, parent,
+    token, depth, mask (uint64)."""
+    cand = [] if pool.invalid else list(range(1, len(pool)))
     if m:
         cand = sorted(cand, key=lambda i: (-float(pool.logv[i]), pool.depth[i], i))[:m]
     order = [0] + sorted(cand, key=lambda i: (pool.depth[i], i))
