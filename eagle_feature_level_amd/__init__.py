@@ -11,7 +11,9 @@ from __future__ import annotations
 import ctypes
 
 from . import _abi
-from ._abi import (EAGLE_COMMIT_BAD_PATH, EAGLE_COMMIT_OVERFLOW, EAGLE_ACT_BF16, EAGLE_SAMPLE_CHILDREN, EAGLE_BF16, EAGLE_F32, EAGLE_HEAD_ONLY, EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK, EAGLE_VERIFY_GREEDY,
+from ._abi import (EAGLE_ACT_BF16, EAGLE_BF16, EAGLE_COMMIT_BAD_PATH, EAGLE_COMMIT_OVERFLOW, EAGLE_F32,
+                   EAGLE_F_BADTREE, EAGLE_F_NAN, EAGLE_F_QEMPTY, EAGLE_F_QZERO, EAGLE_F_ZRES, EAGLE_FEATURES_ONLY,
+                   EAGLE_HEAD_ONLY, EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK, EAGLE_SAMPLE_CHILDREN, EAGLE_VERIFY_GREEDY,
                    EAGLE_VERIFY_IID, EagleError, eagle_draft_out, eagle_kv, eagle_pool, eagle_rows, eagle_shape,
                    eagle_weights)
 
@@ -22,7 +24,8 @@ __all__ = ["eagle_workspace_bytes", "eagle_draft_step", "eagle_softmax_topk", "e
            "eagle_sample_topk", "eagle_fuse_features", "eagle_fuse_workspace_bytes", "eagle_commit",
            "EAGLE_COMMIT_OVERFLOW", "EAGLE_COMMIT_BAD_PATH", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
            "EAGLE_F32", "EAGLE_MAX_SLOTS", "EAGLE_MAX_TOPK", "eagle_profile_enable", "eagle_profile_reset",
-           "eagle_profile_disable", "eagle_profile_read"]
+           "eagle_profile_disable", "eagle_profile_read", "eagle_catchup_rows", "eagle_commit_catchup",
+           "EAGLE_FEATURES_ONLY", "EAGLE_F_ZRES", "EAGLE_F_QZERO", "EAGLE_F_QEMPTY", "EAGLE_F_NAN", "EAGLE_F_BADTREE"]
 
 WEIGHT_NAMES = [f[0] for f in eagle_weights._fields_]
 
@@ -108,6 +111,25 @@ def eagle_commit(shape, batch, n_nodes, path, accept_len, node_slot, tree_k, tre
                           _ptr(tree_k), _ptr(tree_v), _ptr(prefix_k), _ptr(prefix_v), _ptr(prefix_off),
                           _ptr(prefix_len), _ptr(prefix_cap), _ptr(out_flags), _stream(stream))
     _abi.check("eagle_commit", rc)
+
+
+def eagle_catchup_rows(batch, n_nodes, max_depth, tree_token, path, accept_len, next_token, prefix_len, feat_row0,
+                       row_token, row_parent, row_pos, row_slot, row_mask, row_start, last_row, count, stream=None):
+    lib = _abi.load()
+    rc = lib.eagle_catchup_rows(batch, n_nodes, max_depth, _ptr(tree_token), _ptr(path), _ptr(accept_len),
+                                _ptr(next_token), _ptr(prefix_len), feat_row0, _ptr(row_token), _ptr(row_parent),
+                                _ptr(row_pos), _ptr(row_slot), _ptr(row_mask), _ptr(row_start), _ptr(last_row),
+                                _ptr(count), _stream(stream))
+    _abi.check("eagle_catchup_rows", rc)
+
+
+def eagle_commit_catchup(shape, batch, count, tree_k, tree_v, prefix_k, prefix_v, prefix_off, prefix_len, prefix_cap,
+                         feat, last_row, root_feat, out_flags, stream=None):
+    lib = _abi.load()
+    rc = lib.eagle_commit_catchup(ctypes.byref(shape), batch, _ptr(count), _ptr(tree_k), _ptr(tree_v), _ptr(prefix_k),
+                                  _ptr(prefix_v), _ptr(prefix_off), _ptr(prefix_len), _ptr(prefix_cap), _ptr(feat),
+                                  _ptr(last_row), _ptr(root_feat), _ptr(out_flags), _stream(stream))
+    _abi.check("eagle_commit_catchup", rc)
 
 
 def eagle_fuse_workspace_bytes(shape, max_rows):

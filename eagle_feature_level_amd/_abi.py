@@ -16,10 +16,11 @@ c_i32, c_u64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_uint64, ctypes.c_fl
 
 EAGLE_OK, EAGLE_EINVAL, EAGLE_EUNSUPPORTED, EAGLE_EWORKSPACE, EAGLE_EHIP = 0, -1, -2, -3, -4
 EAGLE_F32, EAGLE_BF16 = 0, 1
-EAGLE_HEAD_ONLY, EAGLE_ACT_BF16, EAGLE_SAMPLE_CHILDREN = 1, 2, 4
+EAGLE_HEAD_ONLY, EAGLE_ACT_BF16, EAGLE_SAMPLE_CHILDREN, EAGLE_FEATURES_ONLY = 1, 2, 4, 8
 EAGLE_VERIFY_GREEDY, EAGLE_VERIFY_IID = 1, 2
 EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK = 64, 16
 EAGLE_COMMIT_OVERFLOW, EAGLE_COMMIT_BAD_PATH = 1, 2
+EAGLE_F_ZRES, EAGLE_F_QZERO, EAGLE_F_QEMPTY, EAGLE_F_NAN, EAGLE_F_BADTREE = 1, 2, 4, 8, 16
 ROLES = ("fc", "qkv", "rope", "attn", "o", "gate_up", "down", "lm_head", "topk", "rows")
 
 
@@ -63,6 +64,10 @@ _SIGS = {
     "eagle_fuse_features": (c_i32, [P(eagle_shape), c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "eagle_commit": (c_i32, [P(eagle_shape), c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                              c_vp, c_vp, c_vp]),
+    "eagle_catchup_rows": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                   c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "eagle_commit_catchup": (c_i32, [P(eagle_shape), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                     c_vp, c_vp, c_vp, c_vp]),
     "eagle_sample_topk": (c_i32, [c_i32, c_i32, c_vp, c_i32, c_u64, c_u64, c_i32, c_vp, c_vp, c_vp, c_vp, c_size,
                                   c_vp]),
     "eagle_tree_init": (c_i32, [c_i32, P(eagle_pool), c_vp, c_i32, c_vp]),

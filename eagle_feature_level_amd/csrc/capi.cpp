@@ -304,6 +304,78 @@ int eagle_commit(const eagle_shape* shape, int32_t batch, int32_t n_nodes, const
   return e == hipSuccess ? EAGLE_OK : hip_fail(e);
 }
 
+int eagle_catchup_rows(int32_t batch, int32_t n_nodes, int32_t max_depth, const int32_t* tree_token,
+                       const int32_t* path, const int32_t* accept_len, const int32_t* next_token,
+                       const int32_t* prefix_len, int32_t feat_row0, int32_t* row_token, int32_t* row_parent,
+                       int32_t* row_pos, int32_t* row_slot, uint64_t* row_mask, int32_t* row_start, int32_t* last_row,
+                       int32_t* count, eagle_stream_t stream) {
+  if (batch < 0 || n_nodes < 1 || max_depth < 0 || feat_row0 < 0) return EAGLE_EINVAL;
+  if (batch == 0) return EAGLE_OK;
+  if (!tree_token || !path || !accept_len || !next_token || !prefix_len || !row_token || !row_parent || !row_pos ||
+      !row_slot || !row_mask || !row_start || !last_row || !count)
+    return EAGLE_EINVAL;
+  if (n_nodes > EAGLE_MAX_SLOTS || max_depth + 1 > EAGLE_MAX_SLOTS) return EAGLE_EUNSUPPORTED;
+  int rc = check_device();
+  if (rc) return rc;
+  CatchupArgs a;
+  a.batch = batch;
+  a.n_nodes = n_nodes;
+  a.max_depth = max_depth;
+  a.feat_row0 = feat_row0;
+  a.tree_token = tree_token;
+  a.path = path;
+  a.accept_len = accept_len;
+  a.next_token = next_token;
+  a.prefix_len = prefix_len;
+  a.row_token = row_token;
+  a.row_parent = row_parent;
+  a.row_pos = row_pos;
+  a.row_slot = row_slot;
+  a.row_mask = row_mask;
+  a.row_start = row_start;
+  a.last_row = last_row;
+  a.count = count;
+  hipError_t e = launch_catchup_rows(a, (hipStream_t)stream);
+  return e == hipSuccess ? EAGLE_OK : hip_fail(e);
+}
+
+int eagle_commit_catchup(const eagle_shape* shape, int32_t batch, const int32_t* count, const void* tree_k,
+                         const void* tree_v, void* prefix_k, void* prefix_v, const int64_t* prefix_off,
+                         int32_t* prefix_len, const int32_t* prefix_cap, const float* feat, const int32_t* last_row,
+                         float* root_feat, int32_t* out_flags, eagle_stream_t stream) {
+  if (!shape_ok(shape) || batch < 0) return EAGLE_EINVAL;
+  if (batch == 0) return EAGLE_OK;
+  if (!count || !tree_k || !tree_v || !prefix_k || !prefix_v || !prefix_off || !prefix_len || !out_flags)
+    return EAGLE_EINVAL;
+  if ((feat != nullptr) != (last_row != nullptr) || (feat != nullptr) != (root_feat != nullptr)) return EAGLE_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  CommitArgs a;
+  memset(&a, 0, sizeof(a));
+  a.batch = batch;
+  a.n_nodes = EAGLE_MAX_SLOTS;
+  a.hkv = shape->n_kv_heads;
+  a.hd = shape->head_dim;
+  a.path = nullptr;  // slot mode: slots 0..count[b]-1
+  a.accept_len = count;
+  a.tree_k = tree_k;
+  a.tree_v = tree_v;
+  a.prefix_k = prefix_k;
+  a.prefix_v = prefix_v;
+  a.prefix_off = prefix_off;
+  a.prefix_len = prefix_len;
+  a.prefix_cap = prefix_cap;
+  a.out_flags = out_flags;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_commit(a, shape->dtype == EAGLE_BF16, st);
+  if (e != hipSuccess) return hip_fail(e);
+  if (feat) {
+    e = launch_gather_rows(feat, last_row, batch, shape->d, root_feat, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return EAGLE_OK;
+}
+
 int eagle_sample_topk(int32_t n_rows, int32_t vocab, const float* logits, int32_t topk, uint64_t seed, uint64_t round,
                       int32_t row_base, float* lse, int32_t* topk_idx, float* topk_logq, void* workspace,
                       size_t workspace_bytes, eagle_stream_t stream) {
@@ -324,8 +396,10 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
                      const float* feat_in, const eagle_kv* kv, const eagle_draft_out* out, void* workspace,
                      size_t workspace_bytes, eagle_stream_t stream) {
   if (!shape_ok(shape) || !w || !rows || !out) return EAGLE_EINVAL;
-  if (flags & ~(EAGLE_HEAD_ONLY | EAGLE_ACT_BF16 | EAGLE_SAMPLE_CHILDREN)) return EAGLE_EINVAL;
+  if (flags & ~(EAGLE_HEAD_ONLY | EAGLE_ACT_BF16 | EAGLE_SAMPLE_CHILDREN | EAGLE_FEATURES_ONLY)) return EAGLE_EINVAL;
+  if ((flags & EAGLE_HEAD_ONLY) && (flags & EAGLE_FEATURES_ONLY)) return EAGLE_EINVAL;
   const bool sample = flags & EAGLE_SAMPLE_CHILDREN;
+  const bool feat_only = flags & EAGLE_FEATURES_ONLY;
   if (sample && shape && shape->vocab > TOPK_SAMPLE_MAX_VOCAB) return EAGLE_EUNSUPPORTED;
   const bool head_only = flags & EAGLE_HEAD_ONLY;
   const int act16 = (flags & EAGLE_ACT_BF16) ? 1 : 0;
@@ -333,11 +407,12 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
   const int M = rows->n_rows;
   if (M < 0 || rows->batch <= 0) return EAGLE_EINVAL;
   if (M == 0) return EAGLE_OK;
-  if (!feat_in || !rows->parent || !out->logits || !out->lse || !out->topk_idx || !out->topk_logq || !workspace)
-    return EAGLE_EINVAL;
-  if (!w->lm_head) return EAGLE_EINVAL;
-  if (out->topk < 1 || out->topk > shape->vocab) return EAGLE_EINVAL;
-  if (out->topk > EAGLE_MAX_TOPK) return EAGLE_EUNSUPPORTED;
+  if (!feat_in || !rows->parent || !workspace) return EAGLE_EINVAL;
+  if (!feat_only) {
+    if (!out->logits || !out->lse || !out->topk_idx || !out->topk_logq || !w->lm_head) return EAGLE_EINVAL;
+    if (out->topk < 1 || out->topk > shape->vocab) return EAGLE_EINVAL;
+    if (out->topk > EAGLE_MAX_TOPK) return EAGLE_EUNSUPPORTED;
+  }
   int rc = shape_supported(shape);
   if (rc) return rc;
   const eagle_shape& s = *shape;
@@ -559,6 +634,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       if (e != hipSuccess) return hip_fail(e);
     }
   }
+  if (feat_only) return EAGLE_OK;  // f^ (and the rows' k, v) are all the caller asked for
   // a8 (a0 with HEAD_ONLY): logits = f lm_head^T
   {
     GemmArgs a = gemm_base(M, s.vocab, d);
@@ -705,6 +781,8 @@ int eagle_tree_finalize(int32_t batch, int32_t m, int32_t n_nodes, const eagle_p
     return EAGLE_EINVAL;
   if (n_nodes > EAGLE_MAX_SLOTS) return EAGLE_EUNSUPPORTED;
   if (pool->cap < 1 || pool->cap > 2048) return EAGLE_EUNSUPPORTED;
+  // every kept node must fit: m drafted nodes and the root, or the whole pool when m = 0
+  if ((m > 0 ? m + 1 : pool->cap) > n_nodes) return EAGLE_EINVAL;
   int rc = check_device();
   if (rc) return rc;
   FinalizeArgs a;

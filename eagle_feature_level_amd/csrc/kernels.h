@@ -132,8 +132,8 @@ hipError_t launch_verify(VerifyArgs a, void* ws, hipStream_t s);
 constexpr int kCommitOverflow = 1, kCommitBadPath = 2;  // = EAGLE_COMMIT_OVERFLOW / _BAD_PATH
 struct CommitArgs {
   int batch, n_nodes, hkv, hd;
-  const int32_t* path;        // [batch, n_nodes]: accepted drafted nodes, -1 padded
-  const int32_t* accept_len;  // [batch]: accepted nodes + 1
+  const int32_t* path;        // [batch, n_nodes]: accepted drafted nodes, -1 padded; nullptr: slot mode
+  const int32_t* accept_len;  // [batch]: accepted nodes + 1 (slot mode: slots 0..n-1 to append)
   const int32_t* node_slot;   // [batch, n_nodes] tree slot of each node, or nullptr: slot = node
   const void* tree_k;
   const void* tree_v;
@@ -145,3 +145,17 @@ struct CommitArgs {
   int32_t* out_flags;
 };
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t s);
+
+// catch-up rows of the drafter over each sequence's committed tokens
+struct CatchupArgs {
+  int batch, n_nodes, max_depth, feat_row0;
+  const int32_t* tree_token;  // [batch, n_nodes]
+  const int32_t* path;        // [batch, n_nodes] verified path
+  const int32_t* accept_len;  // [batch]
+  const int32_t* next_token;  // [batch]
+  const int32_t* prefix_len;  // [batch]
+  int32_t *row_token, *row_parent, *row_pos, *row_slot, *row_start, *last_row, *count;
+  uint64_t* row_mask;
+};
+hipError_t launch_catchup_rows(const CatchupArgs& a, hipStream_t s);
+hipError_t launch_gather_rows(const float* feat, const int32_t* rows, int batch, int d, float* out, hipStream_t s);

@@ -34,6 +34,12 @@ constexpr int EX_MAX_CHILD = 256;  // 16 x 16
 // Every global read the kernel needs is issued in its first phase (the
 // frontier, then the frontier nodes' own fields and the sequence's counters),
 // and in the second (the children's top-k entries); the rest works from LDS.
+// Nothing is written to the pool before the expansion is known to be valid:
+// a NaN log-value among the children (a NaN logit row gives every log q of
+// that row NaN), a template asking a node for more children than its row
+// ranks, or a template whose qualifying children differ in number from n_next
+// mark the pool invalid (count = -1, the same as an overflow), so that every
+// rank slot of the next frontier is filled whenever anything is written.
 __global__ void __launch_bounds__(256) tree_expand_kernel(ExpandArgs a) {
   __shared__ int off[65];
   __shared__ int fr[64], fcnt[64], fdep[64], ffrow[64];
@@ -42,10 +48,11 @@ __global__ void __launch_bounds__(256) tree_expand_kernel(ExpandArgs a) {
   __shared__ float clogv[EX_MAX_CHILD];
   __shared__ int cqual[EX_MAX_CHILD], cf[EX_MAX_CHILD], ctok[EX_MAX_CHILD];
   __shared__ int nf[64];
-  __shared__ int s_total, s_cnt, s_plen;
+  __shared__ int s_total, s_cnt, s_plen, s_bad;
   const int b = blockIdx.x, t = threadIdx.x;
   const PoolArgs& p = a.pool;
   const size_t base = (size_t)b * p.cap;
+  if (t < 64) nf[t] = -1;
   if (t < a.n_prev) {
     const int u = p.frontier[(size_t)b * 64 + t];
     fr[t] = u;
@@ -61,43 +68,53 @@ __global__ void __launch_bounds__(256) tree_expand_kernel(ExpandArgs a) {
   }
   __syncthreads();
   if (t == 0) {
-    int acc = 0;
+    int acc = 0, bad = 0;
     for (int f = 0; f < a.n_prev; ++f) {
       off[f] = acc;
       acc += fcnt[f];
+      bad |= (fcnt[f] < 0) | (fcnt[f] > a.topk);
     }
     off[a.n_prev] = acc;
     s_total = acc;
+    s_bad = bad;
   }
   __syncthreads();
   const int total = s_total, cnt = s_cnt;
-  if (cnt < 0 || cnt + total > p.cap || total > EX_MAX_CHILD) {
-    if (t == 0) p.count[b] = -1;  // overflow: pool left unchanged, marked invalid
+  if (s_bad || cnt < 0 || cnt + total > p.cap || total > EX_MAX_CHILD) {
+    if (t == 0) p.count[b] = -1;  // overflow or invalid request: pool left unchanged, marked invalid
     return;
   }
+  bool nan_child = false;
+  int qual = 0;
   if (t < total) {
     int f = 0;
     while (off[f + 1] <= t) ++f;
     const int r = t - off[f];
-    const int u = fr[f];
     const int row = b * a.n_prev + f;
-    const int id = cnt + t;
-    const int tok = a.topk_idx[(size_t)row * a.topk + r];
     const float lv = __fadd_rn(flogv[f], a.topk_logq[(size_t)row * a.topk + r]);
-    p.parent[base + id] = u;
-    p.token[base + id] = tok;
+    clogv[t] = lv;
+    cf[t] = f;
+    ctok[t] = a.topk_idx[(size_t)row * a.topk + r];
+    qual = a.nchild ? (a.nchild[cnt + t] > 0) : 1;
+    cqual[t] = qual;
+    nan_child = lv != lv;
+  }
+  const int n_nan = __syncthreads_count(nan_child);
+  const int n_qual = __syncthreads_count(qual);
+  if (n_nan || (a.nchild && n_qual != a.n_next)) {
+    if (t == 0) p.count[b] = -1;
+    return;
+  }
+  if (t < total) {
+    const int f = cf[t];
+    const int id = cnt + t;
+    p.parent[base + id] = fr[f];
+    p.token[base + id] = ctok[t];
     p.depth[base + id] = fdep[f] + 1;
-    p.logv[base + id] = lv;
+    p.logv[base + id] = clogv[t];
     p.feat_row[base + id] = -1;
     p.slot[base + id] = -1;
     p.mask[base + id] = 0ull;
-    clogv[t] = lv;
-    cf[t] = f;
-    ctok[t] = tok;
-    cqual[t] = a.nchild ? (a.nchild[id] > 0) : 1;
-  }
-  __syncthreads();
-  if (t < total) {
     int rank = 0;
     if (a.nchild) {
 #pragma unroll 8
@@ -115,7 +132,7 @@ __global__ void __launch_bounds__(256) tree_expand_kernel(ExpandArgs a) {
   }
   __syncthreads();
   if (t < a.n_next) {
-    const int c = nf[t];  // the candidate (child index) of rank t
+    const int c = nf[t];  // the candidate (child index) of rank t; filled, as checked above
     const int node = cnt + c, f = cf[c];
     const int slot = a.nchild ? node : a.step * a.k + t;
     const uint64_t mask = fmask[f] | (1ull << slot);

@@ -291,8 +291,8 @@ __device__ __forceinline__ int2 node_step(const VerifyArgs& a, NodeShared<EPT>& 
     S = sums.y;
   }
   if (nk == 0) return make_int2(-1, draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired));
-  if (drow_idx < 0) {  // no draft row for a node with children: invalid input
-    *flags |= 8;
+  if (drow_idx < 0) {  // no draft row for a node with children: a malformed tree
+    *flags |= 16;
     return make_int2(-1, draw_token<EPT>(p, V, philox_uniform(a.seed, a.round, b, u, 64), fred, ired));
   }
   for (int i = 0; i < nk; ++i) {

@@ -2,10 +2,14 @@
 
 Only sequences C-ABI calls; all arithmetic is in the HIP kernels.  The order
 follows the pages' draft loop ("EAGLE 推测解码为什么比 Medusa 快" section 6.1;
-"EAGLE 完全拆解", four-step pipeline): the root distribution from the true
+"EAGLE 完全拆解", four-step pipeline): the root distribution from the root
 feature, then per depth an expansion step and one draft step over the new
 frontier, then rerank/flatten, an optional draft step over every drafted node
-of the flattened tree, and verification.
+of the flattened tree, and verification.  Between rounds, catch_up() rebuilds
+the drafter's rows over the committed tokens from the target's true features
+and commits them ("eagle feature-level speculative decoding", KV commit
+section: the drafter continues from the committed path A-B-X); the next round
+then starts from the root rows it leaves behind (next_round_inputs()).
 
 Feature rows and logit rows share one index space: rows [0, B) are the root
 rows (true features, root logits); each depth step appends B * n rows.
@@ -16,7 +20,8 @@ import dataclasses
 
 import torch
 
-from . import (EAGLE_ACT_BF16, EAGLE_HEAD_ONLY, EAGLE_SAMPLE_CHILDREN, eagle_commit, eagle_draft_step, eagle_tree_expand, eagle_tree_finalize, eagle_tree_init,
+from . import (EAGLE_ACT_BF16, EAGLE_FEATURES_ONLY, EAGLE_HEAD_ONLY, EAGLE_SAMPLE_CHILDREN, eagle_catchup_rows,
+               eagle_commit_catchup, eagle_draft_step, eagle_tree_expand, eagle_tree_finalize, eagle_tree_init,
                eagle_verify, eagle_verify_workspace_bytes, eagle_workspace_bytes, make_kv, make_out, make_pool,
                make_rows, make_shape, make_weights)
 
@@ -39,7 +44,7 @@ class EagleRound:
                  template=None, prefix=None, device="cuda", act_bf16=False):
         """shape: d, n_heads, n_kv_heads, head_dim, ffn, vocab, rms_eps, rope_theta, dtype.
         weights: name -> device tensor.  prefix: dict(k, v, off, len, max_len[, cap]) device tensors (cap:
-        per-sequence capacity of each kv head's positions, needed by commit(); max_len must cover it).
+        per-sequence capacity of each kv head's positions, needed by catch_up(); max_len must cover it).
         act_bf16: False (default: split-bf16 operands, within 2e-2 of the fp64
         oracle at every workload), True (EAGLE_ACT_BF16 on every draft step of a
         bf16 workload), or "auto" (EAGLE_ACT_BF16 on steps over more than
@@ -131,7 +136,17 @@ class EagleRound:
         self.tw_kv = make_kv(prefix["k"], prefix["v"], prefix["off"], prefix["len"], prefix["max_len"],
                              self.tw_tree_k, self.tw_tree_v, prefix.get("cap"))
         self.c_flags = torch.zeros(B, dtype=torch.int32, device=device)
-        max_rows = max([B] + [B * n for n in ns] + [nw])
+        # catch-up rows between rounds: R = depth + 1 rows per sequence (the root and every accepted drafted
+        # node, each joined with the token after it), their f^, which of them starts the next round, and
+        # how many slots each sequence commits
+        R = depth + 1
+        self.cu_R = R
+        self.cu = dict(token=torch.zeros(B * R, **i32), parent=torch.zeros(B * R, **i32),
+                       pos=torch.zeros(B * R, **i32), slot=torch.zeros(B * R, **i32),
+                       mask=torch.zeros(B * R, dtype=torch.int64, device=device), row_start=torch.zeros(B + 1, **i32),
+                       last_row=torch.zeros(B, **i32), count=torch.zeros(B, **i32))
+        self.cu_feat = torch.zeros(B * R, d, dtype=torch.float32, device=device)
+        max_rows = max([B] + [B * n for n in ns] + [nw, B * R])
         ws = max(eagle_workspace_bytes(self.shape, max_rows, B, prefix["max_len"]),
                  eagle_verify_workspace_bytes(B, self.n_nodes))
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
@@ -229,14 +244,34 @@ class EagleRound:
                      self.logits, t["qrow"], seed, round_, flags, self.v_path, self.v_len, self.v_next, self.v_flags,
                      workspace=self.workspace)
 
-    def commit(self):
-        """Append each sequence's verified path (this round's verify) to its
-        prefix KV cache: the accepted drafted nodes' k, v from the tree-wide
-        step's slots (slot = tree node), then the prefix lengths grow in place
-        (eagle_commit).  Needs prefix capacity; per-sequence status in c_flags."""
-        p = self.prefix
-        eagle_commit(self.shape, self.B, self.n_nodes, self.v_path, self.v_len, None, self.tw_tree_k, self.tw_tree_v,
-                     p["k"], p["v"], p["off"], p["len"], p.get("cap"), self.c_flags)
+    def catch_up(self, true_feat: torch.Tensor):
+        """After verify: the drafter's rows over each sequence's committed
+        tokens (the root and the accepted drafted nodes, each joined with the
+        token after it, the verifier's next token last), computed from the
+        target's true features true_feat [B * n_nodes, d] fp32 (row b*N + node:
+        the target's feature at every tree node of this round, root included),
+        committed to the prefix KV cache (eagle_catchup_rows, one draft step
+        with EAGLE_FEATURES_ONLY, eagle_commit_catchup).  The next round's root
+        features land in the engine's root rows and its root tokens are this
+        round's next tokens (next_round_inputs()).  Needs prefix capacity;
+        per-sequence commit status in c_flags."""
+        B, N, R = self.B, self.n_nodes, self.cu_R
+        c, p = self.cu, self.prefix
+        eagle_catchup_rows(B, N, R - 1, self.tree["token"], self.v_path, self.v_len, self.v_next, p["len"], 0,
+                           c["token"], c["parent"], c["pos"], c["slot"], c["mask"], c["row_start"], c["last_row"],
+                           c["count"])
+        rows = make_rows(B * R, B, R, c["row_start"], c["token"], c["parent"], c["pos"], c["slot"], c["mask"])
+        out = make_out(self.cu_feat, None, None, 1, None, None)
+        eagle_draft_step(self.shape, self.weights, EAGLE_FEATURES_ONLY | self.act_flag(B * R), rows, true_feat,
+                         self.kv, out, self.workspace)
+        eagle_commit_catchup(self.shape, B, c["count"], self.tree_k, self.tree_v, p["k"], p["v"], p["off"], p["len"],
+                             p.get("cap"), self.cu_feat, c["last_row"], self.feat[:B], self.c_flags)
+
+    def next_round_inputs(self):
+        """(root features, root tokens) of the round after catch_up(): the
+        engine's own root rows and this round's next tokens; pass them to
+        draft_phase (no copy is made)."""
+        return self.feat[:self.B], self.v_next
 
     # ------------------------------------------------------------ HIP graph
     def capture_round(self, root_feat: torch.Tensor, root_token: torch.Tensor, target_logits: torch.Tensor,

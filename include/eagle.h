@@ -145,14 +145,24 @@ typedef struct {
  *   without-replacement draw that eagle_verify's default rule is exact for
  *   ("eagle feature-level speculative decoding", sampled verification: the
  *   siblings' sampling scheme must match the verifier's). */
-enum { EAGLE_HEAD_ONLY = 1, EAGLE_ACT_BF16 = 2, EAGLE_SAMPLE_CHILDREN = 4 };
+/* EAGLE_FEATURES_ONLY: the step stops after f^ (and the rows' k, v in their
+ *   tree slots): no LM head, no softmax or top-k; out->logits, lse, topk_idx
+ *   and topk_logq may be NULL.  The catch-up step between rounds uses it (see
+ *   eagle_catchup_rows).  Not combinable with EAGLE_HEAD_ONLY. */
+enum { EAGLE_HEAD_ONLY = 1, EAGLE_ACT_BF16 = 2, EAGLE_SAMPLE_CHILDREN = 4, EAGLE_FEATURES_ONLY = 8 };
 
 /* Bytes of workspace needed by eagle_draft_step / eagle_softmax_topk for up
  * to max_rows rows, max_batch sequences and prefixes up to max_prefix_len.
  * Returns 0 for an invalid shape. */
 size_t eagle_workspace_bytes(const eagle_shape *shape, int32_t max_rows, int32_t max_batch, int32_t max_prefix_len);
 
-/* One draft step over a set of tree rows.
+/* One draft step over a set of tree rows ("EAGLE 推测解码为什么比 Medusa 快",
+ * sections 4.1-4.2 (draft head: frozen embedding of the advanced token, FC over
+ * [f ; e], one decoder layer, frozen shared LM head) and 6.1 (the draft loop:
+ * the first distribution from the true feature, later ones from predicted
+ * features); "eagle feature-level speculative decoding", sections on the draft
+ * head and on tree attention (each node sees the prefix, its ancestors and
+ * itself)).
  *
  * Without flags, per row r (sequence b):
  *   a   = [f ; e] with f = feat_in[parent[r]] and e = embed[token[r]]      (2d)
@@ -235,7 +245,11 @@ typedef struct {
 int eagle_tree_init(int32_t batch, const eagle_pool *pool, const int32_t *root_token, int32_t root_feat_row0,
                     eagle_stream_t stream);
 
-/* One expansion step.  The previous draft step ran n_prev rows per sequence
+/* One expansion step ("EAGLE 推测解码为什么比 Medusa 快" section 10.3 and
+ * exercise 5: a node's value is the product of the draft confidences on its
+ * path, and the k most valuable nodes of the newest layer are expanded; the
+ * static templates are the fixed tree shapes of EAGLE-1).
+ * The previous draft step ran n_prev rows per sequence
  * (row b*n_prev + f = frontier position f of sequence b) and produced
  * topk_idx/topk_logq [batch*n_prev, topk].
  *   EAGLE-2 (static_nchild == NULL): every frontier node gets its top `k`
@@ -253,16 +267,23 @@ int eagle_tree_init(int32_t batch, const eagle_pool *pool, const int32_t *root_t
  * the pool id, mask = parent's mask | (1 << slot).  The frontier node at
  * position f gets feature row feat_row0 + b*n_next + f.
  * Limits: k <= topk <= 16, n_prev * k <= 256, slots < 64.  static_nchild must
- * hold pool->cap entries.  If a sequence's pool would exceed pool->cap, its
- * pool->count is set to -1 and nothing is added (its finalize then yields the
- * root only). */
+ * hold pool->cap entries.  A sequence whose expansion cannot be carried out
+ * has its pool->count set to -1 and nothing added (its finalize then yields
+ * the root only): the pool would exceed pool->cap, a new child's log value is
+ * NaN (a NaN logit row makes its lse and every log q NaN), or (templates) a
+ * node asks for more children than topk, or the children with children of
+ * their own are not exactly n_next. */
 int eagle_tree_expand(int32_t batch, int32_t k, int32_t step, const int32_t *static_nchild, const eagle_pool *pool,
                       int32_t n_prev, int32_t topk, const int32_t *topk_idx, const float *topk_logq, int32_t n_next,
                       int32_t feat_row0, const int32_t *prefix_len, int32_t *next_token, int32_t *next_parent,
                       int32_t *next_pos, int32_t *next_slot, uint64_t *next_mask, int32_t *next_row_start,
                       eagle_stream_t stream);
 
-/* Rerank and flatten.  Keeps the m pool nodes (root excluded) of largest logv,
+/* Rerank and flatten ("EAGLE 推测解码为什么比 Medusa 快" section 10.3: keep the
+ * m most valuable nodes of the whole tree, ties to the shallower node, which
+ * is a connected tree; "eagle feature-level speculative decoding", tree
+ * attention section: a node's mask holds its ancestors and itself).
+ * Keeps the m pool nodes (root excluded) of largest logv,
  * ties -> shallower, then earlier creation (m = 0: keep all), which is a
  * connected tree; orders the root first and the rest by (depth, creation), so
  * siblings stay in rank order.  Writes n_nodes = m+1 (or the pool size) nodes
@@ -272,7 +293,12 @@ int eagle_tree_expand(int32_t batch, int32_t k, int32_t step, const int32_t *sta
  * expanded, -1 if never).  Also writes the rows of a "tree-wide" draft step
  * over the n_nodes-1 drafted nodes (row b*(n_nodes-1) + t-1 for node t):
  * token, parent feature row, pos = prefix_len[b] + depth - 1, slot = t,
- * mask = tree_mask. n_nodes <= 64. */
+ * mask = tree_mask. n_nodes <= 64, and every kept node must fit: n_nodes >=
+ * m + 1 (m > 0) or >= pool->cap (m = 0), else EAGLE_EINVAL.  When a sequence
+ * keeps fewer nodes than n_nodes - 1 (a pool smaller than m + 1, or an invalid
+ * pool: the root alone), entries past its last node are padding: tree_parent
+ * -2, token 0, depth 0, tree_pool -1, qrow -1, mask = own bit; its tree-wide
+ * rows there are token 0 at the root's feature row and position L_b. */
 int eagle_tree_finalize(int32_t batch, int32_t m, int32_t n_nodes, const eagle_pool *pool, const int32_t *prefix_len,
                         int32_t *tree_parent, int32_t *tree_token, int32_t *tree_depth, int32_t *tree_pool,
                         uint64_t *tree_mask, int32_t *tree_qrow, int32_t *row_token, int32_t *row_parent,
@@ -281,10 +307,18 @@ int eagle_tree_finalize(int32_t batch, int32_t m, int32_t n_nodes, const eagle_p
 
 /* Flags of eagle_verify. */
 enum { EAGLE_VERIFY_GREEDY = 1, EAGLE_VERIFY_IID = 2 };
-/* Per-sequence status bits written to out_flags. */
-enum { EAGLE_F_ZRES = 1, EAGLE_F_QZERO = 2, EAGLE_F_QEMPTY = 4, EAGLE_F_NAN = 8 };
+/* Per-sequence status bits written to out_flags: ZRES a residual had mass 0
+ * (current p kept), QZERO a candidate had q(x) = 0, QEMPTY q ran out of mass
+ * (remaining siblings skipped), NAN a NaN logit, BADTREE a node with children
+ * but no draft row (draft_row < 0: the correction is drawn from its p). */
+enum { EAGLE_F_ZRES = 1, EAGLE_F_QZERO = 2, EAGLE_F_QEMPTY = 4, EAGLE_F_NAN = 8, EAGLE_F_BADTREE = 16 };
 
-/* Tree-structured recursive rejection sampling, one walk per sequence.
+/* Tree-structured recursive rejection sampling, one walk per sequence
+ * ("EAGLE 推测解码为什么比 Medusa 快" section 6.2: accept with probability
+ * min(1, p/q), else resample from norm(max(0, p - q)), node by node along the
+ * tree; "eagle feature-level speculative decoding", sections "Greedy 验证" and
+ * "随机采样验证"; "EAGLE 完全拆解", EAGLE-2 part: siblings tried as successive
+ * rounds).
  * Tree: n_nodes nodes per sequence (node 0 = root, tree_parent < own index,
  * siblings in rank order).  target_logits [batch*n_nodes, vocab]: row
  * b*n_nodes+i is the target's logits after node i.  q at node i is
@@ -327,12 +361,66 @@ int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t *t
  * copied, length unchanged) or EAGLE_COMMIT_BAD_PATH (a node or slot index out
  * of range: nothing done).  Element type = shape->dtype.  Device arrays,
  * caller-owned; asynchronous on `stream`.  A later draft step must be given a
- * max_prefix_len that covers the grown lengths (e.g. the capacities). */
+ * max_prefix_len that covers the grown lengths (e.g. the capacities).
+ * The slots hold whatever k, v the caller's draft step wrote there.  The
+ * drafter must continue from rows built on the target's TRUE features (the
+ * KV-commit section: after A-B-D was drafted and A-B-X committed, no state
+ * predicted along D, nor the draft's own predicted features of A-B, carries
+ * over; study note section 6.2: the accepted path's true features start the
+ * next round).  The tree-wide step's slots satisfy that for depth-1 nodes
+ * only (their parent is the true root feature); eagle_catchup_rows +
+ * eagle_commit_catchup below build and commit the right rows. */
 enum { EAGLE_COMMIT_OVERFLOW = 1, EAGLE_COMMIT_BAD_PATH = 2 };
 int eagle_commit(const eagle_shape *shape, int32_t batch, int32_t n_nodes, const int32_t *path,
                  const int32_t *accept_len, const int32_t *node_slot, const void *tree_k, const void *tree_v,
                  void *prefix_k, void *prefix_v, const int64_t *prefix_off, int32_t *prefix_len,
                  const int32_t *prefix_cap, int32_t *out_flags, eagle_stream_t stream);
+
+/* Catch-up rows of the drafter between rounds ("eagle feature-level
+ * speculative decoding", KV commit section: the drafter continues from the
+ * committed path A-B-X; "EAGLE 推测解码为什么比 Medusa 快" section 6.2 and
+ * implementation note 3: the true features of the accepted path, which the
+ * target's verification forward computed, start the next round).
+ * Input: a verified tree (tree_token [batch, n_nodes], node 0 = the root at
+ * sequence position L_b = prefix_len[b]) and eagle_verify's out_path,
+ * out_accept_len and out_next_token.  With A = accept_len[b] - 1 accepted
+ * drafted nodes x_1..x_A and the next token X, the drafter's row at sequence
+ * position L_b + i (i = 0..A) joins the true feature there with the embedding
+ * of the token after it:
+ *   row i = [f_true(node at path position i) ; e(x_{i+1})], x_{A+1} = X,
+ * rotary position L_b + i, tree slot i, visible slots 0..i (a chain).  The
+ * true feature of tree node n is feature row feat_row0 + b*n_nodes + n (the
+ * caller's buffer of the target's features at every tree node; the root is
+ * node 0).  Writes R = max_depth + 1 rows per sequence (rows [b*R, (b+1)*R),
+ * row_start[b] = b*R): rows past A repeat row A in their own slot (same
+ * token, parent and position, visible slots 0..A-1 and its own), so the call
+ * has a fixed shape.  last_row[b] = b*R + A (the row of X: its f^ is the next
+ * round's root feature), count[b] = A + 1 (slots to commit), or -1 for a
+ * malformed verification result (accept_len outside 1..min(max_depth,
+ * n_nodes-1)+1 or a path node outside 1..n_nodes-1: its rows are those of
+ * A = 0 and nothing is committed).  Run eagle_draft_step with
+ * EAGLE_FEATURES_ONLY over these rows (feat_in = the true features), then
+ * eagle_commit_catchup.  n_nodes <= 64, max_depth + 1 <= 64, max_depth >= the
+ * deepest accepted path.  Device arrays, caller-owned; asynchronous. */
+int eagle_catchup_rows(int32_t batch, int32_t n_nodes, int32_t max_depth, const int32_t *tree_token,
+                       const int32_t *path, const int32_t *accept_len, const int32_t *next_token,
+                       const int32_t *prefix_len, int32_t feat_row0, int32_t *row_token, int32_t *row_parent,
+                       int32_t *row_pos, int32_t *row_slot, uint64_t *row_mask, int32_t *row_start, int32_t *last_row,
+                       int32_t *count, eagle_stream_t stream);
+
+/* The catch-up commit: tree slots 0..count[b]-1 of sequence b (the catch-up
+ * step's k, v in tree_k/tree_v [batch][64][Hkv][hd]) are appended to its
+ * prefix at positions L_b.. of every kv head and prefix_len[b] grows by
+ * count[b]; out_flags[b] = 0, EAGLE_COMMIT_OVERFLOW (no room: nothing copied,
+ * length unchanged) or EAGLE_COMMIT_BAD_PATH (count outside 0..64: nothing
+ * done).  If feat is not NULL, root_feat[b] = feat[last_row[b]] (d fp32
+ * values: the catch-up step's f^ of X, the next round's root feature); feat,
+ * last_row and root_feat are all given or all NULL.  Element type of the
+ * caches = shape->dtype.  Device arrays, caller-owned; asynchronous. */
+int eagle_commit_catchup(const eagle_shape *shape, int32_t batch, const int32_t *count, const void *tree_k,
+                         const void *tree_v, void *prefix_k, void *prefix_v, const int64_t *prefix_off,
+                         int32_t *prefix_len, const int32_t *prefix_cap, const float *feat, const int32_t *last_row,
+                         float *root_feat, int32_t *out_flags, eagle_stream_t stream);
 
 /* Bytes of workspace eagle_verify uses for batch x n_nodes trees (12 per node
  * plus alignment); 0 for an invalid size. */

@@ -178,7 +178,7 @@ def catchup_step(shape, w, trees, outs, true_feat, prefix_k, prefix_v, prefix_le
     outputs, the new prefix (k, v, lengths), commit flags, and the next
     round's root features (f^ of each sequence's last row) and root tokens."""
     B = len(trees)
-    N = len(trees[0]["parent"])
+    N = len(trees[0]["token"])
     rows = {"seq": [], "token": [], "parent": [], "pos": [], "slot": [], "mask": []}
     last = []
     for b in range(B):

@@ -22,6 +22,8 @@ Readings where the pages are silent:
 * q(x) = 0: accept iff p(x) > 0;
 * residual mass Z = 0 (reachable only through rounding): keep the current p;
 * q's remaining mass 0 after removals: skip the remaining siblings;
+* a node with children but no draft distribution is a malformed tree: it is
+  flagged and the correction is drawn from the node's target distribution;
 * draws use the inverse CDF in ascending token order: the smallest y with
   sum_{z<=y} w(z) > u * sum(w);
 * greedy verification ("eagle feature-level speculative decoding", section
@@ -40,6 +42,7 @@ from .philox import EVENT_DRAW, uniform
 F_ZRES = 1  # residual mass was zero; current p kept
 F_QZERO = 2  # a candidate had q(x) = 0
 F_QEMPTY = 4  # q ran out of mass; remaining siblings skipped
+F_BADTREE = 16  # a node with children had no draft distribution
 
 
 def argmax_low(v) -> int:
@@ -88,6 +91,11 @@ def verify_sequence(parent, token, target_logits, draft_logits, seed: int, rnd: 
         else:
             p = softmax(t)
         if not kids:
+            y, draw_margin = inverse_cdf(p, uniform(seed, rnd, seq, u_node, EVENT_DRAW))
+            return dict(path=path, accept_len=len(path) + 1, next_token=y, flags=flags, margins=margins,
+                        draw_margin=draw_margin, stop_node=u_node)
+        if draft_logits[u_node] is None:
+            flags |= F_BADTREE
             y, draw_margin = inverse_cdf(p, uniform(seed, rnd, seq, u_node, EVENT_DRAW))
             return dict(path=path, accept_len=len(path) + 1, next_token=y, flags=flags, margins=margins,
                         draw_margin=draw_margin, stop_node=u_node)

@@ -67,6 +67,24 @@ def test_argument_errors_need_no_device():
     pool = E.eagle_pool()
     assert lib.eagle_tree_init(1, ctypes.byref(pool), None, 0, None) == _abi.EAGLE_EINVAL
     assert lib.eagle_tree_finalize(1, 60, 65, ctypes.byref(pool), *([None] * 13), None) == _abi.EAGLE_EINVAL
+    # a finalize whose kept nodes cannot fit (m + 1 > n_nodes, or the whole pool with m = 0) is refused
+    pool = E.eagle_pool(200, *([1] * 9))
+    assert lib.eagle_tree_finalize(1, 60, 40, ctypes.byref(pool), *([1] * 13), None) == _abi.EAGLE_EINVAL
+    assert lib.eagle_tree_finalize(1, 0, 61, ctypes.byref(pool), *([1] * 13), None) == _abi.EAGLE_EINVAL
+    # HEAD_ONLY and FEATURES_ONLY together are refused
+    rows = E.make_rows(3, 1, 3, 1, 1, 1, 1, 1, 1)
+    out = E.make_out(1, None, None, 1, None, None)
+    rc = lib.eagle_draft_step(ctypes.byref(shape), ctypes.byref(w), _abi.EAGLE_HEAD_ONLY | _abi.EAGLE_FEATURES_ONLY,
+                              ctypes.byref(rows), 1, None, ctypes.byref(out), 1, 1 << 30, None)
+    assert rc == _abi.EAGLE_EINVAL
+    # catch-up rows: null outputs, too many rows per sequence
+    assert lib.eagle_catchup_rows(1, 5, 4, *([None] * 5), 0, *([None] * 8), None) == _abi.EAGLE_EINVAL
+    assert lib.eagle_catchup_rows(1, 5, 64, *([1] * 5), 0, *([1] * 8), None) == _abi.EAGLE_EUNSUPPORTED
+    assert lib.eagle_catchup_rows(0, 5, 4, *([None] * 5), 0, *([None] * 8), None) == _abi.EAGLE_OK
+    # catch-up commit: the root-feature gather needs all three of feat, last_row and root_feat
+    assert lib.eagle_commit_catchup(ctypes.byref(shape), 1, *([1] * 8), 1, None, None, 1, None) == _abi.EAGLE_EINVAL
+    assert lib.eagle_commit_catchup(ctypes.byref(shape), 1, *([None] * 8), None, None, None, None, None) == \
+        _abi.EAGLE_EINVAL
 
 
 def test_python_binding_raises_on_error():

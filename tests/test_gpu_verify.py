@@ -290,3 +290,27 @@ def test_verify_rare_branches_match_oracle(ws):
         assert list(got["path"][b * N:b * N + len(refs[b]["path"])]) == refs[b]["path"], b
         assert got["next"][b] == refs[b]["next_token"], b
         assert got["flags"][b] == refs[b]["flags"], b
+
+
+@pytest.mark.parametrize("ws", [True, False])
+def test_verify_missing_draft_row_is_a_malformed_tree(ws):
+    """A node with children but no draft row is flagged BADTREE (not NAN), the
+    walk stops there and the correction is drawn from its own p, as the
+    oracle does."""
+    g = np.random.default_rng(21)
+    tmpl = TEMPLATES["static26"]
+    N, V, B = len(tmpl), 512, 3
+    draft, target, tokens = _tree_case(g, tmpl, B, V)
+    draft_row = np.arange(B * N, dtype=np.int32)
+    draft_row[1 * N + 0] = -1  # sequence 1: the root has children but no draft row
+    draft_row[2 * N + 1] = -1  # sequence 2: node 1 (accepted first: q == p at the root) has none
+    got = _run(tmpl, tokens, target, draft, B, N, V, seed=4, rnd=2, draft_row=draft_row, ws=ws)
+    for b in range(B):
+        dl = [draft[b, u] if draft_row[b * N + u] >= 0 else None for u in range(N)]
+        want = verify_sequence(tmpl, tokens[b], target[b], dl, 4, 2, b)
+        assert got["len"][b] == want["accept_len"] and got["next"][b] == want["next_token"], b
+        assert list(got["path"][b * N:b * N + len(want["path"])]) == want["path"], b
+        assert got["flags"][b] == want["flags"], b
+    assert got["flags"][0] & E.EAGLE_F_BADTREE == 0
+    assert got["flags"][1] == E.EAGLE_F_BADTREE and got["len"][1] == 1
+    assert got["flags"][2] & E.EAGLE_F_BADTREE and got["len"][2] == 2

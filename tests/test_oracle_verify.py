@@ -222,3 +222,19 @@ def test_expected_tokens_worked_examples():
             lens.append(out["accept_len"])
         lens = np.array(lens)
         assert abs(lens.mean() - e_len) < 4 * lens.std() / np.sqrt(len(lens)) + 1e-9, case
+
+
+def test_missing_draft_distribution_is_flagged_and_corrected_from_p():
+    """A node with children but no draft distribution: flag BADTREE, stop, and
+    draw the correction from that node's target (a one-hot target makes the
+    draw certain)."""
+    from oracle.verify import F_BADTREE
+    V = 6
+    parent, token = [-1, 0, 0], [0, 2, 4]
+    root = np.full(V, -np.inf)
+    root[3] = 0.0
+    tg = [root, np.zeros(V), np.zeros(V)]
+    for rnd in range(5):
+        out = verify_sequence(parent, token, tg, [None, None, None], 0, rnd, 0)
+        assert out["flags"] == F_BADTREE and out["path"] == [] and out["accept_len"] == 1
+        assert out["next_token"] == 3

@@ -21,7 +21,7 @@ import dataclasses
 import numpy as np
 
 # stream ids: one independent PCG64 stream per kind of input
-S_WEIGHTS, S_EMBED, S_LMHEAD, S_FEAT, S_PREFIX, S_TOKENS, S_LENS, S_NOISE, S_FEATNOISE, S_MISC = range(10)
+S_WEIGHTS, S_EMBED, S_LMHEAD, S_FEAT, S_PREFIX, S_TOKENS, S_LENS, S_NOISE, S_FEATNOISE, S_MISC, S_TRUEFEAT = range(11)
 
 
 def rng(config_id: int, stream: int, sub: int = 0) -> np.random.Generator:
@@ -198,6 +198,22 @@ def make_root_features(cfg: Config) -> np.ndarray:
 
 def make_root_tokens(cfg: Config) -> np.ndarray:
     return rng(cfg.cid, S_TOKENS).integers(0, cfg.shape.vocab, size=cfg.batch, dtype=np.int64).astype(np.int32)
+
+
+def make_true_features(cfg: Config, rnd: int, n_rows: int) -> np.ndarray:
+    """Stand-in for the target's features at the tree nodes of round `rnd`
+    (the target's tree forward is not part of this path): ~N(0, 1), plus
+    U(-0.1, 0.1) noise for the 70B workload, bf16 values for bf16 workloads;
+    one row per (sequence, tree node).  The first round's root rows are the
+    true root features (make_root_features); the caller puts them there."""
+    s = cfg.shape
+    f = normal(rng(cfg.cid, S_TRUEFEAT, 2 * rnd), (n_rows, s.d), 1.0)
+    if cfg.feat_noise:
+        f = (f + rng(cfg.cid, S_TRUEFEAT, 2 * rnd + 1).uniform(-0.1, 0.1, size=f.shape).astype(np.float32)).astype(
+            np.float32)
+    if s.dtype == "bf16":
+        f = bf16_values(f)
+    return f
 
 
 def make_target_noise(cfg: Config, n_rows: int, sub: int = 0, std: float = 0.5) -> np.ndarray:
