@@ -194,6 +194,7 @@ def test_expand_nan_row_and_overflow_invalidate_the_pool():
     pools = [OT.Pool(int(root_tok[b]), b) for b in range(B)]
     fr = [OT.expand(pools[b], [0], idx[b:b + 1], lq[b:b + 1], k) for b in range(B)]
     assert pools[1].invalid and not pools[0].invalid
+    OT.assign_rows(pools[0], fr[0], 0, k, False, B, int(lens[0]))  # the frontier's next-step rows
     for m, n_nodes in ((2, 3), (5, 6)):  # (5, 6): sequence 0 keeps its 3 children and pads 2 entries
         g_tr, g_rw = _finalize(B, m, n_nodes, pool, lens)
         for b in range(B):

@@ -306,8 +306,8 @@ def test_verify_missing_draft_row_is_a_malformed_tree(ws):
     draft_row[2 * N + 1] = -1  # sequence 2: node 1 (accepted first: q == p at the root) has none
     got = _run(tmpl, tokens, target, draft, B, N, V, seed=4, rnd=2, draft_row=draft_row, ws=ws)
     for b in range(B):
-        dl = [draft[b, u] if draft_row[b * N + u] >= 0 else None for u in range(N)]
-        want = verify_sequence(tmpl, tokens[b], target[b], dl, 4, 2, b)
+        dl = [draft[b * N + u] if draft_row[b * N + u] >= 0 else None for u in range(N)]
+        want = verify_sequence(tmpl, tokens[b], target[b * N:(b + 1) * N], dl, 4, 2, b)
         assert got["len"][b] == want["accept_len"] and got["next"][b] == want["next_token"], b
         assert list(got["path"][b * N:b * N + len(want["path"])]) == want["path"], b
         assert got["flags"][b] == want["flags"], b
