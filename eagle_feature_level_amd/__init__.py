@@ -14,7 +14,7 @@ from . import _abi
 from ._abi import (EAGLE_ACT_BF16, EAGLE_BF16, EAGLE_COMMIT_BAD_PATH, EAGLE_COMMIT_OVERFLOW, EAGLE_F32,
                    EAGLE_F_BADTREE, EAGLE_F_NAN, EAGLE_F_QEMPTY, EAGLE_F_QZERO, EAGLE_F_ZRES, EAGLE_FEATURES_ONLY,
                    EAGLE_HEAD_ONLY, EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK, EAGLE_SAMPLE_CHILDREN, EAGLE_VERIFY_GREEDY,
-                   EAGLE_VERIFY_IID, EagleError, eagle_draft_out, eagle_kv, eagle_pool, eagle_rows, eagle_shape,
+                   EAGLE_VERIFY_IID, EAGLE_VERIFY_NOALLOC_MAX_NODES, EagleError, eagle_draft_out, eagle_kv, eagle_pool, eagle_rows, eagle_shape,
                    eagle_weights)
 
 __all__ = ["eagle_workspace_bytes", "eagle_draft_step", "eagle_softmax_topk", "eagle_tree_init", "eagle_tree_expand",
@@ -25,7 +25,7 @@ __all__ = ["eagle_workspace_bytes", "eagle_draft_step", "eagle_softmax_topk", "e
            "EAGLE_COMMIT_OVERFLOW", "EAGLE_COMMIT_BAD_PATH", "EAGLE_VERIFY_GREEDY", "EAGLE_VERIFY_IID", "EAGLE_BF16",
            "EAGLE_F32", "EAGLE_MAX_SLOTS", "EAGLE_MAX_TOPK", "eagle_profile_enable", "eagle_profile_reset",
            "eagle_profile_disable", "eagle_profile_read", "eagle_catchup_rows", "eagle_commit_catchup",
-           "EAGLE_FEATURES_ONLY", "EAGLE_F_ZRES", "EAGLE_F_QZERO", "EAGLE_F_QEMPTY", "EAGLE_F_NAN", "EAGLE_F_BADTREE"]
+           "EAGLE_FEATURES_ONLY", "eagle_verify_noalloc", "EAGLE_VERIFY_NOALLOC_MAX_NODES", "EAGLE_F_ZRES", "EAGLE_F_QZERO", "EAGLE_F_QEMPTY", "EAGLE_F_NAN", "EAGLE_F_BADTREE"]
 
 WEIGHT_NAMES = [f[0] for f in eagle_weights._fields_]
 
@@ -191,6 +191,16 @@ def eagle_verify(batch, n_nodes, vocab, tree_parent, tree_token, target_logits, 
                           _ptr(out_accept_len), _ptr(out_next_token), _ptr(out_flags), _ptr(workspace), nbytes,
                           _stream(stream))
     _abi.check("eagle_verify", rc)
+
+
+def eagle_verify_noalloc(batch, n_nodes, vocab, tree_parent, tree_token, target_logits, draft_logits, draft_row, seed,
+                         round_, flags, out_path, out_accept_len, out_next_token, out_flags, stream=None):
+    """eagle_verify with the library's own per-device scratch (no workspace, nothing allocated)."""
+    lib = _abi.load()
+    rc = lib.eagle_verify_noalloc(batch, n_nodes, vocab, _ptr(tree_parent), _ptr(tree_token), _ptr(target_logits),
+                                  _ptr(draft_logits), _ptr(draft_row), seed, round_, flags, _ptr(out_path),
+                                  _ptr(out_accept_len), _ptr(out_next_token), _ptr(out_flags), _stream(stream))
+    _abi.check("eagle_verify_noalloc", rc)
 
 
 def eagle_verify_workspace_bytes(batch, n_nodes):

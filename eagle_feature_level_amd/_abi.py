@@ -19,6 +19,7 @@ EAGLE_F32, EAGLE_BF16 = 0, 1
 EAGLE_HEAD_ONLY, EAGLE_ACT_BF16, EAGLE_SAMPLE_CHILDREN, EAGLE_FEATURES_ONLY = 1, 2, 4, 8
 EAGLE_VERIFY_GREEDY, EAGLE_VERIFY_IID = 1, 2
 EAGLE_MAX_SLOTS, EAGLE_MAX_TOPK = 64, 16
+EAGLE_VERIFY_NOALLOC_MAX_NODES = 8192
 EAGLE_COMMIT_OVERFLOW, EAGLE_COMMIT_BAD_PATH = 1, 2
 EAGLE_F_ZRES, EAGLE_F_QZERO, EAGLE_F_QEMPTY, EAGLE_F_NAN, EAGLE_F_BADTREE = 1, 2, 4, 8, 16
 ROLES = ("fc", "qkv", "rope", "attn", "o", "gate_up", "down", "lm_head", "topk", "rows")
@@ -78,6 +79,8 @@ _SIGS = {
     "eagle_verify": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_u64, c_u64, c_i32, c_vp, c_vp,
                              c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "eagle_verify_workspace_bytes": (ctypes.c_size_t, [c_i32, c_i32]),
+    "eagle_verify_noalloc": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_u64, c_u64, c_i32, c_vp,
+                                     c_vp, c_vp, c_vp, c_vp]),
     "eagle_profile_enable": (c_i32, [c_i32]),
     "eagle_profile_reset": (c_i32, []),
     "eagle_profile_disable": (c_i32, []),

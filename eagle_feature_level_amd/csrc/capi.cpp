@@ -270,6 +270,7 @@ int eagle_fuse_features(const eagle_shape* shape, const void* w_fuse, const void
   return e == hipSuccess ? EAGLE_OK : hip_fail(e);
 }
 
+static_assert(VERIFY_NOALLOC_MAX_NODES == EAGLE_VERIFY_NOALLOC_MAX_NODES, "verify scratch limit");
 static_assert(kCommitOverflow == EAGLE_COMMIT_OVERFLOW && kCommitBadPath == EAGLE_COMMIT_BAD_PATH, "commit flags");
 
 int eagle_commit(const eagle_shape* shape, int32_t batch, int32_t n_nodes, const int32_t* path,
@@ -808,10 +809,11 @@ int eagle_tree_finalize(int32_t batch, int32_t m, int32_t n_nodes, const eagle_p
   return e == hipSuccess ? EAGLE_OK : hip_fail(e);
 }
 
-int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t* tree_parent, const int32_t* tree_token,
-                 const float* target_logits, const float* draft_logits, const int32_t* draft_row, uint64_t seed,
-                 uint64_t round, int32_t flags, int32_t* out_path, int32_t* out_accept_len, int32_t* out_next_token,
-                 int32_t* out_flags, void* workspace, size_t workspace_bytes, eagle_stream_t stream) {
+// Argument checks shared by eagle_verify and eagle_verify_noalloc.
+static int verify_args_ok(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t* tree_parent,
+                          const int32_t* tree_token, const float* target_logits, const float* draft_logits,
+                          const int32_t* draft_row, int32_t flags, int32_t* out_path, int32_t* out_accept_len,
+                          int32_t* out_next_token, int32_t* out_flags) {
   if (batch < 0 || n_nodes < 1 || vocab < 1) return EAGLE_EINVAL;
   if (batch == 0) return EAGLE_OK;
   if (!tree_parent || !tree_token || !target_logits || !draft_logits || !draft_row || !out_path ||
@@ -819,9 +821,14 @@ int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t* t
     return EAGLE_EINVAL;
   if (flags & ~(EAGLE_VERIFY_GREEDY | EAGLE_VERIFY_IID)) return EAGLE_EINVAL;
   if (n_nodes > EAGLE_MAX_SLOTS || vocab > 32768) return EAGLE_EUNSUPPORTED;
-  if (workspace && workspace_bytes < verify_workspace_bytes(batch, n_nodes)) return EAGLE_EWORKSPACE;
-  int rc = check_device();
-  if (rc) return rc;
+  return EAGLE_OK;
+}
+
+static int verify_launch(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t* tree_parent,
+                         const int32_t* tree_token, const float* target_logits, const float* draft_logits,
+                         const int32_t* draft_row, uint64_t seed, uint64_t round, int32_t flags, int32_t* out_path,
+                         int32_t* out_accept_len, int32_t* out_next_token, int32_t* out_flags, void* workspace,
+                         eagle_stream_t stream) {
   VerifyArgs a;
   a.batch = batch;
   a.n_nodes = n_nodes;
@@ -840,6 +847,37 @@ int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t* t
   a.out_flags = out_flags;
   hipError_t e = launch_verify(a, workspace, (hipStream_t)stream);
   return e == hipSuccess ? EAGLE_OK : hip_fail(e);
+}
+
+int eagle_verify(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t* tree_parent, const int32_t* tree_token,
+                 const float* target_logits, const float* draft_logits, const int32_t* draft_row, uint64_t seed,
+                 uint64_t round, int32_t flags, int32_t* out_path, int32_t* out_accept_len, int32_t* out_next_token,
+                 int32_t* out_flags, void* workspace, size_t workspace_bytes, eagle_stream_t stream) {
+  int rc = verify_args_ok(batch, n_nodes, vocab, tree_parent, tree_token, target_logits, draft_logits, draft_row, flags,
+                          out_path, out_accept_len, out_next_token, out_flags);
+  if (rc || batch == 0) return rc;
+  if (workspace && workspace_bytes < verify_workspace_bytes(batch, n_nodes)) return EAGLE_EWORKSPACE;
+  rc = check_device();
+  if (rc) return rc;
+  return verify_launch(batch, n_nodes, vocab, tree_parent, tree_token, target_logits, draft_logits, draft_row, seed,
+                       round, flags, out_path, out_accept_len, out_next_token, out_flags, workspace, stream);
+}
+
+int eagle_verify_noalloc(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t* tree_parent,
+                         const int32_t* tree_token, const float* target_logits, const float* draft_logits,
+                         const int32_t* draft_row, uint64_t seed, uint64_t round, int32_t flags, int32_t* out_path,
+                         int32_t* out_accept_len, int32_t* out_next_token, int32_t* out_flags, eagle_stream_t stream) {
+  int rc = verify_args_ok(batch, n_nodes, vocab, tree_parent, tree_token, target_logits, draft_logits, draft_row, flags,
+                          out_path, out_accept_len, out_next_token, out_flags);
+  if (rc || batch == 0) return rc;
+  if ((int64_t)batch * n_nodes > VERIFY_NOALLOC_MAX_NODES) return EAGLE_EUNSUPPORTED;
+  rc = check_device();
+  if (rc) return rc;
+  void* scratch = nullptr;  // the library's own per-device array, never an allocation
+  hipError_t e = verify_scratch_address(&scratch);
+  if (e != hipSuccess) return hip_fail(e);
+  return verify_launch(batch, n_nodes, vocab, tree_parent, tree_token, target_logits, draft_logits, draft_row, seed,
+                       round, flags, out_path, out_accept_len, out_next_token, out_flags, scratch, stream);
 }
 
 size_t eagle_verify_workspace_bytes(int32_t batch, int32_t n_nodes) {

@@ -127,6 +127,10 @@ struct VerifyArgs {
 };
 size_t verify_workspace_bytes(int batch, int n_nodes);
 hipError_t launch_verify(VerifyArgs a, void* ws, hipStream_t s);
+// Device address (current device) of the library's own verify scratch, which
+// holds the per-node results of up to VERIFY_NOALLOC_MAX_NODES nodes.
+constexpr int VERIFY_NOALLOC_MAX_NODES = 8192;
+hipError_t verify_scratch_address(void** ptr);
 
 // accepted-path commit of the draft KV cache
 constexpr int kCommitOverflow = 1, kCommitBadPath = 2;  // = EAGLE_COMMIT_OVERFLOW / _BAD_PATH

@@ -25,6 +25,8 @@
 // (coalesced); p lives in registers, q in the thread's own LDS column, a node
 // needs block reductions only, and the inverse-CDF draw is one token-order
 // scan.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -455,4 +457,32 @@ hipError_t launch_verify(VerifyArgs a, void* ws, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(verify_walk_kernel, dim3(a.batch), dim3(64), 0, s, a);
   return hipGetLastError();
+}
+
+// The per-node results of eagle_verify_noalloc live in this file-scope device
+// array instead of a caller workspace: room for VERIFY_NOALLOC_MAX_NODES nodes
+// (the workspace layout above, 12 bytes per node plus alignment).  Each GPU
+// holds its own copy for the life of the process.  Nothing in it needs
+// clearing: the node kernel writes every node's three entries before the walk
+// reads them.  Calls that overlap on one GPU share it and race.
+static __device__ __align__(256) unsigned char scratch[(size_t)VERIFY_NOALLOC_MAX_NODES * 12 + 1024];
+static_assert(sizeof(scratch) >= (size_t)VERIFY_NOALLOC_MAX_NODES * 12 + 1024, "scratch holds the largest call");
+
+hipError_t verify_scratch_address(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {  // first call on this device, with it current: its copy's device address
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }

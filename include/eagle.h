@@ -422,6 +422,21 @@ int eagle_commit_catchup(const eagle_shape *shape, int32_t batch, const int32_t 
                          int32_t *prefix_len, const int32_t *prefix_cap, const float *feat, const int32_t *last_row,
                          float *root_feat, int32_t *out_flags, eagle_stream_t stream);
 
+/* eagle_verify for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, results and per-node kernels as eagle_verify with a
+ * workspace, but the per-node results live in the library's own file-scope
+ * device array (one per GPU, 8192 * 12 + 1024 bytes, held until the process
+ * ends), so the call allocates nothing and takes no workspace.  batch *
+ * n_nodes <= EAGLE_VERIFY_NOALLOC_MAX_NODES, else EAGLE_EUNSUPPORTED.  Calls
+ * that overlap on one GPU (different streams or host threads) share the array
+ * and race; calls ordered on one stream do not. */
+#define EAGLE_VERIFY_NOALLOC_MAX_NODES 8192
+int eagle_verify_noalloc(int32_t batch, int32_t n_nodes, int32_t vocab, const int32_t *tree_parent,
+                         const int32_t *tree_token, const float *target_logits, const float *draft_logits,
+                         const int32_t *draft_row, uint64_t seed, uint64_t round, int32_t flags, int32_t *out_path,
+                         int32_t *out_accept_len, int32_t *out_next_token, int32_t *out_flags, eagle_stream_t stream);
+
 /* Bytes of workspace eagle_verify uses for batch x n_nodes trees (12 per node
  * plus alignment); 0 for an invalid size. */
 size_t eagle_verify_workspace_bytes(int32_t batch, int32_t n_nodes);
