@@ -15,9 +15,16 @@ KV ~N(0, 1), target logits = draft logits + N(0, 0.5) (root: exact copy).
 
 Prints one JSON line.  value = drafted tree nodes per second through draft +
 verify (whole job, one GPU), from K replays of the round captured as one HIP
-graph (--no-graph: K eager rounds; both are reported).  `roofline` covers the dominant kernel, with its
+graph (--no-graph: K eager rounds; both are reported); consecutive rounds use
+two copies of the weights in turn, so no round finds the previous one's
+weights in the Infinity Cache.  `roofline` covers the dominant kernel, with its
 per-launch duration measured by HIP events around each launch on the stream
 it runs on; `cpu_baseline` times the fp64 CPU oracle on a bounded sample.
+Also in the line: the 7B EAGLE-2, 13B and 70B workloads' rounds, each with its
+dominant kernel's HBM roofline; the 13B and 70B tree-wide steps (one draft
+step over every drafted node: 480 / 960 rows) on the bf16 MFMA roofline; and
+a multi-round decode of the headline workload (draft, verify, catch-up and
+commit per round) with its mean accepted length.
 """
 from __future__ import annotations
 
@@ -41,7 +48,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_engine(cid: int):
+def build_engine(cid: int, copies: int = 1, extra: int = 0):
+    """Seeded inputs of workload `cid` and `copies` engines over separate
+    copies of the weights and prefix cache (the same values), each with the
+    root features staged in its own root rows (input resident before the
+    round).  extra > 0 gives every prefix room for that many commits."""
     import torch
     from eagle_feature_level_amd.engine import EagleRound
     from workloads import (CONFIGS, TEMPLATES, make_prefix_kv, make_prefix_lens, make_root_features, make_root_tokens,
@@ -57,101 +68,151 @@ def build_engine(cid: int):
     feat = make_root_features(cfg)
     tok = make_root_tokens(cfg)
     log(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s")
-    wt = dev.weights(w, s.dtype)
-    pf = dev.prefix(ks, vs, lens, s.dtype)
     kind = "dynamic" if cfg.tree == "dynamic" else "static"
-    eng = EagleRound(dev.shape_dict(s), wt, cfg.batch, kind, cfg.topk, cfg.depth, cfg.rerank_m,
-                     TEMPLATES.get(cfg.tree), pf)
+    engines = []
+    for _ in range(copies):
+        eng = EagleRound(dev.shape_dict(s), dev.weights(w, s.dtype), cfg.batch, kind, cfg.topk, cfg.depth,
+                         cfg.rerank_m, TEMPLATES.get(cfg.tree), dev.prefix(ks, vs, lens, s.dtype, extra=extra))
+        eng.root_features().copy_(torch.from_numpy(feat).cuda())
+        engines.append(eng)
     host = dict(w=w, lens=lens, ks=ks, vs=vs, feat=feat, tok=tok)
-    # root features staged into the engine's own rows (input resident before the round)
-    root = eng.root_features()
-    root.copy_(torch.from_numpy(feat).cuda())
-    return cfg, eng, root, dev.ints(tok), host
+    return cfg, engines, dev.ints(tok), host
 
 
-def synth_target(cfg, eng):
-    """Target logits [B*N, V]: root row = the root draft row (q == p), other
-    nodes = tree-wide draft logits + N(0, 0.5) noise."""
+def synth_target(cfg, eng, rnd: int = 0):
+    """Target logits [B*N, V] (the target's tree forward is not part of this
+    path): non-root nodes = tree-wide draft logits + N(0, 0.5) noise; the root
+    row = the root draft row in the first round (its feature is the true one,
+    q == p), + the same noise in later rounds (their root feature is the
+    catch-up's prediction)."""
     import torch
     from workloads import make_target_noise
     B, N, V = cfg.batch, eng.n_nodes, cfg.shape.vocab
     eng.tree_wide()
-    noise = torch.from_numpy(make_target_noise(cfg, B * N)).cuda()
+    noise = torch.from_numpy(make_target_noise(cfg, B * N, sub=rnd)).cuda()
     tgt = torch.empty(B * N, V, device="cuda")
     tw = eng.tw_logits[:B * (N - 1)].view(B, N - 1, V)
     tgt.view(B, N, V)[:, 1:] = tw + noise.view(B, N, V)[:, 1:]
-    tgt.view(B, N, V)[:, 0] = eng.logits[:B]
+    tgt.view(B, N, V)[:, 0] = eng.logits[:B] if rnd == 0 else eng.logits[:B] + noise.view(B, N, V)[:, 0]
     torch.cuda.synchronize()
     return tgt
 
 
-def run_steps(eng, feat, tok, tgt, steps, marks=None):
-    import torch
+def run_steps(engs, tok, tgts, steps, marks=None):
+    """`steps` eager rounds (draft phase + verify), cycling over the engines
+    (one weight copy each)."""
     for i in range(steps):
+        j = i % len(engs)
+        eng = engs[j]
         if marks is not None:
             marks[i][0].record()
-        eng.draft_phase(feat, tok)
+        eng.draft_phase(eng.root_features(), tok)
         if marks is not None:
             marks[i][1].record()
-        eng.verify(tgt, 0, i)
+        eng.verify(tgts[j], 0, i)
         if marks is not None:
             marks[i][2].record()
 
 
+def kernel_table(E, steps):
+    """Per-role launch count, time, bytes and flops from the measurement hook."""
+    kernels = {}
+    for role in E._abi.ROLES:
+        r = E.eagle_profile_read(role)
+        if r["launches"]:
+            kernels[role] = dict(launches_per_step=r["launches"] / steps, avg_us=1e3 * r["ms"] / r["launches"],
+                                 gbs=r["bytes"] / (r["ms"] * 1e-3) / 1e9 if r["ms"] > 0 else None,
+                                 tflops=r["flops"] / (r["ms"] * 1e-3) / 1e12 if r["ms"] > 0 else None,
+                                 bytes_per_launch=r["bytes"] / r["launches"],
+                                 flops_per_launch=r["flops"] / r["launches"], ms_per_step=r["ms"] / steps)
+    return kernels
+
+
+def hbm_roofline(kernels, traffic=None):
+    """The dominant role (largest time per step) against the HBM peak."""
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    kd = kernels[dom]
+    return {"bound": "hbm", "achieved": round(kd["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
+            "avg_launch_us": round(kd["avg_us"], 2), "bytes_per_launch": round(kd["bytes_per_launch"])}
+
+
+def rounded(kernels):
+    return {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()} for k, v in kernels.items()}
+
+
 def cpu_baseline(cfg, host):
-    """The fp64 oracle on one full round of the same workload (root head, every
-    draft step, expansions, rerank, verify), on the host cores."""
+    """The fp64 oracle on full rounds of the same workload (root head, every
+    draft step, expansions, rerank, verify) on the host cores, all BLAS
+    threads; then one round of each of the tiny, 7B static-26 and 7B EAGLE-2
+    workloads on one thread."""
     import numpy as np
     from oracle import pipeline as OP
-    from workloads import TEMPLATES, make_target_noise
+    from workloads import CONFIGS, TEMPLATES, make_prefix_kv, make_prefix_lens, make_root_features, \
+        make_root_tokens, make_target_noise, make_weights
+    blas, cores = "unknown", len(os.sched_getaffinity(0))
+    limits = None
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            cores = max(i.get("num_threads", 1) for i in info)
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in info)
+        limits = threadpoolctl.threadpool_limits
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-    s = cfg.shape
-    kind = "dynamic" if cfg.tree == "dynamic" else "static"
-    # draft phase: whole rounds, repeated until ~10 s of CPU work (at most 20 rounds)
-    t_draft, rounds = 0.0, 0
-    while rounds == 0 or (t_draft < 10.0 and rounds < 20):
+        pass
+
+    def one_round(c, h, verify_rounds=1):
+        kind = "dynamic" if c.tree == "dynamic" else "static"
         t0 = time.perf_counter()
-        res = OP.draft_phase(s, host["w"], host["feat"], host["tok"], host["ks"], host["vs"], host["lens"], kind,
-                             cfg.topk, cfg.depth, cfg.rerank_m, TEMPLATES.get(cfg.tree), tree_wide=False)
-        t_draft += time.perf_counter() - t0
-        rounds += 1
-    # target logits from the oracle's own tree-wide step (not timed), then verify (timed)
-    from oracle import draft as OD
-    B = cfg.batch
-    rows = {k: [] for k in ("seq", "token", "parent", "pos", "slot", "mask")}
-    for b in range(B):
-        tr, pool = res["trees"][b], res["pools"][b]
-        for t in range(1, len(tr["parent"])):
-            pid = int(tr["pool_id"][t])
-            rows["seq"].append(b)
-            rows["token"].append(int(tr["token"][t]))
-            rows["parent"].append(pool.feat_row[pool.parent[pid]])
-            rows["pos"].append(int(host["lens"][b]) + int(tr["depth"][t]) - 1)
-            rows["slot"].append(t)
-            rows["mask"].append(int(tr["mask"][t]))
-    tk, tv = OD.new_tree_kv(s, B)
-    tw = OD.draft_step(s, host["w"], rows, res["feat_buf"], host["ks"], host["vs"], host["lens"], tk, tv,
-                       act_bf16=False)["logits"]
-    N = len(res["trees"][0]["parent"])
-    noise = make_target_noise(cfg, B * N).reshape(B, N, -1)
-    targets = [np.concatenate([res["logits"][b:b + 1], tw[b * (N - 1):(b + 1) * (N - 1)] + noise[b, 1:]])
-               for b in range(B)]
-    qrow = [OP.q_rows(res, b) for b in range(B)]
-    t1 = time.perf_counter()
-    for r in range(rounds):
-        OP.verify_all(res["trees"], targets, res["logits"], qrow, 0, r)
-    t_verify = time.perf_counter() - t1
-    drafted = B * (N - 1) * rounds
-    total = t_draft + t_verify
-    return {"value": drafted / total, "unit": "draft-tree nodes/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rounds} full rounds of the same workload ({B} x {N - 1} drafted nodes each: root head, every "
-                      f"draft step, expansions, rerank, verify) in fp64 numpy; draft {t_draft:.2f}s + verify "
-                      f"{t_verify:.2f}s"}
+        res = OP.draft_phase(c.shape, h["w"], h["feat"], h["tok"], h["ks"], h["vs"], h["lens"], kind, c.topk,
+                             c.depth, c.rerank_m, TEMPLATES.get(c.tree), tree_wide=False)
+        t_draft = time.perf_counter() - t0
+        B = c.batch
+        # target logits from the oracle's own tree-wide step (not timed), then verify (timed)
+        rows = OP.tree_wide_rows(res["trees"], res["pools"], h["lens"])
+        from oracle import draft as OD
+        tk, tv = OD.new_tree_kv(c.shape, B)
+        tw = OD.draft_step(c.shape, h["w"], rows, res["feat_buf"], h["ks"], h["vs"], h["lens"], tk, tv)["logits"]
+        N = len(res["trees"][0]["parent"])
+        noise = make_target_noise(c, B * N).reshape(B, N, -1)
+        targets = [np.concatenate([res["logits"][b:b + 1], tw[b * (N - 1):(b + 1) * (N - 1)] + noise[b, 1:]])
+                   for b in range(B)]
+        qrow = [OP.q_rows(res, b) for b in range(B)]
+        t1 = time.perf_counter()
+        for r in range(verify_rounds):
+            OP.verify_all(res["trees"], targets, res["logits"], qrow, 0, r)
+        return t_draft, (time.perf_counter() - t1) / verify_rounds, B * (N - 1)
+
+    # all threads: whole rounds, repeated until ~10 s of CPU work (at most 20)
+    t_draft = t_verify = 0.0
+    rounds, drafted = 0, 0
+    while rounds == 0 or (t_draft + t_verify < 10.0 and rounds < 20):
+        td, tvv, n = one_round(cfg, host)
+        t_draft, t_verify, drafted, rounds = t_draft + td, t_verify + tvv, drafted + n, rounds + 1
+    out = {"value": drafted / (t_draft + t_verify), "unit": "draft-tree nodes/s", "cores": int(cores),
+           "kind": "oracle", "blas": blas,
+           "sample": f"{rounds} full rounds of {cfg.name} ({drafted // rounds} drafted nodes each: root head, every "
+                     f"draft step, expansions, rerank, verify) in fp64 numpy; draft {t_draft:.2f}s + verify "
+                     f"{t_verify:.2f}s"}
+    # one thread: one round each of the tiny and the two 7B workloads
+    if limits is not None:
+        single = {}
+        with limits(limits=1, user_api="blas"):
+            for cid in (1, 2, 3):
+                c = CONFIGS[cid]
+                if cid == cfg.cid:
+                    h = host
+                else:
+                    lens = make_prefix_lens(c)
+                    ks, vs = make_prefix_kv(c, lens)
+                    h = dict(w=make_weights(c), lens=lens, ks=ks, vs=vs, feat=make_root_features(c),
+                             tok=make_root_tokens(c))
+                td, tvv, n = one_round(c, h)
+                single[c.name] = {"value": round(n / (td + tvv), 3), "unit": "draft-tree nodes/s", "cores": 1,
+                                  "s_per_round": round(td + tvv, 3)}
+        out["single_thread"] = single
+    return out
 
 
 def traffic_for(kernel_role: str, config_name: str):
@@ -172,22 +233,31 @@ def traffic_for(kernel_role: str, config_name: str):
                  r["write_kib_per_dispatch"] * 1024 * c["write_factor"])
 
 
-def round_bench(cid: int, steps: int, warmup: int) -> dict:
+def round_bench(cid: int, steps: int, warmup: int, tree_wide_steps: int = 0) -> dict:
     """One full round (draft phase + verify) of workload `cid`, replayed as a
     HIP graph `steps` times after `warmup` replays; draft / verify split from
-    as many eager rounds with events between the phases."""
+    as many eager rounds with events between the phases; the dominant kernel's
+    HBM roofline from as many eager rounds under the measurement hook; and,
+    with tree_wide_steps > 0, the tree-wide step (one draft step over every
+    drafted node) on the matrix-unit roofline."""
     import torch
-    cfg, eng, feat, tok, _ = build_engine(cid)
+    import eagle_feature_level_amd as E
+    cfg, (eng,), tok, _ = build_engine(cid)
     B, N = cfg.batch, eng.n_nodes
-    eng.draft_phase(feat, tok)
+    eng.draft_phase(eng.root_features(), tok)
     tgt = synth_target(cfg, eng)
     marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    run_steps(eng, feat, tok, tgt, warmup)
-    run_steps(eng, feat, tok, tgt, steps, marks)
+    run_steps([eng], tok, [tgt], warmup)
+    run_steps([eng], tok, [tgt], steps, marks)
     torch.cuda.synchronize()
     ms_draft = sum(m[0].elapsed_time(m[1]) for m in marks) / steps
     ms_verify = sum(m[1].elapsed_time(m[2]) for m in marks) / steps
-    eng.capture_round(feat, tok, tgt, 0, 0)
+    E.eagle_profile_enable(steps * 300)
+    run_steps([eng], tok, [tgt], steps)
+    torch.cuda.synchronize()
+    kernels = kernel_table(E, steps)
+    E.eagle_profile_disable()
+    eng.capture_round(eng.root_features(), tok, tgt, 0, 0)
     for _ in range(warmup):
         eng.replay_round()
     torch.cuda.synchronize()
@@ -203,60 +273,105 @@ def round_bench(cid: int, steps: int, warmup: int) -> dict:
            "value": round(B * (N - 1) / (ms * 1e-3), 1), "unit": "draft-tree nodes/s", "ms_per_round": round(ms, 4),
            "ms_draft_phase_eager": round(ms_draft, 4), "ms_verify_eager": round(ms_verify, 4),
            "draft_nodes_per_s": round(B * (N - 1) / (ms_draft * 1e-3), 1),
-           "verify_nodes_per_s": round(B * N / (ms_verify * 1e-3), 1)}
+           "verify_nodes_per_s": round(B * N / (ms_verify * 1e-3), 1),
+           "roofline": hbm_roofline(kernels), "kernels": rounded(kernels)}
+    if tree_wide_steps:
+        out["tree_wide"] = tree_wide_measure(cfg, eng, tok, tree_wide_steps, warmup)
     del eng, tgt
     torch.cuda.empty_cache()
     return out
 
 
-def tree_wide_bench(args, cfg, eng, feat, tok):
-    """K tree-wide draft steps (B x (N-1) rows in one eagle_draft_step) after one
-    draft phase built the tree; per-role time, TFLOP/s and fraction of the
-    bf16 MFMA peak from the library's measurement hook."""
+def tree_wide_measure(cfg, eng, tok, steps, warmup) -> dict:
+    """`steps` tree-wide draft steps (B x (N-1) rows in one eagle_draft_step)
+    after a draft phase built the tree; per-role time and TFLOP/s from the
+    measurement hook; the dominant GEMM against the bf16 MFMA peak on
+    algorithmic flops (2 M N K per product; the split operands make the matrix
+    units do twice that, mfma_pipe_frac)."""
     import torch
     import eagle_feature_level_amd as E
-    eng.draft_phase(feat, tok)
-    for _ in range(args.warmup):
+    eng.draft_phase(eng.root_features(), tok)
+    for _ in range(warmup):
         eng.tree_wide()
     torch.cuda.synchronize()
     rows = cfg.batch * (eng.n_nodes - 1)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         eng.tree_wide()
     b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / args.steps
-    E.eagle_profile_enable(args.steps * 200)
-    for _ in range(args.steps):
+    ms = a.elapsed_time(b) / steps
+    E.eagle_profile_enable(steps * 200)
+    for _ in range(steps):
         eng.tree_wide()
     torch.cuda.synchronize()
-    kernels = {}
-    for role in E._abi.ROLES:
-        r = E.eagle_profile_read(role)
-        if r["launches"]:
-            kernels[role] = dict(avg_us=round(1e3 * r["ms"] / r["launches"], 2),
-                                 tflops=round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 1) if r["ms"] > 0 else None,
-                                 ms_per_step=round(r["ms"] / args.steps, 4))
+    kernels = kernel_table(E, steps)
     E.eagle_profile_disable()
-    gemm = ["fc", "qkv", "o", "gate_up", "down", "lm_head"]
-    g_ms = sum(kernels[r]["ms_per_step"] for r in gemm if r in kernels)
-    g_fl = sum(kernels[r]["tflops"] * kernels[r]["ms_per_step"] for r in gemm if r in kernels)  # TF/s x ms
+    gemm = [r for r in ("fc", "qkv", "o", "gate_up", "down", "lm_head") if r in kernels]
+    g_ms = sum(kernels[r]["ms_per_step"] for r in gemm)
+    g_fl = sum(kernels[r]["flops_per_launch"] * kernels[r]["launches_per_step"] for r in gemm)
     dom = max(gemm, key=lambda r: kernels[r]["ms_per_step"])
     ach = kernels[dom]["tflops"]
     s = cfg.shape
-    out = {"metric": "tree-wide draft rows/sec (one draft step over every drafted node)",
-           "value": round(rows / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": s.dtype,
-           "data": "synthetic", "config": {"workload": cfg.name, "rows": rows, "d": s.d, "ffn": s.ffn,
-                                           "heads": f"{s.n_heads}q/{s.n_kv_heads}kv x {s.head_dim}",
-                                           "operands": "split bf16 (hi, lo): two MFMAs per product"},
-           "gemm_tflops": round(g_fl / g_ms, 1) if g_ms else None,
-           "roofline": {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(ach / BF16_PEAK_TFLOPS, 4), "mfma_pipe_frac": round(2 * ach / BF16_PEAK_TFLOPS, 4),
-                        "kernel": dom, "avg_launch_us": kernels[dom]["avg_us"]},
-           "kernels": kernels}
-    print(json.dumps(out))
+    return {"metric": "tree-wide draft rows/sec (one draft step over every drafted node)",
+            "value": round(rows / (ms * 1e-3), 1), "unit": "rows/s", "rows": rows, "steps": steps,
+            "ms_per_step": round(ms, 4), "dtype": s.dtype,
+            "operands": "split bf16 (hi, lo): two MFMAs per product",
+            "gemm_tflops": round(g_fl / (g_ms * 1e-3) / 1e12, 1) if g_ms else None,
+            "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                         "mfma_pipe_frac": round(2 * ach / BF16_PEAK_TFLOPS, 4), "kernel": dom,
+                         "avg_launch_us": round(kernels[dom]["avg_us"], 2),
+                         "flops_per_launch": round(kernels[dom]["flops_per_launch"])},
+            "kernels": rounded(kernels)}
+
+
+def decode_bench(cid: int, n_rounds: int) -> dict:
+    """n_rounds rounds of multi-round decode on workload `cid`: draft phase,
+    target stand-in (tree-wide step + noise, not timed), verify, catch-up
+    (the drafter's rows over the committed tokens from the target's true
+    features, committed to the prefix).  Reports the mean accepted length
+    (accepted drafts + the next token) and the time per round of draft +
+    verify + catch-up."""
+    import torch
+    from workloads import make_true_features
+    cfg, (eng,), tok, host = build_engine(cid, extra=n_rounds * (CONFIGS_DEPTH(cid) + 1) + 1)
+    B, N = cfg.batch, eng.n_nodes
+    root_f, root_t = eng.root_features(), tok
+    lens, ms, times = [], [], []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for r in range(n_rounds):
+        ev[0].record()
+        eng.draft_phase(root_f, root_t)
+        ev[1].record()
+        tgt = synth_target(cfg, eng, r)
+        tf = make_true_features(cfg, r, B * N)
+        if r == 0:
+            tf.reshape(B, N, -1)[:, 0] = host["feat"]
+        tf_t = torch.from_numpy(tf).cuda()
+        ev[2].record()
+        eng.verify(tgt, 0, r)
+        ev[3].record()
+        eng.catch_up(tf_t)
+        ev[4].record()
+        torch.cuda.synchronize()
+        lens.append(eng.v_len.cpu().numpy().tolist())
+        times.append((ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3]), ev[3].elapsed_time(ev[4])))
+        root_f, root_t = eng.next_round_inputs()
+    flat = [x for row in lens for x in row]
+    t = [sum(x[i] for x in times[1:]) / max(1, len(times) - 1) for i in range(3)]
+    return {"workload": cfg.name, "rounds": n_rounds, "batch": B,
+            "mean_accept_len": round(sum(flat) / len(flat), 3), "accept_len_per_round": lens,
+            "ms_draft_phase": round(t[0], 4), "ms_verify": round(t[1], 4), "ms_catch_up": round(t[2], 4),
+            "ms_per_round": round(sum(t), 4),
+            "note": "random-init weights and synthetic targets (draft logits + N(0, 0.5)); acceptance says nothing "
+                    "about draft quality"}
+
+
+def CONFIGS_DEPTH(cid):
+    from workloads import CONFIGS
+    return CONFIGS[cid].depth
 
 
 def main():
@@ -267,11 +382,15 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = 7B static-26, the bench line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="one weight copy (default: rounds alternate between two copies of the weights, so that no "
+                         "round finds the previous round's weights in the 256 MB Infinity Cache)")
     ap.add_argument("--headline-only", action="store_true",
-                    help="skip the full-round measurements of the other workloads (7B EAGLE-2, 13B, 70B)")
+                    help="skip the other workloads' rounds, the tree-wide steps and the multi-round decode")
     ap.add_argument("--tree-wide", action="store_true",
-                    help="time only the tree-wide draft step (every drafted node of the flattened tree in one call: "
-                         "the matrix-unit bound shape at batch 8 / 16) and print its own JSON line")
+                    help="time only the tree-wide draft step of --config (every drafted node of the flattened tree "
+                         "in one call) and print its own JSON line")
+    ap.add_argument("--rounds", type=int, default=8, help="rounds of the multi-round decode measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -293,91 +412,93 @@ def main():
         return
     import eagle_feature_level_amd as E
 
-    cfg, eng, feat, tok, host = build_engine(args.config)
-    B, N = cfg.batch, eng.n_nodes
-    drafted = B * (N - 1)
     if args.tree_wide:
-        tree_wide_bench(args, cfg, eng, feat, tok)
+        cfg, (eng,), tok, _ = build_engine(args.config)
+        out = tree_wide_measure(cfg, eng, tok, args.steps, args.warmup)
+        out.update({"n_gpus": 1, "warmup": args.warmup, "higher_is_better": True, "data": "synthetic",
+                    "config": {"workload": cfg.name}})
+        print(json.dumps(out))
         return
-    # target logits resident in HBM before timing
-    eng.draft_phase(feat, tok)
-    tgt = synth_target(cfg, eng)
-    run_steps(eng, feat, tok, tgt, args.warmup)
+
+    copies = 1 if args.no_rotate else 2
+    cfg, engs, tok, host = build_engine(args.config, copies)
+    B, N = cfg.batch, engs[0].n_nodes
+    drafted = B * (N - 1)
+    # target logits resident in HBM before timing (one per weight copy: identical values)
+    tgts = []
+    for eng in engs:
+        eng.draft_phase(eng.root_features(), tok)
+        tgts.append(synth_target(cfg, eng))
+    run_steps(engs, tok, tgts, args.warmup)
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps
+    # timed region: exactly K steps (eager), alternating the weight copies
     marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
-    run_steps(eng, feat, tok, tgt, args.steps, marks)
+    run_steps(engs, tok, tgts, args.steps, marks)
     end.record()
     t_submit = time.perf_counter() - t_wall
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
+    ms_step = start.elapsed_time(end) / args.steps
     ms_draft = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps
     ms_verify = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps
     ms_eager = ms_step
 
-    # the same round captured as one HIP graph (every kernel of the round, the
-    # launches pre-recorded): exactly K replays, timed the same way
-    ms_graph = None
+    # the same rounds captured as HIP graphs (one per weight copy): exactly K replays, alternating
+    ms_graph = ms_graph_same = None
     if not args.no_graph:
-        eng.capture_round(feat, tok, tgt, 0, 0)
-        for _ in range(args.warmup):
-            eng.replay_round()
+        for j, eng in enumerate(engs):
+            eng.capture_round(eng.root_features(), tok, tgts[j], 0, 0)
+        for i in range(args.warmup):
+            engs[i % copies].replay_round()
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t_g = time.perf_counter()
         g0.record()
-        for _ in range(args.steps):
-            eng.replay_round()
+        for i in range(args.steps):
+            engs[i % copies].replay_round()
         g1.record()
         torch.cuda.synchronize()
         t_g = time.perf_counter() - t_g
         ms_graph = g0.elapsed_time(g1) / args.steps
         ms_step, t_wall = ms_graph, t_g  # the step of record: graph replay
+        if copies > 1:  # for reference: the same weight copy every round
+            g0.record()
+            for i in range(args.steps):
+                engs[0].replay_round()
+            g1.record()
+            torch.cuda.synchronize()
+            ms_graph_same = g0.elapsed_time(g1) / args.steps
 
-    # per-kernel durations: HIP events around every draft-step launch, same K steps again
+    # per-kernel durations: HIP events around every draft-step launch, K more eager steps (alternating copies)
     E.eagle_profile_enable(args.steps * 200)
-    run_steps(eng, feat, tok, tgt, args.steps)
+    run_steps(engs, tok, tgts, args.steps)
     torch.cuda.synchronize()
-    kernels = {}
-    for role in E._abi.ROLES:
-        r = E.eagle_profile_read(role)
-        if r["launches"]:
-            kernels[role] = dict(launches_per_step=r["launches"] / args.steps,
-                                 avg_us=1e3 * r["ms"] / r["launches"],
-                                 gbs=r["bytes"] / (r["ms"] * 1e-3) / 1e9 if r["ms"] > 0 else None,
-                                 tflops=r["flops"] / (r["ms"] * 1e-3) / 1e12 if r["ms"] > 0 else None,
-                                 bytes_per_launch=r["bytes"] / r["launches"],
-                                 ms_per_step=r["ms"] / args.steps)
+    kernels = kernel_table(E, args.steps)
     E.eagle_profile_disable()
-    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-    kd = kernels[dom]
-    achieved = kd["gbs"]
-    traffic = traffic_for(dom, cfg.name)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
-                "avg_launch_us": round(kd["avg_us"], 2), "bytes_per_launch": round(kd["bytes_per_launch"])}
+    dom_role = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    roofline = hbm_roofline(kernels, traffic_for(dom_role, cfg.name))
     gemm_roles = ["fc", "qkv", "o", "gate_up", "down", "lm_head"]
     g_ms = sum(kernels[r]["ms_per_step"] for r in gemm_roles if r in kernels)
     g_bytes = sum(kernels[r]["bytes_per_launch"] * kernels[r]["launches_per_step"] for r in gemm_roles if r in kernels)
+    del engs, tgts
+    torch.cuda.empty_cache()
 
-    others = []
+    others, decode = [], None
     if not args.headline_only and args.config == 2:
-        del eng, tgt
-        torch.cuda.empty_cache()
         for cid in (3, 4, 5):
             log(f"[bench] full round of workload {cid} ...")
-            others.append(round_bench(cid, 10, 2))
+            others.append(round_bench(cid, 10, 2, tree_wide_steps=5 if cid in (4, 5) else 0))
+        log(f"[bench] {args.rounds}-round decode of workload {args.config} ...")
+        decode = decode_bench(args.config, args.rounds)
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on one round ...")
+        log("[bench] timing the CPU oracle ...")
         cpu = cpu_baseline(cfg, host)
 
     s = cfg.shape
@@ -397,20 +518,22 @@ def main():
         "config": {"workload": cfg.name, "d": s.d, "heads": f"{s.n_heads}q/{s.n_kv_heads}kv x {s.head_dim}",
                    "ffn": s.ffn, "vocab": s.vocab, "batch": B, "prefix": cfg.prefix[1], "tree": cfg.tree,
                    "drafted_nodes_per_seq": N - 1, "global_batch": B, "seq_len": cfg.prefix[1],
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "weight_copies": copies},
         "draft_nodes_per_s": round(drafted / (ms_draft * 1e-3), 1),
         "verify_nodes_per_s": round(B * N / (ms_verify * 1e-3), 1),
         "ms_per_step_eager": round(ms_eager, 4),
         "ms_per_step_graph": round(ms_graph, 4) if ms_graph is not None else None,
+        "ms_per_step_graph_one_weight_copy": round(ms_graph_same, 4) if ms_graph_same is not None else None,
         "ms_draft_phase": round(ms_draft, 4),
         "ms_verify": round(ms_verify, 4),
         "wall_s_timed": round(t_wall, 4),
         "host_submit_ms_per_step": round(1e3 * t_submit / args.steps, 4),
         "gemm_stream_gbs": round(g_bytes / (g_ms * 1e-3) / 1e9, 1) if g_ms else None,
-        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                    for k, v in kernels.items()},
+        "kernels": rounded(kernels),
         "roofline": roofline,
         "other_workloads": others,
+        "tree_wide": [o["tree_wide"] | {"workload": o["workload"]} for o in others if "tree_wide" in o],
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

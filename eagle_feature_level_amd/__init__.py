@@ -68,10 +68,11 @@ def make_rows(n_rows, batch, max_rows_per_seq, row_start, token, parent, pos=Non
                             _ptr(slot), _ptr(mask)), row_start, token, parent, pos, slot, mask)
 
 
-def make_kv(prefix_k, prefix_v, prefix_off, prefix_len, max_prefix_len, tree_k, tree_v, prefix_cap=None):
+def make_kv(prefix_k, prefix_v, prefix_off, prefix_len, max_prefix_len, tree_k, tree_v, prefix_cap=None,
+            prefix_len_sum=0):
     return _keep(eagle_kv(_ptr(prefix_k), _ptr(prefix_v), _ptr(prefix_off), _ptr(prefix_len), max_prefix_len,
-                          _ptr(tree_k), _ptr(tree_v), _ptr(prefix_cap)), prefix_k, prefix_v, prefix_off, prefix_len,
-                 tree_k, tree_v, prefix_cap)
+                          _ptr(tree_k), _ptr(tree_v), _ptr(prefix_cap), int(prefix_len_sum)), prefix_k, prefix_v,
+                 prefix_off, prefix_len, tree_k, tree_v, prefix_cap)
 
 
 def make_out(feat, logits, lse, topk, topk_idx, topk_logq, seed=0, round_=0, row_base=0):

@@ -42,7 +42,8 @@ class eagle_rows(ctypes.Structure):
 
 class eagle_kv(ctypes.Structure):
     _fields_ = [("prefix_k", c_vp), ("prefix_v", c_vp), ("prefix_off", c_vp), ("prefix_len", c_vp),
-                ("max_prefix_len", c_i32), ("tree_k", c_vp), ("tree_v", c_vp), ("prefix_cap", c_vp)]
+                ("max_prefix_len", c_i32), ("tree_k", c_vp), ("tree_v", c_vp), ("prefix_cap", c_vp),
+                ("prefix_len_sum", ctypes.c_int64)]
 
 
 class eagle_draft_out(ctypes.Structure):

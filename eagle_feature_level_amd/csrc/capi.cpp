@@ -579,9 +579,12 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       const AttnPlan plan = attn_plan(bf16, maxL, rows->batch, s.n_kv_heads, max_q);
       at.split_len = plan.split_len;
       at.n_splits = plan.n_splits;
-      // bytes: each sequence's prefix K and V once, tree slots, q in, output out; flops 4*hd per (query, key)
-      const double kv_bytes = 2.0 * wbytes * s.n_kv_heads * s.head_dim * ((double)kv->max_prefix_len * rows->batch);
-      e = timed(st, EAGLE_ROLE_ATTN, kv_bytes + 8.0 * M * hq, 4.0 * M * s.n_heads * s.head_dim * kv->max_prefix_len,
+      // bytes: each sequence's prefix K and V once (sum of the lengths when the caller gives it), q in,
+      // output out; flops 4*hd per (query, key)
+      const double sum_len =
+          kv->prefix_len_sum > 0 ? (double)kv->prefix_len_sum : (double)kv->max_prefix_len * rows->batch;
+      const double kv_bytes = 2.0 * wbytes * s.n_kv_heads * s.head_dim * sum_len;
+      e = timed(st, EAGLE_ROLE_ATTN, kv_bytes + 8.0 * M * hq, 4.0 * M * s.n_heads * s.head_dim * sum_len / rows->batch,
                 [&] { return launch_attention(at, bf16, s.head_dim, max_q, st); });
       if (e != hipSuccess) return hip_fail(e);
     }

@@ -131,10 +131,12 @@ class EagleRound:
         self.tw_tree_k = torch.zeros_like(self.tree_k)
         self.tw_tree_v = torch.zeros_like(self.tree_v)
         self.prefix = prefix
+        # the prefix lengths' sum at construction, for the measurement hook's byte count only
+        len_sum = int(prefix["len"].sum().item()) if prefix.get("len") is not None else 0
         self.kv = make_kv(prefix["k"], prefix["v"], prefix["off"], prefix["len"], prefix["max_len"], self.tree_k,
-                          self.tree_v, prefix.get("cap"))
+                          self.tree_v, prefix.get("cap"), len_sum)
         self.tw_kv = make_kv(prefix["k"], prefix["v"], prefix["off"], prefix["len"], prefix["max_len"],
-                             self.tw_tree_k, self.tw_tree_v, prefix.get("cap"))
+                             self.tw_tree_k, self.tw_tree_v, prefix.get("cap"), len_sum)
         self.c_flags = torch.zeros(B, dtype=torch.int32, device=device)
         # catch-up rows between rounds: R = depth + 1 rows per sequence (the root and every accepted drafted
         # node, each joined with the token after it), their f^, which of them starts the next round, and

@@ -109,6 +109,9 @@ typedef struct {
   int32_t max_prefix_len;    /* host: max over b of L_b (an upper bound is fine) */
   void *tree_k, *tree_v;     /* written: the rows' slots                        */
   const int32_t *prefix_cap; /* [batch] C_b >= L_b, or NULL (C_b = L_b)         */
+  int64_t prefix_len_sum;    /* host: sum over b of L_b if known, else 0; used
+                                only by the measurement hook's byte count
+                                (0: max_prefix_len per sequence)                */
 } eagle_kv;
 
 /* Outputs of a draft step. */
