@@ -633,33 +633,43 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
 // ---------------------------------------------------------------------------
 // Large-M kernel (M above a few hundred rows, where the matrix units are the
 // bound): WN x WM waves, each owning TN x TM blocks of 16 x 16 outputs
-// (weight rows x activation rows), K staged in blocks of BK through LDS (two
+// (weight rows x activation rows), K staged in blocks of 32 through LDS (two
 // buffers, the next block's global loads in flight in registers), both
 // operands from the prepared bf16 operand (hi and lo halves: two MFMAs per
 // product).  The MFMAs per LDS fragment a wave reads grow with its tile,
-// TN*TM / (TN + NH*TM); the LDS footprint, two buffers of (BN + NH*BM) x
-// (BK + 8) bf16, bounds the workgroup tile.  Consecutive tiles stay on one XCD
-// so the workgroups sharing a weight tile share an L2.  SwiGLU: per wave, TN/2
-// blocks of gate rows, then the up rows of the same ffn columns, so gate and
-// up meet in one lane.
+// TN*TM / (TN + NH*TM).  Consecutive tiles stay on one XCD so the workgroups
+// sharing a weight tile share an L2.  SwiGLU: per wave, TN/2 blocks of gate
+// rows, then the up rows of the same ffn columns, so gate and up meet in one
+// lane.
+// LDS layout: tile rows of 64 bytes (32 bf16 of K, four 16-byte chunks) with
+// no padding; chunk c of row r sits in slot c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1).
+// That spreads the 16 rows an MFMA fragment read touches at one chunk over all
+// banks whether the LDS serves 8 lanes (32 banks) or 16 lanes (64 banks) of a
+// 16-byte access per cycle, and keeps the stores (four lanes per row)
+// contiguous: with rows padded to 80 bytes instead, the stores conflicted
+// two-way and the kernel ran 10-20% slower at the 70B shapes.
 // ---------------------------------------------------------------------------
 template <int WN_, int WM_, int TN_, int TM_, int BK_>
 struct TileCfg {
   static constexpr int WN = WN_, WM = WM_, TN = TN_, TM = TM_, BK = BK_;
-  static constexpr int BN = WN * TN * 16, BM = WM * TM * 16, LD = BK + 8, KC = BK / 32;
-  static_assert(WN * WM == 8, "512 threads");
+  static constexpr int BN = WN * TN * 16, BM = WM * TM * 16;
+  static constexpr int NT = WN * WM * 64;  // threads of a workgroup
   static_assert(BK % 32 == 0, "whole MFMA k-steps");
 };
 
+__device__ __forceinline__ int swz_slot(int row, int c) { return row * 4 + (c ^ ((row >> 1) & 3) ^ ((row >> 3) & 1)); }
+
 template <int EPI, bool SPLIT, class T>
-__global__ void __launch_bounds__(512) gemm_tile(GemmArgs a, const bf16_t* __restrict__ xb, BigPlan p) {
-  constexpr int NH = SPLIT ? 2 : 1;
-  constexpr int BN = T::BN, BM = T::BM, BK = T::BK, LD = T::LD, TN = T::TN, TM = T::TM;
-  constexpr int CPR = BK / 8;                    // 16-byte chunks per tile row and k-block
-  constexpr int ACH = (BN * CPR + 511) / 512;    // weight chunks per thread
-  constexpr int XCH = (BM * CPR + 511) / 512;    // activation chunks per thread and half
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BN][LD];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][NH][BM][LD];
+__global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __restrict__ xb, BigPlan p) {
+  constexpr int NH = SPLIT ? 2 : 1, NT = T::NT;
+  constexpr int BN = T::BN, BM = T::BM, BK = T::BK, TN = T::TN, TM = T::TM;
+  static_assert(BK == 32, "four 16-byte chunks per tile row");
+  constexpr int ASL = BN * 4, BSL = BM * 4;  // 16-byte slots of the weight and activation tiles
+  constexpr int SLOTS = ASL + NH * BSL;       // one buffer
+  static_assert(ASL % NT == 0 && BSL % NT == 0, "whole load rounds");
+  constexpr int AR = ASL / NT, XR = BSL / NT;  // loads per thread and block: weight, activation half
+  constexpr int ROUNDS = AR + NH * XR;
+  __shared__ __attribute__((aligned(16))) u32x4 L[2][SLOTS];
   __shared__ float ssq_s[T::WN][BM];
   const int nwg = gridDim.x, bid = blockIdx.x;
   const int lid = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;  // consecutive tiles on one XCD
@@ -671,8 +681,6 @@ __global__ void __launch_bounds__(512) gemm_tile(GemmArgs a, const bf16_t* __res
   const int r = lane & 15, g = lane >> 4;
   const int kper = a.K / p.splits, kbeg = sp * kper, nkb = kper / BK;
 
-  // logical weight row of tile row i (-1 past the end); SwiGLU: per wave, TN/2
-  // blocks of gate rows, then the up rows of the same ffn columns
   auto wrow_of = [&](int i) -> int {
     if constexpr (EPI == EPI_SWIGLU) {
       constexpr int WR = TN * 16, HR = TN * 8;
@@ -685,44 +693,41 @@ __global__ void __launch_bounds__(512) gemm_tile(GemmArgs a, const bf16_t* __res
       return n < a.N ? n : -1;
     }
   };
-  const bf16_t* ap[ACH];
-  const bf16_t* xp[XCH];
-#pragma unroll
-  for (int u = 0; u < ACH; ++u) {
-    const int c = t + 512 * u;
-    const int n = (c < BN * CPR) ? wrow_of(c / CPR) : -1;
-    ap[u] = (n >= 0) ? wrow<bf16_t>(a, n) + kbeg + (c % CPR) * 8 : nullptr;
-  }
-#pragma unroll
-  for (int u = 0; u < XCH; ++u) {
-    const int c = t + 512 * u;
-    const int m = m0 + c / CPR;
-    xp[u] = (c < BM * CPR && m < a.M) ? xb + (size_t)m * a.K + kbeg + (c % CPR) * 8 : nullptr;
-  }
+  // load u of a block: 16-byte slot q = u*NT + t of the buffer, chunk (q & 3)
+  // of tile row q >> 2.  Rows past the end of W or x are read from row 0
+  // (finite values whose outputs are never stored), so every load is
+  // unconditional.
   const size_t lo_off = (size_t)a.M * a.K;
-  u32x4 ra[ACH], rx[NH][XCH];
-  auto load = [&](int kb) {
+  const bf16_t* src[ROUNDS];
+#pragma unroll
+  for (int u = 0; u < ROUNDS; ++u) {
+    const int q = u * NT + t;
+    if (u < AR) {
+      const int row = q >> 2, n = wrow_of(row);
+      src[u] = wrow<bf16_t>(a, n >= 0 ? n : 0) + kbeg + (q & 3) * 8;
+    } else {
+      const int q2 = q - ASL, h = q2 / BSL, q3 = q2 % BSL;
+      const int row = q3 >> 2, m = m0 + row < a.M ? m0 + row : 0;
+      src[u] = xb + h * lo_off + (size_t)m * a.K + kbeg + (q3 & 3) * 8;
+    }
+  }
+  // LDS slot of load u: the tile row and chunk of slot u*NT + t, swizzled (the
+  // tiles are whole multiples of NT slots, so a load never straddles two tiles)
+  auto dst = [&](int u) -> int {
+    const int q = u * NT + t;
+    const int tq = q < ASL ? q : (q - ASL) % BSL;
+    const int off = q < ASL ? 0 : ASL + ((q - ASL) / BSL) * BSL;
+    return off + swz_slot(tq >> 2, tq & 3);
+  };
+  u32x4 R0[ROUNDS];
+  auto load = [&](u32x4 (&R)[ROUNDS], int kb) {
     const int k0 = kb * BK;
 #pragma unroll
-    for (int u = 0; u < ACH; ++u) ra[u] = ap[u] ? *(const u32x4*)(ap[u] + k0) : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int u = 0; u < XCH; ++u) rx[h][u] = xp[u] ? *(const u32x4*)(xp[u] + h * lo_off + k0) : u32x4{0, 0, 0, 0};
+    for (int u = 0; u < ROUNDS; ++u) R[u] = *(const u32x4*)(src[u] + k0);
   };
-  auto store = [&](int buf) {
+  auto store = [&](const u32x4 (&R)[ROUNDS], int buf) {
 #pragma unroll
-    for (int u = 0; u < ACH; ++u) {
-      const int c = t + 512 * u;
-      if (c < BN * CPR) *(u32x4*)&As[buf][c / CPR][(c % CPR) * 8] = ra[u];
-    }
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int u = 0; u < XCH; ++u) {
-        const int c = t + 512 * u;
-        if (c < BM * CPR) *(u32x4*)&Bs[buf][h][c / CPR][(c % CPR) * 8] = rx[h][u];
-      }
+    for (int u = 0; u < ROUNDS; ++u) L[buf][dst(u)] = R[u];
   };
 
   floatx4 acc[TN][TM];
@@ -731,33 +736,35 @@ __global__ void __launch_bounds__(512) gemm_tile(GemmArgs a, const bf16_t* __res
 #pragma unroll
     for (int mb = 0; mb < TM; ++mb) acc[nb][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  auto compute = [&](int buf) {
+    const u32x4* B0 = L[buf];
+    u32x4 A[TN];
+#pragma unroll
+    for (int nb = 0; nb < TN; ++nb) A[nb] = B0[swz_slot((wn * TN + nb) * 16 + r, g)];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      u32x4 B[TM];
+#pragma unroll
+      for (int mb = 0; mb < TM; ++mb) B[mb] = B0[ASL + h * BSL + swz_slot((wm * TM + mb) * 16 + r, g)];
+#pragma unroll
+      for (int nb = 0; nb < TN; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < TM; ++mb) acc[nb][mb] = mfma16(A[nb], B[mb], acc[nb][mb]);
+    }
+  };
+  // block kb in LDS buffer kb & 1; block kb + 1 arrives in R0 meanwhile and is
+  // stored to the other buffer, then block kb + 2 is requested
   if (nkb > 0) {
-    load(0);
-    store(0);
-    if (nkb > 1) load(1);
+    load(R0, 0);
+    store(R0, 0);
+    if (nkb > 1) load(R0, 1);
   }
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-#pragma unroll
-    for (int kc = 0; kc < T::KC; ++kc) {
-      u32x4 A[TN];
-#pragma unroll
-      for (int nb = 0; nb < TN; ++nb) A[nb] = *(const u32x4*)&As[buf][(wn * TN + nb) * 16 + r][kc * 32 + g * 8];
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        u32x4 B[TM];
-#pragma unroll
-        for (int mb = 0; mb < TM; ++mb) B[mb] = *(const u32x4*)&Bs[buf][h][(wm * TM + mb) * 16 + r][kc * 32 + g * 8];
-#pragma unroll
-        for (int nb = 0; nb < TN; ++nb)
-#pragma unroll
-          for (int mb = 0; mb < TM; ++mb) acc[nb][mb] = mfma16(A[nb], B[mb], acc[nb][mb]);
-      }
-    }
+    compute(kb & 1);
     if (kb + 1 < nkb) {
-      store(buf ^ 1);
-      if (kb + 2 < nkb) load(kb + 2);
+      store(R0, (kb + 1) & 1);
+      if (kb + 2 < nkb) load(R0, kb + 2);
     }
     __syncthreads();
   }
@@ -1160,7 +1167,7 @@ BigPlan plan_tile(int M, int N, int K, bool swiglu) {
 
 template <class T, bool SPLIT>
 hipError_t tile_epi(const GemmArgs& a, int epi, const bf16_t* xb, const BigPlan& p, hipStream_t s) {
-  const dim3 grid(p.tiles_n * p.tiles_m * p.splits), blk(512);
+  const dim3 grid(p.tiles_n * p.tiles_m * p.splits), blk(T::NT);
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL((gemm_tile<EPI_STORE, SPLIT, T>), grid, blk, 0, s, a, xb, p); break;
     case EPI_BIAS_SUMSQ: hipLaunchKernelGGL((gemm_tile<EPI_BIAS_SUMSQ, SPLIT, T>), grid, blk, 0, s, a, xb, p); break;
