@@ -370,9 +370,13 @@ __global__ void __launch_bounds__(128) attn_combine_kernel(AttnArgs a, int hd) {
 //                  the V^T rows use the same order)
 // The next tile's K and V are loaded into registers while the current one is
 // used.  The 64 tree slots ride with the last split as one more tile, masked
-// per query by its row's ancestor bitmask.  With one split the normalised
-// output is written directly; otherwise (max, sum, unnormalised output) per
-// split goes to attn_combine_kernel.
+// per query by its row's ancestor bitmask (a split of their own when few
+// groups share the chip).  With one split the normalised output is written
+// directly; otherwise (max, sum, unnormalised output) per split goes to
+// attn_combine_kernel.  (Merging the splits in the last workgroup to finish
+// needs a device-scope release and acquire per workgroup; on this chip those
+// write back and invalidate the whole L2 of the XCD and cost several times
+// the separate launch.)
 // ---------------------------------------------------------------------------
 constexpr int AQ = 64;          // queries per workgroup
 constexpr int AKROW = 128 + 8;  // K tile row (bf16): 272 B, rows land 4 banks apart
@@ -601,19 +605,22 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a) {
     }
   }
 
-  if (!qv) return;
   // lane (query c, gq) holds dims db*16 + 4*gq + v
   if (a.n_splits == 1) {
+    if (!qv) return;
     const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
     float* dst = a.out + ((size_t)row * a.hq + h) * 128;
 #pragma unroll
     for (int db = 0; db < 8; ++db)
       *(float4*)(dst + db * 16 + gq * 4) =
           make_float4(oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv);
-  } else {
-    float* dst = a.part + (((size_t)s * a.n_rows + row) * a.hq + h) * (128 + 2);
+    return;
+  }
+  const size_t sstride = (size_t)a.n_rows * a.hq * (128 + 2);  // between splits
+  if (qv) {
+    float* dst = a.part + s * sstride + ((size_t)row * a.hq + h) * (128 + 2);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < 8; ++db) {  // rows of hd + 2 floats: 8-byte aligned
       float* d4 = dst + 2 + db * 16 + gq * 4;
       d4[0] = oacc[db][0]; d4[1] = oacc[db][1]; d4[2] = oacc[db][2]; d4[3] = oacc[db][3];
     }
@@ -647,17 +654,28 @@ static AttnPlan plan_scalar(int max_prefix, int batch, int hkv) {
   return AttnPlan{split_len, (max_prefix + split_len - 1) / split_len + 1};
 }
 
-// bf16 matrix-core kernel: splits of whole tiles; the tree slots ride with
-// the last split.  Aim: ~256 workgroups when fewer than 256 (sequence, kv head,
-// query block) units exist, else ~1024.  Measured on the 7B shapes (32 units):
-// 256 workgroups of 2-4 tiles beat 1024 of one tile by 10-43 % (each workgroup
-// pays its set-up, and the split partials must be combined); at 256-1024 units
-// (13B / 70B batched) the ~1024 target was within a few % of the best plan.
+// bf16 matrix-core kernel: splits of whole tiles.  Fewer than 256 (sequence,
+// kv head, query block) units -- single-sequence drafting -- are
+// latency-bound: the tree slots get a split of their own and the prefix
+// splits hold as few tiles as keep every workgroup co-resident (two per
+// compute unit), so no workgroup walks prefix tiles and the tree one after the
+// other.  (Measured on the 7B shapes, 32 units: ~256 workgroups of 2-4 tiles
+// beat 1024 of one tile by 10-43 %: each workgroup pays its set-up and the
+// partials must be combined.)  From 256 units (13B / 70B batched): ~1024
+// workgroups, the tree tile with the last split, within a few % of the best
+// plan measured.
 static AttnPlan plan_mfma(int max_prefix, int batch, int hkv, int max_queries) {
   const long qblocks = (max_queries + AQ - 1) / AQ;
   const long per = (long)batch * hkv * (qblocks > 0 ? qblocks : 1);
   const int tiles = (max_prefix + KT - 1) / KT;
-  const long target = per < 256 ? 256 : 1024;
+  if (tiles <= 1) return AttnPlan{KT, 1};
+  if (per < 256) {
+    int tp = 1;
+    while (tp < tiles && per * ((tiles + tp - 1) / tp + 1) > 512) ++tp;
+    const int split_len = tp * KT;
+    return AttnPlan{split_len, (max_prefix + split_len - 1) / split_len + 1};
+  }
+  const long target = 1024;
   int splits = (int)((target + per - 1) / per);
   if (splits > tiles) splits = tiles;
   if (splits < 1) splits = 1;

@@ -502,6 +502,8 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       e = gemm(a, EPI_BIAS_SUMSQ, &np1, EAGLE_ROLE_FC);
       if (e != hipSuccess) return hip_fail(e);
     }
+    // queries per (sequence, kv head) at most
+    const int max_q = rows->max_rows_per_seq * (s.n_heads / s.n_kv_heads);
     // a3: RMSNorm -> [q; k; v]: (x * g1) [wq; wk; wv]^T, row scale in the epilogue
     {
       GemmArgs a = gemm_base(M, hq + 2 * hkv, d);
@@ -575,7 +577,6 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       at.batch = rows->batch;
       at.hq = s.n_heads;
       at.hkv = s.n_kv_heads;
-      const int max_q = rows->max_rows_per_seq * (s.n_heads / s.n_kv_heads);
       const AttnPlan plan = attn_plan(bf16, maxL, rows->batch, s.n_kv_heads, max_q);
       at.split_len = plan.split_len;
       at.n_splits = plan.n_splits;

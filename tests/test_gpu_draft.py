@@ -168,6 +168,24 @@ def test_draft_step_bf16_gqa(counts, lens):
     _check_topk_valid(ref["logits"], gpu["idx"], tol)
 
 
+# Few (sequence, kv head) groups: the attention plan gives the tree slots a
+# split of their own beside prefix splits of whole tiles.  Cases: one tile
+# (no split), several splits with a ragged last tile, an empty prefix in one
+# sequence, splits past a short sequence's end, 16 queries per kv head, and
+# 1, 2 and 8 query heads per kv head.
+@pytest.mark.parametrize("heads,kv_heads,counts,lens", [(2, 2, [10], [700]), (4, 2, [8, 3], [1000, 129]),
+                                                       (4, 2, [1, 5, 8], [300, 0, 513]), (8, 1, [2, 1], [128, 1]),
+                                                       (8, 1, [1], [2049]), (2, 2, [16, 16], [0, 255])])
+def test_draft_step_bf16_few_queries(heads, kv_heads, counts, lens):
+    shape = Shape(256, heads, kv_heads, 128, 384, 1000)
+    assert max(counts) * heads // kv_heads <= 16
+    ref, gpu, rows, tk, tv = _run_draft(shape, counts, lens, seed=11 + sum(counts) + sum(lens))
+    tol = TOL["bf16"]
+    assert np.max(np.abs(gpu["feat"] - ref["feat"])) < tol
+    assert np.max(np.abs(gpu["logits"] - ref["logits"])) < tol
+    _check_topk_valid(ref["logits"], gpu["idx"], tol)
+
+
 # bf16 GEMM operands (EAGLE_ACT_BF16) against the oracle under the same contract,
 # through the three kernels: up to 16 rows (register-streamed weights), 17..256
 # (wide kernel), 257+ (LDS-tiled kernel); the d = 1024 cases split K over the
