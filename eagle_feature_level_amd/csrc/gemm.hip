@@ -642,12 +642,14 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
 // rows, then the up rows of the same ffn columns, so gate and up meet in one
 // lane.
 // LDS layout: tile rows of 64 bytes (32 bf16 of K, four 16-byte chunks) with
-// no padding; chunk c of row r sits in slot c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1).
-// That spreads the 16 rows an MFMA fragment read touches at one chunk over all
-// banks whether the LDS serves 8 lanes (32 banks) or 16 lanes (64 banks) of a
-// 16-byte access per cycle, and keeps the stores (four lanes per row)
-// contiguous: with rows padded to 80 bytes instead, the stores conflicted
-// two-way and the kernel ran 10-20% slower at the 70B shapes.
+// no padding; chunk c of row r sits in slot c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1),
+// so the stores (four lanes per row) stay contiguous: with rows padded to 80
+// bytes instead the kernel ran 10-20% slower at the 70B shapes.  (The LDS
+// bank-conflict counter still reports ~1.3 cycles per fragment read for this
+// layout, as for plain row-major rows; a layout it reports conflict-free for
+// both the fragment reads and the stores, chunk c of row r of each 16-row
+// block in slot ((r / 8) * 4 + c) * 8 + (r + 2 c) % 8, ran no faster at the
+// 13B and 70B shapes, so counted conflicts are not what bounds this kernel.)
 // ---------------------------------------------------------------------------
 template <int WN_, int WM_, int TN_, int TM_, int BK_>
 struct TileCfg {
