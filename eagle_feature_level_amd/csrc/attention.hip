@@ -403,10 +403,19 @@ __device__ __forceinline__ uint32_t asplit2(float a, float b, uint32_t* lo) {
   return __builtin_amdgcn_perm(ub, ua, 0x07060302u);
 }
 
-__global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t ks[KT][AKROW];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[128][AVROW];
+template <bool KSPLIT>
+__global__ void __launch_bounds__(256, KSPLIT ? 3 : 2) attn_mfma_kernel(AttnArgs a) {
+  // K tile and transposed V tile; with KSPLIT the space then holds the four
+  // waves' partial results for the merge
+  constexpr int KS_BYTES = KT * AKROW * 2, VT_BYTES = 128 * AVROW * 2;
+  static_assert(KS_BYTES + VT_BYTES >= 4 * 16 * (128 + 2) * 4, "merge space");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[KS_BYTES + VT_BYTES];
+  bf16_t(*ks)[AKROW] = reinterpret_cast<bf16_t(*)[AKROW]>(smem);
+  bf16_t(*vt)[AVROW] = reinterpret_cast<bf16_t(*)[AVROW]>(smem + KS_BYTES);
   __shared__ unsigned long long umask_s;
+  // KSPLIT: the B operand of S^T (the same 16 queries in every wave), one copy
+  __shared__ __attribute__((aligned(16))) u32x4 qf[KSPLIT ? 4 : 1][2][64];
+  constexpr int QPB = KSPLIT ? 16 : AQ;  // queries per workgroup
   const int s = blockIdx.x;
   const int g = blockIdx.y % a.hkv, qb = blockIdx.y / a.hkv;
   const int b = blockIdx.z;
@@ -415,7 +424,7 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a) {
   const int G = a.hq / a.hkv;
   const int r0 = a.row_start[b], nr = a.row_start[b + 1] - r0;
   const int nq = nr * G;
-  if (qb * AQ >= nq) return;  // whole workgroup: no queries in this block
+  if (qb * QPB >= nq) return;  // whole workgroup: no queries in this block
   const int L = a.prefix_len[b];
   const int kbeg = s * a.split_len;
   const int kend = min(L, kbeg + a.split_len);
@@ -472,8 +481,9 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a) {
   if (with_tree)
     for (int t = threadIdx.x; t < nr; t += 256) atomicOr(&umask_s, (unsigned long long)a.mask[r0 + t]);
 
-  // this lane's query: q = qb*64 + wv*16 + c -> row r0 + q/G, head g*G + q%G
-  const int qi = qb * AQ + wv * 16 + c;
+  // this lane's query: q = qb*64 + wv*16 + c (KSPLIT: qb*16 + c, the same in
+  // every wave) -> row r0 + q/G, head g*G + q%G
+  const int qi = KSPLIT ? qb * 16 + c : qb * AQ + wv * 16 + c;
   const bool qv = qi < nq;
   const int row = r0 + (qv ? qi / G : 0);
   const int h = g * G + (qv ? qi % G : 0);
@@ -496,8 +506,17 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a) {
       qh[dc][2] = asplit2(v1.x * sc, v1.y * sc, &l); ql[dc][2] = l;
       qh[dc][3] = asplit2(v1.z * sc, v1.w * sc, &l); ql[dc][3] = l;
     }
+    if constexpr (KSPLIT) {
+      if (wv == 0) {
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc) {
+          qf[dc][0][lane] = qh[dc];
+          qf[dc][1][lane] = ql[dc];
+        }
+      }
+    }
   }
-  __syncthreads();  // umask_s complete
+  __syncthreads();  // umask_s complete (and the shared q fragments)
   const uint64_t umask = umask_s;
 
 
@@ -529,36 +548,44 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a) {
     if (t + 1 < n_prefix_tiles) load_prefix_tile(t + 1);
     else if (t + 1 == n_prefix_tiles && with_tree) load_tree_tile(umask);
 
-    // S^T: lane (query c, gq) gets keys kb*16 + 4*gq + v, v < 4
-    floatx4 sacc[4];
+    // S^T: lane (query c, gq) gets keys kb*16 + 4*gq + v, v < 4, for the
+    // wave's key blocks: all four, or (KSPLIT) block wv alone
+    constexpr int NKB = KSPLIT ? 1 : 4;
+    floatx4 sacc[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NKB; ++i) {
+      const int kb = KSPLIT ? wv : i;
+      sacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dc = 0; dc < 4; ++dc) {
         const u32x4 A = *(const u32x4*)&ks[kb * 16 + c][dc * 32 + gq * 8];
-        sacc[kb] = mfma16a(A, qh[dc], sacc[kb]);
-        sacc[kb] = mfma16a(A, ql[dc], sacc[kb]);
+        if constexpr (KSPLIT) {
+          sacc[i] = mfma16a(A, qf[dc][0][lane], sacc[i]);
+          sacc[i] = mfma16a(A, qf[dc][1][lane], sacc[i]);
+        } else {
+          sacc[i] = mfma16a(A, qh[dc], sacc[i]);
+          sacc[i] = mfma16a(A, ql[dc], sacc[i]);
+        }
       }
     }
-    float sv[4][4];
+    float sv[NKB][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int i = 0; i < NKB; ++i)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sv[kb][v] = sacc[kb][v];
+      for (int v = 0; v < 4; ++v) sv[i][v] = sacc[i][v];
     if (tree_tile || tlen < KT) {  // uniform: only the tree tile and a ragged last tile mask keys
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int i = 0; i < NKB; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int kk = kb * 16 + gq * 4 + v;
+          const int kk = (KSPLIT ? wv : i) * 16 + gq * 4 + v;
           const bool ok = tree_tile ? ((qmask >> kk) & 1ull) != 0 : kk < tlen;
-          if (!ok) sv[kb][v] = -INFINITY;
+          if (!ok) sv[i][v] = -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mx = fmaxf(fmaxf(mx, fmaxf(sv[kb][0], sv[kb][1])), fmaxf(sv[kb][2], sv[kb][3]));
+    for (int i = 0; i < NKB; ++i) mx = fmaxf(fmaxf(mx, fmaxf(sv[i][0], sv[i][1])), fmaxf(sv[i][2], sv[i][3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
     mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
     const float mnew = fmaxf(m_run, mx);
@@ -566,11 +593,11 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a) {
     const float mref = (mnew > -INFINITY) ? mnew : 0.f;
     float ps = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int i = 0; i < NKB; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float p = __builtin_amdgcn_exp2f(sv[kb][v] - mref);  // 2^-inf = 0
-        sv[kb][v] = p;
+        const float p = __builtin_amdgcn_exp2f(sv[i][v] - mref);  // 2^-inf = 0
+        sv[i][v] = p;
         ps += p;
       }
     ps += __shfl_xor(ps, 16, WAVE);
@@ -586,15 +613,18 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a) {
     }
     l_run += ps;
     m_run = mnew;
-    // O^T += V^T P^T over two 32-key chunks: chunk kc uses key blocks 2kc, 2kc+1
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      u32x4 Bh, Bl;
-      uint32_t l;
-      Bh[0] = asplit2(sv[2 * kc][0], sv[2 * kc][1], &l); Bl[0] = l;
-      Bh[1] = asplit2(sv[2 * kc][2], sv[2 * kc][3], &l); Bl[1] = l;
-      Bh[2] = asplit2(sv[2 * kc + 1][0], sv[2 * kc + 1][1], &l); Bl[2] = l;
-      Bh[3] = asplit2(sv[2 * kc + 1][2], sv[2 * kc + 1][3], &l); Bl[3] = l;
+    // O^T += V^T P^T over 32-key chunks: chunk kc uses key blocks 2kc, 2kc+1
+    // (KSPLIT: the chunk holding block wv, the other block's weights zero)
+    if constexpr (KSPLIT) {
+      const int kc = wv >> 1;
+      u32x4 Bh = u32x4{0u, 0u, 0u, 0u}, Bl = Bh;
+      uint32_t l0, l1;
+      const uint32_t h0 = asplit2(sv[0][0], sv[0][1], &l0), h1 = asplit2(sv[0][2], sv[0][3], &l1);
+      if (wv & 1) {
+        Bh[2] = h0; Bl[2] = l0; Bh[3] = h1; Bl[3] = l1;
+      } else {
+        Bh[0] = h0; Bl[0] = l0; Bh[1] = h1; Bl[1] = l1;
+      }
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const int d = db * 16 + c;
@@ -602,7 +632,77 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a) {
         oacc[db] = mfma16a(A, Bh, oacc[db]);
         oacc[db] = mfma16a(A, Bl, oacc[db]);
       }
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        u32x4 Bh, Bl;
+        uint32_t l;
+        Bh[0] = asplit2(sv[2 * kc][0], sv[2 * kc][1], &l); Bl[0] = l;
+        Bh[1] = asplit2(sv[2 * kc][2], sv[2 * kc][3], &l); Bl[1] = l;
+        Bh[2] = asplit2(sv[2 * kc + 1][0], sv[2 * kc + 1][1], &l); Bl[2] = l;
+        Bh[3] = asplit2(sv[2 * kc + 1][2], sv[2 * kc + 1][3], &l); Bl[3] = l;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const int d = db * 16 + c;
+          const u32x4 A = *(const u32x4*)&vt[d][(kc * 8 + gq * 2) * 4];
+          oacc[db] = mfma16a(A, Bh, oacc[db]);
+          oacc[db] = mfma16a(A, Bl, oacc[db]);
+        }
+      }
     }
+  }
+
+  if constexpr (KSPLIT) {
+    // merge the four waves (disjoint key blocks of every tile, same queries)
+    // through LDS: wave w's (max, sum) and unnormalised output per query
+    __syncthreads();  // every wave done with the K and V tiles
+    float* mst = reinterpret_cast<float*>(smem);  // [4][16][2] running (max, sum)
+    float* mo = mst + 4 * 16 * 2;                  // [4][16][128] outputs
+    if (gq == 0) {
+      mst[(wv * 16 + c) * 2] = m_run;
+      mst[(wv * 16 + c) * 2 + 1] = l_run;
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *(floatx4*)&mo[(wv * 16 + c) * 128 + db * 16 + gq * 4] = oacc[db];
+    __syncthreads();
+    // thread t: query t / 16, dims (t % 16) * 8 .. + 8
+    const int cq = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
+    const int qq = qb * 16 + cq;
+    if (qq >= nq) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mst[(w * 16 + cq) * 2]);
+    const float mref = (M > -INFINITY) ? M : 0.f;
+    float wt[4], Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wt[w] = __builtin_amdgcn_exp2f(mst[(w * 16 + cq) * 2] - mref);  // -inf -> 0
+      Ls += wt[w] * mst[(w * 16 + cq) * 2 + 1];
+    }
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc += wt[w] * mo[(w * 16 + cq) * 128 + d0 + e];
+      o[e] = acc;
+    }
+    const int qrow = r0 + qq / G, qh_ = g * G + qq % G;
+    if (a.n_splits == 1) {
+      const float inv = (Ls > 0.f) ? 1.f / Ls : 0.f;
+      float* dst = a.out + ((size_t)qrow * a.hq + qh_) * 128 + d0;
+      *(float4*)dst = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+      *(float4*)(dst + 4) = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+    } else {
+      float* dst = a.part + (size_t)s * a.n_rows * a.hq * (128 + 2) + ((size_t)qrow * a.hq + qh_) * (128 + 2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[2 + d0 + e] = o[e];
+      if (d0 == 0) {
+        dst[0] = M * 0.6931471805599453f;  // natural-log units for the combine
+        dst[1] = Ls;
+      }
+    }
+    return;
   }
 
   // lane (query c, gq) holds dims db*16 + 4*gq + v
@@ -657,9 +757,10 @@ static AttnPlan plan_scalar(int max_prefix, int batch, int hkv) {
 // bf16 matrix-core kernel: splits of whole tiles.  Fewer than 256 (sequence,
 // kv head, query block) units -- single-sequence drafting -- are
 // latency-bound: the tree slots get a split of their own and the prefix
-// splits hold as few tiles as keep every workgroup co-resident (two per
-// compute unit), so no workgroup walks prefix tiles and the tree one after the
-// other.  (Measured on the 7B shapes, 32 units: ~256 workgroups of 2-4 tiles
+// splits hold as few tiles as keep ~512 workgroups (two per compute unit), so
+// no workgroup walks prefix tiles and the tree one after the other.  (With the
+// key-split variant three fit per compute unit, but one-tile splits at 7B,
+// 544 workgroups, measured 16.8 -> 19.5 us against two-tile splits.)  (Measured on the 7B shapes, 32 units: ~256 workgroups of 2-4 tiles
 // beat 1024 of one tile by 10-43 %: each workgroup pays its set-up and the
 // partials must be combined.)  From 256 units (13B / 70B batched): ~1024
 // workgroups, the tree tile with the last split, within a few % of the best
@@ -696,7 +797,10 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, int hd, int max_querie
     const int qblocks = (max_queries + AQ - 1) / AQ;
     if (qblocks < 1) return hipSuccess;
     if ((long)qblocks * a.hkv > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_mfma_kernel, dim3(a.n_splits, a.hkv * qblocks, a.batch), dim3(256), 0, s, a);
+    if (max_queries <= 16)  // every query of a kv head in one wave: the waves split the keys
+      hipLaunchKernelGGL(attn_mfma_kernel<true>, dim3(a.n_splits, a.hkv, a.batch), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(attn_mfma_kernel<false>, dim3(a.n_splits, a.hkv * qblocks, a.batch), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_splits == 1) return e;
   } else {
