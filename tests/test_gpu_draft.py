@@ -211,6 +211,19 @@ def test_draft_step_bf16_act(d, counts, lens):
     _check_topk_valid(ref["logits"], gpu["idx"], tol)
 
 
+# More than 64 queries per kv head (eight query heads per kv head): several
+# 64-query blocks over the same keys (80, 128 and 136 queries).
+@pytest.mark.parametrize("counts,lens", [([10, 9], [700, 129]), ([16], [300]), ([17, 3], [64, 1000])])
+def test_draft_step_bf16_many_queries(counts, lens):
+    shape = Shape(256, 8, 1, 128, 384, 1000)
+    assert max(counts) * 8 > 64
+    ref, gpu, rows, tk, tv = _run_draft(shape, counts, lens, seed=31 + sum(counts) + sum(lens))
+    tol = TOL["bf16"]
+    assert np.max(np.abs(gpu["feat"] - ref["feat"])) < tol
+    assert np.max(np.abs(gpu["logits"] - ref["logits"])) < tol
+    _check_topk_valid(ref["logits"], gpu["idx"], tol)
+
+
 # EAGLE_ACT_BF16 at the full 7B draft-head shape: outside the 2e-2 bar (stated
 # beside the flag in eagle.h), so the test records the deviation from the fp64
 # oracle that rounds the same operands and bounds it loosely; without the flag
