@@ -109,6 +109,10 @@ struct DraftWs {
   void* act;
   float* gemm_part;
   void* topk;
+  // split bf16 operands (hi rows, then lo rows) handed from one GEMM's epilogue
+  // to the next GEMM (bf16 weights, more than 16 rows): d wide, ffn wide
+  uint16_t* xb_d;
+  uint16_t* xb_f;
   size_t total;
 };
 
@@ -156,6 +160,10 @@ DraftWs carve(const eagle_shape* s, int M, int B, int max_prefix, char* base) {
   w.act = take((size_t)M * s->ffn * 4);
   w.gemm_part = (float*)take(gp);
   w.topk = take(topk_workspace_bytes(M, s->vocab));
+  if (s->dtype == EAGLE_BF16 && M > 16) {
+    w.xb_d = (uint16_t*)take((size_t)M * s->d * 4);
+    w.xb_f = (uint16_t*)take((size_t)M * s->ffn * 4);
+  }
   w.total = off;
   return w;
 }
@@ -459,6 +467,10 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
   // M = 8 (one 16-row weight tile per workgroup); above, the four-tile QKV variant
   // plus the RoPE launch is faster (measured on the 7B shapes)
   const bool rope_fused = bf16 && M <= 8 && s.head_dim % 16 == 0;
+  // above 16 rows with split bf16 operands, each GEMM whose input is the previous
+  // GEMM's output takes that operand from the producer's epilogue, unscaled, and
+  // applies the RMSNorm row scale in its own epilogue (no operand prep pass)
+  const bool handover = bf16 && M > 16 && !act16;
 
   if (!head_only) {
     // a1: the rows' inputs [f_parent ; e(token)]: gathered by the FC GEMM itself
@@ -499,6 +511,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.sumsq_out = ws.sumsq1;
       a.gain_out = w->norm1;
       a.y2 = ws.xg;
+      if (handover) a.xb_out = ws.xb_d;
       e = gemm(a, EPI_BIAS_SUMSQ, &np1, EAGLE_ROLE_FC);
       if (e != hipSuccess) return hip_fail(e);
     }
@@ -517,6 +530,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.sumsq_in = ws.sumsq1;
       a.n_part_in = np1;
       a.eps = s.rms_eps;
+      if (handover) a.xb_in = ws.xb_d;
       if (rope_fused) {  // a4 in the epilogue: rotated q out, k and v into the rows' tree slots
         a.y = (float*)ws.qrot;
         a.ldy = hq;
@@ -602,6 +616,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.sumsq_out = ws.sumsq2;
       a.gain_out = w->norm2;
       a.y2 = ws.xg;
+      if (handover) a.xb_out = ws.xb_d;
       e = gemm(a, EPI_RESID_SUMSQ, &np2, EAGLE_ROLE_O);
       if (e != hipSuccess) return hip_fail(e);
     }
@@ -621,6 +636,10 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.yb = (float*)ws.act;
       a.ldyb = F;
       a.part = ws.gemm_part;
+      if (handover) {
+        a.xb_in = ws.xb_d;
+        a.xb_out = ws.xb_f;
+      }
       e = gemm(a, EPI_SWIGLU, nullptr, EAGLE_ROLE_GATE_UP);
       if (e != hipSuccess) return hip_fail(e);
     }
@@ -635,6 +654,10 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.y = out->feat;
       a.ldy = d;
       a.part = ws.gemm_part;
+      if (handover) {
+        a.xb_in = ws.xb_f;
+        if (!feat_only) a.xb_out = ws.xb_d;
+      }
       e = gemm(a, EPI_RESID, nullptr, EAGLE_ROLE_DOWN);
       if (e != hipSuccess) return hip_fail(e);
     }
@@ -650,6 +673,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     a.y = out->logits;
     a.ldy = s.vocab;
     a.part = ws.gemm_part;
+    if (handover && !head_only) a.xb_in = ws.xb_d;
     e = gemm(a, EPI_STORE, nullptr, EAGLE_ROLE_LM_HEAD);
     if (e != hipSuccess) return hip_fail(e);
   }

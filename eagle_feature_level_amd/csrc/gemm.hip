@@ -82,17 +82,17 @@ __device__ __forceinline__ float row_scale(const GemmArgs& a, int m) {
 // cooperating: 32 lanes per row, each summing every 32nd partial, then a fixed
 // butterfly across the 32 lanes.  No barrier: readers sync first.
 template <int NT>
-__device__ __forceinline__ void row_scales_lds(const GemmArgs& a, int BM, float* scale) {
+__device__ __forceinline__ void row_scales_lds(const GemmArgs& a, int BM, float* scale, int row0 = 0) {
   constexpr int ROWS = NT / 32;
   const int t = threadIdx.x, c = t & 31;
   for (int m0 = 0; m0 < BM; m0 += ROWS) {
-    const int m = m0 + t / 32;
+    const int m = m0 + t / 32, mg = row0 + m;
     float s = 0.f;
-    if (m < BM && m < a.M)
-      for (int p = c; p < a.n_part_in; p += 32) s += a.sumsq_in[(size_t)p * a.M + m];
+    if (m < BM && mg < a.M)
+      for (int p = c; p < a.n_part_in; p += 32) s += a.sumsq_in[(size_t)p * a.M + mg];
 #pragma unroll
     for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, WAVE);
-    if (c == 0 && m < BM) scale[m] = (m < a.M) ? rms_scale(s, a) : 1.f;
+    if (c == 0 && m < BM) scale[m] = (mg < a.M) ? rms_scale(s, a) : 1.f;
   }
 }
 
@@ -111,6 +111,16 @@ __device__ __forceinline__ uint32_t split2(float a, float b, uint32_t* lo) {
   const float ra = a - __uint_as_float(ua & 0xffff0000u), rb = b - __uint_as_float(ub & 0xffff0000u);
   *lo = __builtin_amdgcn_perm(__float_as_uint(rb) + 0x8000u, __float_as_uint(ra) + 0x8000u, 0x07060302u);
   return __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+}
+
+// Outputs n..n+3 of row m as the next GEMM's split operand: hi at
+// xb_out[m][n], lo at xb_out[M + m][n] (rows of `width` values).
+__device__ __forceinline__ void put_split4(const GemmArgs& a, int m, int n, int width, float4 v) {
+  uint32_t l0, l1;
+  const uint32_t h0 = split2(v.x, v.y, &l0), h1 = split2(v.z, v.w, &l1);
+  bf16_t* hi = (bf16_t*)a.xb_out + (size_t)m * width + n;
+  *(uint2*)hi = make_uint2(h0, h1);
+  *(uint2*)(hi + (size_t)a.M * width) = make_uint2(l0, l1);
 }
 
 __device__ __forceinline__ B8 split8(float4 v0, float4 v1) {
@@ -446,6 +456,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
   constexpr int XCH = (BM * 16 + NT - 1) / NT;  // 16-byte activation chunks per thread per k-step and half
   __shared__ __attribute__((aligned(16))) bf16_t Xs[2][NH][BM][WD_XLD];
   __shared__ float ssq_s[NW][BM];
+  __shared__ float rs_s[BM];  // RMSNorm row scales of an operand handed over unscaled (xb_in)
   const int nwg = gridDim.x, bid = blockIdx.x;
   const int lid = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;  // consecutive tiles on one XCD
   const int mt = lid % p.tiles_m, rest = lid / p.tiles_m;
@@ -453,6 +464,9 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
   const int m0 = mt * BM;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int r = lane & 15, g = lane >> 4;
+  // row scales for the epilogue of an unsplit launch (visible after the main loop's barriers)
+  const bool scale_rows = a.sumsq_in != nullptr && p.splits == 1;
+  if (scale_rows) row_scales_lds<NT>(a, BM, rs_s, m0);
   const int nks_all = a.K / SK_KSTEP;
   const int ks0 = sp * nks_all / p.splits;
   const int nks = (sp + 1) * nks_all / p.splits - ks0;
@@ -570,16 +584,18 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
     for (int mb = 0; mb < MB; ++mb) {
       const int m = m0 + mb * 16 + r;
       if (m >= a.M) continue;
+      const float rs = scale_rows ? rs_s[mb * 16 + r] : 1.f;
 #pragma unroll
       for (int at = 0; at < H; ++at) {
         const int j = wtile * 16 * H + at * 16 + 4 * g;
         if (j >= a.ffn) continue;
         float4 o;
-        o.x = silu_f(acc[at][mb][0]) * acc[at + H][mb][0];
-        o.y = silu_f(acc[at][mb][1]) * acc[at + H][mb][1];
-        o.z = silu_f(acc[at][mb][2]) * acc[at + H][mb][2];
-        o.w = silu_f(acc[at][mb][3]) * acc[at + H][mb][3];
+        o.x = silu_f(acc[at][mb][0] * rs) * (acc[at + H][mb][0] * rs);
+        o.y = silu_f(acc[at][mb][1] * rs) * (acc[at + H][mb][1] * rs);
+        o.z = silu_f(acc[at][mb][2] * rs) * (acc[at + H][mb][2] * rs);
+        o.w = silu_f(acc[at][mb][3] * rs) * (acc[at + H][mb][3] * rs);
         *(float4*)(a.yb + (size_t)m * a.ldyb + j) = o;
+        if (a.xb_out) put_split4(a, m, j, a.ffn, o);
       }
     }
   } else {
@@ -587,12 +603,13 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
     for (int mb = 0; mb < MB; ++mb) {
       const int ml = mb * 16 + r, m = m0 + ml;
       const bool mv = m < a.M;
+      const float rs = (scale_rows && mv) ? rs_s[ml] : 1.f;
       float ss = 0.f;
 #pragma unroll
       for (int at = 0; at < AT; ++at) {
         const int n = wtile * 16 * AT + at * 16 + 4 * g;
         if (!mv || n >= a.N) continue;
-        float4 y = make_float4(acc[at][mb][0], acc[at][mb][1], acc[at][mb][2], acc[at][mb][3]);
+        float4 y = make_float4(acc[at][mb][0] * rs, acc[at][mb][1] * rs, acc[at][mb][2] * rs, acc[at][mb][3] * rs);
         if constexpr (EPI == EPI_BIAS_SUMSQ) {
           const bf16_t* bb = (const bf16_t*)a.bias + n;
           y.x += bf2f(bb[0]); y.y += bf2f(bb[1]); y.z += bf2f(bb[2]); y.w += bf2f(bb[3]);
@@ -602,14 +619,16 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
           y.x += rr.x; y.y += rr.y; y.z += rr.z; y.w += rr.w;
         }
         *(float4*)(a.y + (size_t)m * a.ldy + n) = y;
+        float4 nx = y;  // the next GEMM's operand: y2 when written, else y
         if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
           if (a.y2) {
             const bf16_t* gn = (const bf16_t*)a.gain_out + n;
-            *(float4*)(a.y2 + (size_t)m * a.ldy + n) =
-                make_float4(y.x * bf2f(gn[0]), y.y * bf2f(gn[1]), y.z * bf2f(gn[2]), y.w * bf2f(gn[3]));
+            nx = make_float4(y.x * bf2f(gn[0]), y.y * bf2f(gn[1]), y.z * bf2f(gn[2]), y.w * bf2f(gn[3]));
+            *(float4*)(a.y2 + (size_t)m * a.ldy + n) = nx;
           }
           ss += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
         }
+        if (a.xb_out) put_split4(a, m, n, a.N, nx);
       }
       if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
         ss += __shfl_xor(ss, 16, WAVE);
@@ -673,12 +692,16 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
   constexpr int ROUNDS = AR + NH * XR;
   __shared__ __attribute__((aligned(16))) u32x4 L[2][SLOTS];
   __shared__ float ssq_s[T::WN][BM];
+  __shared__ float rs_s[BM];  // RMSNorm row scales of an operand handed over unscaled (xb_in)
   const int nwg = gridDim.x, bid = blockIdx.x;
   const int lid = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;  // consecutive tiles on one XCD
   const int mt = lid % p.tiles_m, rest = lid / p.tiles_m;
   const int nt = rest % p.tiles_n, sp = rest / p.tiles_n;
   const int m0 = mt * BM;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  // row scales for the epilogue of an unsplit launch (visible after the main loop's barriers)
+  const bool scale_rows = a.sumsq_in != nullptr && p.splits == 1;
+  if (scale_rows) row_scales_lds<NT>(a, BM, rs_s, m0);
   const int wn = wv % T::WN, wm = wv / T::WN;
   const int r = lane & 15, g = lane >> 4;
   const int kper = a.K / p.splits, kbeg = sp * kper, nkb = kper / BK;
@@ -790,18 +813,20 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
     constexpr int H = TN / 2;
 #pragma unroll
     for (int mb = 0; mb < TM; ++mb) {
-      const int m = m0 + (wm * TM + mb) * 16 + r;
+      const int ml = (wm * TM + mb) * 16 + r, m = m0 + ml;
       if (m >= a.M) continue;
+      const float rs = scale_rows ? rs_s[ml] : 1.f;
 #pragma unroll
       for (int nb = 0; nb < H; ++nb) {
         const int j = nt * (BN / 2) + wn * (TN * 8) + nb * 16 + 4 * g;
         if (j >= a.ffn) continue;
         float4 o;
-        o.x = silu_f(acc[nb][mb][0]) * acc[nb + H][mb][0];
-        o.y = silu_f(acc[nb][mb][1]) * acc[nb + H][mb][1];
-        o.z = silu_f(acc[nb][mb][2]) * acc[nb + H][mb][2];
-        o.w = silu_f(acc[nb][mb][3]) * acc[nb + H][mb][3];
+        o.x = silu_f(acc[nb][mb][0] * rs) * (acc[nb + H][mb][0] * rs);
+        o.y = silu_f(acc[nb][mb][1] * rs) * (acc[nb + H][mb][1] * rs);
+        o.z = silu_f(acc[nb][mb][2] * rs) * (acc[nb + H][mb][2] * rs);
+        o.w = silu_f(acc[nb][mb][3] * rs) * (acc[nb + H][mb][3] * rs);
         *(float4*)(a.yb + (size_t)m * a.ldyb + j) = o;
+        if (a.xb_out) put_split4(a, m, j, a.ffn, o);
       }
     }
   } else {
@@ -809,12 +834,13 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
     for (int mb = 0; mb < TM; ++mb) {
       const int ml = (wm * TM + mb) * 16 + r, m = m0 + ml;
       const bool mv = m < a.M;
+      const float rs = (scale_rows && mv) ? rs_s[ml] : 1.f;
       float ss = 0.f;
 #pragma unroll
       for (int nb = 0; nb < TN; ++nb) {
         const int n = nt * BN + (wn * TN + nb) * 16 + 4 * g;
         if (!mv || n >= a.N) continue;
-        float4 y = make_float4(acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]);
+        float4 y = make_float4(acc[nb][mb][0] * rs, acc[nb][mb][1] * rs, acc[nb][mb][2] * rs, acc[nb][mb][3] * rs);
         if constexpr (EPI == EPI_BIAS_SUMSQ) {
           const bf16_t* bb = (const bf16_t*)a.bias + n;
           y.x += bf2f(bb[0]); y.y += bf2f(bb[1]); y.z += bf2f(bb[2]); y.w += bf2f(bb[3]);
@@ -824,14 +850,16 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
           y.x += rr.x; y.y += rr.y; y.z += rr.z; y.w += rr.w;
         }
         *(float4*)(a.y + (size_t)m * a.ldy + n) = y;
+        float4 nx = y;  // the next GEMM's operand: y2 when written, else y
         if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
           if (a.y2) {
             const bf16_t* gn = (const bf16_t*)a.gain_out + n;
-            *(float4*)(a.y2 + (size_t)m * a.ldy + n) =
-                make_float4(y.x * bf2f(gn[0]), y.y * bf2f(gn[1]), y.z * bf2f(gn[2]), y.w * bf2f(gn[3]));
+            nx = make_float4(y.x * bf2f(gn[0]), y.y * bf2f(gn[1]), y.z * bf2f(gn[2]), y.w * bf2f(gn[3]));
+            *(float4*)(a.y2 + (size_t)m * a.ldy + n) = nx;
           }
           ss += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
         }
+        if (a.xb_out) put_split4(a, m, n, a.N, nx);
       }
       if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
         ss += __shfl_xor(ss, 16, WAVE);
@@ -929,6 +957,7 @@ __global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a) {
       u.x *= rs; u.y *= rs; u.z *= rs; u.w *= rs;
       const float4 o = {silu_f(s.x) * u.x, silu_f(s.y) * u.y, silu_f(s.z) * u.z, silu_f(s.w) * u.w};
       *(float4*)(a.yb + (size_t)m * a.ldyb + n) = o;
+      if (a.xb_out) put_split4(a, m, n, nout, o);
     } else {
       if constexpr (EPI == EPI_BIAS_SUMSQ) {
         const bf16_t* b = (const bf16_t*)a.bias + n;
@@ -939,13 +968,15 @@ __global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a) {
         s.x += rr.x; s.y += rr.y; s.z += rr.z; s.w += rr.w;
       }
       *(float4*)(a.y + (size_t)m * a.ldy + n) = s;
+      float4 nx = s;  // the next GEMM's operand: y2 when written, else y
       if (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
         if (a.y2) {
           const bf16_t* gn = (const bf16_t*)a.gain_out + n;
-          const float4 o = {s.x * bf2f(gn[0]), s.y * bf2f(gn[1]), s.z * bf2f(gn[2]), s.w * bf2f(gn[3])};
-          *(float4*)(a.y2 + (size_t)m * a.ldy + n) = o;
+          nx = {s.x * bf2f(gn[0]), s.y * bf2f(gn[1]), s.z * bf2f(gn[2]), s.w * bf2f(gn[3])};
+          *(float4*)(a.y2 + (size_t)m * a.ldy + n) = nx;
         }
       }
+      if (a.xb_out) put_split4(a, m, n, a.N, nx);
       ss = s.x * s.x + s.y * s.y + s.z * s.z + s.w * s.w;
     }
   }
@@ -1211,12 +1242,20 @@ template <bool SPLIT>
 hipError_t prepared_launch(GemmArgs a, int epi, int* n_part_out, hipStream_t s) {
   const bool sw = (epi == EPI_SWIGLU);
   if (a.part == nullptr) return hipErrorInvalidValue;  // scratch: bf16 operand (+ partials)
-  bf16_t* xb = (bf16_t*)a.part;
-  a.part = (float*)((char*)a.part + align_up256((size_t)a.M * a.K * 2 * (SPLIT ? 2 : 1)));
-  hipLaunchKernelGGL(act_prep<SPLIT>, dim3((a.K + 2047) / 2048, a.M), dim3(256), 0, s, a, xb);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  a.sumsq_in = nullptr;  // the row scale is in the prepared operand
+  if (!SPLIT && (a.xb_in || a.xb_out)) return hipErrorInvalidValue;  // hand-over is for split operands
+  hipError_t e = hipSuccess;
+  const bf16_t* xb;
+  if (a.xb_in) {  // written by the previous GEMM's epilogue, unscaled: the row scale goes in this epilogue
+    xb = (const bf16_t*)a.xb_in;
+  } else {
+    bf16_t* prep = (bf16_t*)a.part;
+    a.part = (float*)((char*)a.part + align_up256((size_t)a.M * a.K * 2 * (SPLIT ? 2 : 1)));
+    hipLaunchKernelGGL(act_prep<SPLIT>, dim3((a.K + 2047) / 2048, a.M), dim3(256), 0, s, a, prep);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.sumsq_in = nullptr;  // the row scale is in the prepared operand
+    xb = prep;
+  }
   int splits, tiles_n;
   if (a.M >= BIG16_MIN_M) {
     const BigPlan p = plan_tile<LargeTile>(a.M, a.N, a.K, sw);
@@ -1265,6 +1304,7 @@ hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s)
   if (a.K % SK_KSTEP) return hipErrorInvalidValue;  // every kernel steps K in whole 128-element blocks
   if (a.gfeat && (a.gd % SK_KSTEP || a.K != 2 * a.gd)) return hipErrorInvalidValue;
   if ((epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) && a.y2 && !a.gain_out) return hipErrorInvalidValue;
+  if (a.M <= 16 && (a.xb_in || a.xb_out)) return hipErrorInvalidValue;  // operand hand-over: tiled kernels only
   if (a.M <= 16) return a.act_bf16 ? skinny_launch<true>(a, epi, n_part_out, s) : skinny_launch<false>(a, epi, n_part_out, s);
   if (epi == EPI_ROPE) return hipErrorInvalidValue;  // the fused rotary epilogue is the skinny kernel's
   if (a.N % 4 || (epi == EPI_SWIGLU && a.ffn % 4)) return hipErrorInvalidValue;  // float4 epilogue stores
@@ -1272,6 +1312,7 @@ hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s)
 }
 
 hipError_t launch_gemm_f32(GemmArgs a, int epi, int* n_part_out, hipStream_t s) {
+  if (a.xb_in || a.xb_out) return hipErrorInvalidValue;
   if ((epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) && a.y2 && !a.gain_out) return hipErrorInvalidValue;
   const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
   dim3 grid((nout + 63) / 64, a.M), blk(64);
