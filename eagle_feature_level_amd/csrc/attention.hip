@@ -344,14 +344,22 @@ __global__ void __launch_bounds__(128) attn_combine_kernel(AttnArgs a, int hd) {
 #pragma unroll
       for (int s = 0; s < CMB_PRE; ++s)
         if (s < a.n_splits) acc += wsplit[s] * v[s];
-      a.out[((size_t)row * a.hq + h) * hd + t] = acc * s_inv;
+      const size_t o = ((size_t)row * a.hq + h) * hd + t;
+      if (a.outb)
+        put_split1((bf16_t*)a.outb + o, (size_t)a.n_rows * a.hq * hd, acc * s_inv);
+      else
+        a.out[o] = acc * s_inv;
     }
     return;
   }
   for (int dd = t; dd < hd; dd += 128) {
     float acc = 0.f;
     for (int s = 0; s < a.n_splits; ++s) acc += wsplit[s] * base[s * stride + 2 + dd];
-    a.out[((size_t)row * a.hq + h) * hd + dd] = acc * s_inv;
+    const size_t o = ((size_t)row * a.hq + h) * hd + dd;
+    if (a.outb)
+      put_split1((bf16_t*)a.outb + o, (size_t)a.n_rows * a.hq * hd, acc * s_inv);
+    else
+      a.out[o] = acc * s_inv;
   }
 }
 
@@ -690,9 +698,15 @@ __global__ void __launch_bounds__(256, KSPLIT ? 3 : 2) attn_mfma_kernel(AttnArgs
     const int qrow = r0 + qq / G, qh_ = g * G + qq % G;
     if (a.n_splits == 1) {
       const float inv = (Ls > 0.f) ? 1.f / Ls : 0.f;
-      float* dst = a.out + ((size_t)qrow * a.hq + qh_) * 128 + d0;
-      *(float4*)dst = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-      *(float4*)(dst + 4) = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+      const size_t off = ((size_t)qrow * a.hq + qh_) * 128 + d0;
+      const float4 v0 = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+      const float4 v1 = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+      if (a.outb) {
+        put_split8((bf16_t*)a.outb + off, (size_t)a.n_rows * a.hq * 128, v0, v1);
+      } else {
+        *(float4*)(a.out + off) = v0;
+        *(float4*)(a.out + off + 4) = v1;
+      }
     } else {
       float* dst = a.part + (size_t)s * a.n_rows * a.hq * (128 + 2) + ((size_t)qrow * a.hq + qh_) * (128 + 2);
 #pragma unroll
@@ -709,11 +723,15 @@ __global__ void __launch_bounds__(256, KSPLIT ? 3 : 2) attn_mfma_kernel(AttnArgs
   if (a.n_splits == 1) {
     if (!qv) return;
     const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-    float* dst = a.out + ((size_t)row * a.hq + h) * 128;
+    const size_t off = ((size_t)row * a.hq + h) * 128;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      *(float4*)(dst + db * 16 + gq * 4) =
-          make_float4(oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv);
+    for (int db = 0; db < 8; ++db) {
+      const float4 v = make_float4(oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv);
+      if (a.outb)
+        put_split4((bf16_t*)a.outb + off + db * 16 + gq * 4, (size_t)a.n_rows * a.hq * 128, v);
+      else
+        *(float4*)(a.out + off + db * 16 + gq * 4) = v;
+    }
     return;
   }
   const size_t sstride = (size_t)a.n_rows * a.hq * (128 + 2);  // between splits
@@ -792,6 +810,7 @@ AttnPlan attn_plan(bool bf16, int max_prefix, int batch, int hkv, int max_querie
 
 hipError_t launch_attention(const AttnArgs& a, bool bf16, int hd, int max_queries, hipStream_t s) {
   if (a.n_splits > 1024 || a.n_splits < 1) return hipErrorInvalidValue;  // combine keeps a weight per split in LDS
+  if (a.outb && !bf16) return hipErrorInvalidValue;
   if (bf16) {
     if (hd != 128) return hipErrorInvalidValue;
     const int qblocks = (max_queries + AQ - 1) / AQ;

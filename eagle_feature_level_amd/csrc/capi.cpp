@@ -110,7 +110,8 @@ struct DraftWs {
   float* gemm_part;
   void* topk;
   // split bf16 operands (hi rows, then lo rows) handed from one GEMM's epilogue
-  // to the next GEMM (bf16 weights, more than 16 rows): d wide, ffn wide
+  // (or attention) to the next GEMM (bf16 weights, more than 16 rows): d wide,
+  // max(ffn, hq) wide
   uint16_t* xb_d;
   uint16_t* xb_f;
   size_t total;
@@ -162,7 +163,7 @@ DraftWs carve(const eagle_shape* s, int M, int B, int max_prefix, char* base) {
   w.topk = take(topk_workspace_bytes(M, s->vocab));
   if (s->dtype == EAGLE_BF16 && M > 16) {
     w.xb_d = (uint16_t*)take((size_t)M * s->d * 4);
-    w.xb_f = (uint16_t*)take((size_t)M * s->ffn * 4);
+    w.xb_f = (uint16_t*)take((size_t)M * (s->ffn > hq ? s->ffn : hq) * 4);
   }
   w.total = off;
   return w;
@@ -451,7 +452,9 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
     const double out_bytes = (epi == EPI_ROPE) ? 4.0 * a.M * a.rp_hq * a.rp_hd + 2.0 * wbytes * a.M * a.rp_hkv * a.rp_hd
                                                : 4.0 * a.M * nout;
-    const double bytes = wbytes * a.N * a.K + 4.0 * a.M * a.K + out_bytes + (a.y2 ? 4.0 * a.M * a.N : 0.0);
+    // (the normalised copy of a SUMSQ epilogue counts once, whether written as y2 or handed over)
+    const bool normed = a.y2 || (a.gain_out && a.xb_out);
+    const double bytes = wbytes * a.N * a.K + 4.0 * a.M * a.K + out_bytes + (normed ? 4.0 * a.M * a.N : 0.0);
     const double flops = 2.0 * a.M * a.N * a.K;
     return timed(
         st, role, bytes, flops,
@@ -467,9 +470,11 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
   // M = 8 (one 16-row weight tile per workgroup); above, the four-tile QKV variant
   // plus the RoPE launch is faster (measured on the 7B shapes)
   const bool rope_fused = bf16 && M <= 8 && s.head_dim % 16 == 0;
-  // above 16 rows with split bf16 operands, each GEMM whose input is the previous
-  // GEMM's output takes that operand from the producer's epilogue, unscaled, and
-  // applies the RMSNorm row scale in its own epilogue (no operand prep pass)
+  // above 16 rows with split bf16 operands, each GEMM takes its operand from
+  // the producer's epilogue (the previous GEMM's, or attention's), unscaled, and
+  // applies the RMSNorm row scale in its own epilogue: no operand prep pass, and
+  // the fp32 copies only a GEMM would read (x * g, attention out, SwiGLU out)
+  // are not written
   const bool handover = bf16 && M > 16 && !act16;
 
   if (!head_only) {
@@ -510,7 +515,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.ldy = d;
       a.sumsq_out = ws.sumsq1;
       a.gain_out = w->norm1;
-      a.y2 = ws.xg;
+      a.y2 = handover ? nullptr : ws.xg;
       if (handover) a.xb_out = ws.xb_d;
       e = gemm(a, EPI_BIAS_SUMSQ, &np1, EAGLE_ROLE_FC);
       if (e != hipSuccess) return hip_fail(e);
@@ -574,7 +579,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     }
     // a5: tree attention
     {
-      AttnArgs at;
+      AttnArgs at{};
       at.q = (const float*)ws.qrot;
       at.mask = rows->mask;
       at.row_start = rows->row_start;
@@ -587,6 +592,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       at.tree_v = kv->tree_v;
       at.part = ws.attn_part;
       at.out = (float*)ws.attn;
+      at.outb = handover ? ws.xb_f : nullptr;
       at.n_rows = M;
       at.batch = rows->batch;
       at.hq = s.n_heads;
@@ -615,8 +621,11 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.ldy = d;
       a.sumsq_out = ws.sumsq2;
       a.gain_out = w->norm2;
-      a.y2 = ws.xg;
-      if (handover) a.xb_out = ws.xb_d;
+      a.y2 = handover ? nullptr : ws.xg;
+      if (handover) {
+        a.xb_in = ws.xb_f;
+        a.xb_out = ws.xb_d;
+      }
       e = gemm(a, EPI_RESID_SUMSQ, &np2, EAGLE_ROLE_O);
       if (e != hipSuccess) return hip_fail(e);
     }
@@ -633,7 +642,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.sumsq_in = ws.sumsq2;
       a.n_part_in = np2;
       a.eps = s.rms_eps;
-      a.yb = (float*)ws.act;
+      a.yb = handover ? nullptr : (float*)ws.act;
       a.ldyb = F;
       a.part = ws.gemm_part;
       if (handover) {

@@ -26,6 +26,42 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
 }
 
+// Two fp32 values as packed bf16 pairs (value a in the low half): hi = x with
+// its low 16 bits dropped (so x - hi is exact in fp32), lo = x - hi rounded to
+// bf16, ties away from zero.  |x - hi - lo| <= 2^-15 |x|.  Byte permutes and
+// three integer/float ops per value: this runs once per operand element per
+// wave, so it must stay cheap next to the weight stream.
+__device__ __forceinline__ uint32_t split2(float a, float b, uint32_t* lo) {
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  const float ra = a - __uint_as_float(ua & 0xffff0000u), rb = b - __uint_as_float(ub & 0xffff0000u);
+  *lo = __builtin_amdgcn_perm(__float_as_uint(rb) + 0x8000u, __float_as_uint(ra) + 0x8000u, 0x07060302u);
+  return __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+}
+
+// Consecutive values of one row as the split operand of the next GEMM: hi at
+// hi[0..], lo at hi[lo_off + 0..] (aligned to the store width).
+__device__ __forceinline__ void put_split4(bf16_t* hi, size_t lo_off, float4 v) {
+  uint32_t l0, l1;
+  const uint32_t h0 = split2(v.x, v.y, &l0), h1 = split2(v.z, v.w, &l1);
+  *(uint2*)hi = make_uint2(h0, h1);
+  *(uint2*)(hi + lo_off) = make_uint2(l0, l1);
+}
+__device__ __forceinline__ void put_split8(bf16_t* hi, size_t lo_off, float4 v0, float4 v1) {
+  u32x4 h, l;
+  uint32_t t;
+  h[0] = split2(v0.x, v0.y, &t); l[0] = t;
+  h[1] = split2(v0.z, v0.w, &t); l[1] = t;
+  h[2] = split2(v1.x, v1.y, &t); l[2] = t;
+  h[3] = split2(v1.z, v1.w, &t); l[3] = t;
+  *(u32x4*)hi = h;
+  *(u32x4*)(hi + lo_off) = l;
+}
+__device__ __forceinline__ void put_split1(bf16_t* hi, size_t lo_off, float v) {
+  const uint32_t u = __float_as_uint(v);
+  hi[0] = (bf16_t)(u >> 16);
+  hi[lo_off] = (bf16_t)((__float_as_uint(v - __uint_as_float(u & 0xffff0000u)) + 0x8000u) >> 16);
+}
+
 // Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
 // as 1, 2, 3", SC'11): counter (c0, c1, c2, c3), key (k0, k1), 10 rounds; a
 // round maps (x0, x1, x2, x3) to (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3

@@ -54,11 +54,12 @@ struct GemmArgs {
   float* part;
   int splits;
   // M > 16, split operands (act_bf16 == 0) only.  xb_out: the epilogue also
-  // writes the next GEMM's operand from this GEMM's output -- y2 when it is
-  // written, else y (yb for SwiGLU) -- as hi / lo bf16 halves, hi [M][Nout] at
-  // xb_out and lo at xb_out + M*Nout.  xb_in: this GEMM's operand so written by
-  // the previous one (the prep pass is skipped); with sumsq_in set, the RMSNorm
-  // row scale is then applied in the epilogue.
+  // writes the next GEMM's operand from this GEMM's output -- y * gain_out when
+  // gain_out is set (y2 may then be null), else y (the SwiGLU output, yb may
+  // then be null) -- as hi / lo bf16 halves, hi [M][Nout] at xb_out and lo at
+  // xb_out + M*Nout.  xb_in: this GEMM's operand so written by the previous
+  // one or by attention (the prep pass is skipped); with sumsq_in set, the
+  // RMSNorm row scale is then applied in the epilogue.
   uint16_t* xb_out;
   const uint16_t* xb_in;
   // activation precision: 0 = each fp32 activation enters the matrix units as

@@ -101,26 +101,10 @@ struct B8 {
   u32x4 hi, lo;
 };
 
-// Two fp32 values as packed bf16 pairs (value a in the low half): hi = x with
-// its low 16 bits dropped (so x - hi is exact in fp32), lo = x - hi rounded to
-// bf16, ties away from zero.  |x - hi - lo| <= 2^-15 |x|.  Byte permutes and
-// three integer/float ops per value: this runs once per operand element per
-// wave, so it must stay cheap next to the weight stream.
-__device__ __forceinline__ uint32_t split2(float a, float b, uint32_t* lo) {
-  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
-  const float ra = a - __uint_as_float(ua & 0xffff0000u), rb = b - __uint_as_float(ub & 0xffff0000u);
-  *lo = __builtin_amdgcn_perm(__float_as_uint(rb) + 0x8000u, __float_as_uint(ra) + 0x8000u, 0x07060302u);
-  return __builtin_amdgcn_perm(ub, ua, 0x07060302u);
-}
-
 // Outputs n..n+3 of row m as the next GEMM's split operand: hi at
 // xb_out[m][n], lo at xb_out[M + m][n] (rows of `width` values).
 __device__ __forceinline__ void put_split4(const GemmArgs& a, int m, int n, int width, float4 v) {
-  uint32_t l0, l1;
-  const uint32_t h0 = split2(v.x, v.y, &l0), h1 = split2(v.z, v.w, &l1);
-  bf16_t* hi = (bf16_t*)a.xb_out + (size_t)m * width + n;
-  *(uint2*)hi = make_uint2(h0, h1);
-  *(uint2*)(hi + (size_t)a.M * width) = make_uint2(l0, l1);
+  put_split4((bf16_t*)a.xb_out + (size_t)m * width + n, (size_t)a.M * width, v);
 }
 
 __device__ __forceinline__ B8 split8(float4 v0, float4 v1) {
@@ -594,7 +578,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
         o.y = silu_f(acc[at][mb][1] * rs) * (acc[at + H][mb][1] * rs);
         o.z = silu_f(acc[at][mb][2] * rs) * (acc[at + H][mb][2] * rs);
         o.w = silu_f(acc[at][mb][3] * rs) * (acc[at + H][mb][3] * rs);
-        *(float4*)(a.yb + (size_t)m * a.ldyb + j) = o;
+        if (a.yb) *(float4*)(a.yb + (size_t)m * a.ldyb + j) = o;
         if (a.xb_out) put_split4(a, m, j, a.ffn, o);
       }
     }
@@ -621,10 +605,10 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
         *(float4*)(a.y + (size_t)m * a.ldy + n) = y;
         float4 nx = y;  // the next GEMM's operand: y2 when written, else y
         if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
-          if (a.y2) {
+          if (a.gain_out) {
             const bf16_t* gn = (const bf16_t*)a.gain_out + n;
             nx = make_float4(y.x * bf2f(gn[0]), y.y * bf2f(gn[1]), y.z * bf2f(gn[2]), y.w * bf2f(gn[3]));
-            *(float4*)(a.y2 + (size_t)m * a.ldy + n) = nx;
+            if (a.y2) *(float4*)(a.y2 + (size_t)m * a.ldy + n) = nx;
           }
           ss += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
         }
@@ -825,7 +809,7 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
         o.y = silu_f(acc[nb][mb][1] * rs) * (acc[nb + H][mb][1] * rs);
         o.z = silu_f(acc[nb][mb][2] * rs) * (acc[nb + H][mb][2] * rs);
         o.w = silu_f(acc[nb][mb][3] * rs) * (acc[nb + H][mb][3] * rs);
-        *(float4*)(a.yb + (size_t)m * a.ldyb + j) = o;
+        if (a.yb) *(float4*)(a.yb + (size_t)m * a.ldyb + j) = o;
         if (a.xb_out) put_split4(a, m, j, a.ffn, o);
       }
     }
@@ -852,10 +836,10 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
         *(float4*)(a.y + (size_t)m * a.ldy + n) = y;
         float4 nx = y;  // the next GEMM's operand: y2 when written, else y
         if constexpr (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
-          if (a.y2) {
+          if (a.gain_out) {
             const bf16_t* gn = (const bf16_t*)a.gain_out + n;
             nx = make_float4(y.x * bf2f(gn[0]), y.y * bf2f(gn[1]), y.z * bf2f(gn[2]), y.w * bf2f(gn[3]));
-            *(float4*)(a.y2 + (size_t)m * a.ldy + n) = nx;
+            if (a.y2) *(float4*)(a.y2 + (size_t)m * a.ldy + n) = nx;
           }
           ss += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
         }
@@ -956,7 +940,7 @@ __global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a) {
       }
       u.x *= rs; u.y *= rs; u.z *= rs; u.w *= rs;
       const float4 o = {silu_f(s.x) * u.x, silu_f(s.y) * u.y, silu_f(s.z) * u.z, silu_f(s.w) * u.w};
-      *(float4*)(a.yb + (size_t)m * a.ldyb + n) = o;
+      if (a.yb) *(float4*)(a.yb + (size_t)m * a.ldyb + n) = o;
       if (a.xb_out) put_split4(a, m, n, nout, o);
     } else {
       if constexpr (EPI == EPI_BIAS_SUMSQ) {
@@ -970,10 +954,10 @@ __global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a) {
       *(float4*)(a.y + (size_t)m * a.ldy + n) = s;
       float4 nx = s;  // the next GEMM's operand: y2 when written, else y
       if (EPI == EPI_BIAS_SUMSQ || EPI == EPI_RESID_SUMSQ) {
-        if (a.y2) {
+        if (a.gain_out) {
           const bf16_t* gn = (const bf16_t*)a.gain_out + n;
           nx = {s.x * bf2f(gn[0]), s.y * bf2f(gn[1]), s.z * bf2f(gn[2]), s.w * bf2f(gn[3])};
-          *(float4*)(a.y2 + (size_t)m * a.ldy + n) = nx;
+          if (a.y2) *(float4*)(a.y2 + (size_t)m * a.ldy + n) = nx;
         }
       }
       if (a.xb_out) put_split4(a, m, n, a.N, nx);
@@ -1305,6 +1289,7 @@ hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s)
   if (a.gfeat && (a.gd % SK_KSTEP || a.K != 2 * a.gd)) return hipErrorInvalidValue;
   if ((epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) && a.y2 && !a.gain_out) return hipErrorInvalidValue;
   if (a.M <= 16 && (a.xb_in || a.xb_out)) return hipErrorInvalidValue;  // operand hand-over: tiled kernels only
+  if (epi == EPI_SWIGLU && !a.yb && !a.xb_out) return hipErrorInvalidValue;
   if (a.M <= 16) return a.act_bf16 ? skinny_launch<true>(a, epi, n_part_out, s) : skinny_launch<false>(a, epi, n_part_out, s);
   if (epi == EPI_ROPE) return hipErrorInvalidValue;  // the fused rotary epilogue is the skinny kernel's
   if (a.N % 4 || (epi == EPI_SWIGLU && a.ffn % 4)) return hipErrorInvalidValue;  // float4 epilogue stores

@@ -29,6 +29,9 @@ struct AttnArgs {
   const void* tree_v;
   float* part;  // [n_splits, n_rows, hq, hd + 2]
   float* out;   // [n_rows, hq hd]
+  // or, when set (bf16 K/V), the output as the split bf16 operand of the next
+  // GEMM instead of out: hi [n_rows, hq hd], then lo [n_rows, hq hd]
+  uint16_t* outb;
   int n_rows, batch, hq, hkv, split_len, n_splits;
 };
 
