@@ -48,6 +48,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+BLOCKED = True  # the engines keep blocked weight copies (--row-major-weights: not)
+
+
 def build_engine(cid: int, copies: int = 1, extra: int = 0):
     """Seeded inputs of workload `cid` and `copies` engines over separate
     copies of the weights and prefix cache (the same values), each with the
@@ -72,7 +75,8 @@ def build_engine(cid: int, copies: int = 1, extra: int = 0):
     engines = []
     for _ in range(copies):
         eng = EagleRound(dev.shape_dict(s), dev.weights(w, s.dtype), cfg.batch, kind, cfg.topk, cfg.depth,
-                         cfg.rerank_m, TEMPLATES.get(cfg.tree), dev.prefix(ks, vs, lens, s.dtype, extra=extra))
+                         cfg.rerank_m, TEMPLATES.get(cfg.tree), dev.prefix(ks, vs, lens, s.dtype, extra=extra),
+                         blocked=BLOCKED)
         eng.root_features().copy_(torch.from_numpy(feat).cuda())
         engines.append(eng)
     host = dict(w=w, lens=lens, ks=ks, vs=vs, feat=feat, tok=tok)
@@ -382,6 +386,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = 7B static-26, the bench line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--row-major-weights", action="store_true",
+                    help="GEMMs read the row-major weight matrices only (no blocked copies)")
     ap.add_argument("--no-rotate", action="store_true",
                     help="one weight copy (default: rounds alternate between two copies of the weights, so that no "
                          "round finds the previous round's weights in the 256 MB Infinity Cache)")
@@ -394,6 +400,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
+    global BLOCKED
+    BLOCKED = not args.row_major_weights
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path here is single-GPU.",
               file=sys.stderr)

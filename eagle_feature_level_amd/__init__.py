@@ -17,7 +17,7 @@ from ._abi import (EAGLE_ACT_BF16, EAGLE_BF16, EAGLE_COMMIT_BAD_PATH, EAGLE_COMM
                    EAGLE_VERIFY_IID, EAGLE_VERIFY_NOALLOC_MAX_NODES, EagleError, eagle_draft_out, eagle_kv, eagle_pool, eagle_rows, eagle_shape,
                    eagle_weights)
 
-__all__ = ["eagle_workspace_bytes", "eagle_draft_step", "eagle_softmax_topk", "eagle_tree_init", "eagle_tree_expand",
+__all__ = ["eagle_blocked_weight_bytes", "eagle_block_weight", "eagle_workspace_bytes", "eagle_draft_step", "eagle_softmax_topk", "eagle_tree_init", "eagle_tree_expand",
            "eagle_tree_finalize", "eagle_verify", "eagle_verify_workspace_bytes", "make_shape", "make_weights",
            "make_rows", "make_kv", "make_out",
            "make_pool", "EagleError", "EAGLE_HEAD_ONLY", "EAGLE_ACT_BF16", "EAGLE_SAMPLE_CHILDREN",
@@ -60,7 +60,17 @@ def make_shape(d, n_heads, n_kv_heads, head_dim, ffn, vocab, rms_eps=1e-5, rope_
 
 
 def make_weights(tensors: dict):
-    return _keep(eagle_weights(*[_ptr(tensors[n]) for n in WEIGHT_NAMES]), *[tensors[n] for n in WEIGHT_NAMES])
+    """Weight tensors by name; the blocked copies (names ending in _b) are optional."""
+    return _keep(eagle_weights(*[_ptr(tensors.get(n)) for n in WEIGHT_NAMES]), *[tensors.get(n) for n in WEIGHT_NAMES])
+
+
+def eagle_blocked_weight_bytes(rows, cols) -> int:
+    return int(_abi.load().eagle_blocked_weight_bytes(rows, cols))
+
+
+def eagle_block_weight(w, rows, cols, out, stream=None):
+    lib = _abi.load()
+    _abi.check("eagle_block_weight", lib.eagle_block_weight(_ptr(w), rows, cols, _ptr(out), _stream(stream)))
 
 
 def make_rows(n_rows, batch, max_rows_per_seq, row_start, token, parent, pos=None, slot=None, mask=None):

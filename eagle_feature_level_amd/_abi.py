@@ -32,7 +32,8 @@ class eagle_shape(ctypes.Structure):
 
 class eagle_weights(ctypes.Structure):
     _fields_ = [(n, c_vp) for n in ("embed", "fc_w", "fc_b", "norm1", "norm2", "wq", "wk", "wv", "wo", "w_gate",
-                                    "w_up", "w_down", "lm_head")]
+                                    "w_up", "w_down", "lm_head", "fc_w_b", "wq_b", "wk_b", "wv_b", "wo_b",
+                                    "w_gate_b", "w_up_b", "w_down_b", "lm_head_b")]
 
 
 class eagle_rows(ctypes.Structure):
@@ -82,6 +83,8 @@ _SIGS = {
     "eagle_verify_workspace_bytes": (ctypes.c_size_t, [c_i32, c_i32]),
     "eagle_verify_noalloc": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_u64, c_u64, c_i32, c_vp,
                                      c_vp, c_vp, c_vp, c_vp]),
+    "eagle_blocked_weight_bytes": (ctypes.c_size_t, [c_i32, c_i32]),
+    "eagle_block_weight": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp]),
     "eagle_profile_enable": (c_i32, [c_i32]),
     "eagle_profile_reset": (c_i32, []),
     "eagle_profile_disable": (c_i32, []),

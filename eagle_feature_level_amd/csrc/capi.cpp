@@ -197,6 +197,20 @@ const char* eagle_strerror(int code) {
 
 int eagle_last_hip_error(void) { return g_last_hip; }
 
+size_t eagle_blocked_weight_bytes(int32_t rows, int32_t cols) {
+  if (rows <= 0 || cols <= 0 || cols % 128) return 0;
+  return blocked_weight_bytes(rows, cols);
+}
+
+int eagle_block_weight(const void* w, int32_t rows, int32_t cols, void* out, eagle_stream_t stream) {
+  if (!w || !out || rows <= 0 || cols <= 0 || cols % 128 || ((uintptr_t)w & 15) || ((uintptr_t)out & 15))
+    return EAGLE_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = launch_block_weight(w, rows, cols, out, (hipStream_t)stream);
+  return e == hipSuccess ? EAGLE_OK : hip_fail(e);
+}
+
 size_t eagle_workspace_bytes(const eagle_shape* shape, int32_t max_rows, int32_t max_batch, int32_t max_prefix_len) {
   if (!shape_ok(shape) || max_rows <= 0 || max_batch <= 0 || max_prefix_len < 0) return 0;
   return carve(shape, max_rows, max_batch, max_prefix_len, nullptr).total;
@@ -500,6 +514,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     {
       GemmArgs a = gemm_base(M, d, 2 * d);
       a.w0 = w->fc_w;
+      if (bf16) a.wb0 = w->fc_w_b;
       if (gather) {
         a.gfeat = feat_in;
         a.gparent = rows->parent;
@@ -530,6 +545,11 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.w1 = w->wk;
       a.n_seg1 = hkv;
       a.w2 = w->wv;
+      if (bf16 && w->wq_b && w->wk_b && w->wv_b) {
+        a.wb0 = w->wq_b;
+        a.wb1 = w->wk_b;
+        a.wb2 = w->wv_b;
+      }
       a.x = ws.xg;
       a.ldx = d;
       a.sumsq_in = ws.sumsq1;
@@ -613,6 +633,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     {
       GemmArgs a = gemm_base(M, d, hq);
       a.w0 = w->wo;
+      if (bf16) a.wb0 = w->wo_b;
       a.x = (const float*)ws.attn;
       a.ldx = hq;
       a.resid = ws.x;
@@ -636,6 +657,10 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
       a.n_seg0 = F;
       a.w1 = w->w_up;
       a.n_seg1 = F;
+      if (bf16 && w->w_gate_b && w->w_up_b) {
+        a.wb0 = w->w_gate_b;
+        a.wb1 = w->w_up_b;
+      }
       a.ffn = F;
       a.x = ws.xg;
       a.ldx = d;
@@ -656,6 +681,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
     {
       GemmArgs a = gemm_base(M, d, F);
       a.w0 = w->w_down;
+      if (bf16) a.wb0 = w->w_down_b;
       a.x = (const float*)ws.act;
       a.ldx = F;
       a.resid = ws.h;
@@ -676,6 +702,7 @@ int eagle_draft_step(const eagle_shape* shape, const eagle_weights* w, int32_t f
   {
     GemmArgs a = gemm_base(M, s.vocab, d);
     a.w0 = w->lm_head;
+    if (bf16) a.wb0 = w->lm_head_b;
     a.x = head_only ? feat_in : out->feat;
     a.xrows = head_only ? rows->parent : nullptr;
     a.ldx = d;

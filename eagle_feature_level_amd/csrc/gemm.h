@@ -22,6 +22,12 @@ struct GemmArgs {
   const void* w1;
   const void* w2;
   int n_seg0, n_seg1;
+  // optional (bf16, M <= 256): the same segments in the blocked layout of
+  // launch_block_weight, read instead of w0..w2 by the skinny and wide kernels
+  // (all of the GEMM's segments, or none)
+  const void* wb0;
+  const void* wb1;
+  const void* wb2;
   int N, K, M;
   // activations: x fp32 [M, K] (ldx), row m read from row xrows[m] if xrows is set
   const float* x;
@@ -91,3 +97,11 @@ hipError_t launch_gemm_bf16(GemmArgs a, int epi, int* n_part_out, hipStream_t s)
 void gemm_set_kernel_events(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_gemm_f32(GemmArgs a, int epi, int* n_part_out, hipStream_t s);
 size_t gemm_bf16_partial_bytes(int M, int N, int K);
+// Blocked copy of a bf16 matrix W [rows, cols] (cols a multiple of 128): 16-row
+// by 128-column blocks of 4 KB, the blocks of a 16-row band in column order,
+// inside a block the four 32-column quarters one after the other, each 16 rows
+// of 32 values:
+// out[(t * (cols / 128) + s) * 2048 + ((c / 32) * 16 + r) * 32 + c % 32] = W[16 t + r][128 s + c],
+// rows past the end 0.  out holds blocked_weight_bytes(rows, cols) bytes.
+size_t blocked_weight_bytes(int rows, int cols);
+hipError_t launch_block_weight(const void* w, int rows, int cols, void* out, hipStream_t s);

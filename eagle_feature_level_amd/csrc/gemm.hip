@@ -67,6 +67,25 @@ __device__ __forceinline__ const T* wrow(const GemmArgs& a, int n) {
   return (const T*)a.w2 + (size_t)n * a.K;
 }
 
+// Logical row n in the blocked copies wb0..wb2: the start of its first 32
+// columns in the first block of its 16-row band.  Columns 32 g.. of the row
+// are 512 g further, the next k-step's slice one block (2048 values) further;
+// lane (r, g) of a 16-row tile thus reads the 64 bytes at 64 (16 g + r) of the
+// block, adjacent lanes adjacent bytes.
+__device__ __forceinline__ const bf16_t* wrow_blocked(const GemmArgs& a, int n) {
+  const void* base;
+  if (n < a.n_seg0) {
+    base = a.wb0;
+  } else if (n - a.n_seg0 < a.n_seg1) {
+    base = a.wb1;
+    n -= a.n_seg0;
+  } else {
+    base = a.wb2;
+    n -= a.n_seg0 + a.n_seg1;
+  }
+  return (const bf16_t*)base + (size_t)(n >> 4) * (a.K / 128) * 2048 + (n & 15) * 32;
+}
+
 __device__ __forceinline__ float rms_scale(float sumsq, const GemmArgs& a) {
   return 1.0f / sqrtf(sumsq / (float)a.K + a.eps);
 }
@@ -195,12 +214,15 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
   const int r = lane & 15, g = lane >> 4;
   const int tile = blockIdx.x;
 
+  // weights row-major (a k-step further: 128 values) or blocked (one 4 KB block)
+  const bool blocked = a.wb0 != nullptr;
+  const size_t kstride = blocked ? 2048 : SK_KSTEP;
   const bf16_t* ap[AT];
 #pragma unroll
   for (int at = 0; at < AT; ++at) {
     bool ok;
     const int n = tile_row<AT, EPI>(a, tile, at, r, &ok);
-    ap[at] = wrow<bf16_t>(a, n) + g * 32;
+    ap[at] = blocked ? wrow_blocked(a, n) + g * 512 : wrow<bf16_t>(a, n) + g * 32;
   }
   // coalesced chunk: quad q of lane l covers row xm[q], columns xc..xc+3 of the k-step.
   // Gathered rows: columns below gd from the parent's feature row (fp32), the
@@ -233,7 +255,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
 #pragma unroll
     for (int at = 0; at < AT; ++at)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st.A[at][j] = *(const u32x4*)(ap[at] + (size_t)ks * SK_KSTEP + j * 8);
+      for (int j = 0; j < 4; ++j) st.A[at][j] = *(const u32x4*)(ap[at] + (size_t)ks * kstride + j * 8);
     const int k0 = ks * SK_KSTEP;
     if (!gather || k0 < a.gd) {  // uniform: ks is the wave's
 #pragma unroll
@@ -456,12 +478,15 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
   const int nks = (sp + 1) * nks_all / p.splits - ks0;
 
   const int wtile = nt * NW + wv;  // this wave's tile of 16*AT weight rows
+  // weights row-major (a k-step further: 128 values) or blocked (one 4 KB block)
+  const bool blocked = a.wb0 != nullptr;
+  const size_t kstride = blocked ? 2048 : SK_KSTEP;
   const bf16_t* ap[AT];
 #pragma unroll
   for (int at = 0; at < AT; ++at) {
     bool ok;
     const int n = tile_row<AT, EPI>(a, wtile, at, r, &ok);
-    ap[at] = wrow<bf16_t>(a, n) + g * 32;
+    ap[at] = blocked ? wrow_blocked(a, n) + g * 512 : wrow<bf16_t>(a, n) + g * 32;
   }
   // activation chunks: chunk c = t + NT u covers tile row c / 16, columns 8 (c % 16) .. + 7
   const bf16_t* xp[XCH];
@@ -499,7 +524,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_wide(GemmArgs a, const bf16_t* _
 #pragma unroll
     for (int at = 0; at < AT; ++at)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st.A[at][j] = *(const u32x4*)(ap[at] + (size_t)ks * SK_KSTEP + j * 8);
+      for (int j = 0; j < 4; ++j) st.A[at][j] = *(const u32x4*)(ap[at] + (size_t)ks * kstride + j * 8);
   };
 
   floatx4 acc[AT][MB];
@@ -1263,6 +1288,35 @@ hipError_t prepared_launch(GemmArgs a, int epi, int* n_part_out, hipStream_t s) 
 }
 
 }  // namespace
+
+namespace {
+
+// The blocked copy: one thread per 16 bytes (8 values) of the output.
+__global__ void __launch_bounds__(256) block_weight_kernel(const bf16_t* __restrict__ w, int rows, int cols,
+                                                           bf16_t* __restrict__ out, size_t n8) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const size_t e = i * 8;  // output element: block e / 2048, in it (c / 32, r, c % 32)
+  const int b = (int)(e % 2048), r = (b / 32) % 16, c = (b / 512) * 32 + b % 32;
+  const size_t blk = e / 2048, nks = (size_t)(cols / 128);
+  const size_t row = blk / nks * 16 + r, k = blk % nks * 128 + c;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (row < (size_t)rows) v = *(const u32x4*)(w + row * cols + k);
+  *(u32x4*)(out + e) = v;
+}
+
+}  // namespace
+
+size_t blocked_weight_bytes(int rows, int cols) { return (size_t)((rows + 15) / 16) * 16 * cols * 2; }
+
+hipError_t launch_block_weight(const void* w, int rows, int cols, void* out, hipStream_t s) {
+  if (!w || !out || rows <= 0 || cols <= 0 || cols % 128 || ((uintptr_t)w & 15) || ((uintptr_t)out & 15))
+    return hipErrorInvalidValue;
+  const size_t n8 = blocked_weight_bytes(rows, cols) / 16;
+  hipLaunchKernelGGL(block_weight_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, (const bf16_t*)w, rows,
+                     cols, (bf16_t*)out, n8);
+  return hipGetLastError();
+}
 
 void gemm_set_kernel_events(hipEvent_t start, hipEvent_t stop) {
   g_kev_start = start;

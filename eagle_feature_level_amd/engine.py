@@ -20,10 +20,10 @@ import dataclasses
 
 import torch
 
-from . import (EAGLE_ACT_BF16, EAGLE_FEATURES_ONLY, EAGLE_HEAD_ONLY, EAGLE_SAMPLE_CHILDREN, eagle_catchup_rows,
-               eagle_commit_catchup, eagle_draft_step, eagle_tree_expand, eagle_tree_finalize, eagle_tree_init,
-               eagle_verify, eagle_verify_workspace_bytes, eagle_workspace_bytes, make_kv, make_out, make_pool,
-               make_rows, make_shape, make_weights)
+from . import (EAGLE_ACT_BF16, EAGLE_FEATURES_ONLY, EAGLE_HEAD_ONLY, EAGLE_SAMPLE_CHILDREN, eagle_block_weight,
+               eagle_blocked_weight_bytes, eagle_catchup_rows, eagle_commit_catchup, eagle_draft_step,
+               eagle_tree_expand, eagle_tree_finalize, eagle_tree_init, eagle_verify, eagle_verify_workspace_bytes,
+               eagle_workspace_bytes, make_kv, make_out, make_pool, make_rows, make_shape, make_weights)
 
 
 @dataclasses.dataclass
@@ -41,7 +41,7 @@ class Step:
 
 class EagleRound:
     def __init__(self, shape: dict, weights: dict, batch: int, kind: str, k: int, depth: int, m: int = 0,
-                 template=None, prefix=None, device="cuda", act_bf16=False):
+                 template=None, prefix=None, device="cuda", act_bf16=False, blocked=True):
         """shape: d, n_heads, n_kv_heads, head_dim, ffn, vocab, rms_eps, rope_theta, dtype.
         weights: name -> device tensor.  prefix: dict(k, v, off, len, max_len[, cap]) device tensors (cap:
         per-sequence capacity of each kv head's positions, needed by catch_up(); max_len must cover it).
@@ -50,12 +50,22 @@ class EagleRound:
         bf16 workload), or "auto" (EAGLE_ACT_BF16 on steps over more than
         ACT_BF16_MIN_ROWS rows, where one MFMA per product instead of two matters).
         Rounding the activations to bf16 measured 0.03-0.18 max-abs off the fp64
-        logits at the 7B-70B shapes, so it is opt-in."""
+        logits at the 7B-70B shapes, so it is opt-in.
+        blocked (bf16 workloads): also keep the weight matrices in the blocked
+        layout (eagle_block_weight) for the draft steps' weight-streaming GEMMs;
+        the same results, one more copy of the weights in device memory."""
         self.act_bf16 = act_bf16
         self.shape_d = shape
         self.shape = make_shape(**shape)
-        self.weights_t = weights
-        self.weights = make_weights(weights)
+        self.weights_t = dict(weights)
+        if blocked and shape["dtype"] == "bf16":
+            for n in ("fc_w", "wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "lm_head"):
+                t = weights[n]
+                rows, cols = t.shape[0], t.numel() // t.shape[0]
+                out = torch.empty(eagle_blocked_weight_bytes(rows, cols), dtype=torch.uint8, device=device)
+                eagle_block_weight(t, rows, cols, out)
+                self.weights_t[n + "_b"] = out
+        self.weights = make_weights(self.weights_t)
         self.B, self.kind, self.k, self.depth, self.m = batch, kind, k, depth, m
         self.dev = device
         d, V = shape["d"], shape["vocab"]

@@ -79,6 +79,14 @@ typedef struct {
  * w_gate/w_up [ffn, d], w_down [d, ffn]. */
 typedef struct {
   const void *embed, *fc_w, *fc_b, *norm1, *norm2, *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down, *lm_head;
+  /* Optional, bf16 workloads (NULL: not given): copies of the nine weight
+   * matrices above in the blocked layout written by eagle_block_weight.
+   * Where all of a product's matrices have one (wq, wk and wv together;
+   * w_gate and w_up together), the draft step's weight-streaming GEMMs (steps
+   * over up to 256 rows) read the copies, whose every 4 KB block is one
+   * k-step of 16 rows, instead of the row-major matrices, which remain
+   * required; results are identical. */
+  const void *fc_w_b, *wq_b, *wk_b, *wv_b, *wo_b, *w_gate_b, *w_up_b, *w_down_b, *lm_head_b;
 } eagle_weights;
 
 /* Rows of one draft step (device arrays of n_rows entries unless stated).
@@ -157,6 +165,20 @@ typedef struct {
  *   and topk_logq may be NULL.  The catch-up step between rounds uses it (see
  *   eagle_catchup_rows).  Not combinable with EAGLE_HEAD_ONLY. */
 enum { EAGLE_HEAD_ONLY = 1, EAGLE_ACT_BF16 = 2, EAGLE_SAMPLE_CHILDREN = 4, EAGLE_FEATURES_ONLY = 8 };
+
+/* Blocked copy of a bf16 weight matrix W [rows, cols] (row-major, cols a
+ * multiple of 128): 16-row by 128-column blocks of 4 KB, the blocks of each
+ * 16-row band in column order, inside a block the four 32-column quarters in
+ * turn, each 16 rows of 32 values:
+ *   out[(t * cols/128 + s) * 2048 + ((c / 32) * 16 + r) * 32 + c % 32]
+ *     = W[16 t + r][128 s + c]
+ * (rows past the end are 0), so that a GEMM streaming 16-row bands reads each
+ * band as one contiguous run, its lanes' reads adjacent.  The layout only serves the kernels' memory
+ * access; the pages' method is unchanged.  eagle_blocked_weight_bytes gives
+ * the size of out (0 for an invalid shape); w and out are 16-byte aligned
+ * device buffers, written on `stream`. */
+size_t eagle_blocked_weight_bytes(int32_t rows, int32_t cols);
+int eagle_block_weight(const void *w, int32_t rows, int32_t cols, void *out, eagle_stream_t stream);
 
 /* Bytes of workspace needed by eagle_draft_step / eagle_softmax_topk for up
  * to max_rows rows, max_batch sequences and prefixes up to max_prefix_len.

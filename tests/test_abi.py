@@ -44,6 +44,11 @@ def test_argument_errors_need_no_device():
     assert lib.eagle_workspace_bytes(ctypes.byref(shape), 5, 1, 1024) > 0
     bad = E.make_shape(4096, 30, 4, 128, 11008, 32000)  # heads not a multiple of kv heads
     assert lib.eagle_workspace_bytes(ctypes.byref(bad), 5, 1, 1024) == 0
+    # blocked weight copies: columns a multiple of 128, rows padded to 16
+    assert lib.eagle_blocked_weight_bytes(40, 384) == 48 * 384 * 2
+    assert lib.eagle_blocked_weight_bytes(32000, 4096) == 32000 * 4096 * 2
+    assert lib.eagle_blocked_weight_bytes(16, 100) == 0 and lib.eagle_blocked_weight_bytes(0, 128) == 0
+    assert lib.eagle_block_weight(None, 16, 128, None, None) == _abi.EAGLE_EINVAL
     # draft step with null pointers
     w = E.eagle_weights()
     rows = E.make_rows(3, 1, 3, None, None, None)

@@ -89,7 +89,7 @@ def _rows(cfg, counts, lens, seed, n_feat):
     return rows, start
 
 
-def _run_draft(shape, counts, lens, seed, head_only=False, topk=4, act=False, std=0.05):
+def _run_draft(shape, counts, lens, seed, head_only=False, topk=4, act=False, std=0.05, blocked=False, oracle=True):
     cfg, w, ks, vs = _setup(shape, len(counts), lens, seed, std=std)
     B = len(counts)
     n_feat = 9
@@ -109,6 +109,12 @@ def _run_draft(shape, counts, lens, seed, head_only=False, topk=4, act=False, st
     tree_k = dev.tensor(tk0.reshape(-1), shape.dtype).view(B, 64, hkv, hd)
     tree_v = dev.tensor(tv0.reshape(-1), shape.dtype).view(B, 64, hkv, hd)
     es = E.make_shape(**dev.shape_dict(shape))
+    if blocked:
+        for n in ("fc_w", "wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "lm_head"):
+            t = wt[n]
+            r_, c_ = t.shape[0], t.numel() // t.shape[0]
+            wt[n + "_b"] = torch.empty(E.eagle_blocked_weight_bytes(r_, c_), dtype=torch.uint8, device="cuda")
+            E.eagle_block_weight(t, r_, c_, wt[n + "_b"])
     ew = E.make_weights(wt)
     t_rows = {k: dev.ints(rows[k]) for k in ("token", "parent", "pos", "slot")}
     t_mask = dev.masks(rows["mask"])
@@ -128,6 +134,10 @@ def _run_draft(shape, counts, lens, seed, head_only=False, topk=4, act=False, st
     flags = (E.EAGLE_HEAD_ONLY if head_only else 0) | (E.EAGLE_ACT_BF16 if act else 0)
     E.eagle_draft_step(es, ew, flags, er, f_in, kv, out, ws)
     torch.cuda.synchronize()
+    gpu = dict(logits=o_log.cpu().numpy(), feat=o_feat.cpu().numpy(), idx=o_idx.cpu().numpy(),
+               lse=o_lse.cpu().numpy(), tree_k=tree_k.float().cpu().numpy(), tree_v=tree_v.float().cpu().numpy())
+    if not oracle:
+        return None, gpu, rows, None, None
     # oracle
     tk, tv = tk0.astype(np.float64).copy(), tv0.astype(np.float64).copy()
     if head_only:
@@ -135,8 +145,6 @@ def _run_draft(shape, counts, lens, seed, head_only=False, topk=4, act=False, st
         ref = {"logits": head_logits(shape, w, feat[rows["parent"]], act_bf16=act)}
     else:
         ref = OD.draft_step(shape, w, rows, feat, ks, vs, lens, tk, tv, mirror=True, act_bf16=act)
-    gpu = dict(logits=o_log.cpu().numpy(), feat=o_feat.cpu().numpy(), idx=o_idx.cpu().numpy(),
-               lse=o_lse.cpu().numpy(), tree_k=tree_k.float().cpu().numpy(), tree_v=tree_v.float().cpu().numpy())
     return ref, gpu, rows, tk, tv
 
 
@@ -326,3 +334,37 @@ def test_fuse_features_matches_oracle(dtype, rows, bias):
     torch.cuda.synchronize()
     ref = OD.fuse_features(shape, w, b, low, mid, high)
     assert np.max(np.abs(out.cpu().numpy() - ref)) < TOL[dtype]
+
+
+def test_block_weight_layout():
+    """eagle_block_weight: 16-row x 128-column blocks of 4 KB, each band's
+    blocks in column order, in a block the 32-column quarters in turn (16 rows
+    of 32 values each), rows past the end 0 (a rearrangement, bit-exact)."""
+    rows, cols = 40, 384
+    w = bf16_values(normal_array(77, 0, (rows, cols)))
+    t = dev.tensor(w.reshape(-1), "bf16").view(rows, cols)
+    out = torch.full((E.eagle_blocked_weight_bytes(rows, cols),), 0x7F, dtype=torch.uint8, device="cuda")
+    E.eagle_block_weight(t, rows, cols, out)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
+    pad = np.zeros((48, cols), dtype=np.uint16)
+    pad[:rows] = bits
+    want = pad.reshape(3, 16, 3, 4, 32).transpose(0, 2, 3, 1, 4).ravel()
+    assert got.shape == want.shape and np.array_equal(got, want)
+
+
+# The blocked copies change only where the GEMMs read their weights: the
+# skinny (<= 16 rows) and wide (17..256 rows) kernels read them and sum the
+# same products in the same order; above 256 rows the row-major matrices are
+# read.  Every output must be bit-identical with and without them.
+@pytest.mark.parametrize("counts,lens", [([3, 2], [0, 70]), ([9, 0, 8], [130, 5, 64]), ([20, 20, 1], [130, 0, 77]),
+                                         ([56, 50, 40, 56, 54], [200, 64, 1, 90, 33]),
+                                         ([56, 56, 56, 56, 56, 20], [30, 64, 1, 90, 33, 7])])
+def test_blocked_weights_give_identical_results(counts, lens):
+    shape = Shape(256, 4, 2, 128, 384, 1000)
+    seed = 41 + sum(counts)
+    _, g0, _, _, _ = _run_draft(shape, counts, lens, seed=seed, oracle=False)
+    _, g1, _, _, _ = _run_draft(shape, counts, lens, seed=seed, oracle=False, blocked=True)
+    for k in g0:
+        assert np.array_equal(g0[k], g1[k], equal_nan=True), k
