@@ -22,9 +22,9 @@ struct GemmArgs {
   const void* w1;
   const void* w2;
   int n_seg0, n_seg1;
-  // optional (bf16, M <= 256): the same segments in the blocked layout of
-  // launch_block_weight, read instead of w0..w2 by the skinny and wide kernels
-  // (all of the GEMM's segments, or none)
+  // optional (bf16): the same segments in the blocked layout of
+  // launch_block_weight, read instead of w0..w2 (all of the GEMM's segments,
+  // or none)
   const void* wb0;
   const void* wb1;
   const void* wb2;

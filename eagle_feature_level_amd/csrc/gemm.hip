@@ -731,14 +731,19 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
   // of tile row q >> 2.  Rows past the end of W or x are read from row 0
   // (finite values whose outputs are never stored), so every load is
   // unconditional.
+  // Blocked weights: a 32-column block of a 16-row band is 16 rows of 32
+  // values, 512 values after the previous one (also across 128-column blocks),
+  // so the K blocks of a row step by 512 instead of 32.
+  const bool blocked = a.wb0 != nullptr;
+  const int wstep = blocked ? 16 : 1;
   const size_t lo_off = (size_t)a.M * a.K;
   const bf16_t* src[ROUNDS];
 #pragma unroll
   for (int u = 0; u < ROUNDS; ++u) {
     const int q = u * NT + t;
     if (u < AR) {
-      const int row = q >> 2, n = wrow_of(row);
-      src[u] = wrow<bf16_t>(a, n >= 0 ? n : 0) + kbeg + (q & 3) * 8;
+      const int row = q >> 2, n = wrow_of(row), nn = n >= 0 ? n : 0;
+      src[u] = (blocked ? wrow_blocked(a, nn) : wrow<bf16_t>(a, nn)) + (size_t)kbeg * wstep + (q & 3) * 8;
     } else {
       const int q2 = q - ASL, h = q2 / BSL, q3 = q2 % BSL;
       const int row = q3 >> 2, m = m0 + row < a.M ? m0 + row : 0;
@@ -757,7 +762,7 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
   auto load = [&](u32x4 (&R)[ROUNDS], int kb) {
     const int k0 = kb * BK;
 #pragma unroll
-    for (int u = 0; u < ROUNDS; ++u) R[u] = *(const u32x4*)(src[u] + k0);
+    for (int u = 0; u < ROUNDS; ++u) R[u] = *(const u32x4*)(src[u] + (size_t)k0 * (u < AR ? wstep : 1));
   };
   auto store = [&](const u32x4 (&R)[ROUNDS], int buf) {
 #pragma unroll
