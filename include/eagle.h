@@ -82,10 +82,9 @@ typedef struct {
   /* Optional, bf16 workloads (NULL: not given): copies of the nine weight
    * matrices above in the blocked layout written by eagle_block_weight.
    * Where all of a product's matrices have one (wq, wk and wv together;
-   * w_gate and w_up together), the draft step's weight-streaming GEMMs (steps
-   * over up to 256 rows) read the copies, whose every 4 KB block is one
-   * k-step of 16 rows, instead of the row-major matrices, which remain
-   * required; results are identical. */
+   * w_gate and w_up together), the draft step's GEMMs read the copies, whose
+   * every 4 KB block is one 128-column step of 16 rows, instead of the
+   * row-major matrices, which remain required; results are identical. */
   const void *fc_w_b, *wq_b, *wk_b, *wv_b, *wo_b, *w_gate_b, *w_up_b, *w_down_b, *lm_head_b;
 } eagle_weights;
 
