@@ -775,21 +775,25 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
 #pragma unroll
     for (int mb = 0; mb < TM; ++mb) acc[nb][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf) {
+  // a wave's LDS fragments of one block: TN weight blocks, then TM activation
+  // blocks per operand half
+  constexpr int NF = TN + NH * TM;
+  auto read_frags = [&](u32x4 (&F)[NF], int buf) {
     const u32x4* B0 = L[buf];
-    u32x4 A[TN];
 #pragma unroll
-    for (int nb = 0; nb < TN; ++nb) A[nb] = B0[swz_slot((wn * TN + nb) * 16 + r, g)];
+    for (int nb = 0; nb < TN; ++nb) F[nb] = B0[swz_slot((wn * TN + nb) * 16 + r, g)];
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      u32x4 B[TM];
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int mb = 0; mb < TM; ++mb) B[mb] = B0[ASL + h * BSL + swz_slot((wm * TM + mb) * 16 + r, g)];
+      for (int mb = 0; mb < TM; ++mb) F[TN + h * TM + mb] = B0[ASL + h * BSL + swz_slot((wm * TM + mb) * 16 + r, g)];
+  };
+  auto mfma_frags = [&](const u32x4 (&F)[NF]) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int nb = 0; nb < TN; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < TM; ++mb) acc[nb][mb] = mfma16(A[nb], B[mb], acc[nb][mb]);
-    }
+        for (int mb = 0; mb < TM; ++mb) acc[nb][mb] = mfma16(F[nb], F[TN + h * TM + mb], acc[nb][mb]);
   };
   // block kb in LDS buffer kb & 1; block kb + 1 arrives in R0 meanwhile and is
   // stored to the other buffer, then block kb + 2 is requested
@@ -799,14 +803,33 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
     if (nkb > 1) load(R0, 1);
   }
   __syncthreads();
+  // Two wave groups, one wave of each per SIMD (waves w and w + NW/2 share a
+  // SIMD), run a block in two phases separated by barriers: LDS phase (read
+  // the block's fragments into registers, store the next block, request the
+  // one after) and matrix phase (the block's MFMAs).  The second group starts
+  // one barrier later, so while one wave of a SIMD reads LDS the other keeps
+  // the matrix pipe busy.  Every wave passes the same number of barriers (the
+  // first group takes its extra one after the loop); the group test is on a
+  // wave-uniform scalar, so the skipped barrier is a scalar branch.
+  // Buffer hazards: a block's two halves are stored one phase apart (first
+  // group, then second) and read no earlier than the phase after the second
+  // store; a buffer is overwritten two phases after its last reader.
+  const bool late = __builtin_amdgcn_readfirstlane(wv) >= T::WN * T::WM / 2;
+  if (late) __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
-    compute(kb & 1);
+    u32x4 F[NF];
+    read_frags(F, kb & 1);
     if (kb + 1 < nkb) {
       store(R0, (kb + 1) & 1);
       if (kb + 2 < nkb) load(R0, kb + 2);
     }
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_frags(F);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
   }
+  if (!late) __syncthreads();
 
   // lane (r, g): acc[nb][mb][v] = tile row (wn*TN + nb)*16 + 4g + v, activation row (wm*TM + mb)*16 + r
   if (p.splits > 1) {
