@@ -713,7 +713,9 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
   if (scale_rows) row_scales_lds<NT>(a, BM, rs_s, m0);
   const int wn = wv % T::WN, wm = wv / T::WN;
   const int r = lane & 15, g = lane >> 4;
-  const int kper = a.K / p.splits, kbeg = sp * kper, nkb = kper / BK;
+  // K blocks of this split: the K / BK blocks spread evenly over the splits
+  const int nkb_all = a.K / BK, kb0 = sp * nkb_all / p.splits;
+  const int kbeg = kb0 * BK, nkb = (sp + 1) * nkb_all / p.splits - kb0;
 
   auto wrow_of = [&](int i) -> int {
     if constexpr (EPI == EPI_SWIGLU) {
@@ -1222,16 +1224,32 @@ hipError_t wide_mb(const GemmArgs& a, int epi, const bf16_t* xb, const WidePlan&
   }
 }
 
-// Tiles of gemm_tile plus a K split (powers of 2) while the grid has fewer
-// workgroups than CUs.
+// Tiles of gemm_tile plus a K split (any count; the K blocks spread evenly,
+// at least 16 per split).  A workgroup takes about the same time per K block
+// whatever the split, and the grid runs in rounds of one workgroup per CU, so
+// the count minimises (rounds x K blocks per split) plus the partial sums'
+// write and re-read in gemm_reduce, priced at TILE_BLOCK_US per K block and
+// REDUCE_BYTES_PER_US (measured at the 13B / 70B tree-wide shapes: about 1.45
+// us per block, the reduce near 4 TB/s).  E.g. the 70B QKV product (160 tiles,
+// 256 K blocks) takes 3 splits, 480 workgroups in two rounds of 86 blocks,
+// instead of 2 splits in two rounds of 128.
+constexpr double TILE_BLOCK_US = 1.45, REDUCE_BYTES_PER_US = 4.0e6;
 template <class T>
 BigPlan plan_tile(int M, int N, int K, bool swiglu) {
   BigPlan p;
   p.tiles_n = swiglu ? (N / 2 + T::BN / 2 - 1) / (T::BN / 2) : (N + T::BN - 1) / T::BN;
   p.tiles_m = (M + T::BM - 1) / T::BM;
+  const int base = p.tiles_n * p.tiles_m, nkb = K / T::BK;
   p.splits = 1;
-  while (p.tiles_n * p.tiles_m * p.splits < 256 && K % (T::BK * p.splits * 2) == 0 && K / (p.splits * 2) >= 512)
-    p.splits *= 2;
+  double best = 0.0;
+  for (int s = 1; s <= 16 && nkb / s >= 16; ++s) {
+    const int rounds = (base * s + 255) / 256, per = (nkb + s - 1) / s;
+    const double cost = rounds * per * TILE_BLOCK_US + (s > 1 ? 2.0 * s * M * N * 4 / REDUCE_BYTES_PER_US : 0.0);
+    if (s == 1 || cost < best) {
+      best = cost;
+      p.splits = s;
+    }
+  }
   return p;
 }
 
@@ -1356,7 +1374,8 @@ size_t gemm_bf16_partial_bytes(int M, int N, int K) {
   // the prepared operand (hi and lo halves), then the partials of the K split
   int splits;
   if (M >= BIG16_MIN_M) {
-    splits = plan_tile<LargeTile>(M, N, K, false).splits;  // N/2-wide SwiGLU tiles give no more splits
+    const int s0 = plan_tile<LargeTile>(M, N, K, false).splits, s1 = plan_tile<LargeTile>(M, N, K, true).splits;
+    splits = s0 > s1 ? s0 : s1;
   } else {
     int mb;
     const WidePlan w = plan_wide(M, N, K, false, WideDefault::bn, 8, &mb);

@@ -219,6 +219,21 @@ def test_draft_step_bf16_act(d, counts, lens):
     _check_topk_valid(ref["logits"], gpu["idx"], tol)
 
 
+# Split operands through the large-M kernel with K split over the grid in
+# uneven parts: at d = 1024 the K of 1024, 2048 and 2816 are 32, 64 and 88
+# blocks of 32, spread over up to five splits.
+@pytest.mark.parametrize("counts,lens", [([56, 56, 56, 56, 56], [40, 0, 3, 77, 128]),
+                                         ([56, 56, 56, 56, 48, 30], [5, 64, 0, 9, 300, 1])])
+def test_draft_step_bf16_tile_ksplit(counts, lens):
+    d = 1024
+    shape = Shape(d, d // 128 * 2, d // 128, 128, 2816, 4096)
+    ref, gpu, rows, tk, tv = _run_draft(shape, counts, lens, seed=9 + sum(counts), std=0.02)
+    tol = TOL["bf16"]
+    assert np.max(np.abs(gpu["feat"] - ref["feat"])) < tol
+    assert np.max(np.abs(gpu["logits"] - ref["logits"])) < tol
+    _check_topk_valid(ref["logits"], gpu["idx"], tol)
+
+
 # More than 64 queries per kv head (eight query heads per kv head): several
 # 64-query blocks over the same keys (80, 128 and 136 queries).
 @pytest.mark.parametrize("counts,lens", [([10, 9], [700, 129]), ([16], [300]), ([17, 3], [64, 1000])])
