@@ -430,8 +430,12 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny(GemmArgs a) {
 }
 
 // Grid of the large-M kernel: weight tiles x activation tiles x K splits.
+// With a split tail, the first `full` tiles (whole weight tiles, a multiple
+// of 8 workgroups) run unsplit and the remaining tiles run `splits`-way split,
+// so that the last round of workgroups is filled with shorter ones.
 struct BigPlan {
   int tiles_n, tiles_m, splits;
+  int full;  // tiles launched unsplit before the split ones (0: every tile split `splits` ways)
 };
 
 // ---------------------------------------------------------------------------
@@ -702,20 +706,27 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
   __shared__ __attribute__((aligned(16))) u32x4 L[2][SLOTS];
   __shared__ float ssq_s[T::WN][BM];
   __shared__ float rs_s[BM];  // RMSNorm row scales of an operand handed over unscaled (xb_in)
-  const int nwg = gridDim.x, bid = blockIdx.x;
-  const int lid = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;  // consecutive tiles on one XCD
-  const int mt = lid % p.tiles_m, rest = lid / p.tiles_m;
-  const int nt = rest % p.tiles_n, sp = rest / p.tiles_n;
+  // workgroups [0, full) take whole tiles, the rest the split tiles; within
+  // each part consecutive tiles stay on one XCD (both parts are whole
+  // multiples of 8 workgroups when full > 0)
+  const int bid = blockIdx.x;
+  const bool head = bid < p.full;
+  const int nwg = head ? p.full : gridDim.x - p.full, b = head ? bid : bid - p.full;
+  const int lid = (nwg % 8 == 0) ? (b % 8) * (nwg / 8) + b / 8 : b;
+  const int splits = head ? 1 : p.splits;
+  const int ntail = p.tiles_n * p.tiles_m - p.full;  // tiles of the split part
+  const int tile = head ? lid : p.full + lid % ntail, sp = head ? 0 : lid / ntail;
+  const int mt = tile % p.tiles_m, nt = tile / p.tiles_m;
   const int m0 = mt * BM;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   // row scales for the epilogue of an unsplit launch (visible after the main loop's barriers)
-  const bool scale_rows = a.sumsq_in != nullptr && p.splits == 1;
+  const bool scale_rows = a.sumsq_in != nullptr && splits == 1;
   if (scale_rows) row_scales_lds<NT>(a, BM, rs_s, m0);
   const int wn = wv % T::WN, wm = wv / T::WN;
   const int r = lane & 15, g = lane >> 4;
   // K blocks of this split: the K / BK blocks spread evenly over the splits
-  const int nkb_all = a.K / BK, kb0 = sp * nkb_all / p.splits;
-  const int kbeg = kb0 * BK, nkb = (sp + 1) * nkb_all / p.splits - kb0;
+  const int nkb_all = a.K / BK, kb0 = sp * nkb_all / splits;
+  const int kbeg = kb0 * BK, nkb = (sp + 1) * nkb_all / splits - kb0;
 
   auto wrow_of = [&](int i) -> int {
     if constexpr (EPI == EPI_SWIGLU) {
@@ -834,7 +845,7 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
   if (!late) __syncthreads();
 
   // lane (r, g): acc[nb][mb][v] = tile row (wn*TN + nb)*16 + 4g + v, activation row (wm*TM + mb)*16 + r
-  if (p.splits > 1) {
+  if (splits > 1) {
     float* P = a.part + (size_t)sp * a.M * a.N;
 #pragma unroll
     for (int mb = 0; mb < TM; ++mb) {
@@ -967,10 +978,10 @@ __global__ void __launch_bounds__(256) act_prep(GemmArgs a, bf16_t* __restrict__
 
 // Sum split-K partials and apply the epilogue.  grid (ceil(Nout/1024), M).
 template <int EPI>
-__global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a) {
+__global__ void __launch_bounds__(256) gemm_reduce(GemmArgs a, int n0) {
   __shared__ float red[4];
   const int m = blockIdx.y;
-  const int n = blockIdx.x * 1024 + threadIdx.x * 4;
+  const int n = n0 + blockIdx.x * 1024 + threadIdx.x * 4;
   const int nout = (EPI == EPI_SWIGLU) ? a.ffn : a.N;
   const size_t stride = (size_t)a.M * a.N;
   float rs = 1.f;
@@ -1234,11 +1245,17 @@ hipError_t wide_mb(const GemmArgs& a, int epi, const bf16_t* xb, const WidePlan&
 // 256 K blocks) takes 3 splits, 480 workgroups in two rounds of 86 blocks,
 // instead of 2 splits in two rounds of 128.
 constexpr double TILE_BLOCK_US = 1.45, REDUCE_BYTES_PER_US = 4.0e6;
+// tail_ok: the epilogue has no per-tile sums of squares, so a split tail is
+// allowed: with R whole rounds of tiles and a partial one, the tiles of the
+// last round are split as far as one round holds them (the 70B gate/up
+// product: 896 tiles, 768 unsplit and 128 split 2 ways, 3.5 rounds of full-K
+// workgroups become 3 of them plus one of half length).
 template <class T>
-BigPlan plan_tile(int M, int N, int K, bool swiglu) {
+BigPlan plan_tile(int M, int N, int K, bool swiglu, bool tail_ok) {
   BigPlan p;
   p.tiles_n = swiglu ? (N / 2 + T::BN / 2 - 1) / (T::BN / 2) : (N + T::BN - 1) / T::BN;
   p.tiles_m = (M + T::BM - 1) / T::BM;
+  p.full = 0;
   const int base = p.tiles_n * p.tiles_m, nkb = K / T::BK;
   p.splits = 1;
   double best = 0.0;
@@ -1250,12 +1267,25 @@ BigPlan plan_tile(int M, int N, int K, bool swiglu) {
       p.splits = s;
     }
   }
+  const int full = base / 256 * 256, ntail = base - full;
+  if (tail_ok && full > 0 && ntail > 0 && full % p.tiles_m == 0) {
+    int s2 = 1;
+    while ((s2 + 1) * ntail <= 256 && nkb / (s2 + 1) >= 16) ++s2;
+    if (s2 > 1) {
+      const double cost = (full / 256) * nkb * TILE_BLOCK_US + (nkb + s2 - 1) / s2 * TILE_BLOCK_US +
+                          2.0 * s2 * ntail * T::BM * T::BN * 4 / REDUCE_BYTES_PER_US;
+      if (cost < best) {
+        p.full = full;
+        p.splits = s2;
+      }
+    }
+  }
   return p;
 }
 
 template <class T, bool SPLIT>
 hipError_t tile_epi(const GemmArgs& a, int epi, const bf16_t* xb, const BigPlan& p, hipStream_t s) {
-  const dim3 grid(p.tiles_n * p.tiles_m * p.splits), blk(T::NT);
+  const dim3 grid(p.full + (p.tiles_n * p.tiles_m - p.full) * p.splits), blk(T::NT);
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL((gemm_tile<EPI_STORE, SPLIT, T>), grid, blk, 0, s, a, xb, p); break;
     case EPI_BIAS_SUMSQ: hipLaunchKernelGGL((gemm_tile<EPI_BIAS_SUMSQ, SPLIT, T>), grid, blk, 0, s, a, xb, p); break;
@@ -1267,15 +1297,19 @@ hipError_t tile_epi(const GemmArgs& a, int epi, const bf16_t* xb, const BigPlan&
   return hipGetLastError();
 }
 
-hipError_t reduce_launch(const GemmArgs& a, int epi, int* n_part_out, hipStream_t s) {
+// Reduce of the K-split partials and the epilogue, over output columns
+// [n0, end): n0 > 0 (a split tail, whose earlier columns were written by the
+// unsplit tiles) only for epilogues without per-block sums of squares.
+hipError_t reduce_launch(const GemmArgs& a, int epi, int* n_part_out, hipStream_t s, int n0 = 0) {
   const int nout = (epi == EPI_SWIGLU) ? a.ffn : a.N;
-  dim3 rgrid((nout + 1023) / 1024, a.M), rblk(256);
+  if (n0 && (epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ)) return hipErrorInvalidValue;
+  dim3 rgrid((nout - n0 + 1023) / 1024, a.M), rblk(256);
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL(gemm_reduce<EPI_STORE>, rgrid, rblk, 0, s, a); break;
-    case EPI_BIAS_SUMSQ: hipLaunchKernelGGL(gemm_reduce<EPI_BIAS_SUMSQ>, rgrid, rblk, 0, s, a); *n_part_out = rgrid.x; break;
-    case EPI_RESID: hipLaunchKernelGGL(gemm_reduce<EPI_RESID>, rgrid, rblk, 0, s, a); break;
-    case EPI_RESID_SUMSQ: hipLaunchKernelGGL(gemm_reduce<EPI_RESID_SUMSQ>, rgrid, rblk, 0, s, a); *n_part_out = rgrid.x; break;
-    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_reduce<EPI_SWIGLU>, rgrid, rblk, 0, s, a); break;
+    case EPI_STORE: hipLaunchKernelGGL(gemm_reduce<EPI_STORE>, rgrid, rblk, 0, s, a, n0); break;
+    case EPI_BIAS_SUMSQ: hipLaunchKernelGGL(gemm_reduce<EPI_BIAS_SUMSQ>, rgrid, rblk, 0, s, a, n0); *n_part_out = rgrid.x; break;
+    case EPI_RESID: hipLaunchKernelGGL(gemm_reduce<EPI_RESID>, rgrid, rblk, 0, s, a, n0); break;
+    case EPI_RESID_SUMSQ: hipLaunchKernelGGL(gemm_reduce<EPI_RESID_SUMSQ>, rgrid, rblk, 0, s, a, n0); *n_part_out = rgrid.x; break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_reduce<EPI_SWIGLU>, rgrid, rblk, 0, s, a, n0); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1311,11 +1345,12 @@ hipError_t prepared_launch(GemmArgs a, int epi, int* n_part_out, hipStream_t s) 
     a.sumsq_in = nullptr;  // the row scale is in the prepared operand
     xb = prep;
   }
-  int splits, tiles_n;
+  int splits, tiles_n, n0 = 0;
   if (a.M >= BIG16_MIN_M) {
-    const BigPlan p = plan_tile<LargeTile>(a.M, a.N, a.K, sw);
+    const BigPlan p = plan_tile<LargeTile>(a.M, a.N, a.K, sw, epi == EPI_STORE || sw);
     a.splits = splits = p.splits;
     tiles_n = p.tiles_n;
+    n0 = p.full / p.tiles_m * (sw ? LargeTile::BN / 2 : LargeTile::BN);  // first column of the split tiles
     e = tile_epi<LargeTile, SPLIT>(a, epi, xb, p, s);
   } else {
     using C = WideDefault;
@@ -1330,7 +1365,7 @@ hipError_t prepared_launch(GemmArgs a, int epi, int* n_part_out, hipStream_t s) 
     if (epi == EPI_BIAS_SUMSQ || epi == EPI_RESID_SUMSQ) *n_part_out = tiles_n;
     return hipSuccess;
   }
-  return reduce_launch(a, epi, n_part_out, s);
+  return reduce_launch(a, epi, n_part_out, s, n0);
 }
 
 }  // namespace
@@ -1374,8 +1409,11 @@ size_t gemm_bf16_partial_bytes(int M, int N, int K) {
   // the prepared operand (hi and lo halves), then the partials of the K split
   int splits;
   if (M >= BIG16_MIN_M) {
-    const int s0 = plan_tile<LargeTile>(M, N, K, false).splits, s1 = plan_tile<LargeTile>(M, N, K, true).splits;
-    splits = s0 > s1 ? s0 : s1;
+    splits = 1;  // the most any epilogue's plan (with or without a split tail) takes
+    for (int v = 0; v < 4; ++v) {
+      const int sv = plan_tile<LargeTile>(M, N, K, v & 1, v >> 1).splits;
+      splits = sv > splits ? sv : splits;
+    }
   } else {
     int mb;
     const WidePlan w = plan_wide(M, N, K, false, WideDefault::bn, 8, &mb);

@@ -234,6 +234,19 @@ def test_draft_step_bf16_tile_ksplit(counts, lens):
     _check_topk_valid(ref["logits"], gpu["idx"], tol)
 
 
+# Grids of more than one round of 256 workgroups with a partial last round:
+# the large-M kernel runs whole rounds of unsplit tiles and the remaining
+# tiles split over K (the SwiGLU product: 130 x 2 tiles, the LM head: 157 x 2).
+def test_draft_step_bf16_tile_split_tail():
+    shape = Shape(1024, 16, 8, 128, 16640, 40000)
+    counts, lens = [56, 56, 56, 56, 56, 20], [12, 0, 300, 64, 5, 77]
+    ref, gpu, rows, tk, tv = _run_draft(shape, counts, lens, seed=77, std=0.02)
+    tol = TOL["bf16"]
+    assert np.max(np.abs(gpu["feat"] - ref["feat"])) < tol
+    assert np.max(np.abs(gpu["logits"] - ref["logits"])) < tol
+    _check_topk_valid(ref["logits"], gpu["idx"], tol)
+
+
 # More than 64 queries per kv head (eight query heads per kv head): several
 # 64-query blocks over the same keys (80, 128 and 136 queries).
 @pytest.mark.parametrize("counts,lens", [([10, 9], [700, 129]), ([16], [300]), ([17, 3], [64, 1000])])
