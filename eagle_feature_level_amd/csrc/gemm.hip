@@ -692,6 +692,12 @@ struct TileCfg {
 };
 
 __device__ __forceinline__ int swz_slot(int row, int c) { return row * 4 + (c ^ ((row >> 1) & 3) ^ ((row >> 3) & 1)); }
+// the chunk of tile row `row` that the layout keeps in that row's slot s
+__device__ __forceinline__ int swz_chunk(int row, int s) { return s ^ ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr unsigned WAIT_VM0 = 0x0F70;         // vmcnt(0)
+constexpr unsigned WAIT_LGKM0_VM0 = 0x0070;   // vmcnt(0) lgkmcnt(0)
+constexpr unsigned WAIT_LGKM0 = 0x0070;       // lgkmcnt(0), vmcnt(n) with n in bits 3:0 (n < 16)
 
 template <int EPI, bool SPLIT, class T>
 __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __restrict__ xb, BigPlan p) {
@@ -703,7 +709,8 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
   static_assert(ASL % NT == 0 && BSL % NT == 0, "whole load rounds");
   constexpr int AR = ASL / NT, XR = BSL / NT;  // loads per thread and block: weight, activation half
   constexpr int ROUNDS = AR + NH * XR;
-  __shared__ __attribute__((aligned(16))) u32x4 L[2][SLOTS];
+  static_assert(ROUNDS < 16, "vmcnt immediate");
+  __shared__ __attribute__((aligned(16))) u32x4 L[3][SLOTS];
   __shared__ float ssq_s[T::WN][BM];
   __shared__ float rs_s[BM];  // RMSNorm row scales of an operand handed over unscaled (xb_in)
   // workgroups [0, full) take whole tiles, the rest the split tiles; within
@@ -756,30 +763,23 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
     const int q = u * NT + t;
     if (u < AR) {
       const int row = q >> 2, n = wrow_of(row), nn = n >= 0 ? n : 0;
-      src[u] = (blocked ? wrow_blocked(a, nn) : wrow<bf16_t>(a, nn)) + (size_t)kbeg * wstep + (q & 3) * 8;
+      src[u] = (blocked ? wrow_blocked(a, nn) : wrow<bf16_t>(a, nn)) + (size_t)kbeg * wstep + swz_chunk(row, q & 3) * 8;
     } else {
       const int q2 = q - ASL, h = q2 / BSL, q3 = q2 % BSL;
       const int row = q3 >> 2, m = m0 + row < a.M ? m0 + row : 0;
-      src[u] = xb + h * lo_off + (size_t)m * a.K + kbeg + (q3 & 3) * 8;
+      src[u] = xb + h * lo_off + (size_t)m * a.K + kbeg + swz_chunk(row, q3 & 3) * 8;
     }
   }
-  // LDS slot of load u: the tile row and chunk of slot u*NT + t, swizzled (the
-  // tiles are whole multiples of NT slots, so a load never straddles two tiles)
-  auto dst = [&](int u) -> int {
-    const int q = u * NT + t;
-    const int tq = q < ASL ? q : (q - ASL) % BSL;
-    const int off = q < ASL ? 0 : ASL + ((q - ASL) / BSL) * BSL;
-    return off + swz_slot(tq >> 2, tq & 3);
-  };
-  u32x4 R0[ROUNDS];
-  auto load = [&](u32x4 (&R)[ROUNDS], int kb) {
+  // Block kb goes straight from memory to LDS (global_load_lds: lane l of a
+  // wave writes 16 bytes at the wave's base + 16 l), load u of thread t into
+  // slot u*NT + t, so each lane loads the chunk the swizzled layout keeps
+  // there.  Nothing passes through registers.
+  auto dma = [&](int kb, int buf) {
     const int k0 = kb * BK;
 #pragma unroll
-    for (int u = 0; u < ROUNDS; ++u) R[u] = *(const u32x4*)(src[u] + (size_t)k0 * (u < AR ? wstep : 1));
-  };
-  auto store = [&](const u32x4 (&R)[ROUNDS], int buf) {
-#pragma unroll
-    for (int u = 0; u < ROUNDS; ++u) L[buf][dst(u)] = R[u];
+    for (int u = 0; u < ROUNDS; ++u)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[u] + (size_t)k0 * (u < AR ? wstep : 1)),
+                                       (__attribute__((address_space(3))) void*)&L[buf][u * NT + wv * 64], 16, 0, 0);
   };
 
   floatx4 acc[TN][TM];
@@ -808,39 +808,49 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
 #pragma unroll
         for (int mb = 0; mb < TM; ++mb) acc[nb][mb] = mfma16(F[nb], F[TN + h * TM + mb], acc[nb][mb]);
   };
-  // block kb in LDS buffer kb & 1; block kb + 1 arrives in R0 meanwhile and is
-  // stored to the other buffer, then block kb + 2 is requested
-  if (nkb > 0) {
-    load(R0, 0);
-    store(R0, 0);
-    if (nkb > 1) load(R0, 1);
-  }
+  // Three LDS buffers, block kb in buffer kb % 3; blocks 0 and 1 are in flight
+  // before the loop.
+  if (nkb > 0) dma(0, 0);
+  if (nkb > 1) dma(1, 1);
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0);  // this thread's loads have landed
   __syncthreads();
   // Two wave groups, one wave of each per SIMD (waves w and w + NW/2 share a
-  // SIMD), run a block in two phases separated by barriers: LDS phase (read
-  // the block's fragments into registers, store the next block, request the
-  // one after) and matrix phase (the block's MFMAs).  The second group starts
-  // one barrier later, so while one wave of a SIMD reads LDS the other keeps
-  // the matrix pipe busy.  Every wave passes the same number of barriers (the
-  // first group takes its extra one after the loop); the group test is on a
-  // wave-uniform scalar, so the skipped barrier is a scalar branch.
-  // Buffer hazards: a block's two halves are stored one phase apart (first
-  // group, then second) and read no earlier than the phase after the second
-  // store; a buffer is overwritten two phases after its last reader.
+  // SIMD), run a block in two phases separated by barriers: an LDS phase (the
+  // block's fragments into registers, block kb + 2 requested into the buffer
+  // of block kb - 1) and a matrix phase (the block's MFMAs).  The second group
+  // starts one barrier later, so while one wave of a SIMD reads LDS the other
+  // keeps the matrix pipe busy.  Every wave passes the same number of barriers
+  // (the first group takes its extra one after the loop); the group test is on
+  // a wave-uniform scalar, so the skipped barrier is a scalar branch.
+  // Ordering (phases counted from the first group's first LDS phase, 2kb + 1
+  // for its block kb and 2kb + 2 for the second group's): block kb + 2 is
+  // requested in phases 2kb + 1 and 2kb + 2 into the buffer of block kb - 1,
+  // whose last reader ran in phase 2kb; each wave ends its LDS phase waiting
+  // for all but the loads it has just issued, so block kb + 1 has landed
+  // before the barrier that precedes its first reader (phase 2kb + 3).  The
+  // in-loop barriers carry no memory fence (a fence would wait for the loads
+  // just issued); the explicit waits and scheduling barriers order the LDS
+  // traffic instead.
   const bool late = __builtin_amdgcn_readfirstlane(wv) >= T::WN * T::WM / 2;
   if (late) __syncthreads();
+  int buf = 0;
   for (int kb = 0; kb < nkb; ++kb) {
     u32x4 F[NF];
-    read_frags(F, kb & 1);
-    if (kb + 1 < nkb) {
-      store(R0, (kb + 1) & 1);
-      if (kb + 2 < nkb) load(R0, kb + 2);
-    }
-    __syncthreads();
+    read_frags(F, buf);
+    const bool more = kb + 2 < nkb;
+    if (more) dma(kb + 2, buf == 0 ? 2 : buf - 1);
+    if (more)
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0 | ROUNDS);  // only the block just requested may still fly
+    else
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0_VM0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     mfma_frags(F);
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    buf = buf == 2 ? 0 : buf + 1;
   }
   if (!late) __syncthreads();
 
