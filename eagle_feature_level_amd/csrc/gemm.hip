@@ -705,12 +705,13 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
   constexpr int BN = T::BN, BM = T::BM, BK = T::BK, TN = T::TN, TM = T::TM;
   static_assert(BK == 32, "four 16-byte chunks per tile row");
   constexpr int ASL = BN * 4, BSL = BM * 4;  // 16-byte slots of the weight and activation tiles
-  constexpr int SLOTS = ASL + NH * BSL;       // one buffer
-  static_assert(ASL % NT == 0 && BSL % NT == 0, "whole load rounds");
-  constexpr int AR = ASL / NT, XR = BSL / NT;  // loads per thread and block: weight, activation half
-  constexpr int ROUNDS = AR + NH * XR;
+  constexpr int SLOTS = ASL + NH * BSL;       // one block
+  static_assert(ASL % NT == 0, "whole load rounds of weights");
+  constexpr int AR = ASL / NT;                              // loads per thread and block: weights
+  constexpr int ROUNDS = (SLOTS + NT - 1) / NT;             // all loads per thread and block
+  constexpr int SLOTS_PAD = ROUNDS * NT;  // a buffer: the last round's spare lanes load into the padding
   static_assert(ROUNDS < 16, "vmcnt immediate");
-  __shared__ __attribute__((aligned(16))) u32x4 L[3][SLOTS];
+  __shared__ __attribute__((aligned(16))) u32x4 L[3][SLOTS_PAD];
   __shared__ float ssq_s[T::WN][BM];
   __shared__ float rs_s[BM];  // RMSNorm row scales of an operand handed over unscaled (xb_in)
   // workgroups [0, full) take whole tiles, the rest the split tiles; within
@@ -764,6 +765,8 @@ __global__ void __launch_bounds__(T::NT) gemm_tile(GemmArgs a, const bf16_t* __r
     if (u < AR) {
       const int row = q >> 2, n = wrow_of(row), nn = n >= 0 ? n : 0;
       src[u] = (blocked ? wrow_blocked(a, nn) : wrow<bf16_t>(a, nn)) + (size_t)kbeg * wstep + swz_chunk(row, q & 3) * 8;
+    } else if (q >= SLOTS) {
+      src[u] = xb + kbeg;  // padding slot: any readable 16 bytes
     } else {
       const int q2 = q - ASL, h = q2 / BSL, q3 = q2 % BSL;
       const int row = q3 >> 2, m = m0 + row < a.M ? m0 + row : 0;
@@ -1332,6 +1335,12 @@ hipError_t reduce_launch(const GemmArgs& a, int epi, int* n_part_out, hipStream_
 // than 256 x 128 with 64 x 64 per wave (fewer LDS fragment reads per MFMA).
 constexpr int BIG16_MIN_M = 257;
 using LargeTile = TileCfg<2, 4, 8, 4, 32>;
+// From 129 to 160 rows (the 70B per-depth steps: 16 sequences x 10 rows) the
+// same kernel with 256 weight rows x 160 activation rows per workgroup (8
+// waves of 64 x 80): every workgroup streams its weights once, where the wide
+// kernel's two 80-row tiles read each weight tile twice through L2.
+constexpr int MID16_MIN_M = 129;
+using MidTile = TileCfg<4, 2, 4, 5, 32>;
 
 // Launch for M > 16 on a prepared operand: the prep pass (RMSNorm row scale
 // applied, then split into hi/lo halves or rounded once to bf16), then the
@@ -1362,6 +1371,12 @@ hipError_t prepared_launch(GemmArgs a, int epi, int* n_part_out, hipStream_t s) 
     tiles_n = p.tiles_n;
     n0 = p.full / p.tiles_m * (sw ? LargeTile::BN / 2 : LargeTile::BN);  // first column of the split tiles
     e = tile_epi<LargeTile, SPLIT>(a, epi, xb, p, s);
+  } else if (a.M >= MID16_MIN_M && a.M <= MidTile::BM) {
+    const BigPlan p = plan_tile<MidTile>(a.M, a.N, a.K, sw, epi == EPI_STORE || sw);
+    a.splits = splits = p.splits;
+    tiles_n = p.tiles_n;
+    n0 = p.full / p.tiles_m * (sw ? MidTile::BN / 2 : MidTile::BN);
+    e = tile_epi<MidTile, SPLIT>(a, epi, xb, p, s);
   } else {
     using C = WideDefault;
     int mb;
@@ -1418,10 +1433,11 @@ size_t gemm_bf16_partial_bytes(int M, int N, int K) {
   if (M <= 16) return 0;
   // the prepared operand (hi and lo halves), then the partials of the K split
   int splits;
-  if (M >= BIG16_MIN_M) {
+  if (M >= BIG16_MIN_M || (M >= MID16_MIN_M && M <= MidTile::BM)) {
     splits = 1;  // the most any epilogue's plan (with or without a split tail) takes
     for (int v = 0; v < 4; ++v) {
-      const int sv = plan_tile<LargeTile>(M, N, K, v & 1, v >> 1).splits;
+      const int sv = M >= BIG16_MIN_M ? plan_tile<LargeTile>(M, N, K, v & 1, v >> 1).splits
+                                      : plan_tile<MidTile>(M, N, K, v & 1, v >> 1).splits;
       splits = sv > splits ? sv : splits;
     }
   } else {

@@ -234,6 +234,21 @@ def test_draft_step_bf16_tile_ksplit(counts, lens):
     _check_topk_valid(ref["logits"], gpu["idx"], tol)
 
 
+# 129 to 160 rows: the large-M kernel with one 160-row activation tile per
+# workgroup, K split over the grid (d = 1024), split operands and EAGLE_ACT_BF16.
+@pytest.mark.parametrize("counts,lens,act", [([56, 56, 17], [40, 0, 300], False), ([56, 56, 38], [12, 77, 5], False),
+                                             ([56, 56, 48], [3, 64, 128], True)])
+def test_draft_step_bf16_mid_tile(counts, lens, act):
+    d = 1024
+    shape = Shape(d, d // 128 * 2, d // 128, 128, 2816, 4096)
+    assert 129 <= sum(counts) <= 160
+    ref, gpu, rows, tk, tv = _run_draft(shape, counts, lens, seed=13 + sum(counts), act=act, std=0.02)
+    tol = TOL["bf16"]
+    assert np.max(np.abs(gpu["feat"] - ref["feat"])) < tol
+    assert np.max(np.abs(gpu["logits"] - ref["logits"])) < tol
+    _check_topk_valid(ref["logits"], gpu["idx"], tol)
+
+
 # Grids of more than one round of 256 workgroups with a partial last round:
 # the large-M kernel runs whole rounds of unsplit tiles and the remaining
 # tiles split over K (the SwiGLU product: 130 x 2 tiles, the LM head: 157 x 2).
