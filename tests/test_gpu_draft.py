@@ -234,14 +234,17 @@ def test_draft_step_bf16_tile_ksplit(counts, lens):
     _check_topk_valid(ref["logits"], gpu["idx"], tol)
 
 
-# 129 to 160 rows: the large-M kernel with one 160-row activation tile per
-# workgroup, K split over the grid (d = 1024), split operands and EAGLE_ACT_BF16.
-@pytest.mark.parametrize("counts,lens,act", [([56, 56, 17], [40, 0, 300], False), ([56, 56, 38], [12, 77, 5], False),
+# 65 to 80 rows (the wide kernel, one 80-row tile) and 129 to 160 rows (the
+# large-M kernel with one 160-row activation tile per workgroup), K split over
+# the grid (d = 1024), split operands and EAGLE_ACT_BF16.
+@pytest.mark.parametrize("counts,lens,act", [([40, 25], [7, 200], False), ([56, 24], [64, 0], False),
+                                             ([30, 40, 10], [1, 90, 33], True),
+                                             ([56, 56, 17], [40, 0, 300], False), ([56, 56, 38], [12, 77, 5], False),
                                              ([56, 56, 48], [3, 64, 128], True)])
 def test_draft_step_bf16_mid_tile(counts, lens, act):
     d = 1024
     shape = Shape(d, d // 128 * 2, d // 128, 128, 2816, 4096)
-    assert 129 <= sum(counts) <= 160
+    assert 65 <= sum(counts) <= 80 or 129 <= sum(counts) <= 160
     ref, gpu, rows, tk, tv = _run_draft(shape, counts, lens, seed=13 + sum(counts), act=act, std=0.02)
     tol = TOL["bf16"]
     assert np.max(np.abs(gpu["feat"] - ref["feat"])) < tol
