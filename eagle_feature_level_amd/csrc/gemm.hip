@@ -4,15 +4,19 @@
 // call; with a few rows they are bound by HBM, not by the matrix units
 // (arithmetic intensity ~M flop/byte against a ridge of ~315); the tree-wide
 // step over hundreds of rows is bound by the matrix units.  So:
-//  * W (bf16) is the MFMA "A" operand and goes straight from HBM to VGPRs, each
-//    lane pulling 64 contiguous bytes of a row per step; W is never staged
-//    through LDS because every W element is used by exactly one wave.
+//  * W (bf16) is the MFMA "A" operand.  In the skinny and wide kernels it goes
+//    straight from HBM to VGPRs, each lane pulling 64 contiguous bytes of a row
+//    per step, never through LDS, because every W element is used by exactly
+//    one wave there.
 //  * x (fp32) is the MFMA "B" operand (M padded to 16).  The skinny kernel
 //    (M <= 16) loads each k-step's rows of x coalesced and re-reads them in the
-//    B layout from the wave's own LDS slice.  Above 16 rows a prep pass writes
-//    the operand once in bf16 (hi and lo halves, or one rounded half), and the
-//    wide kernel (weights to VGPRs, activation tile shared through LDS) or the
-//    large-M kernel (both operands through LDS) consume it.
+//    B layout from the wave's own LDS slice.  Above 16 rows the operand arrives
+//    in bf16 (hi and lo halves, or one rounded half), written by the producing
+//    GEMM's epilogue or a prep pass, and the wide kernel (weights to VGPRs,
+//    activation tile shared through LDS: up to 128 and from 161 to 256 rows) or
+//    the large-M kernel (both operands loaded straight into LDS, shared by the
+//    waves: from 129 to 160 rows with 160-row tiles, from 257 rows with
+//    256-row tiles) consumes it.
 //  * Activations enter the matrix units as a pair of bf16 values, hi = x cut
 //    to bf16 and lo = bf16(x - hi), two MFMAs into one fp32 accumulator: the
 //    product then carries ~16 significant bits of x instead of 8, which keeps a
